@@ -1,0 +1,412 @@
+/*
+ * gg_oracle.c -- plain, slow CPU oracle for the grouped GEMMs of the MoE
+ * expert backward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg load this library.  The HIP product path never calls it,
+ * and it shares no code, header, table or constant with that path.
+ *
+ * What it follows (NVIDIA cuDNN frontend documentation pages):
+ *   [W] "Grouped GEMM + WGrad (Unified)": section "Operation" (the per-expert
+ *       token slice and the accumulate/overwrite rule), section "BF16
+ *       contract" (shapes, strides and majors of A, B, offsets and outputs).
+ *   [G] "Grouped GEMM + dGLU (SM100)": "BF16 contract / Tensors, layouts, and
+ *       equation" (R_g = alpha_g^2 A_g B_g^T, X_g = beta_g C_g, the dSwiGLU and
+ *       dGeGLU formulas, dprob and dbias), and "Block-scaled contract /
+ *       Equations", steps 1 and 2 (interleave order, dprob reduction).
+ *   [S] "Grouped GEMM + dsReLU (SM100)": "Equations" (G, D_row, dprob), and
+ *       "Shapes" (per-expert Amax).
+ *
+ * Arithmetic: every input is decoded exactly into double; every sum is taken
+ * in double in the plain index order; outputs are rounded once, to nearest
+ * even, by the encoders below.  The one deliberate fp32 step is X = beta*C of
+ * [G], formed as a single fp32 product, because the clamp and filter tests of
+ * dGeGLU compare X with +-7 and the product is what the method feeds them.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* dtype codes used by this file (its own numbering) */
+enum { ORC_BF16 = 0, ORC_F16 = 1, ORC_F32 = 2 };
+
+/* ------------------------------------------------------------------------ */
+/* Decoders: bit pattern -> exact double.                                    */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 is the upper half of an IEEE binary32: shift it back in place. */
+double orc_bf16_to_double(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double orc_f16_to_double(uint16_t h) {
+    int s = (h >> 15) & 1, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                    /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 15 - 10);   /* 1.m * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 fraction bits; no
+ * infinities; S.1111.111 is NaN; largest finite 448.  The dGLU page names the
+ * torch dtype float8_e4m3fn for FP8 operands. */
+double orc_e4m3_to_double(uint8_t q) {
+    int s = (q >> 7) & 1, e = (q >> 3) & 0xf, m = q & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);                     /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexp((double)(m + 8), e - 7 - 3);        /* 1.m * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* OCP E8M0 scale ("float8_e8m0fnu"): the byte is a biased power-of-two
+ * exponent, value 2^(e-127); 0xFF is NaN. */
+double orc_e8m0_to_double(uint8_t e) {
+    if (e == 0xff)
+        return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+double orc_decode(const void* base, int dtype, int64_t i) {
+    switch (dtype) {
+    case ORC_BF16: return orc_bf16_to_double(((const uint16_t*)base)[i]);
+    case ORC_F16:  return orc_f16_to_double(((const uint16_t*)base)[i]);
+    default:       return (double)((const float*)base)[i];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Encoders: double -> nearest representable value, ties to even, rounded    */
+/* once from the double (no intermediate fp32 step).                         */
+/* ------------------------------------------------------------------------ */
+
+/* Round |x| to a binary format with p significand bits (hidden bit included)
+ * and minimum normal exponent emin; returns the rounded magnitude as a double
+ * (exact in that format) or +inf when it exceeds maxfin after rounding. */
+static double round_format(double ax, int p, int emin, double maxfin) {
+    int E;
+    if (ax == 0.0 || isnan(ax) || isinf(ax))
+        return ax;
+    frexp(ax, &E);                 /* ax = f * 2^E, f in [0.5, 1) */
+    int e = E - 1;                 /* ax in [2^e, 2^(e+1)) */
+    if (e < emin)
+        e = emin;                  /* subnormal range: fixed spacing */
+    int ulp = e - (p - 1);
+    double q = ldexp(ax, -ulp);    /* exact: scaling by a power of two */
+    double r = nearbyint(q);       /* default rounding mode: ties to even */
+    double y = ldexp(r, ulp);
+    /* Overflow: IEEE rounds to infinity once the rounded value passes the
+     * largest finite number. */
+    if (y > maxfin)
+        return INFINITY;
+    return y;
+}
+
+uint16_t orc_double_to_bf16(double x) {
+    if (isnan(x))
+        return 0x7fc0;
+    double y = round_format(fabs(x), 8, -126, ldexp(255.0, 120)); /* max (2-2^-7)*2^127 */
+    float f = (float)y;            /* exact: y is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)((u >> 16) | (signbit(x) ? 0x8000u : 0u));
+}
+
+uint16_t orc_double_to_f16(double x) {
+    if (isnan(x))
+        return 0x7e00;
+    uint16_t s = signbit(x) ? 0x8000u : 0u;
+    double y = round_format(fabs(x), 11, -14, 65504.0);
+    if (isinf(y))
+        return s | 0x7c00;
+    if (y == 0.0)
+        return s;
+    int E;
+    frexp(y, &E);
+    int e = E - 1;
+    if (e < -14)                                   /* subnormal: y = m * 2^-24 */
+        return s | (uint16_t)(int)ldexp(y, 24);
+    int m = (int)(ldexp(y, -e) * 1024.0) - 1024;   /* exact: 10 fraction bits */
+    return s | (uint16_t)(((e + 15) << 10) | m);
+}
+
+float orc_double_to_f32(double x) {
+    if (isnan(x))
+        return NAN;
+    double y = round_format(fabs(x), 24, -126, ldexp(16777215.0, 104));
+    float f = (float)y;            /* exact */
+    return signbit(x) ? -f : f;
+}
+
+/* Round n doubles to dtype and store them into out (uint16 or float). */
+void orc_round_array(const double* in, int64_t n, int dtype, void* out) {
+    for (int64_t i = 0; i < n; i++) {
+        if (dtype == ORC_BF16)
+            ((uint16_t*)out)[i] = orc_double_to_bf16(in[i]);
+        else if (dtype == ORC_F16)
+            ((uint16_t*)out)[i] = orc_double_to_f16(in[i]);
+        else
+            ((float*)out)[i] = orc_double_to_f32(in[i]);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* [W] Grouped wgrad.                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Expert e owns the token slice [begin, end): begin is 0 for the first expert
+ * and offsets[e-1] otherwise, end is offsets[e] ([W] "Operation").  The result
+ * is Wgrad[e] = A[:, begin:end] @ B[begin:end, :].
+ *
+ * A is (hidden, T): a_major 0 = K-major, element (h,t) at h*T + t;
+ *                    a_major 1 = M-major, element (h,t) at t*hidden + h.
+ * B is (T, inter):  b_major 0 = K-major, element (t,i) at i*T + t;
+ *                    b_major 1 = N-major, element (t,i) at t*inter + i.
+ * ([W] "BF16 contract": strides (T,1) / (1,hidden) for A and (1,T) /
+ * (inter,1) for B.)
+ *
+ * out is the exact product, in double, for the rows listed in hrows (all
+ * hidden rows when hrows is NULL), as out[(e*nrows + r)*inter + i].  The
+ * accumulate/overwrite rule and the output rounding are applied by
+ * orc_wgrad_finish. */
+void orc_wgrad(const uint16_t* A, int a_major, const uint16_t* B, int b_major,
+               const int32_t* offsets, int E, int64_t T, int hidden, int inter,
+               const int32_t* hrows, int nrows, double* out) {
+    if (!hrows)
+        nrows = hidden;
+    for (int e = 0; e < E; e++) {
+        int64_t begin = e ? offsets[e - 1] : 0;
+        int64_t end = offsets[e];
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; r++) {
+            int h = hrows ? hrows[r] : r;
+            double* o = out + ((int64_t)e * nrows + r) * inter;
+            for (int i = 0; i < inter; i++) {
+                double acc = 0.0;
+                for (int64_t t = begin; t < end; t++) {
+                    int64_t ia = a_major == 0 ? (int64_t)h * T + t : t * hidden + h;
+                    int64_t ib = b_major == 0 ? (int64_t)i * T + t : t * inter + i;
+                    acc += orc_bf16_to_double(A[ia]) * orc_bf16_to_double(B[ib]);
+                }
+                o[i] = acc;
+            }
+        }
+    }
+}
+
+/* [W] "Operation": with accumulate on, the result is added to the existing
+ * output; with it off the output is overwritten (an empty expert therefore
+ * yields zero).  One rounding to the output dtype after the sum.
+ * old and res have n elements in the output dtype; exact holds the doubles. */
+void orc_wgrad_finish(const double* exact, int64_t n, int accumulate,
+                      const void* old, int dtype, void* res) {
+    for (int64_t j = 0; j < n; j++) {
+        double y = exact[j];
+        if (accumulate)
+            y += orc_decode(old, dtype, j);
+        if (dtype == ORC_BF16)
+            ((uint16_t*)res)[j] = orc_double_to_bf16(y);
+        else if (dtype == ORC_F16)
+            ((uint16_t*)res)[j] = orc_double_to_f16(y);
+        else
+            ((float*)res)[j] = orc_double_to_f32(y);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Groups of rows (dGLU and dsReLU pages): group g owns rows                 */
+/* [padded_offsets[g-1], padded_offsets[g]), with padded_offsets[-1] = 0.    */
+/* ------------------------------------------------------------------------ */
+static int group_of_row(const int32_t* po, int L, int64_t m) {
+    int64_t lo = 0;
+    for (int g = 0; g < L; g++) {
+        if (m >= lo && m < po[g])
+            return g;
+        lo = po[g];
+    }
+    return -1;                     /* at or beyond valid_m = po[L-1] */
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* ------------------------------------------------------------------------ */
+/* [G] Grouped dgrad + dSwiGLU / dGeGLU.                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Inputs:
+ *   A (M, K) bf16, row-major (K-major): A[m*K + k].
+ *   Bp[g] -> expert g's (N, K) bf16 matrix; b_major 0: (n,k) at n*K + k,
+ *            b_major 1: (n,k) at k*N + n.  (Dense B of shape (N,K,L) is the
+ *            case Bp[g] = B + g*N*K with b_major 0.)
+ *   C (M, 2N), row-major, c_dtype; alpha, beta (L) fp32; prob (M) fp32.
+ *   act 0 = dSwiGLU, 1 = dGeGLU with constants ga (1.702), clamp_lo (-7),
+ *   clamp_hi (7) and linear offset lo (1).
+ *   gate_first 0: in every 64-column pair of C and D the first 32 columns are
+ *   the input block and the next 32 the gate block ("interleaved input/gate",
+ *   and the step that interleaves [ab, dswiglu]); 1 swaps the two.
+ *   mask_filter 0: dGeGLU's filters carry the raw value, as the page defines
+ *   gate_filter / input_filter; 1: they are the 0/1 indicator.
+ * Rows listed in rows (all rows < M when rows is NULL) are computed; a row at
+ * or beyond valid_m = po[L-1] belongs to no group and is left untouched.
+ * Outputs (double, unrounded):
+ *   D[r*2N + c]     the interleaved gradient for listed row r;
+ *   dprob_sum[r]    sum over n of R * (unscaled activation);
+ *   dbias_sum[g*2N + c]  (if non-NULL) sum over the listed rows of group g. */
+void orc_dglu(const uint16_t* A, int64_t M, int K,
+              const uint16_t* const* Bp, int b_major, int N,
+              const void* C, int c_dtype, const int32_t* po, int L,
+              const float* alpha, const float* beta, const float* prob,
+              int act, double ga, double clamp_lo, double clamp_hi, double lo,
+              int gate_first, int mask_filter,
+              const int64_t* rows, int64_t nrows,
+              double* D, double* dprob_sum, double* dbias_sum) {
+    if (!rows)
+        nrows = M;
+    int64_t N2 = 2 * (int64_t)N;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t m = rows ? rows[r] : r;
+        int g = group_of_row(po, L, m);
+        if (g < 0)
+            continue;
+        const uint16_t* Bg = Bp[g];
+        double a2 = (double)alpha[g] * (double)alpha[g];
+        double pr = (double)prob[m];
+        double dp = 0.0;
+        for (int n = 0; n < N; n++) {
+            /* R_g[m, n] = alpha_g^2 * sum_k A[m,k] * B_g[n,k] */
+            double acc = 0.0;
+            for (int k = 0; k < K; k++) {
+                int64_t ib = b_major == 0 ? (int64_t)n * K + k : (int64_t)k * N + n;
+                acc += orc_bf16_to_double(A[m * K + k]) * orc_bf16_to_double(Bg[ib]);
+            }
+            double R = a2 * acc;
+            /* 32-wide blocks: compact column n sits in pair p at offset j. */
+            int p = n / 32, j = n % 32;
+            int64_t c_in = 64 * (int64_t)p + (gate_first ? 32 : 0) + j;
+            int64_t c_gt = 64 * (int64_t)p + (gate_first ? 0 : 32) + j;
+            /* X = beta_g * C as one fp32 product (see the file header). */
+            float xin = beta[g] * (float)orc_decode(C, c_dtype, m * N2 + c_in);
+            float xgt = beta[g] * (float)orc_decode(C, c_dtype, m * N2 + c_gt);
+            double u = xin, gt = xgt, d_in, d_gt, a;
+            if (act == 0) {
+                /* dSwiGLU with s = sigmoid(gate):
+                 *   dinput = R prob gate s
+                 *   dgate  = R prob input s (1 + gate (1 - s))
+                 * and the unscaled activation is swish(gate) * input. */
+                double s = sigmoid(gt);
+                d_in = R * pr * gt * s;
+                d_gt = R * pr * u * s * (1.0 + gt * (1.0 - s));
+                a = gt * s * u;
+            } else {
+                /* dGeGLU: clamped values feed the activation, the filters
+                 * carry the raw value where it lies inside the clamp. */
+                double gc = gt < clamp_hi ? gt : clamp_hi;
+                double uc = u < clamp_lo ? clamp_lo : (u > clamp_hi ? clamp_hi : u);
+                int g_in = gt <= clamp_hi;
+                int u_in = u >= clamp_lo && u <= clamp_hi;
+                double gf = g_in ? (mask_filter ? 1.0 : gt) : 0.0;
+                double uf = u_in ? (mask_filter ? 1.0 : u) : 0.0;
+                double s = sigmoid(ga * gc);
+                d_gt = R * pr * (uc + lo) * s * (1.0 + ga * gc * (1.0 - s)) * gf;
+                d_in = R * pr * gc * s * uf;
+                a = gc * s * (uc + lo);
+            }
+            dp += R * a;
+            D[r * N2 + c_in] = d_in;
+            D[r * N2 + c_gt] = d_gt;
+        }
+        dprob_sum[r] = dp;
+    }
+    /* dbias: per-expert row reduction of the interleaved output. */
+    if (dbias_sum) {
+        for (int64_t r = 0; r < nrows; r++) {
+            int64_t m = rows ? rows[r] : r;
+            int g = group_of_row(po, L, m);
+            if (g < 0)
+                continue;
+            for (int64_t c = 0; c < N2; c++)
+                dbias_sum[g * N2 + c] += D[r * N2 + c];
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* [S] Grouped dgrad + dsReLU on MXFP8 operands.                             */
+/* ------------------------------------------------------------------------ */
+
+/* Inputs:
+ *   A (M, K) e4m3 codes, row-major; SFA (M, K/32) e8m0, row-major: one scale
+ *   for each 32-element K block of each row.
+ *   Bp[g] -> expert g's (N, K) e4m3 codes (n,k) at n*K + k; SFBp[g] -> its
+ *   (N, K/32) e8m0 scales.
+ *   C (M, N) row-major, c_dtype; alpha (L) fp32; prob (M) fp32.
+ * With dequantize(q, s) = e4m3(q) * 2^(s-127):
+ *   G[m,n]     = alpha_g * sum_k deq(A[m,k]) * deq(B_g[n,k])
+ *   D_row[m,n] = prob[m] * 2 * C[m,n] * relu(G[m,n])
+ *   dprob[m]   = sum_n C[m,n] * relu(G[m,n])^2
+ *   amax[g]    = max |D_row| over the group's rows, before output rounding;
+ *                amax is only raised here, the caller starts it at 0.
+ * Outputs (double): D[r*N + n], dprob_sum[r], amax[g] for the listed rows. */
+void orc_dsrelu(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
+                const uint8_t* const* Bp, const uint8_t* const* SFBp, int N,
+                const void* C, int c_dtype, const int32_t* po, int L,
+                const float* alpha, const float* prob,
+                const int64_t* rows, int64_t nrows,
+                double* D, double* dprob_sum, double* amax) {
+    if (!rows)
+        nrows = M;
+    int KB = K / 32;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t m = rows ? rows[r] : r;
+        int g = group_of_row(po, L, m);
+        if (g < 0)
+            continue;
+        const uint8_t* Bg = Bp[g];
+        const uint8_t* Sg = SFBp[g];
+        double pr = (double)prob[m];
+        double dp = 0.0;
+        for (int n = 0; n < N; n++) {
+            double acc = 0.0;
+            for (int k = 0; k < K; k++) {
+                double da = orc_e4m3_to_double(A[m * K + k]) *
+                            orc_e8m0_to_double(SFA[m * KB + k / 32]);
+                double db = orc_e4m3_to_double(Bg[(int64_t)n * K + k]) *
+                            orc_e8m0_to_double(Sg[(int64_t)n * KB + k / 32]);
+                acc += da * db;
+            }
+            double G = (double)alpha[g] * acc;
+            double rl = G > 0.0 ? G : 0.0;
+            double c = orc_decode(C, c_dtype, m * (int64_t)N + n);
+            double d = pr * 2.0 * c * rl;
+            D[r * (int64_t)N + n] = d;
+            dp += c * rl * rl;
+        }
+        dprob_sum[r] = dp;
+    }
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t m = rows ? rows[r] : r;
+        int g = group_of_row(po, L, m);
+        if (g < 0)
+            continue;
+        for (int n = 0; n < N; n++) {
+            double v = fabs(D[r * (int64_t)N + n]);
+            if (v > amax[g])
+                amax[g] = v;
+        }
+    }
+}
