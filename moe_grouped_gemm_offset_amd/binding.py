@@ -1,0 +1,177 @@
+"""ctypes binding of libgg_moe (include/gg_moe.h) -- argument marshalling only.
+
+Each function takes torch tensors (device memory allocated by PyTorch) or
+raw integers for pointers, converts them to the C arguments, calls the C
+entry point of the same name and raises GGError on a non-GG_OK status.
+Every step of the computation runs in the library's HIP kernels; if the
+library has not been built, loading it raises.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgg_moe.so")
+
+# enums of gg_moe.h
+GG_BF16, GG_F16, GG_F32, GG_F8E4M3 = 0, 1, 2, 3
+GG_MAJOR_K, GG_MAJOR_M, GG_MAJOR_N = 0, 1, 2
+GG_DSWIGLU, GG_DGEGLU = 0, 1
+GG_FLAG_GATE_FIRST, GG_FLAG_GEGLU_MASK_FILTER, GG_FLAG_VALIDATE_OFFSETS = 1, 2, 4
+GG_DEVERR_DECREASING, GG_DEVERR_GRANULE, GG_DEVERR_LAST, GG_DEVERR_SKIPPED = 1, 2, 4, 8
+STATUS_NAMES = ["GG_OK", "GG_ERR_NULL", "GG_ERR_SHAPE", "GG_ERR_DTYPE", "GG_ERR_LAYOUT",
+                "GG_ERR_ALIGN", "GG_ERR_MODE", "GG_ERR_WORKSPACE", "GG_ERR_UNSUPPORTED",
+                "GG_ERR_DEVICE", "GG_ERR_HIP", "GG_ERR_OFFSETS"]
+EXPORTS = ["gg_abi_version", "gg_last_error", "gg_device_error", "gg_wgrad_workspace_size",
+           "gg_wgrad", "gg_dglu_workspace_size", "gg_dglu", "gg_dsrelu_workspace_size",
+           "gg_dsrelu"]
+
+_TORCH_DTYPE = {torch.bfloat16: GG_BF16, torch.float16: GG_F16, torch.float32: GG_F32,
+                torch.float8_e4m3fn: GG_F8E4M3}
+
+
+class GGError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{name}: {message}")
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libgg_moe.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() or "
+                           "python moe_grouped_gemm_offset_amd/build.py")
+    L = ctypes.CDLL(path)
+    P, I32, I64, U32, SZ, F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                               ctypes.c_uint32, ctypes.c_size_t, ctypes.c_float)
+    L.gg_abi_version.restype = ctypes.c_int
+    L.gg_abi_version.argtypes = []
+    L.gg_last_error.restype = ctypes.c_char_p
+    L.gg_last_error.argtypes = []
+    L.gg_device_error.restype = ctypes.c_int
+    L.gg_device_error.argtypes = [P, P, ctypes.POINTER(I32)]
+    L.gg_wgrad_workspace_size.restype = SZ
+    L.gg_wgrad_workspace_size.argtypes = [I32]
+    L.gg_dglu_workspace_size.restype = SZ
+    L.gg_dglu_workspace_size.argtypes = [I32, I32, I32]
+    L.gg_dsrelu_workspace_size.restype = SZ
+    L.gg_dsrelu_workspace_size.argtypes = [I32]
+    L.gg_wgrad.restype = ctypes.c_int
+    L.gg_wgrad.argtypes = [P, I32, P, I32, P, I32, I64, I32, I32, P, P, I32, I32, U32, P, SZ, P]
+    L.gg_dglu.restype = ctypes.c_int
+    L.gg_dglu.argtypes = [P, I64, I32, P, P, I32, I32, P, I32, P, I32, P, P, P, P, I32, P, P,
+                          I32, F, F, F, F, U32, P, SZ, P]
+    L.gg_dsrelu.restype = ctypes.c_int
+    L.gg_dsrelu.argtypes = [P, P, I64, I32, P, P, P, P, I32, P, I32, P, I32, P, P, P, I32, P, P,
+                            U32, P, SZ, P]
+    _lib = L
+    return L
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status):
+    if status != 0:
+        raise GGError(status, gg_last_error())
+
+
+def gg_abi_version():
+    return load_library().gg_abi_version()
+
+
+def gg_last_error():
+    return load_library().gg_last_error().decode()
+
+
+def gg_wgrad_workspace_size(num_experts):
+    return load_library().gg_wgrad_workspace_size(num_experts)
+
+
+def gg_dglu_workspace_size(L, n, generate_dbias):
+    return load_library().gg_dglu_workspace_size(L, n, int(bool(generate_dbias)))
+
+
+def gg_dsrelu_workspace_size(L):
+    return load_library().gg_dsrelu_workspace_size(L)
+
+
+def _workspace(ws, nbytes, like):
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=like.device)
+    return t, t.numel()
+
+
+def gg_device_error(workspace, stream=None):
+    code = ctypes.c_int32(0)
+    _check(load_library().gg_device_error(_ptr(workspace), _stream(stream), ctypes.byref(code)))
+    return code.value
+
+
+def gg_wgrad(a, a_major, b, b_major, offsets, tokens_sum, hidden, intermediate,
+             wgrad_dense=None, wgrad_ptrs=None, wgrad_dtype=None, accumulate=False, flags=0,
+             workspace=None, stream=None):
+    """Grouped wgrad (gg_wgrad of gg_moe.h).  a_major: GG_MAJOR_K/GG_MAJOR_M,
+    b_major: GG_MAJOR_K/GG_MAJOR_N.  Returns the workspace used."""
+    L = load_library()
+    E = offsets.numel()
+    if wgrad_dtype is None:
+        wgrad_dtype = _TORCH_DTYPE[wgrad_dense.dtype]
+    ws, nbytes = _workspace(workspace, L.gg_wgrad_workspace_size(E), offsets)
+    _check(L.gg_wgrad(_ptr(a), a_major, _ptr(b), b_major, _ptr(offsets), E, tokens_sum, hidden,
+                      intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
+                      int(bool(accumulate)), flags, _ptr(ws), nbytes, _stream(stream)))
+    return ws
+
+
+def gg_dglu(a, b_dense, b_ptrs, b_major, n, c, padded_offsets, alpha, beta, prob, d_row, dprob,
+            dbias=None, act=GG_DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0, clamp_max=7.0,
+            linear_offset=1.0, flags=0, workspace=None, stream=None):
+    """Grouped dgrad + dSwiGLU/dGeGLU (gg_dglu of gg_moe.h).  Returns the
+    workspace used."""
+    L = load_library()
+    nl = padded_offsets.numel()
+    ws, nbytes = _workspace(workspace, L.gg_dglu_workspace_size(nl, n, dbias is not None), a)
+    _check(L.gg_dglu(_ptr(a), a.shape[0], a.shape[1], _ptr(b_dense), _ptr(b_ptrs), b_major, n,
+                     _ptr(c), _TORCH_DTYPE[c.dtype], _ptr(padded_offsets), nl, _ptr(alpha),
+                     _ptr(beta), _ptr(prob), _ptr(d_row), _TORCH_DTYPE[d_row.dtype], _ptr(dprob),
+                     _ptr(dbias), act, geglu_alpha, clamp_min, clamp_max, linear_offset, flags,
+                     _ptr(ws), nbytes, _stream(stream)))
+    return ws
+
+
+def gg_dsrelu(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, prob, d_row, dprob,
+              amax=None, flags=0, workspace=None, stream=None):
+    """Grouped MXFP8 dgrad + dsReLU (gg_dsrelu of gg_moe.h).  Returns the
+    workspace used."""
+    L = load_library()
+    nl = padded_offsets.numel()
+    ws, nbytes = _workspace(workspace, L.gg_dsrelu_workspace_size(nl), a)
+    _check(L.gg_dsrelu(_ptr(a), _ptr(sfa), a.shape[0], a.shape[1], _ptr(b), _ptr(sfb),
+                       _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
+                       _ptr(padded_offsets), nl, _ptr(alpha), _ptr(prob), _ptr(d_row),
+                       _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(amax), flags, _ptr(ws),
+                       nbytes, _stream(stream)))
+    return ws

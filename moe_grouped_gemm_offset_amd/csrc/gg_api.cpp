@@ -1,0 +1,396 @@
+// gg_api.cpp -- the C ABI of libgg_moe (declared in include/gg_moe.h).
+//
+// Every entry point validates its arguments on the host first (pointers,
+// enums, sizes, alignment, the one-of output / weight modes), so a rejected
+// call queues no device work.  Only then does it check that the current
+// device is a gfx950, and queue: a set-up kernel (clears the workspace,
+// checks offsets on the device, ranks experts), the grouped GEMM, and for
+// dGLU with dbias a finalize kernel -- all on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/gg_moe.h"
+#include "gg_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+gg_status fail(gg_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+gg_status ok() {
+    g_err.clear();
+    return GG_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int dtype_bytes(gg_dtype d) { return d == GG_F32 ? 4 : (d == GG_F8E4M3 ? 1 : 2); }
+
+bool is_out_dtype(gg_dtype d) { return d == GG_BF16 || d == GG_F16 || d == GG_F32; }
+
+// Current device must be a gfx950; the answer is cached per device ordinal.
+gg_status check_device() {
+    static std::mutex mu;
+    static std::vector<int> cache;   // 0 unknown, 1 gfx950, 2 other
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(GG_ERR_DEVICE, "no HIP device is available");
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)cache.size() <= dev)
+        cache.resize(dev + 1, 0);
+    if (cache[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(GG_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+        cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (cache[dev] != 1)
+            return fail(GG_ERR_DEVICE, "device %d is %s; this library is built for gfx950", dev,
+                        prop.gcnArchName);
+    }
+    if (cache[dev] != 1)
+        return fail(GG_ERR_DEVICE, "device %d is not a gfx950", dev);
+    return GG_OK;
+}
+
+gg_status hip_fail(hipError_t e, const char* what) {
+    return fail(GG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// GG_FLAG_VALIDATE_OFFSETS: read the offsets on the host and apply the
+// pages' rules.  dgrad: last <= total; wgrad: last == total.
+gg_status validate_offsets_host(const int32_t* offsets, int n, int64_t total, bool dgrad,
+                                hipStream_t s) {
+    std::vector<int32_t> h(n);
+    hipError_t e = hipMemcpyAsync(h.data(), offsets, n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+        return hip_fail(e, "reading offsets");
+    int64_t prev = 0;
+    for (int i = 0; i < n; i++) {
+        if (h[i] < prev)
+            return fail(GG_ERR_OFFSETS, "offsets[%d] = %d is smaller than its predecessor %lld", i,
+                        h[i], (long long)prev);
+        if ((h[i] - prev) % 256 != 0)
+            return fail(GG_ERR_OFFSETS, "group %d has %lld rows, not a multiple of 256", i,
+                        (long long)(h[i] - prev));
+        prev = h[i];
+    }
+    if (dgrad ? prev > total : prev != total)
+        return fail(GG_ERR_OFFSETS, "last offset %lld %s %lld", (long long)prev,
+                    dgrad ? "exceeds the row count" : "differs from tokens_sum", (long long)total);
+    return GG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gg_abi_version(void) { return GG_ABI_VERSION; }
+
+const char* gg_last_error(void) { return g_err.c_str(); }
+
+gg_status gg_device_error(const void* workspace, void* stream, int32_t* code) {
+    if (!workspace || !code)
+        return fail(GG_ERR_NULL, "workspace and code must be non-NULL");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess)
+        e = hipMemcpy(code, workspace, sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return hip_fail(e, "reading the device error word");
+    return ok();
+}
+
+size_t gg_wgrad_workspace_size(int32_t num_experts) {
+    if (num_experts < 0)
+        num_experts = 0;
+    return round256(gg::kWsHeader + sizeof(int32_t) * (size_t)num_experts);
+}
+
+size_t gg_dglu_workspace_size(int32_t L, int32_t n, int32_t generate_dbias) {
+    size_t extra = generate_dbias && L > 0 && n > 0 ? sizeof(float) * (size_t)L * 2 * (size_t)n : 0;
+    return round256(gg::kWsHeader + extra);
+}
+
+size_t gg_dsrelu_workspace_size(int32_t L) {
+    (void)L;
+    return round256(gg::kWsHeader);
+}
+
+gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_major,
+                   const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                   int32_t hidden, int32_t intermediate, void* wgrad_dense,
+                   const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype, int32_t accumulate,
+                   uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!offsets || !workspace)
+        return fail(GG_ERR_NULL, "offsets and workspace must be non-NULL");
+    if ((!a || !b) && tokens_sum > 0)
+        return fail(GG_ERR_NULL, "a and b must be non-NULL");
+    if (a_major != GG_MAJOR_K && a_major != GG_MAJOR_M)
+        return fail(GG_ERR_LAYOUT, "a_major must be GG_MAJOR_K or GG_MAJOR_M");
+    if (b_major != GG_MAJOR_K && b_major != GG_MAJOR_N)
+        return fail(GG_ERR_LAYOUT, "b_major must be GG_MAJOR_K or GG_MAJOR_N");
+    if (!is_out_dtype(wgrad_dtype))
+        return fail(GG_ERR_DTYPE, "wgrad_dtype must be GG_BF16, GG_F16 or GG_F32");
+    if ((wgrad_dense != nullptr) == (wgrad_ptrs != nullptr))
+        return fail(GG_ERR_MODE, "exactly one of wgrad_dense and wgrad_ptrs must be given");
+    if (num_experts < 1 || num_experts > 1024)
+        return fail(GG_ERR_SHAPE, "num_experts must be in 1..1024 (got %d)", num_experts);
+    if (tokens_sum < 0 || tokens_sum > INT32_MAX)
+        return fail(GG_ERR_SHAPE, "tokens_sum must be in 0..2^31-1");
+    if (hidden <= 0 || intermediate <= 0)
+        return fail(GG_ERR_SHAPE, "hidden and intermediate must be positive");
+    if (hidden % 64 || intermediate % 64)
+        return fail(GG_ERR_UNSUPPORTED, "hidden and intermediate must be multiples of 64");
+    if (tokens_sum % 8)
+        return fail(GG_ERR_ALIGN, "tokens_sum must be a multiple of 8 (16-byte rows)");
+    // tile-relative 32-bit buffer offsets: 256 rows of the largest pitch
+    if (tokens_sum > (1 << 21) || hidden > (1 << 21) || intermediate > (1 << 21))
+        return fail(GG_ERR_UNSUPPORTED, "tokens_sum, hidden and intermediate are limited to 2^21");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(wgrad_dense) || !aligned16(wgrad_ptrs) ||
+        ((uintptr_t)offsets & 3u))
+        return fail(GG_ERR_ALIGN, "a, b and the output must be 16-byte aligned");
+    if ((uintptr_t)workspace & 255u)
+        return fail(GG_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < gg_wgrad_workspace_size(num_experts))
+        return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                    gg_wgrad_workspace_size(num_experts));
+    if (flags & ~(uint32_t)GG_FLAG_VALIDATE_OFFSETS)
+        return fail(GG_ERR_MODE, "unsupported flags 0x%x for gg_wgrad", flags);
+    gg_status st = check_device();
+    if (st != GG_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (flags & GG_FLAG_VALIDATE_OFFSETS) {
+        st = validate_offsets_host(offsets, num_experts, tokens_sum, false, s);
+        if (st != GG_OK)
+            return st;
+    }
+    int32_t* ws = (int32_t*)workspace;
+    hipError_t e = gg::launch_prologue(offsets, num_experts, tokens_sum, 0, ws,
+                                       ws + gg::kWsHeader / 4, nullptr, 0, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "launching the wgrad prologue");
+    gg::WgradArgs p;
+    p.a = a;
+    p.b = b;
+    p.offsets = offsets;
+    p.ws = ws;
+    p.out_dense = wgrad_dense;
+    p.out_ptrs = wgrad_ptrs;
+    p.T = tokens_sum;
+    p.hidden = hidden;
+    p.inter = intermediate;
+    p.E = num_experts;
+    p.a_kmajor = a_major == GG_MAJOR_K;
+    p.b_kmajor = b_major == GG_MAJOR_K;
+    p.out_dtype = (int)wgrad_dtype;
+    p.accumulate = accumulate ? 1 : 0;
+    e = gg::launch_wgrad(p, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "launching gg_wgrad");
+    return ok();
+}
+
+static gg_status check_rows(const int32_t* po, int32_t L, int64_t m_rows, const void* c,
+                            const float* prob, const void* d_row, const float* dprob,
+                            void* workspace) {
+    if (!po || !c || !prob || !d_row || !dprob || !workspace)
+        return fail(GG_ERR_NULL, "padded_offsets, c, prob, d_row, dprob and workspace must be non-NULL");
+    if (L < 1 || L > 1024)
+        return fail(GG_ERR_SHAPE, "the expert count must be in 1..1024 (got %d)", L);
+    if (m_rows < 0 || m_rows > INT32_MAX)
+        return fail(GG_ERR_SHAPE, "m_rows must be in 0..2^31-1");
+    if (!aligned16(c) || !aligned16(d_row) || ((uintptr_t)prob & 3u) || ((uintptr_t)dprob & 3u) ||
+        ((uintptr_t)po & 3u))
+        return fail(GG_ERR_ALIGN, "c and d_row must be 16-byte aligned, prob/dprob 4-byte");
+    if ((uintptr_t)workspace & 255u)
+        return fail(GG_ERR_ALIGN, "workspace must be 256-byte aligned");
+    return GG_OK;
+}
+
+gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k, const void* b_dense,
+                  const int64_t* b_ptrs, gg_major b_major, int32_t n, const void* c,
+                  gg_dtype c_dtype, const int32_t* padded_offsets, int32_t L, const float* alpha,
+                  const float* beta, const float* prob, void* d_row, gg_dtype d_dtype,
+                  float* dprob, void* dbias, gg_act act, float geglu_alpha, float clamp_min,
+                  float clamp_max, float linear_offset, uint32_t flags, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    gg_status st = check_rows(padded_offsets, L, m_rows, c, prob, d_row, dprob, workspace);
+    if (st != GG_OK)
+        return st;
+    if (!a || !alpha || !beta)
+        return fail(GG_ERR_NULL, "a, alpha and beta must be non-NULL");
+    if ((b_dense != nullptr) == (b_ptrs != nullptr))
+        return fail(GG_ERR_MODE, "exactly one of b_dense and b_ptrs must be given");
+    if (b_major != GG_MAJOR_K && b_major != GG_MAJOR_N)
+        return fail(GG_ERR_LAYOUT, "b_major must be GG_MAJOR_K or GG_MAJOR_N");
+    if (b_dense && b_major != GG_MAJOR_K)
+        return fail(GG_ERR_LAYOUT, "dense B must be K-major");
+    if (!is_out_dtype(c_dtype) || !is_out_dtype(d_dtype))
+        return fail(GG_ERR_DTYPE, "c_dtype and d_dtype must be GG_BF16, GG_F16 or GG_F32");
+    if (act != GG_DSWIGLU && act != GG_DGEGLU)
+        return fail(GG_ERR_MODE, "act must be GG_DSWIGLU or GG_DGEGLU");
+    if (n <= 0 || n % 32)
+        return fail(GG_ERR_SHAPE, "n must be a positive multiple of 32 (got %d)", n);
+    if (k <= 0)
+        return fail(GG_ERR_SHAPE, "k must be positive");
+    if (k % 64)
+        return fail(GG_ERR_UNSUPPORTED, "k must be a multiple of 64");
+    if (k > (1 << 21) || n > (1 << 21))
+        return fail(GG_ERR_UNSUPPORTED, "k and n are limited to 2^21");
+    if (!aligned16(a) || !aligned16(b_dense) || !aligned16(b_ptrs) || !aligned16(dbias) ||
+        ((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u))
+        return fail(GG_ERR_ALIGN, "a, b and dbias must be 16-byte aligned");
+    if (flags & ~(uint32_t)(GG_FLAG_GATE_FIRST | GG_FLAG_GEGLU_MASK_FILTER | GG_FLAG_VALIDATE_OFFSETS))
+        return fail(GG_ERR_MODE, "unsupported flags 0x%x for gg_dglu", flags);
+    size_t need = gg_dglu_workspace_size(L, n, dbias != nullptr);
+    if (workspace_bytes < need)
+        return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    st = check_device();
+    if (st != GG_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (flags & GG_FLAG_VALIDATE_OFFSETS) {
+        st = validate_offsets_host(padded_offsets, L, m_rows, true, s);
+        if (st != GG_OK)
+            return st;
+    }
+    int32_t* ws = (int32_t*)workspace;
+    float* acc = dbias ? (float*)((char*)workspace + gg::kWsHeader) : nullptr;
+    const int64_t nacc = dbias ? (int64_t)L * 2 * n : 0;
+    hipError_t e = gg::launch_prologue(padded_offsets, L, m_rows, 1, ws, nullptr, acc, nacc, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "launching the dglu prologue");
+    gg::DgluArgs p;
+    p.a = a;
+    p.b_dense = b_dense;
+    p.b_ptrs = b_ptrs;
+    p.c = c;
+    p.po = padded_offsets;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.prob = prob;
+    p.d = d_row;
+    p.dprob = dprob;
+    p.dbias = dbias;
+    p.ws = ws;
+    p.m_rows = m_rows;
+    p.K = k;
+    p.N = n;
+    p.L = L;
+    p.b_kmajor = b_major == GG_MAJOR_K;
+    p.c_dtype = (int)c_dtype;
+    p.d_dtype = (int)d_dtype;
+    p.act = act == GG_DGEGLU;
+    p.gate_first = (flags & GG_FLAG_GATE_FIRST) != 0;
+    p.mask_filter = (flags & GG_FLAG_GEGLU_MASK_FILTER) != 0;
+    p.geglu_alpha = geglu_alpha;
+    p.clamp_min = clamp_min;
+    p.clamp_max = clamp_max;
+    p.linear_offset = linear_offset;
+    e = gg::launch_dglu(p, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "launching gg_dglu");
+    if (dbias) {
+        e = gg::launch_dbias_finalize((uint16_t*)dbias, acc, nacc, s);
+        if (e != hipSuccess)
+            return hip_fail(e, "launching the dbias finalize");
+    }
+    return ok();
+}
+
+gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
+                    const void* b_fp8, const uint8_t* sfb, const int64_t* b_ptrs,
+                    const int64_t* sfb_ptrs, int32_t n, const void* c, gg_dtype c_dtype,
+                    const int32_t* padded_offsets, int32_t L, const float* alpha,
+                    const float* prob, void* d_row, gg_dtype d_dtype, float* dprob, float* amax,
+                    uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+    gg_status st = check_rows(padded_offsets, L, m_rows, c, prob, d_row, dprob, workspace);
+    if (st != GG_OK)
+        return st;
+    if (!a_fp8 || !sfa || !alpha)
+        return fail(GG_ERR_NULL, "a_fp8, sfa and alpha must be non-NULL");
+    const bool dense = b_fp8 || sfb;
+    const bool discrete = b_ptrs || sfb_ptrs;
+    if (dense == discrete || (dense && (!b_fp8 || !sfb)) || (discrete && (!b_ptrs || !sfb_ptrs)))
+        return fail(GG_ERR_MODE, "give exactly one of (b_fp8, sfb) and (b_ptrs, sfb_ptrs)");
+    if (!is_out_dtype(c_dtype) || !is_out_dtype(d_dtype))
+        return fail(GG_ERR_DTYPE, "c_dtype and d_dtype must be GG_BF16, GG_F16 or GG_F32");
+    if (n <= 0 || n % 32)
+        return fail(GG_ERR_SHAPE, "n must be a positive multiple of 32 (got %d)", n);
+    if (k <= 0)
+        return fail(GG_ERR_SHAPE, "k must be positive");
+    if (k % 128)
+        return fail(GG_ERR_UNSUPPORTED, "k must be a multiple of 128");
+    if (k > (1 << 21) || n > (1 << 21))
+        return fail(GG_ERR_UNSUPPORTED, "k and n are limited to 2^21");
+    if (!aligned16(a_fp8) || !aligned16(b_fp8) || !aligned16(b_ptrs) || !aligned16(sfb_ptrs) ||
+        ((uintptr_t)sfa & 3u) || ((uintptr_t)sfb & 3u) || ((uintptr_t)alpha & 3u) ||
+        ((uintptr_t)amax & 3u))
+        return fail(GG_ERR_ALIGN, "operands must be 16-byte aligned, scales 4-byte aligned");
+    if (flags & ~(uint32_t)GG_FLAG_VALIDATE_OFFSETS)
+        return fail(GG_ERR_MODE, "unsupported flags 0x%x for gg_dsrelu", flags);
+    size_t need = gg_dsrelu_workspace_size(L);
+    if (workspace_bytes < need)
+        return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    st = check_device();
+    if (st != GG_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (flags & GG_FLAG_VALIDATE_OFFSETS) {
+        st = validate_offsets_host(padded_offsets, L, m_rows, true, s);
+        if (st != GG_OK)
+            return st;
+    }
+    int32_t* ws = (int32_t*)workspace;
+    hipError_t e = gg::launch_prologue(padded_offsets, L, m_rows, 1, ws, nullptr, amax,
+                                       amax ? L : 0, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "launching the dsrelu prologue");
+    gg::DsreluArgs p;
+    p.a = (const uint8_t*)a_fp8;
+    p.sfa = sfa;
+    p.b_dense = (const uint8_t*)b_fp8;
+    p.sfb_dense = sfb;
+    p.b_ptrs = b_ptrs;
+    p.sfb_ptrs = sfb_ptrs;
+    p.c = c;
+    p.po = padded_offsets;
+    p.alpha = alpha;
+    p.prob = prob;
+    p.d = d_row;
+    p.dprob = dprob;
+    p.amax = amax;
+    p.ws = ws;
+    p.m_rows = m_rows;
+    p.K = k;
+    p.N = n;
+    p.L = L;
+    p.c_dtype = (int)c_dtype;
+    p.d_dtype = (int)d_dtype;
+    e = gg::launch_dsrelu(p, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "launching gg_dsrelu");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// gg_internal.hpp -- parameter blocks and launchers shared between the host
+// API (gg_api.cpp) and the kernel translation units.  Not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gg {
+
+// Workspace layout (every op): a 256-byte header whose first int32 is the
+// device error word, followed by the op's own region.
+constexpr size_t kWsHeader = 256;
+
+struct WgradArgs {
+    const void* a;
+    const void* b;
+    const int32_t* offsets;
+    int32_t* ws;              // header + int32 order[E]
+    void* out_dense;
+    const int64_t* out_ptrs;
+    int64_t T;
+    int hidden, inter, E;
+    int a_kmajor, b_kmajor;
+    int out_dtype, accumulate;
+};
+
+struct DgluArgs {
+    const void* a;
+    const void* b_dense;
+    const int64_t* b_ptrs;
+    const void* c;
+    const int32_t* po;
+    const float* alpha;
+    const float* beta;
+    const float* prob;
+    void* d;
+    float* dprob;
+    void* dbias;
+    int32_t* ws;              // header + float dbias accumulators [L][2N]
+    int64_t m_rows;
+    int K, N, L;
+    int b_kmajor;
+    int c_dtype, d_dtype;
+    int act;                  // 0 dSwiGLU, 1 dGeGLU
+    int gate_first, mask_filter;
+    float geglu_alpha, clamp_min, clamp_max, linear_offset;
+};
+
+struct DsreluArgs {
+    const uint8_t* a;
+    const uint8_t* sfa;
+    const uint8_t* b_dense;
+    const uint8_t* sfb_dense;
+    const int64_t* b_ptrs;
+    const int64_t* sfb_ptrs;
+    const void* c;
+    const int32_t* po;
+    const float* alpha;
+    const float* prob;
+    void* d;
+    float* dprob;
+    float* amax;
+    int32_t* ws;
+    int64_t m_rows;
+    int K, N, L;
+    int c_dtype, d_dtype;
+};
+
+// Launchers (return the HIP status of the launch).
+hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s);
+hipError_t launch_dglu(const DgluArgs& p, hipStream_t s);
+hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s);
+
+// Prologue: clears the error word and `nclear` floats at `clear`, checks the
+// offsets (wgrad: last == total; dgrad: last <= total) and, when order is
+// non-NULL, writes the experts sorted by count, largest first.
+hipError_t launch_prologue(const int32_t* offsets, int n, int64_t total, int dgrad,
+                           int32_t* err, int32_t* order, float* clear, int64_t nclear,
+                           hipStream_t s);
+// dbias[i] = bf16(float(dbias[i]) + acc[i]) for i < n.
+hipError_t launch_dbias_finalize(uint16_t* dbias, const float* acc, int64_t n, hipStream_t s);
+
+}  // namespace gg

@@ -194,14 +194,18 @@ void orc_wgrad(const uint16_t* A, int a_major, const uint16_t* B, int b_major,
         for (int r = 0; r < nrows; r++) {
             int h = hrows ? hrows[r] : r;
             double* o = out + ((int64_t)e * nrows + r) * inter;
-            for (int i = 0; i < inter; i++) {
-                double acc = 0.0;
-                for (int64_t t = begin; t < end; t++) {
-                    int64_t ia = a_major == 0 ? (int64_t)h * T + t : t * hidden + h;
+            /* o[i] = sum over t = begin .. end-1, in that order, of A(h,t) B(t,i):
+             * the t loop is outside so that B's rows are read in order; each
+             * o[i] still adds its terms in increasing t. */
+            for (int i = 0; i < inter; i++)
+                o[i] = 0.0;
+            for (int64_t t = begin; t < end; t++) {
+                int64_t ia = a_major == 0 ? (int64_t)h * T + t : t * hidden + h;
+                double av = orc_bf16_to_double(A[ia]);
+                for (int i = 0; i < inter; i++) {
                     int64_t ib = b_major == 0 ? (int64_t)i * T + t : t * inter + i;
-                    acc += orc_bf16_to_double(A[ia]) * orc_bf16_to_double(B[ib]);
+                    o[i] += av * orc_bf16_to_double(B[ib]);
                 }
-                o[i] = acc;
             }
         }
     }

@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/gg_moe.h declares, and rejects invalid arguments on the host (before
+any device call) with the documented status codes.  Pointers here are fake
+aligned addresses: validation never dereferences them."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from moe_grouped_gemm_offset_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gg_moe.h")
+
+OK, NULL, SHAPE, DTYPE, LAYOUT, ALIGN, MODE, WORKSPACE, UNSUPPORTED, DEVICE, HIP, OFFSETS = range(12)
+
+P = 1 << 20          # a fake 256-byte aligned device address
+WS = 1 << 24
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(gg_\w+)\s*\(", src, re.M)))
+
+
+def test_loads_and_exports_every_declared_symbol():
+    lib = B.load_library()
+    names = declared()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert B.gg_abi_version() == 1
+
+
+def test_workspace_sizes():
+    assert B.gg_wgrad_workspace_size(64) == 512
+    assert B.gg_wgrad_workspace_size(1024) == 256 + 4096
+    assert B.gg_dglu_workspace_size(32, 1536, 1) == 256 + 32 * 3072 * 4
+    assert B.gg_dglu_workspace_size(32, 1536, 0) == 256
+    assert B.gg_dsrelu_workspace_size(16) == 256
+
+
+def wgrad(**kw):
+    args = dict(a=P, a_major=0, b=P, b_major=2, offsets=P, E=4, T=1024, hidden=256, inter=256,
+                dense=P, ptrs=None, dtype=2, acc=0, flags=0, ws=WS, wsb=4096, stream=None)
+    args.update(kw)
+    lib = B.load_library()
+    return lib.gg_wgrad(args["a"], args["a_major"], args["b"], args["b_major"], args["offsets"],
+                        args["E"], args["T"], args["hidden"], args["inter"], args["dense"],
+                        args["ptrs"], args["dtype"], args["acc"], args["flags"], args["ws"],
+                        args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(offsets=None), NULL),
+    (dict(ws=None), NULL),
+    (dict(a=None), NULL),
+    (dict(a_major=2), LAYOUT),
+    (dict(b_major=1), LAYOUT),
+    (dict(dtype=3), DTYPE),
+    (dict(ptrs=P), MODE),
+    (dict(dense=None), MODE),
+    (dict(E=0), SHAPE),
+    (dict(E=1025), SHAPE),
+    (dict(T=-8), SHAPE),
+    (dict(hidden=96), UNSUPPORTED),
+    (dict(T=1020), ALIGN),
+    (dict(a=P + 8), ALIGN),
+    (dict(dense=P + 4), ALIGN),
+    (dict(ws=WS + 16), ALIGN),
+    (dict(wsb=100), WORKSPACE),
+    (dict(flags=1), MODE),
+    (dict(T=1 << 22), UNSUPPORTED),
+])
+def test_wgrad_rejects(kw, status):
+    assert wgrad(**kw) == status
+    assert B.gg_last_error() != ""
+
+
+def dglu(**kw):
+    args = dict(a=P, M=1024, k=256, bd=P, bp=None, bm=0, n=256, c=P, cdt=0, po=P, L=4, alpha=P,
+                beta=P, prob=P, d=P, ddt=0, dprob=P, dbias=None, act=0, flags=0, ws=WS, wsb=1 << 20)
+    args.update(kw)
+    lib = B.load_library()
+    return lib.gg_dglu(args["a"], args["M"], args["k"], args["bd"], args["bp"], args["bm"], args["n"],
+                       args["c"], args["cdt"], args["po"], args["L"], args["alpha"], args["beta"],
+                       args["prob"], args["d"], args["ddt"], args["dprob"], args["dbias"], args["act"],
+                       1.702, -7.0, 7.0, 1.0, args["flags"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(po=None), NULL),
+    (dict(alpha=None), NULL),
+    (dict(bp=P), MODE),
+    (dict(bd=None), MODE),
+    (dict(bm=2), LAYOUT),
+    (dict(bm=1, bd=None, bp=P), LAYOUT),
+    (dict(cdt=3), DTYPE),
+    (dict(act=2), MODE),
+    (dict(n=48), SHAPE),
+    (dict(k=96), UNSUPPORTED),
+    (dict(L=0), SHAPE),
+    (dict(L=1025), SHAPE),
+    (dict(c=P + 2), ALIGN),
+    (dict(flags=8), MODE),
+    (dict(dbias=P, wsb=256), WORKSPACE),
+])
+def test_dglu_rejects(kw, status):
+    assert dglu(**kw) == status
+
+
+def dsrelu(**kw):
+    args = dict(a=P, sfa=P, M=1024, k=512, b=P, sfb=P, bp=None, sp=None, n=256, c=P, cdt=0, po=P,
+                L=4, alpha=P, prob=P, d=P, ddt=0, dprob=P, amax=P, flags=0, ws=WS, wsb=256)
+    args.update(kw)
+    lib = B.load_library()
+    return lib.gg_dsrelu(args["a"], args["sfa"], args["M"], args["k"], args["b"], args["sfb"],
+                         args["bp"], args["sp"], args["n"], args["c"], args["cdt"], args["po"],
+                         args["L"], args["alpha"], args["prob"], args["d"], args["ddt"], args["dprob"],
+                         args["amax"], args["flags"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sfa=None), NULL),
+    (dict(b=None, sfb=None), MODE),
+    (dict(bp=P, sp=P), MODE),
+    (dict(sfb=None), MODE),
+    (dict(k=192), UNSUPPORTED),
+    (dict(n=40), SHAPE),
+    (dict(ddt=3), DTYPE),
+    (dict(sfa=P + 1), ALIGN),
+    (dict(wsb=16), WORKSPACE),
+])
+def test_dsrelu_rejects(kw, status):
+    assert dsrelu(**kw) == status
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_valid_call_without_a_gpu_reports_device():
+    assert wgrad() == DEVICE
+    assert dglu() == DEVICE
+    assert dsrelu() == DEVICE

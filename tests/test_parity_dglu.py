@@ -1,0 +1,142 @@
+"""GPU parity of gg_dglu against the oracle (through the C ABI).
+
+Small cases span several 256-row tiles, a partial N tile, an empty group and
+rows past valid_m; they cover dSwiGLU and dGeGLU (value and mask filters),
+dense / discrete K-major / discrete N-major B, the gate-first order, dbias,
+and C/D dtypes.  The two named workloads (dSwiGLU: L 8, K 2048, N 1024,
+M 16384; dGeGLU: L 32, K 4096, N 1536, M 32768, discrete B, dbias) run at
+full size in the bench's launch configuration and are checked on sampled
+rows, dbias by the per-expert column sums of the kernel's own D.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from moe_grouped_gemm_offset_amd import synth
+from tests.parity_util import ORC_DT, TOL, assert_close, normwise, say, values
+
+pytestmark = pytest.mark.gpu
+
+
+def gg():
+    from moe_grouped_gemm_offset_amd import binding
+    binding.load_library()
+    return binding
+
+
+def run_gpu(inp, act, flags=0, d_dtype=torch.bfloat16, dbias=False):
+    b = gg()
+    dev = lambda x: x.cuda()
+    M, N, L = inp["M"], inp["N"], inp["L"]
+    a = dev(inp["a"])
+    if inp["b_dense"] is not None:
+        bd, bp, keep = dev(inp["b_dense"]), None, None
+    else:
+        keep = [dev(x) for x in inp["b_list"]]
+        bd, bp = None, torch.tensor([x.data_ptr() for x in keep], dtype=torch.int64, device="cuda")
+    d = torch.full((M, 2 * N), float("nan"), dtype=d_dtype, device="cuda")
+    dprob = torch.zeros(M, dtype=torch.float32, device="cuda")
+    db = torch.zeros(L, 2 * N, dtype=torch.bfloat16, device="cuda") if dbias else None
+    ws = b.gg_dglu(a, bd, bp, 0 if inp["b_major"] == "k" else 2, N, dev(inp["c"]),
+                   dev(inp["padded_offsets"]), dev(inp["alpha"]), dev(inp["beta"]), dev(inp["prob"]),
+                   d, dprob, db, act=act, flags=flags)
+    torch.cuda.synchronize()
+    err = b.gg_device_error(ws)
+    return d.cpu(), dprob.cpu(), (db.cpu() if dbias else None), err
+
+
+def run_oracle(inp, act, flags=0, d_dtype=torch.bfloat16, dbias=False, rows=None):
+    L, N = inp["L"], inp["N"]
+    return orc.dglu(synth.bits(inp["a"]), inp["M"], inp["K"], [synth.bits(x) for x in inp["b_list"]],
+                    0 if inp["b_major"] == "k" else 1, N, synth.bits(inp["c"]), ORC_DT[inp["c"].dtype],
+                    inp["padded_offsets"].numpy(), inp["alpha"].numpy(), inp["beta"].numpy(),
+                    inp["prob"].numpy(), act=act, gate_first=bool(flags & 1), mask_filter=bool(flags & 2),
+                    d_dtype=ORC_DT[d_dtype],
+                    dbias_in=np.zeros((L, 2 * N), np.uint16) if dbias else None, rows=rows)
+
+
+def check(inp, act, flags=0, d_dtype=torch.bfloat16, dbias=False, name=""):
+    say(name, "act", act, "flags", flags, d_dtype, "dbias" if dbias else "")
+    d, dprob, db, err = run_gpu(inp, act, flags, d_dtype, dbias)
+    assert err in (0,), f"device error word {err}"
+    ref = run_oracle(inp, act, flags, d_dtype, dbias)
+    vm = inp["valid_m"]
+    odt = ORC_DT[d_dtype]
+    assert_close(values(d[:vm]), ref["D"][:vm], odt, f"{name} D_row")
+    assert torch.all(torch.isnan(d[vm:])), "rows past valid_m must not be written"
+    assert_close(values(dprob[:vm]), ref["dprob"][:vm], orc.F32, f"{name} dprob")
+    assert torch.all(dprob[vm:] == 0)
+    start = 0
+    for g, cnt in enumerate(inp["counts"]):
+        if cnt:
+            e = normwise(values(d[start:start + cnt]), ref["D"][start:start + cnt])
+            assert e <= TOL[odt], f"{name}: group {g} D error {e:.3e}"
+        start += cnt
+    if dbias:
+        assert_close(values(db), ref["dbias"], orc.BF16, f"{name} dbias")
+        for g, cnt in enumerate(inp["counts"]):
+            if cnt == 0:
+                assert torch.all(db[g] == 0), "an empty group's dbias must stay zero"
+
+
+def small(seed, c_std=2.0, discrete=False, b_major="k", c_dtype=torch.bfloat16):
+    counts = [256, 0, 512, 256]
+    return synth.dglu_inputs(4, 256, 320, counts, a_std=0.05, b_std=0.05, c_std=c_std,
+                             c_dtype=c_dtype, m_extra=64, seed=seed, discrete=discrete,
+                             b_major=b_major)
+
+
+@pytest.mark.parametrize("act", [orc.DSWIGLU, orc.DGEGLU])
+@pytest.mark.parametrize("mode", ["dense", "discrete_k", "discrete_n"])
+def test_small(act, mode):
+    inp = small(51 + act, c_std=4.0 if act == orc.DGEGLU else 2.0, discrete=mode != "dense",
+                b_major="n" if mode == "discrete_n" else "k")
+    check(inp, act, dbias=True, name=f"small {mode}")
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_flags(flags):
+    inp = small(55, c_std=4.0)
+    check(inp, orc.DGEGLU, flags=flags, name="flags")
+
+
+@pytest.mark.parametrize("c_dtype", [torch.float16, torch.float32])
+@pytest.mark.parametrize("d_dtype", [torch.float16, torch.float32])
+def test_dtypes(c_dtype, d_dtype):
+    inp = small(56, c_dtype=c_dtype)
+    check(inp, orc.DSWIGLU, d_dtype=d_dtype, name="dtypes")
+
+
+def _full(name, device="cuda"):
+    w = synth.WORKLOADS[name]
+    counts = synth.workload_counts(name)
+    return synth.dglu_inputs(w["L"], w["K"], w["N"], counts, c_std=w["c_std"], seed=w["seed"],
+                             device=device, discrete=w["discrete"]), w
+
+
+@pytest.mark.parametrize("name", ["dswiglu", "dgeglu"])
+def test_workload_sampled(name):
+    inp, w = _full(name)
+    act = orc.DSWIGLU if w["act"] == "dswiglu" else orc.DGEGLU
+    say(name, "counts", inp["counts"].tolist())
+    d, dprob, db, err = run_gpu(inp, act, dbias=w["dbias"])
+    assert err == 0
+    cpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    cpu["b_list"] = [x.cpu() for x in inp["b_list"]]
+    starts = np.concatenate([[0], np.cumsum(inp["counts"])[:-1]])
+    rows = []
+    for s, c in zip(starts, inp["counts"]):
+        if c:
+            rows += [s, s + 1, s + c - 1]
+    rows = np.array(sorted(set(rows)), np.int64)
+    ref = run_oracle(cpu, act, rows=rows)
+    assert_close(values(d[rows]), ref["D"], orc.BF16, f"{name} D_row (sampled rows)")
+    assert_close(values(dprob[rows]), ref["dprob"], orc.F32, f"{name} dprob (sampled rows)")
+    if w["dbias"]:
+        # dbias against the per-expert column sums of the kernel's own D
+        dv = values(d)
+        want = np.zeros((inp["L"], 2 * inp["N"]))
+        for g, (s, c) in enumerate(zip(starts, inp["counts"])):
+            want[g] = dv[s:s + c].sum(0)
+        assert_close(values(db), want, orc.BF16, f"{name} dbias vs sum of D")

@@ -1,0 +1,132 @@
+"""GPU parity of gg_dsrelu against the oracle (through the C ABI).
+
+Small cases span several tiles, a partial N tile, an empty group, rows past
+valid_m, per-row scale spreads, dense and discrete B, and C/D dtypes; the
+MoE-scale workload (L 16, K 7168, N 2048, M 65536) runs at full size in the
+bench's launch configuration and is checked on sampled rows, Amax against
+the maximum of the kernel's own D per expert.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from moe_grouped_gemm_offset_amd import synth
+from tests.parity_util import ORC_DT, TOL, assert_close, normwise, say, values
+
+pytestmark = pytest.mark.gpu
+
+
+def gg():
+    from moe_grouped_gemm_offset_amd import binding
+    binding.load_library()
+    return binding
+
+
+def run_gpu(inp, d_dtype=torch.bfloat16, with_amax=True):
+    b = gg()
+    dev = lambda x: x.cuda()
+    M, N, L = inp["M"], inp["N"], inp["L"]
+    a = dev(inp["a"]).view(torch.uint8)
+    if inp["b_dense"] is not None:
+        bd, sd = dev(inp["b_dense"]).view(torch.uint8), dev(inp["sfb_dense"])
+        bp = sp = None
+    else:
+        kb = [dev(x).view(torch.uint8) for x in inp["b_list"]]
+        ks = [dev(x) for x in inp["sfb_list"]]
+        bp = torch.tensor([x.data_ptr() for x in kb], dtype=torch.int64, device="cuda")
+        sp = torch.tensor([x.data_ptr() for x in ks], dtype=torch.int64, device="cuda")
+        bd = sd = None
+    d = torch.full((M, N), float("nan"), dtype=d_dtype, device="cuda")
+    dprob = torch.zeros(M, dtype=torch.float32, device="cuda")
+    amax = torch.full((L,), -1.0, dtype=torch.float32, device="cuda") if with_amax else None
+    ws = b.gg_dsrelu(a, dev(inp["sfa"]), bd, sd, bp, sp, N, dev(inp["c"]), dev(inp["padded_offsets"]),
+                     dev(inp["alpha"]), dev(inp["prob"]), d, dprob, amax)
+    torch.cuda.synchronize()
+    err = b.gg_device_error(ws)
+    if not inp["b_dense"] is None:
+        pass
+    return d.cpu(), dprob.cpu(), (amax.cpu() if with_amax else None), err
+
+
+def run_oracle(inp, d_dtype=torch.bfloat16, rows=None):
+    return orc.dsrelu(synth.bits(inp["a"]), synth.bits(inp["sfa"]), inp["M"], inp["K"],
+                      [synth.bits(x) for x in inp["b_list"]], [synth.bits(x) for x in inp["sfb_list"]],
+                      inp["N"], synth.bits(inp["c"]), ORC_DT[inp["c"].dtype],
+                      inp["padded_offsets"].numpy(), inp["alpha"].numpy(), inp["prob"].numpy(),
+                      d_dtype=ORC_DT[d_dtype], rows=rows)
+
+
+def small(seed, discrete=False, c_dtype=torch.bfloat16, spread=3):
+    counts = [256, 512, 0, 256]
+    return synth.dsrelu_inputs(4, 512, 320, counts, c_dtype=c_dtype, m_extra=64, seed=seed,
+                               discrete=discrete, scale_spread=spread)
+
+
+@pytest.mark.parametrize("discrete", [False, True])
+def test_small(discrete):
+    inp = small(61, discrete)
+    say("dsrelu small", "discrete" if discrete else "dense")
+    d, dprob, amax, err = run_gpu(inp)
+    assert err == 0
+    ref = run_oracle(inp)
+    vm = inp["valid_m"]
+    assert_close(values(d[:vm]), ref["D"][:vm], orc.BF16, "D_row")
+    assert torch.all(torch.isnan(d[vm:]))
+    assert_close(values(dprob[:vm]), ref["dprob"][:vm], orc.F32, "dprob")
+    assert torch.all(dprob[vm:] == 0)
+    assert_close(amax.numpy(), ref["amax"], orc.F32, "amax")
+    assert amax[2] == 0.0, "an empty expert's amax is 0"
+    start = 0
+    for g, c in enumerate(inp["counts"]):
+        if c:
+            e = normwise(values(d[start:start + c]), ref["D"][start:start + c])
+            assert e <= TOL[orc.BF16], f"group {g}: {e:.3e}"
+            assert abs(amax[g].item() - ref["amax"][g]) <= 1e-3 * ref["amax"][g]
+        start += c
+
+
+@pytest.mark.parametrize("c_dtype", [torch.float16, torch.float32])
+@pytest.mark.parametrize("d_dtype", [torch.float16, torch.float32])
+def test_dtypes(c_dtype, d_dtype):
+    inp = small(62, c_dtype=c_dtype)
+    d, dprob, amax, err = run_gpu(inp, d_dtype)
+    ref = run_oracle(inp, d_dtype)
+    vm = inp["valid_m"]
+    assert_close(values(d[:vm]), ref["D"][:vm], ORC_DT[d_dtype], "D_row")
+    assert_close(values(dprob[:vm]), ref["dprob"][:vm], orc.F32, "dprob")
+
+
+def test_unit_scales_no_amax():
+    inp = small(63, spread=0)
+    inp["sfa"] = torch.full_like(inp["sfa"], 127)
+    d, dprob, amax, err = run_gpu(inp, with_amax=False)
+    ref = run_oracle(inp)
+    vm = inp["valid_m"]
+    assert_close(values(d[:vm]), ref["D"][:vm], orc.BF16, "D_row")
+
+
+def test_workload_sampled():
+    w = synth.WORKLOADS["dsrelu_mxfp8"]
+    counts = synth.workload_counts("dsrelu_mxfp8")
+    inp = synth.dsrelu_inputs(w["L"], w["K"], w["N"], counts, seed=w["seed"], device="cuda")
+    say("dsrelu_mxfp8 counts", counts.tolist())
+    d, dprob, amax, err = run_gpu(inp)
+    assert err == 0
+    cpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    cpu["b_list"] = [x.cpu() for x in inp["b_list"]]
+    cpu["sfb_list"] = [x.cpu() for x in inp["sfb_list"]]
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    rows = []
+    for s, c in zip(starts, counts):
+        if c:
+            rows += [s, s + c - 1]
+    rows = np.array(sorted(set(rows)), np.int64)
+    ref = run_oracle(cpu, rows=rows)
+    assert_close(values(d[rows]), ref["D"], orc.BF16, "D_row (sampled rows)")
+    assert_close(values(dprob[rows]), ref["dprob"], orc.F32, "dprob (sampled rows)")
+    # Amax against the kernel's own D (bf16-rounded: within 2^-8 relative)
+    dv = np.abs(values(d))
+    for g, (s, c) in enumerate(zip(starts, counts)):
+        want = dv[s:s + c].max() if c else 0.0
+        assert abs(amax[g].item() - want) <= 2.0 ** -8 * max(want, 1e-30), (g, amax[g].item(), want)

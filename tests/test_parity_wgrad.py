@@ -1,0 +1,140 @@
+"""GPU parity of gg_wgrad against the oracle (through the C ABI).
+
+Cases span several 256x256 tiles, partial N tiles, ragged token counts
+(multiples of 8, not of 64), empty experts, all four operand majors, the
+three output dtypes, dense and pointer outputs, accumulate and overwrite;
+plus the 256x256 / 4-expert workload in full and the MoE-scale workload
+(hidden 4096, intermediate 2048, 64 Zipf experts) on sampled rows in the
+launch configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from moe_grouped_gemm_offset_amd import synth
+from tests.parity_util import TOL, assert_close, normwise, say, values
+
+pytestmark = pytest.mark.gpu
+
+MAJ = {"k": 0, "m": 1, "n": 2}
+
+
+def gg():
+    from moe_grouped_gemm_offset_amd import binding
+    binding.load_library()
+    return binding
+
+
+def run_gpu(inp, out_dtype, accumulate=False, old=None, discrete=False):
+    b = gg()
+    E = len(inp["counts"])
+    a, bb = inp["a"].cuda(), inp["b"].cuda()
+    off = inp["offsets"].cuda()
+    h, i = inp["hidden"], inp["inter"]
+    if discrete:
+        outs = [torch.empty(h, i, dtype=out_dtype, device="cuda") for _ in range(E)]
+        if accumulate:
+            for e in range(E):
+                outs[e].copy_(old[e])
+        ptrs = torch.tensor([o.data_ptr() for o in outs], dtype=torch.int64, device="cuda")
+        ws = b.gg_wgrad(a, MAJ[inp["a_major"]], bb, MAJ[inp["b_major"]], off, inp["tokens_sum"], h, i,
+                        wgrad_ptrs=ptrs, wgrad_dtype=b._TORCH_DTYPE[out_dtype], accumulate=accumulate)
+        torch.cuda.synchronize()
+        res = torch.stack(outs)
+    else:
+        res = old.clone().cuda() if accumulate else torch.full((E, h, i), float("nan"), dtype=out_dtype,
+                                                               device="cuda")
+        ws = b.gg_wgrad(a, MAJ[inp["a_major"]], bb, MAJ[inp["b_major"]], off, inp["tokens_sum"], h, i,
+                        wgrad_dense=res, accumulate=accumulate)
+        torch.cuda.synchronize()
+    return res.cpu(), b.gg_device_error(ws)
+
+
+def run_oracle(inp, out_dtype, accumulate=False, old=None, hrows=None):
+    od = {torch.float32: orc.F32, torch.bfloat16: orc.BF16, torch.float16: orc.F16}[out_dtype]
+    return orc.wgrad(synth.bits(inp["a"]), 0 if inp["a_major"] == "k" else 1, synth.bits(inp["b"]),
+                     0 if inp["b_major"] == "k" else 1, inp["offsets"].numpy(), inp["hidden"],
+                     inp["inter"], inp["tokens_sum"], out_dtype=od, accumulate=accumulate,
+                     old=None if old is None else synth.bits(old), hrows=hrows), od
+
+
+def compare(got, inp, out_dtype, accumulate=False, old=None, hrows=None, name=""):
+    (exact, _), od = run_oracle(inp, out_dtype, accumulate, old, hrows)
+    g = values(got if hrows is None else got[:, hrows, :])
+    assert_close(g, exact, od, f"{name} all experts")
+    for e, cnt in enumerate(inp["counts"]):
+        if cnt == 0 and not accumulate:
+            assert np.all(g[e] == 0), f"{name}: empty expert {e} not exactly zero"
+        elif cnt == 0 and accumulate:
+            want = values(old[e] if hrows is None else old[e][hrows])
+            assert np.array_equal(g[e], want), f"{name}: empty expert {e} changed in accumulate mode"
+        else:
+            err = normwise(g[e], exact[e])
+            assert err <= TOL[od], f"{name}: expert {e} normwise error {err:.3e}"
+
+
+def test_small_workload_exact():
+    """hidden 256, intermediate 256, counts [256, 0, 512, 256], fp32 dense,
+    overwrite: the full output, expert 1 exactly zero."""
+    w = synth.WORKLOADS["wgrad_small"]
+    inp = synth.wgrad_inputs(w["hidden"], w["inter"], w["counts"], w["a_major"], w["b_major"],
+                             seed=w["seed"])
+    say("wgrad_small", w["counts"])
+    got, err = run_gpu(inp, torch.float32)
+    assert err == 0
+    compare(got, inp, torch.float32, name="wgrad_small")
+
+
+@pytest.mark.parametrize("a_major", ["k", "m"])
+@pytest.mark.parametrize("b_major", ["k", "n"])
+def test_majors_ragged(a_major, b_major):
+    counts = [520, 0, 256, 72, 8, 320]
+    inp = synth.wgrad_inputs(512, 384, counts, a_major, b_major, seed=41)
+    say("ragged", a_major, b_major, counts)
+    got, err = run_gpu(inp, torch.float32)
+    assert err == 2  # GG_DEVERR_GRANULE: counts not multiples of 256 (still computed)
+    compare(got, inp, torch.float32, name=f"{a_major}{b_major}")
+
+
+def test_exact_integers_bit_exact():
+    counts = [256, 512, 0, 256]
+    inp = synth.wgrad_inputs(256, 320, counts, "m", "n", seed=42, ints=True)
+    got, _ = run_gpu(inp, torch.float32)
+    (exact, res), _ = run_oracle(inp, torch.float32)
+    assert np.array_equal(got.numpy(), res), "integer-valued wgrad must be bit-exact"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("discrete", [False, True])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_outputs_and_modes(dtype, discrete, accumulate):
+    counts = [256, 0, 768, 512]
+    inp = synth.wgrad_inputs(320, 256, counts, "m", "n", seed=43)
+    old = synth.wgrad_initial(len(counts), 320, 256, dtype, seed=44) if accumulate else None
+    say("modes", dtype, "discrete" if discrete else "dense", "acc" if accumulate else "overwrite")
+    got, err = run_gpu(inp, dtype, accumulate, old, discrete)
+    assert err == 0
+    compare(got, inp, dtype, accumulate, old, name=f"{dtype} {discrete} {accumulate}")
+
+
+def test_tokens_sum_zero():
+    inp = synth.wgrad_inputs(256, 256, [0, 0], "k", "n", seed=45)
+    got, err = run_gpu(inp, torch.bfloat16)
+    assert err == 0 and torch.all(got == 0)
+
+
+@pytest.mark.parametrize("a_major", ["k", "m"])
+def test_moe_scale_sampled(a_major):
+    """The MoE-scale workload, bf16 dense output, on the device; the oracle
+    checks sampled hidden rows of every expert."""
+    w = synth.WORKLOADS["wgrad_moe"]
+    counts = synth.workload_counts("wgrad_moe")
+    inp = synth.wgrad_inputs(w["hidden"], w["inter"], counts, a_major, w["b_major"],
+                             seed=w["seed"], device="cuda")
+    say("wgrad_moe", a_major, "experts", len(counts), "empty", int(np.sum(counts == 0)))
+    got, err = run_gpu(inp, torch.bfloat16)
+    assert err == 0
+    inp_cpu = dict(inp, a=inp["a"].cpu(), b=inp["b"].cpu(), offsets=inp["offsets"].cpu())
+    rows = np.array([0, 1, 255, 256, 2047, 2048, 4000, 4095], np.int32)
+    compare(got, inp_cpu, torch.bfloat16, hrows=rows, name="wgrad_moe")
