@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped MoE backward GEMMs on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic
+inputs already resident in HBM:
+
+  dswiglu       gg_dglu,   dSwiGLU, L 8,  K 2048, N 1024, M 16384, dense B
+  wgrad_moe     gg_wgrad,  hidden 4096, intermediate 2048, 64 experts,
+                           65536 tokens (Zipf 1.2), A M-major, B N-major,
+                           bf16 dense output, overwrite
+  dgeglu        gg_dglu,   dGeGLU, L 32, K 4096, N 1536, M 32768,
+                           discrete K-major B, dbias
+  dsrelu_mxfp8  gg_dsrelu, MXFP8, L 16, K 7168, N 2048, M 65536, dense B
+
+value = algorithmic FLOPs of the step (2 sum_e M_e N_e K_e per GEMM) over the
+measured wall time of K steps.  Every call is also bracketed by HIP events on
+the stream it runs on, which gives each kernel's average duration; the kernel
+with the largest share is reported against its MFMA roofline.  The CPU oracle
+is timed on a bounded sample of rows of the same workloads (cpu_baseline).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "fp8": 5000.0}        # MI355X dense MFMA, TFLOP/s
+HBM_PEAK = 8000.0                              # GB/s
+KERNEL_SOURCES = ["gg_tile.hpp", "gg_wgrad.hip", "gg_dglu.hip", "gg_dsrelu.hip",
+                  "gg_prologue.hip", "gg_api.cpp"]
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "moe_grouped_gemm_offset_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Op:
+    """One grouped-GEMM call of the step: inputs on the device and a run()."""
+
+    def __init__(self, name, kernel, flops, dtype, run, alg_bytes, oracle_sample):
+        self.name, self.kernel, self.flops, self.dtype = name, kernel, flops, dtype
+        self.run, self.alg_bytes, self.oracle_sample = run, alg_bytes, oracle_sample
+
+
+def _cpu(d):
+    import torch
+    out = {}
+    for k, v in d.items():
+        if isinstance(v, torch.Tensor):
+            out[k] = v.cpu()
+        elif isinstance(v, list) and v and isinstance(v[0], torch.Tensor):
+            out[k] = [x.cpu() for x in v]
+        else:
+            out[k] = v
+    return out
+
+
+def make_dglu(name, dev):
+    import numpy as np
+    import torch
+    from moe_grouped_gemm_offset_amd import binding as B, synth
+    from oracle import oracle as orc
+    w = synth.WORKLOADS[name]
+    counts = synth.workload_counts(name)
+    inp = synth.dglu_inputs(w["L"], w["K"], w["N"], counts, c_std=w["c_std"], seed=w["seed"],
+                            device=dev, discrete=w["discrete"])
+    M, N, K, L = inp["M"], inp["N"], inp["K"], inp["L"]
+    act = B.GG_DSWIGLU if w["act"] == "dswiglu" else B.GG_DGEGLU
+    bptrs = None
+    if inp["b_dense"] is None:
+        bptrs = torch.tensor([x.data_ptr() for x in inp["b_list"]], dtype=torch.int64, device=dev)
+    d = torch.empty(M, 2 * N, dtype=torch.bfloat16, device=dev)
+    dprob = torch.zeros(M, dtype=torch.float32, device=dev)
+    dbias = torch.zeros(L, 2 * N, dtype=torch.bfloat16, device=dev) if w["dbias"] else None
+    ws = torch.empty(B.gg_dglu_workspace_size(L, N, dbias is not None), dtype=torch.uint8, device=dev)
+
+    def run():
+        B.gg_dglu(inp["a"], inp["b_dense"], bptrs, B.GG_MAJOR_K, N, inp["c"], inp["padded_offsets"],
+                  inp["alpha"], inp["beta"], inp["prob"], d, dprob, dbias, act=act, workspace=ws)
+
+    vm = inp["valid_m"]
+    alg = 2 * (M * K + L * N * K + 2 * M * 2 * N) + 8 * M + (L * 2 * N * 4 if dbias is not None else 0)
+
+    def sample(nrows):
+        cpu = _cpu(inp)
+        rows = np.linspace(0, vm - 1, nrows).astype(np.int64)
+        t0 = time.perf_counter()
+        orc.dglu(synth.bits(cpu["a"]), M, K, [synth.bits(x) for x in cpu["b_list"]], 0, N,
+                 synth.bits(cpu["c"]), orc.BF16, cpu["padded_offsets"].numpy(), cpu["alpha"].numpy(),
+                 cpu["beta"].numpy(), cpu["prob"].numpy(), act=act, rows=rows)
+        return time.perf_counter() - t0, 2.0 * nrows * N * K
+
+    return Op(name, "dglu_kernel", synth.flops_dgrad(vm, N, K), "bf16", run, alg, sample)
+
+
+def make_wgrad(dev, a_major="m"):
+    import numpy as np
+    import torch
+    from moe_grouped_gemm_offset_amd import binding as B, synth
+    from oracle import oracle as orc
+    w = synth.WORKLOADS["wgrad_moe"]
+    counts = synth.workload_counts("wgrad_moe")
+    inp = synth.wgrad_inputs(w["hidden"], w["inter"], counts, a_major, w["b_major"], seed=w["seed"],
+                             device=dev)
+    E, h, i, T = len(counts), inp["hidden"], inp["inter"], inp["tokens_sum"]
+    out = torch.empty(E, h, i, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(B.gg_wgrad_workspace_size(E), dtype=torch.uint8, device=dev)
+    am = B.GG_MAJOR_K if a_major == "k" else B.GG_MAJOR_M
+
+    def run():
+        B.gg_wgrad(inp["a"], am, inp["b"], B.GG_MAJOR_N, inp["offsets"], T, h, i,
+                   wgrad_dense=out, workspace=ws)
+
+    alg = 2 * (h * T + T * i) + 2 * E * h * i
+
+    def sample(nrows):
+        cpu = _cpu(inp)
+        rows = np.linspace(0, h - 1, nrows).astype(np.int32)
+        t0 = time.perf_counter()
+        orc.wgrad(synth.bits(cpu["a"]), 0 if a_major == "k" else 1, synth.bits(cpu["b"]), 1,
+                  cpu["offsets"].numpy(), h, i, T, out_dtype=orc.BF16, hrows=rows)
+        return time.perf_counter() - t0, 2.0 * nrows * i * T
+
+    return Op("wgrad_moe", "wgrad_kernel", synth.flops_wgrad(h, i, counts), "bf16", run, alg, sample)
+
+
+def make_dsrelu(dev):
+    import numpy as np
+    import torch
+    from moe_grouped_gemm_offset_amd import binding as B, synth
+    from oracle import oracle as orc
+    w = synth.WORKLOADS["dsrelu_mxfp8"]
+    counts = synth.workload_counts("dsrelu_mxfp8")
+    inp = synth.dsrelu_inputs(w["L"], w["K"], w["N"], counts, seed=w["seed"], device=dev)
+    M, N, K, L = inp["M"], inp["N"], inp["K"], inp["L"]
+    d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    dprob = torch.zeros(M, dtype=torch.float32, device=dev)
+    amax = torch.zeros(L, dtype=torch.float32, device=dev)
+    ws = torch.empty(B.gg_dsrelu_workspace_size(L), dtype=torch.uint8, device=dev)
+    a8 = inp["a"].view(torch.uint8)
+    b8 = inp["b_dense"].view(torch.uint8)
+
+    def run():
+        B.gg_dsrelu(a8, inp["sfa"], b8, inp["sfb_dense"], None, None, N, inp["c"], inp["padded_offsets"],
+                    inp["alpha"], inp["prob"], d, dprob, amax, workspace=ws)
+
+    vm = inp["valid_m"]
+    alg = M * K + L * N * K + (M + L * N) * K // 32 + 2 * M * N * 2 + 8 * M
+
+    def sample(nrows):
+        cpu = _cpu(inp)
+        rows = np.linspace(0, vm - 1, nrows).astype(np.int64)
+        t0 = time.perf_counter()
+        orc.dsrelu(synth.bits(cpu["a"]), synth.bits(cpu["sfa"]), M, K,
+                   [synth.bits(x) for x in cpu["b_list"]], [synth.bits(x) for x in cpu["sfb_list"]],
+                   N, synth.bits(cpu["c"]), orc.BF16, cpu["padded_offsets"].numpy(),
+                   cpu["alpha"].numpy(), cpu["prob"].numpy(), rows=rows)
+        return time.perf_counter() - t0, 2.0 * nrows * N * K
+
+    return Op("dsrelu_mxfp8", "dsrelu_kernel", synth.flops_dgrad(vm, N, K), "fp8", run, alg, sample)
+
+
+WORKLOAD_OPS = {
+    "moe_backward": ["dswiglu", "wgrad_moe", "dgeglu", "dsrelu_mxfp8"],
+    "dswiglu": ["dswiglu"],
+    "wgrad_moe": ["wgrad_moe"],
+    "wgrad_moe_kmajor": ["wgrad_moe_kmajor"],
+    "dgeglu": ["dgeglu"],
+    "dsrelu_mxfp8": ["dsrelu_mxfp8"],
+}
+
+
+def build_op(name, dev):
+    if name in ("dswiglu", "dgeglu"):
+        return make_dglu(name, dev)
+    if name == "wgrad_moe":
+        return make_wgrad(dev, "m")
+    if name == "wgrad_moe_kmajor":
+        op = make_wgrad(dev, "k")
+        op.name = name
+        return op
+    return make_dsrelu(dev)
+
+
+def cpu_baseline(ops, budget_s):
+    """Oracle throughput on a bounded row sample of each op, extrapolated to
+    the step: total FLOPs over the sum of the projected per-op times."""
+    from oracle import oracle as orc
+    threads = orc.num_threads()
+    per = budget_s / len(ops)
+    proj, parts = 0.0, []
+    for op in ops:
+        t, f = op.oracle_sample(threads)                # calibration: one row per thread
+        rate = f / max(t, 1e-9)
+        n = max(threads, int(threads * max(1.0, per / max(t, 1e-9))))
+        t, f = op.oracle_sample(n)
+        rate = f / t
+        proj += op.flops / rate
+        parts.append(f"{op.name}: {n} rows, {t:.1f} s, {rate / 1e9:.2f} GFLOP/s")
+    total = sum(op.flops for op in ops)
+    return {"value": total / proj / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(parts) + " (rows spread over every group, extrapolated by FLOPs)"}
+
+
+def traffic_for(kernel, workload, src_hash):
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(f"{kernel}:{workload}")
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="moe_backward", choices=sorted(WORKLOAD_OPS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_grouped_gemm_offset_amd import binding as B
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    B.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
+    ops = [build_op(n, dev) for n in WORKLOAD_OPS[args.workload]]
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for op in ops:
+            op.run()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    ev = {op.name: [] for op in ops}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for op in ops:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            op.run()
+            e.record()
+            ev[op.name].append((s, e))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    kernels = {}
+    for op in ops:
+        ms = sum(s.elapsed_time(e) for s, e in ev[op.name]) / len(ev[op.name])
+        tf = op.flops / (ms * 1e-3) / 1e12
+        kernels[op.name] = {"kernel": op.kernel, "ms": round(ms, 4), "gflop": round(op.flops / 1e9, 2),
+                            "tflops": round(tf, 1), "peak_frac": round(tf / PEAK[op.dtype], 4),
+                            "dtype": op.dtype, "alg_gb_s": round(op.alg_bytes / (ms * 1e-3) / 1e9, 1)}
+    total_flops = sum(op.flops for op in ops)
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    dom = max(ops, key=lambda o: kernels[o.name]["ms"])
+    kd = kernels[dom.name]
+    achieved = dom.flops / (kd["ms"] * 1e-3) / 1e12
+    src = source_hash()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK[dom.dtype],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK[dom.dtype], 4),
+                "traffic": traffic_for(dom.kernel, dom.name, src), "kernel": dom.kernel,
+                "workload": dom.name, "source_hash": src}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a row sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(ops, args.cpu_budget)
+    dtypes = sorted({op.dtype for op in ops})
+    line = {
+        "metric": "grouped-GEMM TFLOP/s and % of MI355X bf16/fp8 MFMA peak, 1 GPU",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "+".join("bf16" if d == "bf16" else "mxfp8" for d in dtypes),
+        "data": "synthetic",
+        "config": {"workload": args.workload, "ops": [op.name for op in ops],
+                   "gflop_per_step": round(total_flops / 1e9, 1), "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,6 +29,10 @@ def flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             # no packed-fp32 instructions anywhere in this library
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # the fused epilogues walk every accumulator register with
+            # compile-time indices; without a higher limit LLVM leaves the
+            # loop rolled and demotes the accumulators to scratch memory
+            "-mllvm", "-pragma-unroll-threshold=1000000",
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 

@@ -8,25 +8,26 @@
 // and the per-expert Amax of |D_row| ("Shapes").
 //
 // Design: the M-grouped tiling of the dGLU kernel with 128 fp8 values of K
-// per LDS step.  The scales never go through LDS: for each K step every lane
-// loads the 32-bit word holding the four scale bytes of its fragment row and
-// shifts it so that the byte of the K block it feeds to
-// v_mfma_scale_f32_32x32x64_f8f6f4 sits in byte 0.  Both the data and the
-// scales of step k+1 are fetched before the MFMAs of step k.  The epilogue
-// applies alpha, relu, prob and C in registers, reduces dprob across lanes
-// (one atomic per row and wave) and Amax across the wave (one atomicMax on
-// the fp32 bit pattern, valid because |D| >= 0).
+// per LDS stage, fed to v_mfma_scale_f32_32x32x64_f8f6f4.  The scales never
+// go through LDS: with the data of step k+1, every lane also fetches the
+// 32-bit word holding the four scale bytes of each of its fragment rows; at
+// the top of step k+1 the word is shifted so that the byte of the K block the
+// lane feeds to the MFMA sits in byte 0.  The epilogue applies alpha, relu,
+// prob and C in registers, reduces dprob across lanes (one atomic per row
+// and wave) and Amax across the wave (one atomicMax on the fp32 bit pattern,
+// which orders like the value because |D| >= 0).
 #include "gg_internal.hpp"
 #include "gg_tile.hpp"
 #include "../../include/gg_moe.h"
 
 namespace gg {
 
-template <int TM, int TN>
-__global__ void __launch_bounds__(kThreads, 1) dsrelu_kernel(DsreluArgs p) {
-    constexpr int MB = TM / 64, NB = TN / 64;
-    constexpr int kBufBytes = (TM + TN) * kRowBytes;
-    __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+using DsreluCfg = Cfg<256, 256, 4, 2>;
+
+template <class C>
+__global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
+    constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
 
     const int tiles_n = (p.N + TN - 1) / TN;
     const int tiles_m = (int)((p.m_rows + TM - 1) / TM);
@@ -47,7 +48,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     const int cols_valid = p.N - n0;
 
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / C::WN, wn = w % C::WN;
+    const int am0 = wm * (TM / C::WM), bn0 = wn * (TN / C::WN);
     const int lr = l & 31, lh = l >> 5;
 
     f32x16 acc[MB][NB];
@@ -64,27 +66,25 @@ __global__ void __launch_bounds__(kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                                : (const char*)p.b_ptrs[g] + (int64_t)n0 * K;
     const char* sfb = p.sfb_dense ? (const char*)p.sfb_dense + ((int64_t)g * p.N + n0) * KB
                                   : (const char*)p.sfb_ptrs[g] + (int64_t)n0 * KB;
-    KLoader<TM> la;
-    KLoader<TN> lb;
-    uint32_t swa[MB], swb[NB];                 // raw scale words of the next step
-    auto load = [&](int kt) {
-        la.load(a, K, rows_valid, (int64_t)kt * 128, K);
-        lb.load(bg, K, cols_valid, (int64_t)kt * 128, K);
+    uint32_t swa[MB], swb[NB];                 // raw scale words, prefetched one step ahead
+    uint32_t sa[2][MB], sb[2][NB];             // per sub-step, byte 0 = this lane's block
+    auto issue = [&](char* st, int kt) {
+        stage_k<C, TM>(st, a, K, rows_valid, (int64_t)kt * 128, K);
+        stage_k<C, TN>(st + TM * kRowBytes, bg, K, cols_valid, (int64_t)kt * 128, K);
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(sfa + kt * 4);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(sfb + kt * 4);
 #pragma unroll
         for (int i = 0; i < MB; i++) {
-            const int r = wm * (TM / 2) + 32 * i + lr;
+            const int r = am0 + 32 * i + lr;
             swa[i] = buf_load4(ra, r < rows_valid ? (uint32_t)(r * KB) : kInvalid);
         }
 #pragma unroll
         for (int j = 0; j < NB; j++) {
-            const int r = wn * (TN / 2) + 32 * j + lr;
+            const int r = bn0 + 32 * j + lr;
             swb[j] = buf_load4(rb, r < cols_valid ? (uint32_t)(r * KB) : kInvalid);
         }
     };
-    uint32_t sa[2][MB], sb[2][NB];             // per sub-step, byte 0 = this lane's block
-    auto take_scales = [&]() {
+    auto begin = [&](int) {
 #pragma unroll
         for (int i = 0; i < MB; i++) {
             sa[0][i] = swa[i] >> (8 * lh);
@@ -96,26 +96,10 @@ __global__ void __launch_bounds__(kThreads, 1) dsrelu_kernel(DsreluArgs p) {
             sb[1][j] = swb[j] >> (16 + 8 * lh);
         }
     };
-    const int nk = p.K / 128;
-    load(0);
-    la.store(smem);
-    lb.store(smem + TM * kRowBytes);
-    take_scales();
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-        char* cur = smem + (kt & 1) * kBufBytes;
-        char* nxt = smem + ((kt + 1) & 1) * kBufBytes;
-        const bool more = kt + 1 < nk;
-        if (more)
-            load(kt + 1);
-        mfma_step_mx8<MB, NB>(cur, cur + TM * kRowBytes, wm * (TM / 2), wn * (TN / 2), sa, sb, acc);
-        if (more) {
-            la.store(nxt);
-            lb.store(nxt + TM * kRowBytes);
-            take_scales();
-        }
-        __syncthreads();
-    }
+    auto compute = [&](char* st, int) {
+        mfma_stage_mx8<C>(st, st + TM * kRowBytes, am0, bn0, sa, sb, acc);
+    };
+    mainloop<C>(smem, p.K / 128, issue, compute, begin);
 
     // ---------------- epilogue ----------------
     const float al = p.alpha[g];
@@ -129,24 +113,23 @@ __global__ void __launch_bounds__(kThreads, 1) dsrelu_kernel(DsreluArgs p) {
             rowsum[i][r] = 0.0f;
 #pragma unroll
     for (int j = 0; j < NB; j++) {
-        const int col = n0 + wn * (TN / 2) + 32 * j + lr;
-        if (n0 + wn * (TN / 2) + 32 * j >= p.N)
-            continue;
+        const int col = n0 + bn0 + 32 * j + lr;
+        const bool jok = n0 + bn0 + 32 * j < p.N;
 #pragma unroll
         for (int i = 0; i < MB; i++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int rr = wm * (TM / 2) + 32 * i + acc_row(r, l);
-                if (rr >= rows_valid)
-                    continue;
-                const int64_t row = m0 + rr;
-                const float G = al * acc[i][j][r];
-                const float rl = fmaxf(G, 0.0f);
-                const float c = load_elem(p.c, p.c_dtype, row * N + col);
-                const float d = p.prob[row] * 2.0f * c * rl;
-                rowsum[i][r] += c * rl * rl;
-                amax = fmaxf(amax, fabsf(d));
-                store_elem(p.d, p.d_dtype, row * N + col, d);
+                const int rr = am0 + 32 * i + acc_row(r, l);
+                if (jok && rr < rows_valid) {
+                    const int64_t row = m0 + rr;
+                    const float G = al * acc[i][j][r];
+                    const float rl = fmaxf(G, 0.0f);
+                    const float c = load_elem(p.c, p.c_dtype, row * N + col);
+                    const float d = p.prob[row] * 2.0f * c * rl;
+                    rowsum[i][r] += c * rl * rl;
+                    amax = fmaxf(amax, fabsf(d));
+                    store_elem(p.d, p.d_dtype, row * N + col, d);
+                }
             }
     }
 #pragma unroll
@@ -159,8 +142,8 @@ __global__ void __launch_bounds__(kThreads, 1) dsrelu_kernel(DsreluArgs p) {
             v += __shfl_xor(v, 4);
             v += __shfl_xor(v, 8);
             v += __shfl_xor(v, 16);
-            const int rr = wm * (TM / 2) + 32 * i + acc_row(r, l);
-            if (lr == 0 && rr < rows_valid && n0 + wn * (TN / 2) < p.N)
+            const int rr = am0 + 32 * i + acc_row(r, l);
+            if (lr == 0 && rr < rows_valid && n0 + bn0 < p.N)
                 atomicAdd(p.dprob + m0 + rr, v);
         }
     if (p.amax) {
@@ -172,15 +155,13 @@ __global__ void __launch_bounds__(kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     }
 }
 
-template <int TM, int TN>
-static hipError_t launch_dsrelu_t(const DsreluArgs& p, hipStream_t s) {
-    const int64_t tiles = ((p.m_rows + TM - 1) / TM) * ((p.N + TN - 1) / TN);
+hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s) {
+    using C = DsreluCfg;
+    const int64_t tiles = ((p.m_rows + C::TM - 1) / C::TM) * ((p.N + C::TN - 1) / C::TN);
     if (tiles == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((dsrelu_kernel<TM, TN>), dim3((unsigned)tiles), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((dsrelu_kernel<C>), dim3((unsigned)tiles), dim3(C::kThreads), 0, s, p);
     return hipGetLastError();
 }
-
-hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s) { return launch_dsrelu_t<256, 256>(p, s); }
 
 }  // namespace gg

@@ -1,18 +1,31 @@
 // gg_tile.hpp -- device building blocks shared by the gfx950 grouped-GEMM
-// kernels: MFMA fragment types, the swizzled LDS tile layout, global->LDS
-// tile loaders (K-contiguous sources copied, MN-contiguous sources transposed
-// in registers), and the work-item remap that keeps neighbouring tiles on one
-// XCD.
+// kernels: MFMA fragment types, the LDS stage layouts, global->LDS stage
+// loaders, fragment readers, the pipelined MFMA main loop, and the work-item
+// remap that keeps neighbouring tiles on one XCD.
 //
-// Geometry used throughout:
-//   * a workgroup is 256 threads = 4 wave64s arranged 2 x 2 over the
-//     TM x TN macro tile; each wave owns (TM/2) x (TN/2) as 32x32 MFMA blocks;
-//   * one K step stages 128 bytes of every tile row in LDS (64 bf16 or
-//     128 fp8 values), double-buffered;
-//   * an LDS tile row is 8 chunks of 16 bytes; chunk c of row r is stored at
-//     chunk position c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 7, so that the
-//     MFMA fragment reads (8 consecutive rows, one chunk) and the transposed
-//     stores (rows 8 apart, one chunk) both hit 8 distinct 16-byte bank groups.
+// Geometry (Cfg below): a TM x TN macro tile per workgroup, WM x WN wave64s,
+// each wave owning (TM/WM) x (TN/WN) as 32x32 MFMA blocks.  One K step
+// stages 128 bytes of K (64 bf16 or 128 fp8 values) of every tile row;
+// two stages alternate in LDS.
+//
+// Global -> LDS: buffer loads that write LDS directly (no register staging).
+// One wave instruction moves 1 KiB: lane l's 16 bytes land at base + 16 l.
+// Each lane therefore computes which global 16 bytes belong at its LDS slot.
+// An offset past the descriptor's range loads zeros, which masks rows past
+// the tile edge and K past a group's end.
+//
+// LDS stage layouts:
+//  * K-contiguous operand ("K layout"): tile row r holds 128 bytes of K as 8
+//    chunks of 16 bytes; chunk c sits at chunk position c ^ swz(r),
+//    swz(r) = (r ^ (r >> 3)) & 7.  MFMA fragments are 16-byte reads.
+//  * M/N-contiguous bf16 operand ("MN layout", 256 columns): K row k holds
+//    the tile's 256 columns as 32 units of 16 bytes; unit u sits at position
+//    u ^ (4 (k & 3)).  Fragments are read with ds_read_b64_tr_b16: within a
+//    16-lane group, lane 4q + j receives element j of the 8-byte pieces
+//    addressed by lanes q, 4+q, 8+q, 12+q; when lane 4e + q addresses K row
+//    kb + e at columns c + 4q, lane i gets column c + i at K rows kb..kb+3 --
+//    the K-contiguous register fragment the MFMA needs.
+// Both layouts read without bank conflicts (64 banks of 4 bytes).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,9 +36,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;   // bytes of one LDS tile row per K step
+#define GG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int kRowBytes = 128;   // bytes of one K-layout tile row per K step
+
+template <int TM_, int TN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+    static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+    static constexpr int MB = TM / WM / 32, NB = TN / WN / 32;   // MFMA blocks per wave
+    static constexpr int kStage = (TM + TN) * kRowBytes;         // bytes per LDS stage
+    static constexpr int kLds = 2 * kStage;
+};
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
@@ -37,24 +61,13 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * kRowBytes + ((chunk ^ swz(row)) << 4);
 }
 
-__device__ __forceinline__ u32x4 ld_global16(const void* p) {
-    return *reinterpret_cast<const u32x4*>(p);
-}
-
-__device__ __forceinline__ void st_lds16(char* lds, int off, u32x4 v) {
-    *reinterpret_cast<u32x4*>(lds + off) = v;
-}
-
 __device__ __forceinline__ u32x4 ld_lds16(const char* lds, int off) {
     return *reinterpret_cast<const u32x4*>(lds + off);
 }
 
 // ---------------------------------------------------------------------------
-// Buffer loads: the descriptor (scalar registers) holds a base that the
-// caller advances per K step; each thread supplies a 32-bit byte offset.
-// An offset of kInvalid lies past num_records, and the hardware returns
-// zeros for it -- that is how masked rows and ragged K tails are zero-filled.
-// Valid offsets stay far below 2^31 because every base is tile-relative.
+// Buffer descriptors: a scalar base advanced per K step; 32-bit offsets per
+// lane.  kInvalid lies past num_records: such loads return (or write) zeros.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kInvalid = 0x80000000u;
 
@@ -63,195 +76,211 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                              0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// ---------------------------------------------------------------------------
-// Loader for a source whose K axis is contiguous.  `tile` points at the
-// tile's first row at K byte 0; tile row r is `ld` bytes further per row.
-// A K step covers bytes [kbyte, kbyte + 128) of each row.  Thread t moves
-// chunk t&7 of rows (t>>3) + 32 i.  Rows at or past `rows_valid` (counted
-// from the tile's first row) and chunks at or past `kbytes_valid` read as
-// zero.
-// ---------------------------------------------------------------------------
-template <int R>
-struct KLoader {
-    static constexpr int N = R / 32;
-    u32x4 v[N];
-
-    __device__ __forceinline__ void load(const char* tile, int64_t ld_bytes, int rows_valid,
-                                         int64_t kbyte, int64_t kbytes_valid) {
-        const int t = threadIdx.x;
-        const int c = t & 7;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile + kbyte);
-        const bool cvalid = kbyte + c * 16 < kbytes_valid;
-#pragma unroll
-        for (int i = 0; i < N; i++) {
-            const int r = (t >> 3) + 32 * i;
-            const uint32_t off = (uint32_t)(r * ld_bytes) + c * 16;
-            v[i] = buf_load16(rs, (cvalid & (r < rows_valid)) ? off : kInvalid);
-        }
-    }
-
-    __device__ __forceinline__ void store(char* lds) const {
-        const int t = threadIdx.x;
-        const int c = t & 7;
-#pragma unroll
-        for (int i = 0; i < N; i++)
-            st_lds16(lds, lds_off((t >> 3) + 32 * i, c), v[i]);
-    }
-};
-
-// Pack the low (or high) 16-bit halves of two words: result = {b.h, a.h}.
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+// LDS byte address of a pointer into workgroup memory.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
-// ---------------------------------------------------------------------------
-// Loader for a 16-bit source whose M (or N) axis is contiguous: global row
-// k holds the tile's R rows side by side.  Thread t owns an 8 (k) x 8 (m)
-// block: it reads 8 global rows of 16 bytes, transposes the 8x8 block of
-// 16-bit values in registers, and writes 8 K-contiguous chunks to LDS.
-// `tile` points at global row 0 of this K step's first k and at the tile's
-// first column.  K rows at or past `k_rows_valid` (counted from that k) and
-// columns at or past `cols_valid` (counted from the tile's first column)
-// read as zero.
-// ---------------------------------------------------------------------------
-template <int R>
-struct MNLoader16 {
-    static constexpr int kBlocksM = R / 8;                  // 8-wide m blocks
-    static constexpr int kBlocks = kBlocksM * 8;            // x 8 k blocks of 8
-    static constexpr int N = (kBlocks + kThreads - 1) / kThreads;
-    u32x4 v[N][8];
+// The LDS-writing buffer load is issued through inline assembly: the
+// compiler neither sees nor waits for it, so reads of the other stage are
+// not held back.  Completion is awaited explicitly (wait_vm0) before the
+// barrier that hands the stage to the MFMA waves.  M0 holds the wave's LDS
+// base; lane l writes base + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(uniform((int)lds_addr(lds))), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
 
-    __device__ __forceinline__ void load(const char* tile, int64_t ld_bytes, int cols_valid,
+// s_waitcnt vmcnt(0): every outstanding vector memory operation of this
+// wave, including the LDS-writing loads, has completed.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// ---------------------------------------------------------------------------
+// Stage loaders.
+// K layout, R rows: `tile` is the global address of the tile's row 0 at K
+// byte 0, rows `ld` bytes apart; this K step covers bytes [kbyte, kbyte+128).
+// Rows at or past rows_valid and K bytes at or past kbytes_valid load zeros.
+// ---------------------------------------------------------------------------
+template <class C, int R>
+__device__ __forceinline__ void stage_k(char* lds, const char* tile, int64_t ld, int rows_valid,
+                                        int64_t kbyte, int64_t kbytes_valid) {
+    constexpr int kBlocks = R / 8;                       // 1 KiB blocks of 8 rows
+    static_assert(kBlocks % C::kWaves == 0, "blocks must split evenly over waves");
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile + kbyte);
+#pragma unroll
+    for (int i = 0; i < kBlocks / C::kWaves; i++) {
+        const int b = w * (kBlocks / C::kWaves) + i;
+        const int row = 8 * b + (l >> 3);
+        const int c = (l & 7) ^ swz(row);
+        const bool ok = (row < rows_valid) & (kbyte + c * 16 < kbytes_valid);
+        dma16(rs, lds + b * 1024, ok ? (uint32_t)(row * ld) + c * 16 : kInvalid);
+    }
+}
+
+// MN layout (bf16, 256 columns, 64 K rows): `tile` is the global address of
+// this K step's first K row at the tile's first column; K rows are `ld` bytes
+// apart.  K rows at or past k_rows_valid and columns at or past cols_valid
+// load zeros.
+template <class C>
+__device__ __forceinline__ void stage_mn(char* lds, const char* tile, int64_t ld, int cols_valid,
                                          int64_t k_rows_valid) {
-        const int t = threadIdx.x;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile);
+    constexpr int kBlocks = 32;                          // 1 KiB = 2 K rows of 512 B
+    static_assert(kBlocks % C::kWaves == 0, "blocks must split evenly over waves");
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile);
 #pragma unroll
-        for (int i = 0; i < N; i++) {
-            const int blk = t + i * kThreads;
-            if (kBlocks % kThreads != 0 && blk >= kBlocks)
-                break;
-            const int mb = blk % kBlocksM, kb = blk / kBlocksM;
-            const bool cvalid = mb * 8 < cols_valid;
-#pragma unroll
-            for (int r = 0; r < 8; r++) {
-                const int k = kb * 8 + r;
-                const uint32_t off = (uint32_t)(k * ld_bytes) + mb * 16;
-                v[i][r] = buf_load16(rs, (cvalid & (k < k_rows_valid)) ? off : kInvalid);
-            }
-        }
+    for (int i = 0; i < kBlocks / C::kWaves; i++) {
+        const int b = w * (kBlocks / C::kWaves) + i;
+        const int k = 2 * b + (l >> 5);
+        const int u = (l & 31) ^ (4 * (k & 3));
+        const bool ok = (k < k_rows_valid) & (u * 8 < cols_valid);
+        dma16(rs, lds + b * 1024, ok ? (uint32_t)(k * ld) + u * 16 : kInvalid);
     }
-
-    __device__ __forceinline__ void store(char* lds) const {
-        const int t = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < N; i++) {
-            const int blk = t + i * kThreads;
-            if (kBlocks % kThreads != 0 && blk >= kBlocks)
-                break;
-            const int mb = blk % kBlocksM, kb = blk / kBlocksM;
-            // word w of v[r] holds m = 2w (low half) and 2w+1 (high half);
-            // output chunk for m holds k = 0..7 as words (k0,k1) .. (k6,k7).
-#pragma unroll
-            for (int w = 0; w < 4; w++) {
-                u32x4 lo, hi;
-                lo.x = pack_lo(v[i][0][w], v[i][1][w]);
-                lo.y = pack_lo(v[i][2][w], v[i][3][w]);
-                lo.z = pack_lo(v[i][4][w], v[i][5][w]);
-                lo.w = pack_lo(v[i][6][w], v[i][7][w]);
-                hi.x = pack_hi(v[i][0][w], v[i][1][w]);
-                hi.y = pack_hi(v[i][2][w], v[i][3][w]);
-                hi.z = pack_hi(v[i][4][w], v[i][5][w]);
-                hi.w = pack_hi(v[i][6][w], v[i][7][w]);
-                st_lds16(lds, lds_off(mb * 8 + 2 * w, kb), lo);
-                st_lds16(lds, lds_off(mb * 8 + 2 * w + 1, kb), hi);
-            }
-        }
-    }
-};
+}
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA over one staged K step (64 values = 4 sub-steps of 16).
-// Fragment of block i: lane l reads row base + 32 i + (l & 31), chunk
-// 2 ks + (l >> 5): the K layout of v_mfma_f32_32x32x16_bf16 (row l%32, eight
-// consecutive K values starting at 8 (l/32)).
+// Fragment readers (bf16, v_mfma_f32_32x32x16_bf16: lane l supplies row / col
+// l % 32 with K values 8 (l / 32) .. 8 (l / 32) + 7 of the 16-value sub-step).
 // ---------------------------------------------------------------------------
-template <int MB, int NB>
-__device__ __forceinline__ void mfma_step_bf16(const char* sa, const char* sb, int arow0,
-                                               int brow0, f32x16 (&acc)[MB][NB]) {
+__device__ __forceinline__ bf16x8 frag_k(const char* lds, int row0, int ks) {
     const int l = threadIdx.x & 63;
-    const int lr = l & 31, lh = l >> 5;
+    return __builtin_bit_cast(bf16x8, ld_lds16(lds, lds_off(row0 + (l & 31), 2 * ks + (l >> 5))));
+}
+
+__device__ __forceinline__ int mn_addr(int k, int col) {
+    const int u = col >> 3;
+    return k * 512 + ((u ^ (4 * (k & 3))) << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ bf16x8 frag_mn(const char* lds, int col0, int ks) {
+    const int l = threadIdx.x & 63;
+    const int g = l >> 4, s = l & 15;
+    const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+    const int k = 16 * ks + 8 * (g >> 1) + (s >> 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)GG_LDS(lds + mn_addr(k, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)GG_LDS(lds + mn_addr(k + 4, col)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ bf16x8 frag_bf16(const char* lds, int base, int ks) {
+    if constexpr (KMAJOR)
+        return frag_k(lds, base, ks);
+    else
+        return frag_mn(lds, base, ks);
+}
+
+// One staged K step of bf16 MFMAs (4 sub-steps of 16); fragments of sub-step
+// ks+1 are read while the MFMAs of ks run.
+template <class C, bool A_K, bool B_K>
+__device__ __forceinline__ void mfma_stage_bf16(const char* sa, const char* sb, int a0, int b0,
+                                                f32x16 (&acc)[C::MB][C::NB]) {
+    bf16x8 af[2][C::MB], bfr[2][C::NB];
+    auto read = [&](int ks, int buf) {
+#pragma unroll
+        for (int i = 0; i < C::MB; i++)
+            af[buf][i] = frag_bf16<A_K>(sa, a0 + 32 * i, ks);
+#pragma unroll
+        for (int j = 0; j < C::NB; j++)
+            bfr[buf][j] = frag_bf16<B_K>(sb, b0 + 32 * j, ks);
+    };
+    read(0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-        bf16x8 af[MB], bfr[NB];
+        const int cur = ks & 1;
+        if (ks + 1 < 4)
+            read(ks + 1, cur ^ 1);
 #pragma unroll
-        for (int i = 0; i < MB; i++) {
-            u32x4 x = ld_lds16(sa, lds_off(arow0 + 32 * i + lr, 2 * ks + lh));
-            af[i] = __builtin_bit_cast(bf16x8, x);
-        }
+        for (int i = 0; i < C::MB; i++)
 #pragma unroll
-        for (int j = 0; j < NB; j++) {
-            u32x4 x = ld_lds16(sb, lds_off(brow0 + 32 * j + lr, 2 * ks + lh));
-            bfr[j] = __builtin_bit_cast(bf16x8, x);
-        }
+            for (int j = 0; j < C::NB; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
+                                                                    0, 0, 0);
+    }
+}
+
+// One staged K step of MX-scaled fp8 MFMAs (2 sub-steps of 64).
+// v_mfma_scale_f32_32x32x64_f8f6f4: lane l (row l%32, h = l/32) supplies K
+// bytes [16h, 16h+16) and [32+16h, 32+16h+16) of the sub-step, and the E8M0
+// scale of K block h of its row in byte 0 of its scale operand (op_sel 0).
+// sa_w[ks][i] / sb_w[ks][j] hold, per sub-step and fragment, the scale word
+// already shifted so that byte 0 is block 2 ks + h.
+template <class C>
+__device__ __forceinline__ void mfma_stage_mx8(const char* sa, const char* sb, int a0, int b0,
+                                               const uint32_t (&sa_w)[2][C::MB],
+                                               const uint32_t (&sb_w)[2][C::NB],
+                                               f32x16 (&acc)[C::MB][C::NB]) {
+    const int l = threadIdx.x & 63;
+    const int lr = l & 31, lh = l >> 5;
+    i32x8 af[2][C::MB], bfr[2][C::NB];
+    auto frag = [&](const char* s, int r, int ks) {
+        const u32x4 x0 = ld_lds16(s, lds_off(r, 4 * ks + lh));
+        const u32x4 x1 = ld_lds16(s, lds_off(r, 4 * ks + 2 + lh));
+        return i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    };
+    auto read = [&](int ks) {
 #pragma unroll
-        for (int i = 0; i < MB; i++)
+        for (int i = 0; i < C::MB; i++)
+            af[ks][i] = frag(sa, a0 + 32 * i + lr, ks);
 #pragma unroll
-            for (int j = 0; j < NB; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < C::NB; j++)
+            bfr[ks][j] = frag(sb, b0 + 32 * j + lr, ks);
+    };
+    read(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+        if (ks == 0)
+            read(1);
+#pragma unroll
+        for (int i = 0; i < C::MB; i++)
+#pragma unroll
+            for (int j = 0; j < C::NB; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0, (int)sa_w[ks][i], 0, (int)sb_w[ks][j]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// MX-scaled fp8 MFMA over one staged K step (128 values = 2 sub-steps of 64).
-// v_mfma_scale_f32_32x32x64_f8f6f4: lane l (row l%32, h = l/32) supplies K
-// bytes [16h, 16h+16) and [32+16h, 32+16h+16) of the 64-value sub-step, and
-// the E8M0 scale of K block h of its row (scale byte selected by op_sel).
-// sA_w[ks][i] / sB_w[ks][j]: per sub-step and fragment, the 32-bit word of
-// this K step's four scale bytes shifted right so that byte 0 is the scale of
-// K block 2 ks + h (op_sel 0 then picks it).
+// Pipelined main loop over nk K steps.  issue(stage, kt) queues the direct
+// LDS loads of step kt into `stage`; compute(stage) runs the MFMAs of a
+// staged step.  The loads of step kt+1 are in flight while step kt computes;
+// one wait + barrier per step hands the stage over.
 // ---------------------------------------------------------------------------
-template <int MB, int NB>
-__device__ __forceinline__ void mfma_step_mx8(const char* sa, const char* sb, int arow0, int brow0,
-                                              const uint32_t (&sA_w)[2][MB], const uint32_t (&sB_w)[2][NB],
-                                              f32x16 (&acc)[MB][NB]) {
-    const int l = threadIdx.x & 63;
-    const int lr = l & 31, lh = l >> 5;
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-        i32x8 af[MB], bfr[NB];
-#pragma unroll
-        for (int i = 0; i < MB; i++) {
-            const int r = arow0 + 32 * i + lr;
-            u32x4 x0 = ld_lds16(sa, lds_off(r, 4 * ks + lh));
-            u32x4 x1 = ld_lds16(sa, lds_off(r, 4 * ks + 2 + lh));
-            af[i] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        }
-#pragma unroll
-        for (int j = 0; j < NB; j++) {
-            const int r = brow0 + 32 * j + lr;
-            u32x4 x0 = ld_lds16(sb, lds_off(r, 4 * ks + lh));
-            u32x4 x1 = ld_lds16(sb, lds_off(r, 4 * ks + 2 + lh));
-            bfr[j] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                           (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        }
-#pragma unroll
-        for (int i = 0; i < MB; i++)
-#pragma unroll
-            for (int j = 0; j < NB; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[i], bfr[j], acc[i][j], 0, 0, 0, (int)sA_w[ks][i], 0, (int)sB_w[ks][j]);
+// begin(kt) runs at the top of step kt, before the loads of step kt+1 are
+// queued (dsReLU uses it to take the scale words prefetched for step kt).
+struct NoBegin {
+    __device__ void operator()(int) const {}
+};
+
+template <class C, class Issue, class Compute, class Begin = NoBegin>
+__device__ __forceinline__ void mainloop(char* smem, int nk, Issue issue, Compute compute,
+                                         Begin begin = Begin()) {
+    if (nk <= 0)
+        return;
+    issue(smem, 0);
+    wait_vm0();
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt++) {
+        char* cur = smem + (kt & 1) * C::kStage;
+        char* nxt = smem + ((kt + 1) & 1) * C::kStage;
+        begin(kt);
+        if (kt + 1 < nk)
+            issue(nxt, kt + 1);
+        compute(cur, kt);
+        wait_vm0();
+        __syncthreads();
     }
 }
 

@@ -26,8 +26,12 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
+
+/* Threads the OpenMP loops of this file use (reported with its timings). */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* dtype codes used by this file (its own numbering) */
 enum { ORC_BF16 = 0, ORC_F16 = 1, ORC_F32 = 2 };

@@ -65,8 +65,15 @@ def lib():
         L.orc_dsrelu.argtypes = [P, P, I64, I, P, P, I, P, I, P, I, P, P,
                                  P, I64, P, P, P]
         L.orc_dsrelu.restype = None
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = I
         _lib = L
     return _lib
+
+
+def num_threads():
+    """Threads the oracle's OpenMP loops use."""
+    return lib().orc_num_threads()
 
 
 def _p(a):
