@@ -33,6 +33,10 @@ def flags():
             # compile-time indices; without a higher limit LLVM leaves the
             # loop rolled and demotes the accumulators to scratch memory
             "-mllvm", "-pragma-unroll-threshold=1000000",
+            # buffers are reinterpreted (bf16/fp8 bytes as 32-bit words, LDS
+            # staging written as floats and read as vectors): no type-based
+            # alias assumptions
+            "-fno-strict-aliasing",
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 

@@ -15,7 +15,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/gg_moe.h"
+#include "gg_moe.h"
 #include "gg_internal.hpp"
 
 namespace {

@@ -20,7 +20,7 @@
 // into the bf16 dbias.
 #include "gg_internal.hpp"
 #include "gg_tile.hpp"
-#include "../../include/gg_moe.h"
+#include "gg_moe.h"
 
 namespace gg {
 
@@ -87,91 +87,95 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
     mainloop<C>(smem, p.K / 64, issue, compute);
 
     // ---------------- epilogue ----------------
+    // Rows of 8 compact columns per lane: the 8 input and 8 gate columns of C
+    // and D are each one 16-byte access (32 for fp32).
     const float al = p.alpha[g];
     const float a2 = al * al;
     const float bet = p.beta[g];
     const int64_t N2 = 2 * (int64_t)p.N;
-    const int lr = l & 31;
-    float rowsum[MB][16];
-#pragma unroll
-    for (int i = 0; i < MB; i++)
-#pragma unroll
-        for (int r = 0; r < 16; r++)
-            rowsum[i][r] = 0.0f;
     float* dbias_ws = p.dbias ? (float*)((char*)p.ws + kWsHeader) + (int64_t)g * N2 : nullptr;
-
+    float rowsum[8], bs_in[8], bs_gt[8];
 #pragma unroll
-    for (int j = 0; j < NB; j++) {
-        const int nblk = n0 + bn0 + 32 * j;   // compact block start
-        const bool jok = nblk < p.N;
-        const int64_t pair = nblk / 32;
-        const int64_t c_in = 64 * pair + (p.gate_first ? 32 : 0) + lr;
-        const int64_t c_gt = 64 * pair + (p.gate_first ? 0 : 32) + lr;
-        float bsum_in = 0.0f, bsum_gt = 0.0f;
+    for (int k = 0; k < 8; k++)
+        rowsum[k] = bs_in[k] = bs_gt[k] = 0.0f;
+    for_each_row8<C>(acc, (float*)(smem + w * kEpiWaveBytes), [&](int t, int r, int c, float (&v)[8]) {
+        const int rr = am0 + r;
+        const int n = n0 + bn0 + c;                     // first compact column
+        const int64_t c_in = 64 * (int64_t)(n / 32) + (p.gate_first ? 32 : 0) + n % 32;
+        const int64_t c_gt = 64 * (int64_t)(n / 32) + (p.gate_first ? 0 : 32) + n % 32;
+        if (rr < rows_valid && n < p.N) {
+            const int64_t row = m0 + rr;
+            float xin[8], xgt[8], din[8], dgt[8];
+            load8(p.c, p.c_dtype, row * N2 + c_in, xin);
+            load8(p.c, p.c_dtype, row * N2 + c_gt, xgt);
+            const float pr = p.prob[row];
 #pragma unroll
-        for (int i = 0; i < MB; i++) {
+            for (int k = 0; k < 8; k++) {
+                const float R = a2 * v[k];
+                const float u = scaled_x(bet, xin[k]);
+                const float gt = scaled_x(bet, xgt[k]);
+                const float Rp = R * pr;
+                float act;
+                if (p.act == 0) {
+                    const float s = sigmoidf_(gt);
+                    din[k] = Rp * gt * s;
+                    dgt[k] = Rp * u * s * (1.0f + gt * (1.0f - s));
+                    act = gt * s * u;
+                } else {
+                    const float gc = fminf(gt, p.clamp_max);
+                    const float uc = fminf(fmaxf(u, p.clamp_min), p.clamp_max);
+                    const bool g_in = gt <= p.clamp_max;
+                    const bool u_in = (u >= p.clamp_min) & (u <= p.clamp_max);
+                    const float gf = g_in ? (p.mask_filter ? 1.0f : gt) : 0.0f;
+                    const float uf = u_in ? (p.mask_filter ? 1.0f : u) : 0.0f;
+                    const float s = sigmoidf_(p.geglu_alpha * gc);
+                    const float ul = uc + p.linear_offset;
+                    dgt[k] = Rp * ul * s * (1.0f + p.geglu_alpha * gc * (1.0f - s)) * gf;
+                    din[k] = Rp * gc * s * uf;
+                    act = gc * s * ul;
+                }
+                rowsum[t] += R * act;
+                bs_in[k] += din[k];
+                bs_gt[k] += dgt[k];
+            }
+            store8(p.d, p.d_dtype, row * N2 + c_in, din);
+            store8(p.d, p.d_dtype, row * N2 + c_gt, dgt);
+        }
+        if (t == 7 && dbias_ws) {
+            // column sums over the wave's 64 rows: lanes sharing l & 7 hold
+            // the same 8 columns
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int rr = am0 + 32 * i + acc_row(r, l);
-                if (jok && rr < rows_valid) {
-                    const int64_t row = m0 + rr;
-                    const float R = a2 * acc[i][j][r];
-                    const float u = scaled_x(bet, load_elem(p.c, p.c_dtype, row * N2 + c_in));
-                    const float gt = scaled_x(bet, load_elem(p.c, p.c_dtype, row * N2 + c_gt));
-                    const float Rp = R * p.prob[row];
-                    float d_in, d_gt, act;
-                    if (p.act == 0) {
-                        const float s = sigmoidf_(gt);
-                        d_in = Rp * gt * s;
-                        d_gt = Rp * u * s * (1.0f + gt * (1.0f - s));
-                        act = gt * s * u;
-                    } else {
-                        const float gc = fminf(gt, p.clamp_max);
-                        const float uc = fminf(fmaxf(u, p.clamp_min), p.clamp_max);
-                        const bool g_in = gt <= p.clamp_max;
-                        const bool u_in = (u >= p.clamp_min) & (u <= p.clamp_max);
-                        const float gf = g_in ? (p.mask_filter ? 1.0f : gt) : 0.0f;
-                        const float uf = u_in ? (p.mask_filter ? 1.0f : u) : 0.0f;
-                        const float s = sigmoidf_(p.geglu_alpha * gc);
-                        const float ul = uc + p.linear_offset;
-                        d_gt = Rp * ul * s * (1.0f + p.geglu_alpha * gc * (1.0f - s)) * gf;
-                        d_in = Rp * gc * s * uf;
-                        act = gc * s * ul;
-                    }
-                    rowsum[i][r] += R * act;
-                    bsum_in += d_in;
-                    bsum_gt += d_gt;
-                    store_elem(p.d, p.d_dtype, row * N2 + c_in, d_in);
-                    store_elem(p.d, p.d_dtype, row * N2 + c_gt, d_gt);
+            for (int k = 0; k < 8; k++) {
+#pragma unroll
+                for (int o = 8; o < 64; o <<= 1) {
+                    bs_in[k] += __shfl_xor(bs_in[k], o);
+                    bs_gt[k] += __shfl_xor(bs_gt[k], o);
                 }
             }
-        }
-        if (dbias_ws) {
-            // lanes l and l + 32 hold the same column, different rows
-            bsum_in += __shfl_xor(bsum_in, 32);
-            bsum_gt += __shfl_xor(bsum_gt, 32);
-            if (l < 32 && jok) {
-                atomicAdd(dbias_ws + c_in, bsum_in);
-                atomicAdd(dbias_ws + c_gt, bsum_gt);
+            if (l < 8 && n < p.N) {
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    atomicAdd(dbias_ws + c_in + k, bs_in[k]);
+                    atomicAdd(dbias_ws + c_gt + k, bs_gt[k]);
+                }
             }
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                bs_in[k] = bs_gt[k] = 0.0f;
         }
+    });
+    // dprob: the 8 lanes of a row hold its partial sums; one atomic per row
+    // and wave.
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        float v = rowsum[t];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        const int rr = am0 + (l >> 3) + 8 * t;
+        if ((l & 7) == 0 && rr < rows_valid && n0 + bn0 < p.N)
+            atomicAdd(p.dprob + m0 + rr, v);
     }
-    // dprob: sum each row over the 32 columns of the lane group, one atomic
-    // per row per wave.
-#pragma unroll
-    for (int i = 0; i < MB; i++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            float v = rowsum[i][r];
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            v += __shfl_xor(v, 8);
-            v += __shfl_xor(v, 16);
-            const int rr = am0 + 32 * i + acc_row(r, l);
-            if (lr == 0 && rr < rows_valid && n0 + bn0 < p.N)
-                atomicAdd(p.dprob + m0 + rr, v);
-        }
 }
 
 hipError_t launch_dglu(const DgluArgs& p, hipStream_t s) {

@@ -18,7 +18,7 @@
 // which orders like the value because |D| >= 0).
 #include "gg_internal.hpp"
 #include "gg_tile.hpp"
-#include "../../include/gg_moe.h"
+#include "gg_moe.h"
 
 namespace gg {
 
@@ -102,50 +102,42 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     mainloop<C>(smem, p.K / 128, issue, compute, begin);
 
     // ---------------- epilogue ----------------
+    // Rows of 8 columns per lane: C and D are 16-byte accesses (32 for fp32).
     const float al = p.alpha[g];
     const int64_t N = p.N;
     float amax = 0.0f;
-    float rowsum[MB][16];
+    float rowsum[8];
 #pragma unroll
-    for (int i = 0; i < MB; i++)
+    for (int k = 0; k < 8; k++)
+        rowsum[k] = 0.0f;
+    for_each_row8<C>(acc, (float*)(smem + w * kEpiWaveBytes), [&](int t, int r, int c, float (&v)[8]) {
+        const int rr = am0 + r;
+        const int col = n0 + bn0 + c;
+        if (rr < rows_valid && col < p.N) {
+            const int64_t row = m0 + rr;
+            float cv[8], d[8];
+            load8(p.c, p.c_dtype, row * N + col, cv);
+            const float pr2 = p.prob[row] * 2.0f;
 #pragma unroll
-        for (int r = 0; r < 16; r++)
-            rowsum[i][r] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NB; j++) {
-        const int col = n0 + bn0 + 32 * j + lr;
-        const bool jok = n0 + bn0 + 32 * j < p.N;
-#pragma unroll
-        for (int i = 0; i < MB; i++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int rr = am0 + 32 * i + acc_row(r, l);
-                if (jok && rr < rows_valid) {
-                    const int64_t row = m0 + rr;
-                    const float G = al * acc[i][j][r];
-                    const float rl = fmaxf(G, 0.0f);
-                    const float c = load_elem(p.c, p.c_dtype, row * N + col);
-                    const float d = p.prob[row] * 2.0f * c * rl;
-                    rowsum[i][r] += c * rl * rl;
-                    amax = fmaxf(amax, fabsf(d));
-                    store_elem(p.d, p.d_dtype, row * N + col, d);
-                }
+            for (int k = 0; k < 8; k++) {
+                const float rl = fmaxf(al * v[k], 0.0f);
+                d[k] = pr2 * cv[k] * rl;
+                rowsum[t] += cv[k] * rl * rl;
+                amax = fmaxf(amax, fabsf(d[k]));
             }
-    }
-#pragma unroll
-    for (int i = 0; i < MB; i++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            float v = rowsum[i][r];
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            v += __shfl_xor(v, 8);
-            v += __shfl_xor(v, 16);
-            const int rr = am0 + 32 * i + acc_row(r, l);
-            if (lr == 0 && rr < rows_valid && n0 + bn0 < p.N)
-                atomicAdd(p.dprob + m0 + rr, v);
+            store8(p.d, p.d_dtype, row * N + col, d);
         }
+    });
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        float v = rowsum[t];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        const int rr = am0 + (l >> 3) + 8 * t;
+        if ((l & 7) == 0 && rr < rows_valid && n0 + bn0 < p.N)
+            atomicAdd(p.dprob + m0 + rr, v);
+    }
     if (p.amax) {
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1)

@@ -8,7 +8,7 @@
 // wgrad ranks the experts by token count, largest first, so that the longest
 // reductions are dispatched first.
 #include "gg_internal.hpp"
-#include "../../include/gg_moe.h"
+#include "gg_moe.h"
 
 namespace gg {
 

@@ -42,13 +42,21 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowBytes = 128;   // bytes of one K-layout tile row per K step
 
+// Epilogue staging: each wave owns a private LDS region holding a 64 x 64
+// fp32 slice of its accumulators, rows kEpiPitch floats apart (68: the
+// 16-byte row reads of 8 lanes of one row and 8 of the next fall on
+// disjoint banks).
+constexpr int kEpiPitch = 68;
+constexpr int kEpiWaveBytes = 64 * kEpiPitch * 4;
+
 template <int TM_, int TN_, int WM_, int WN_>
 struct Cfg {
     static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
     static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
     static constexpr int MB = TM / WM / 32, NB = TN / WN / 32;   // MFMA blocks per wave
     static constexpr int kStage = (TM + TN) * kRowBytes;         // bytes per LDS stage
-    static constexpr int kLds = 2 * kStage;
+    static constexpr int kLds = 2 * kStage > kWaves * kEpiWaveBytes ? 2 * kStage
+                                                                     : kWaves * kEpiWaveBytes;
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -339,6 +347,94 @@ __device__ __forceinline__ void store_elem(void* base, int dtype, int64_t i, flo
         ((uint16_t*)base)[i] = f32_to_f16(v);
     else
         ((float*)base)[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Eight consecutive elements of a bf16 / fp16 / fp32 row as fp32 (16 or 32
+// bytes; the element index is a multiple of 8).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void unpack8_16(u32x4 w, int dtype, float (&v)[8]) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        if (dtype == kBF16) {
+            v[2 * k] = __builtin_bit_cast(float, ws[k] << 16);
+            v[2 * k + 1] = __builtin_bit_cast(float, ws[k] & 0xffff0000u);
+        } else {
+            v[2 * k] = f16_to_f32((uint16_t)(ws[k] & 0xffffu));
+            v[2 * k + 1] = f16_to_f32((uint16_t)(ws[k] >> 16));
+        }
+    }
+}
+
+__device__ __forceinline__ void load8(const void* base, int dtype, int64_t i, float (&v)[8]) {
+    if (dtype == kF32) {
+        // (no __builtin_bit_cast of vector components: clang reads element 0
+        // for every component that way)
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 a = *reinterpret_cast<const f32x4*>((const float*)base + i);
+        const f32x4 b = *reinterpret_cast<const f32x4*>((const float*)base + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        unpack8_16(*reinterpret_cast<const u32x4*>((const uint16_t*)base + i), dtype, v);
+    }
+}
+
+__device__ __forceinline__ void store8(void* base, int dtype, int64_t i, const float (&v)[8]) {
+    if (dtype == kF32) {
+        u32x4 a, b;
+        a.x = __builtin_bit_cast(uint32_t, v[0]); a.y = __builtin_bit_cast(uint32_t, v[1]);
+        a.z = __builtin_bit_cast(uint32_t, v[2]); a.w = __builtin_bit_cast(uint32_t, v[3]);
+        b.x = __builtin_bit_cast(uint32_t, v[4]); b.y = __builtin_bit_cast(uint32_t, v[5]);
+        b.z = __builtin_bit_cast(uint32_t, v[6]); b.w = __builtin_bit_cast(uint32_t, v[7]);
+        *reinterpret_cast<u32x4*>((float*)base + i) = a;
+        *reinterpret_cast<u32x4*>((float*)base + i + 4) = b;
+    } else {
+        uint32_t ws[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t lo = dtype == kBF16 ? f32_to_bf16(v[2 * k]) : f32_to_f16(v[2 * k]);
+            const uint32_t hi = dtype == kBF16 ? f32_to_bf16(v[2 * k + 1]) : f32_to_f16(v[2 * k + 1]);
+            ws[k] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>((uint16_t*)base + i) = u32x4{ws[0], ws[1], ws[2], ws[3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row walk of a wave's accumulators (MB == 2: 64 rows x 32 NB columns).  The
+// MFMA layout gives a lane one column and 16 rows of a block; stores want a
+// lane to own consecutive columns of one row.  The walk stages 64 columns at
+// a time through the wave's private LDS region and calls
+//   fn(t, r, c, v)  for the 8 columns [c, c+8) of wave-tile row r, v fp32,
+// where lane l visits rows (l >> 3) + 8 t, t = 0..7, at c = 8 (l & 7) + 64 h.
+// Only this wave touches `lds`; the caller separates it from the main loop
+// with a barrier.
+// ---------------------------------------------------------------------------
+template <class C, class Fn>
+__device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB], float* lds, Fn fn) {
+    static_assert(C::MB == 2 && C::NB % 2 == 0, "row walk expects 64-row wave tiles");
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int h = 0; h < C::NB / 2; h++) {
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    lds[(32 * i + acc_row(r, l)) * kEpiPitch + 32 * jj + (l & 31)] = acc[i][2 * h + jj][r];
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            const int row = (l >> 3) + 8 * t, c = 8 * (l & 7);
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            const f32x4 a = *reinterpret_cast<const f32x4*>(lds + row * kEpiPitch + c);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(lds + row * kEpiPitch + c + 4);
+            float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            fn(t, row, 64 * h + c, v);
+        }
+    }
 }
 
 // Group of an M tile: the g with po[g-1] <= m < po[g] (po[-1] = 0), by binary

@@ -17,34 +17,32 @@
 // untransposed in the MN layout and transposed by the LDS transpose reads.
 #include "gg_internal.hpp"
 #include "gg_tile.hpp"
-#include "../../include/gg_moe.h"
+#include "gg_moe.h"
 
 namespace gg {
 
 using WgradCfg = Cfg<256, 256, 4, 2>;
 
-template <int DT, class C>
-__device__ __forceinline__ void wgrad_epilogue(const f32x16 (&acc)[C::MB][C::NB], void* out,
-                                               int hidden, int inter, int row0, int col0,
-                                               int accumulate) {
-    const int l = threadIdx.x & 63;
+// Output: rows of 8 consecutive columns per lane (16-byte bf16/fp16 or
+// 32-byte fp32 accesses), accumulate mode adding the old values.
+template <class C>
+__device__ __forceinline__ void wgrad_epilogue(const f32x16 (&acc)[C::MB][C::NB], float* lds,
+                                               void* out, int dtype, int hidden, int inter,
+                                               int row0, int col0, int accumulate) {
+    for_each_row8<C>(acc, lds, [&](int, int r, int c, float (&v)[8]) {
+        const int row = row0 + r, col = col0 + c;
+        if (row < hidden && col < inter) {
+            const int64_t idx = (int64_t)row * inter + col;
+            if (accumulate) {
+                float o[8];
+                load8(out, dtype, idx, o);
 #pragma unroll
-    for (int i = 0; i < C::MB; i++)
-#pragma unroll
-        for (int j = 0; j < C::NB; j++) {
-            const int col = col0 + 32 * j + (l & 31);
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int row = row0 + 32 * i + acc_row(r, l);
-                if (row < hidden && col < inter) {
-                    const int64_t idx = (int64_t)row * inter + col;
-                    float v = acc[i][j][r];
-                    if (accumulate)
-                        v += load_elem(out, DT, idx);
-                    store_elem(out, DT, idx, v);
-                }
+                for (int k = 0; k < 8; k++)
+                    v[k] += o[k];
             }
+            store8(out, dtype, idx, v);
         }
+    });
 }
 
 template <class C, bool A_K, bool B_K>
@@ -110,14 +108,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         ? (void*)((char*)p.out_dense +
                   (int64_t)e * p.hidden * p.inter * (p.out_dtype == kF32 ? 4 : 2))
         : (void*)p.out_ptrs[e];
-    const int row0 = m0 + am0, col0 = n0 + bn0;
     const int accumulate = cnt > 0 ? p.accumulate : 0;
-    if (p.out_dtype == kBF16)
-        wgrad_epilogue<kBF16, C>(acc, out, p.hidden, p.inter, row0, col0, accumulate);
-    else if (p.out_dtype == kF16)
-        wgrad_epilogue<kF16, C>(acc, out, p.hidden, p.inter, row0, col0, accumulate);
-    else
-        wgrad_epilogue<kF32, C>(acc, out, p.hidden, p.inter, row0, col0, accumulate);
+    wgrad_epilogue<C>(acc, (float*)(smem + w * kEpiWaveBytes), out, p.out_dtype, p.hidden,
+                      p.inter, m0 + am0, n0 + bn0, accumulate);
 }
 
 hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s) {
