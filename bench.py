@@ -213,6 +213,68 @@ def cpu_baseline(ops, budget_s):
             "sample": "; ".join(parts) + " (rows spread over every group, extrapolated by FLOPs)"}
 
 
+COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
+
+
+def calibrate_copy(dev, reps=3):
+    """A plain device-to-device copy of COPY_BYTES, so that rocprofv3's
+    FETCH_SIZE / WRITE_SIZE can be scaled by what they read for known bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def summarize_pmc(fetch_csv, write_csv, workload_kernels, src_hash, out_path):
+    """Per-launch HBM traffic of our kernels from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled
+    by COPY_BYTES over what it reads for the calibration copy."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        vals = collections.defaultdict(list)
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            vals[row["Kernel_Name"]].append(float(row["Counter_Value"]) * 1024.0)
+        return vals
+
+    out = {}
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            out = {k: v for k, v in json.load(f).items() if not k.startswith("_")}
+    scales = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        # the calibration copy is a same-dtype device copy, which the runtime
+        # runs as its copyBuffer kernel; it is the largest such dispatch
+        copies = [max(v) for k, v in vals.items() if "copyBuffer" in k]
+        measured = max(copies) if copies else None
+        scale = COPY_BYTES / measured if measured else None
+        scales[counter] = {"copy_measured_bytes": measured, "scale": scale}
+        for name, (kernel, workload) in workload_kernels.items():
+            hits = [v for k, v in vals.items() if kernel in k]
+            if not hits or scale is None:
+                continue
+            samples = [x for v in hits for x in v]
+            key = f"{kernel}:{workload}"
+            if counter == "FETCH_SIZE" or key not in out:
+                out[key] = {"source_hash": src_hash}
+            out[key][counter.lower() + "_bytes"] = sum(samples) / len(samples) * scale
+            out[key][counter.lower() + "_scale"] = scale
+    for ent in out.values():
+        if "fetch_size_bytes" in ent and "write_size_bytes" in ent:
+            ent["bytes_per_launch"] = ent["fetch_size_bytes"] + ent["write_size_bytes"]
+    out["_scale"] = scales
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    return out
+
+
 def traffic_for(kernel, workload, src_hash):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
@@ -233,7 +295,23 @@ def main():
     ap.add_argument("--workload", default="moe_backward", choices=sorted(WORKLOAD_OPS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="with a single-op --workload: record its per-launch HBM traffic from "
+                         "two rocprofv3 --pmc runs in profiles/hbm_traffic.json, and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        names = WORKLOAD_OPS[args.workload]
+        if len(names) != 1:
+            sys.exit("--summarize-pmc needs a single-op --workload")
+        kernel = {"dswiglu": "dglu_kernel", "dgeglu": "dglu_kernel", "wgrad_moe": "wgrad_kernel",
+                  "wgrad_moe_kmajor": "wgrad_kernel", "dsrelu_mxfp8": "dsrelu_kernel"}[names[0]]
+        path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+        res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                            {names[0]: (kernel, names[0])}, source_hash(), path)
+        print(json.dumps(res, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus})",
               file=sys.stderr)
@@ -250,6 +328,8 @@ def main():
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
     ops = [build_op(n, dev) for n in WORKLOAD_OPS[args.workload]]
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        calibrate_copy(dev)
 
     for _ in range(args.warmup):
         for op in ops:
