@@ -1,34 +1,48 @@
 // gg_tile.hpp -- device building blocks shared by the gfx950 grouped-GEMM
-// kernels: MFMA fragment types, the LDS stage layouts, global->LDS stage
-// loaders, fragment readers, the pipelined MFMA main loop, and the work-item
-// remap that keeps neighbouring tiles on one XCD.
+// kernels: MFMA fragment types, the LDS layouts, global->LDS loaders,
+// fragment readers, the pipelined MFMA main loop, and the work-item remap
+// that keeps neighbouring tiles on one XCD.
 //
-// Geometry (Cfg below): a TM x TN macro tile per workgroup, WM x WN wave64s,
-// each wave owning (TM/WM) x (TN/WN) as 32x32 MFMA blocks.  One K step
-// stages 128 bytes of K (64 bf16 or 128 fp8 values) of every tile row;
-// two stages alternate in LDS.
+// Geometry (Cfg below): a TM x TN macro tile per workgroup of WM x WN wave64s,
+// each wave owning (TM/WM) x (TN/WN) as 32x32 MFMA blocks held in
+// accumulation registers.  The bf16 kernels run 4 x 2 waves (two per SIMD,
+// 64 x 128 each: a stalled wave leaves the MFMA pipe to the other); the fp8
+// kernel, whose fragments are twice as large, runs 2 x 2 (one per SIMD,
+// 128 x 128 each, 512 registers).
+//
+// K is walked in stages of 64 bytes of every tile row (32 bf16 or 64 fp8
+// values); a wave reads the next stage's MFMA fragments from LDS into one
+// register set while its MFMAs consume the other.  Loads into LDS move two
+// stages at a time (a "load unit", 128 bytes of every row): the load path
+// of a CU moves about one 128-byte cache line per three clocks whether the
+// line is wanted whole or in halves, so a unit fetches each line once.  Two
+// unit buffers alternate: unit u+1 is in flight while unit u is read.
 //
 // Global -> LDS: buffer loads that write LDS directly (no register staging).
 // One wave instruction moves 1 KiB: lane l's 16 bytes land at base + 16 l.
 // Each lane therefore computes which global 16 bytes belong at its LDS slot.
-// An offset past the descriptor's range loads zeros, which masks rows past
-// the tile edge and K past a group's end.
+// An offset past the descriptor's record count loads zeros, which masks rows
+// past the tile edge and K past a group's end.
 //
-// LDS stage layouts:
+// LDS layouts of a unit:
 //  * K-contiguous operand ("K layout"): tile row r holds 128 bytes of K as 8
 //    chunks of 16 bytes; chunk c sits at chunk position c ^ swz(r),
-//    swz(r) = (r ^ (r >> 3)) & 7.  MFMA fragments are 16-byte reads.
-//  * M/N-contiguous bf16 operand ("MN layout", 256 columns): K row k holds
-//    the tile's 256 columns as 32 units of 16 bytes; unit u sits at position
-//    u ^ (4 (k & 3)).  Fragments are read with ds_read_b64_tr_b16: within a
-//    16-lane group, lane 4q + j receives element j of the 8-byte pieces
-//    addressed by lanes q, 4+q, 8+q, 12+q; when lane 4e + q addresses K row
-//    kb + e at columns c + 4q, lane i gets column c + i at K rows kb..kb+3 --
-//    the K-contiguous register fragment the MFMA needs.
-// Both layouts read without bank conflicts (64 banks of 4 bytes).
+//    swz(r) = (r ^ (r >> 3)) & 7.  Stage h (0, 1) of the unit is chunks
+//    4h .. 4h+3.  MFMA fragments are 16-byte reads.
+//  * M/N-contiguous bf16 operand ("MN layout", 256 columns): K row k (0..63)
+//    holds the tile's 256 columns as 32 units of 16 bytes; unit u sits at
+//    position u ^ (4 (k & 3)).  Stage h is K rows 32h .. 32h+31.  Fragments
+//    are read with ds_read_b64_tr_b16: within a 16-lane group, lane 4q + j
+//    receives element j of the 8-byte pieces addressed by lanes q, 4+q, 8+q,
+//    12+q; when lane 4e + q addresses K row kb + e at columns c + 4q, lane i
+//    gets column c + i at K rows kb..kb+3 -- the K-contiguous register
+//    fragment the MFMA needs.
+// Both layouts read without bank conflicts (64 banks of 4 bytes; a 16-byte
+// read is served 16 lanes at a time).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace gg {
 
@@ -40,7 +54,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 #define GG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int kRowBytes = 128;   // bytes of one K-layout tile row per K step
+constexpr int kRowBytes = 128;   // bytes of one K-layout tile row per load unit
 
 // Epilogue staging: each wave owns a private LDS region holding a 64 x 64
 // fp32 slice of its accumulators, rows kEpiPitch floats apart (68: the
@@ -54,9 +68,9 @@ struct Cfg {
     static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
     static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
     static constexpr int MB = TM / WM / 32, NB = TN / WN / 32;   // MFMA blocks per wave
-    static constexpr int kStage = (TM + TN) * kRowBytes;         // bytes per LDS stage
-    static constexpr int kLds = 2 * kStage > kWaves * kEpiWaveBytes ? 2 * kStage
-                                                                     : kWaves * kEpiWaveBytes;
+    static constexpr int kUnit = (TM + TN) * kRowBytes;          // bytes per load unit
+    static constexpr int kLds = 2 * kUnit > kWaves * kEpiWaveBytes ? 2 * kUnit
+                                                                    : kWaves * kEpiWaveBytes;
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -74,18 +88,16 @@ __device__ __forceinline__ u32x4 ld_lds16(const char* lds, int off) {
 }
 
 // ---------------------------------------------------------------------------
-// Buffer descriptors: a scalar base advanced per K step; 32-bit offsets per
-// lane.  kInvalid lies past num_records: such loads return (or write) zeros.
+// Buffer descriptors: 32-bit offsets per lane from a scalar base; kInvalid
+// lies past any record count used here, so such loads return (or write)
+// zeros.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kInvalid = 0x80000000u;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7ffffff0,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                        uint32_t records = 0x7ffffff0u) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)records,
                                              0x00020000);
-}
-
-__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
 // LDS byte address of a pointer into workgroup memory.
@@ -94,72 +106,122 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 }
 
 // The LDS-writing buffer load is issued through inline assembly: the
-// compiler neither sees nor waits for it, so reads of the other stage are
-// not held back.  Completion is awaited explicitly (wait_vm0) before the
-// barrier that hands the stage to the MFMA waves.  M0 holds the wave's LDS
-// base; lane l writes base + 16 l.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
+// compiler neither sees nor waits for it, so it cannot hold back reads of
+// the other buffer.  Completion is awaited explicitly (vm_wait) before the
+// barrier that hands a unit to the MFMA waves.  M0 holds the wave's LDS
+// byte address (workgroup-uniform); lane l writes lds + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(uniform((int)lds_addr(lds))), "v"(off), "s"(r)
+                 : "s"(uniform((int)lds)), "v"(off), "s"(r)
                  : "memory", "m0");
 }
 
-// s_waitcnt vmcnt(0): every outstanding vector memory operation of this
-// wave, including the LDS-writing loads, has completed.
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Dword form: lane l's 4 bytes land at lds + 4 l (one wave moves 256 B).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(uniform((int)lds)), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N of this wave's vector memory
+// operations (which complete in issue order, the LDS-writing loads
+// included) are outstanding, and all its LDS operations have completed.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+__device__ __forceinline__ void wait_all() { vm_wait<0>(); }
+
+// Workgroup barrier that lets the compiler move neither memory accesses nor,
+// through the scheduling barriers, any other instruction across it.  (The
+// fence of __syncthreads would add waits of its own.)
+__device__ __forceinline__ void unit_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------
-// Stage loaders.
-// K layout, R rows: `tile` is the global address of the tile's row 0 at K
-// byte 0, rows `ld` bytes apart; this K step covers bytes [kbyte, kbyte+128).
-// Rows at or past rows_valid and K bytes at or past kbytes_valid load zeros.
+// Unit loaders.  Each lane's byte offsets within a unit are fixed for the
+// whole K loop and computed once (init); per unit only the scalar buffer
+// descriptor moves.  Its record count masks what lies past the data.
+//
+// K layout, R rows, rows `ld` bytes apart; rows at or past rows_valid load
+// zeros.  issue() loads the 128 bytes at `tile` (row 0, the unit's first K
+// byte) with kleft valid K bytes left from there (<= 0: all zeros).  With
+// RAGGED, kleft may end inside the unit (per-lane check); otherwise a unit
+// is either wholly inside K or wholly past it.
 // ---------------------------------------------------------------------------
 template <class C, int R>
-__device__ __forceinline__ void stage_k(char* lds, const char* tile, int64_t ld, int rows_valid,
-                                        int64_t kbyte, int64_t kbytes_valid) {
-    constexpr int kBlocks = R / 8;                       // 1 KiB blocks of 8 rows
-    static_assert(kBlocks % C::kWaves == 0, "blocks must split evenly over waves");
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile + kbyte);
+struct LoadK {
+    static constexpr int kN = R / 8 / C::kWaves;         // 1 KiB loads (8 rows) per wave
+    static_assert(kN * 8 * C::kWaves == R, "rows must split evenly over waves");
+    uint32_t off[kN], c16[kN];
+    __device__ __forceinline__ void init(int64_t ld, int rows_valid) {
+        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < kBlocks / C::kWaves; i++) {
-        const int b = w * (kBlocks / C::kWaves) + i;
-        const int row = 8 * b + (l >> 3);
-        const int c = (l & 7) ^ swz(row);
-        const bool ok = (row < rows_valid) & (kbyte + c * 16 < kbytes_valid);
-        dma16(rs, lds + b * 1024, ok ? (uint32_t)(row * ld) + c * 16 : kInvalid);
+        for (int i = 0; i < kN; i++) {
+            const int row = 8 * (w * kN + i) + (l >> 3);
+            const int c = (l & 7) ^ swz(row);
+            off[i] = row < rows_valid ? (uint32_t)(row * ld) + c * 16 : kInvalid;
+            c16[i] = c * 16;
+        }
     }
-}
+    // Load i (0 .. kN-1) of this wave.
+    template <bool RAGGED>
+    __device__ __forceinline__ void issue(uint32_t lds, const char* tile, int64_t kleft, int i) const {
+        const int w = uniform(threadIdx.x >> 6);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, kleft > 0 ? 0x7ffffff0u : 0u);
+        const uint32_t kl = (uint32_t)(kleft < 128 ? (kleft < 0 ? 0 : kleft) : 128);
+        dma16(rs, lds + (w * kN + i) * 1024, !RAGGED || c16[i] < kl ? off[i] : kInvalid);
+    }
+};
 
-// MN layout (bf16, 256 columns, 64 K rows): `tile` is the global address of
-// this K step's first K row at the tile's first column; K rows are `ld` bytes
-// apart.  K rows at or past k_rows_valid and columns at or past cols_valid
-// load zeros.
+// MN layout (bf16, 256 columns, 64 K rows), K rows `ld` bytes apart;
+// columns at or past cols_valid load zeros.  issue() loads the K rows
+// starting at `tile` (the unit's first K row at the tile's first column)
+// with krows valid K rows left from there.
 template <class C>
-__device__ __forceinline__ void stage_mn(char* lds, const char* tile, int64_t ld, int cols_valid,
-                                         int64_t k_rows_valid) {
-    constexpr int kBlocks = 32;                          // 1 KiB = 2 K rows of 512 B
-    static_assert(kBlocks % C::kWaves == 0, "blocks must split evenly over waves");
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile);
+struct LoadMN {
+    static constexpr int kN = 32 / C::kWaves;            // 1 KiB loads (2 K rows) per wave
+    static_assert(kN * C::kWaves == 32, "K rows must split evenly over waves");
+    uint32_t off[kN];
+    uint32_t ld;
+    __device__ __forceinline__ void init(int64_t ld_, int cols_valid) {
+        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+        ld = (uint32_t)ld_;
 #pragma unroll
-    for (int i = 0; i < kBlocks / C::kWaves; i++) {
-        const int b = w * (kBlocks / C::kWaves) + i;
-        const int k = 2 * b + (l >> 5);
-        const int u = (l & 31) ^ (4 * (k & 3));
-        const bool ok = (k < k_rows_valid) & (u * 8 < cols_valid);
-        dma16(rs, lds + b * 1024, ok ? (uint32_t)(k * ld) + u * 16 : kInvalid);
+        for (int i = 0; i < kN; i++) {
+            const int k = 2 * (w * kN + i) + (l >> 5);
+            const int u = (l & 31) ^ (4 * (k & 3));
+            off[i] = u * 8 < cols_valid ? (uint32_t)(k * ld_) + u * 16 : kInvalid;
+        }
     }
-}
+    // A lane at K row k < krows and a valid column has k ld + 16 u < krows ld
+    // (16 u < 2 cols_valid <= ld), so the record count krows ld masks exactly
+    // the K rows past the end.
+    // Load i (0 .. kN-1) of this wave.
+    __device__ __forceinline__ void issue(uint32_t lds, const char* tile, int64_t krows, int i) const {
+        const int w = uniform(threadIdx.x >> 6);
+        const uint32_t kr = (uint32_t)(krows < 64 ? (krows < 0 ? 0 : krows) : 64);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, kr * ld);
+        dma16(rs, lds + (w * kN + i) * 1024, off[i]);
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Fragment readers (bf16, v_mfma_f32_32x32x16_bf16: lane l supplies row / col
-// l % 32 with K values 8 (l / 32) .. 8 (l / 32) + 7 of the 16-value sub-step).
+// l % 32 with K values 8 (l / 32) .. 8 (l / 32) + 7 of a 16-value sub-step;
+// stage h of a unit has sub-steps ks = 0, 1).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bf16x8 frag_k(const char* lds, int row0, int ks) {
+__device__ __forceinline__ bf16x8 frag_k(const char* lds, int row0, int chunk) {
     const int l = threadIdx.x & 63;
-    return __builtin_bit_cast(bf16x8, ld_lds16(lds, lds_off(row0 + (l & 31), 2 * ks + (l >> 5))));
+    return __builtin_bit_cast(bf16x8, ld_lds16(lds, lds_off(row0 + (l & 31), chunk + (l >> 5))));
 }
 
 __device__ __forceinline__ int mn_addr(int k, int col) {
@@ -167,11 +229,11 @@ __device__ __forceinline__ int mn_addr(int k, int col) {
     return k * 512 + ((u ^ (4 * (k & 3))) << 4) + ((col & 7) << 1);
 }
 
-__device__ __forceinline__ bf16x8 frag_mn(const char* lds, int col0, int ks) {
+__device__ __forceinline__ bf16x8 frag_mn(const char* lds, int col0, int k0) {
     const int l = threadIdx.x & 63;
     const int g = l >> 4, s = l & 15;
     const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
-    const int k = 16 * ks + 8 * (g >> 1) + (s >> 2);
+    const int k = k0 + 8 * (g >> 1) + (s >> 2);
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)GG_LDS(lds + mn_addr(k, col)));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -181,115 +243,174 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* lds, int col0, int ks) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Sub-step ks of stage h: K chunk 4h + 2ks (K layout) or K row 32h + 16ks
+// (MN layout).
 template <bool KMAJOR>
-__device__ __forceinline__ bf16x8 frag_bf16(const char* lds, int base, int ks) {
+__device__ __forceinline__ bf16x8 frag_bf16(const char* lds, int base, int h, int ks) {
     if constexpr (KMAJOR)
-        return frag_k(lds, base, ks);
+        return frag_k(lds, base, 4 * h + 2 * ks);
     else
-        return frag_mn(lds, base, ks);
+        return frag_mn(lds, base, 32 * h + 16 * ks);
 }
 
-// One staged K step of bf16 MFMAs (4 sub-steps of 16); fragments of sub-step
-// ks+1 are read while the MFMAs of ks run.
+// One wave's bf16 fragments of a stage (two sub-steps of 16 K values).
+template <class C>
+struct FragBf16 {
+    bf16x8 a[2][C::MB], b[2][C::NB];
+};
+
+// Fragment group g of stage h: A rows a0 + 32 g of `sa` (g < MB) or B rows /
+// columns b0 + 32 (g - MB) of `sb`, both sub-steps.
 template <class C, bool A_K, bool B_K>
-__device__ __forceinline__ void mfma_stage_bf16(const char* sa, const char* sb, int a0, int b0,
-                                                f32x16 (&acc)[C::MB][C::NB]) {
-    bf16x8 af[2][C::MB], bfr[2][C::NB];
-    auto read = [&](int ks, int buf) {
+__device__ __forceinline__ void read_bf16(const char* sa, const char* sb, int a0, int b0, int h,
+                                          FragBf16<C>& f, int g) {
 #pragma unroll
-        for (int i = 0; i < C::MB; i++)
-            af[buf][i] = frag_bf16<A_K>(sa, a0 + 32 * i, ks);
-#pragma unroll
-        for (int j = 0; j < C::NB; j++)
-            bfr[buf][j] = frag_bf16<B_K>(sb, b0 + 32 * j, ks);
-    };
-    read(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-        const int cur = ks & 1;
-        if (ks + 1 < 4)
-            read(ks + 1, cur ^ 1);
-#pragma unroll
-        for (int i = 0; i < C::MB; i++)
-#pragma unroll
-            for (int j = 0; j < C::NB; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
-                                                                    0, 0, 0);
+    for (int ks = 0; ks < 2; ks++) {
+        if (g < C::MB)
+            f.a[ks][g] = frag_bf16<A_K>(sa, a0 + 32 * g, h, ks);
+        else
+            f.b[ks][g - C::MB] = frag_bf16<B_K>(sb, b0 + 32 * (g - C::MB), h, ks);
     }
 }
 
-// One staged K step of MX-scaled fp8 MFMAs (2 sub-steps of 64).
-// v_mfma_scale_f32_32x32x64_f8f6f4: lane l (row l%32, h = l/32) supplies K
-// bytes [16h, 16h+16) and [32+16h, 32+16h+16) of the sub-step, and the E8M0
-// scale of K block h of its row in byte 0 of its scale operand (op_sel 0).
-// sa_w[ks][i] / sb_w[ks][j] hold, per sub-step and fragment, the scale word
-// already shifted so that byte 0 is block 2 ks + h.
+// MFMAs m0 .. m1-1 of a stage, m = (ks MB + i) NB + j.
 template <class C>
-__device__ __forceinline__ void mfma_stage_mx8(const char* sa, const char* sb, int a0, int b0,
-                                               const uint32_t (&sa_w)[2][C::MB],
-                                               const uint32_t (&sb_w)[2][C::NB],
-                                               f32x16 (&acc)[C::MB][C::NB]) {
+__device__ __forceinline__ void mma_bf16(const FragBf16<C>& f, f32x16 (&acc)[C::MB][C::NB], int m0,
+                                         int m1) {
+#pragma unroll
+    for (int m = 0; m < 2 * C::MB * C::NB; m++) {
+        if (m < m0 || m >= m1)
+            continue;
+        const int ks = m / (C::MB * C::NB), i = (m / C::NB) % C::MB, j = m % C::NB;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
+    }
+}
+
+// One wave's MX fp8 fragments of a stage (64 K values) with their scales.
+// v_mfma_scale_f32_32x32x64_f8f6f4: lane l (row l%32, q = l/32) supplies K
+// bytes [16q, 16q+16) and [32+16q, 32+16q+16), and the E8M0 scale of K block
+// q of its row in byte 0 of its scale operand (op_sel 0).
+template <class C>
+struct FragMx8 {
+    i32x8 a[C::MB], b[C::NB];
+    uint32_t sa[C::MB], sb[C::NB];
+};
+
+// Fragment group g of stage h: A row block g (g < MB) or B row block g - MB.
+template <class C>
+__device__ __forceinline__ void read_mx8(const char* sa, const char* sb, int a0, int b0, int h,
+                                         FragMx8<C>& f, int g) {
     const int l = threadIdx.x & 63;
-    const int lr = l & 31, lh = l >> 5;
-    i32x8 af[2][C::MB], bfr[2][C::NB];
-    auto frag = [&](const char* s, int r, int ks) {
-        const u32x4 x0 = ld_lds16(s, lds_off(r, 4 * ks + lh));
-        const u32x4 x1 = ld_lds16(s, lds_off(r, 4 * ks + 2 + lh));
+    const int lr = l & 31, lq = l >> 5;
+    auto frag = [&](const char* s, int r) {
+        const u32x4 x0 = ld_lds16(s, lds_off(r, 4 * h + lq));
+        const u32x4 x1 = ld_lds16(s, lds_off(r, 4 * h + 2 + lq));
         return i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     };
-    auto read = [&](int ks) {
+    if (g < C::MB)
+        f.a[g] = frag(sa, a0 + 32 * g + lr);
+    else
+        f.b[g - C::MB] = frag(sb, b0 + 32 * (g - C::MB) + lr);
+}
+
+// MFMAs m0 .. m1-1 of a stage, m = i NB + j.
+template <class C>
+__device__ __forceinline__ void mma_mx8(const FragMx8<C>& f, f32x16 (&acc)[C::MB][C::NB], int m0,
+                                        int m1) {
 #pragma unroll
-        for (int i = 0; i < C::MB; i++)
-            af[ks][i] = frag(sa, a0 + 32 * i + lr, ks);
-#pragma unroll
-        for (int j = 0; j < C::NB; j++)
-            bfr[ks][j] = frag(sb, b0 + 32 * j + lr, ks);
-    };
-    read(0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-        if (ks == 0)
-            read(1);
-#pragma unroll
-        for (int i = 0; i < C::MB; i++)
-#pragma unroll
-            for (int j = 0; j < C::NB; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0, (int)sa_w[ks][i], 0, (int)sb_w[ks][j]);
+    for (int m = 0; m < C::MB * C::NB; m++) {
+        if (m < m0 || m >= m1)
+            continue;
+        const int i = m / C::NB, j = m % C::NB;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.a[i], f.b[j], acc[i][j], 0, 0, 0, (int)f.sa[i], 0, (int)f.sb[j]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined main loop over nk K steps.  issue(stage, kt) queues the direct
-// LDS loads of step kt into `stage`; compute(stage) runs the MFMAs of a
-// staged step.  The loads of step kt+1 are in flight while step kt computes;
-// one wait + barrier per step hands the stage over.
+// Pipelined main loop over nk stages (nk rounded up to whole units; the
+// stages past nk load zeros).
+//   issue(lds, u, i)     queues load i (0 .. VM-1) of this wave for unit u
+//                        (stages 2u, 2u+1) into the unit buffer at LDS
+//                        address lds; for units past the end every load must
+//                        be masked (it then writes zeros and reads no memory);
+//   read(buf, kt, f, g)  queues this wave's LDS reads of fragment group g
+//                        (0 .. kGroups-1) of stage kt (unit buffer buf, half
+//                        kt & 1) into f;
+//   mma(f, m0, m1)       runs MFMAs m0 .. m1-1 (of kMfma) on a fragment set.
+// Unit u lives in buffer u & 1.  Iteration u runs stage 2u ("even half")
+// while reading stage 2u+1's fragments from the same unit, then awaits unit
+// u+1, passes one barrier (which also certifies that every wave has read all
+// of unit u), and runs stage 2u+1 ("odd half") while loading unit u+2 into
+// unit u's buffer and reading stage 2u+2 from unit u+1.
+//
+// The issue order is fixed instruction by instruction (scheduling barriers
+// between the pieces): one MFMA, then the loads and reads due after it.  The
+// load path of a CU accepts one 1 KiB load every 16 clocks or so, and a wave
+// whose load waits for it cannot issue its next MFMA: loads spread over the
+// MFMAs keep the MFMA pipes fed, where a burst of loads would stall them.
+// Loads are issued past the end as well, so the loop body has no branch (a
+// branch would let the compiler sink one iteration's MFMAs into the next and
+// hold three fragment sets).  The trailing wait and barrier let the caller
+// reuse the LDS.
 // ---------------------------------------------------------------------------
-// begin(kt) runs at the top of step kt, before the loads of step kt+1 are
-// queued (dsReLU uses it to take the scale words prefetched for step kt).
-struct NoBegin {
-    __device__ void operator()(int) const {}
-};
-
-template <class C, class Issue, class Compute, class Begin = NoBegin>
-__device__ __forceinline__ void mainloop(char* smem, int nk, Issue issue, Compute compute,
-                                         Begin begin = Begin()) {
+template <class C, int VM, int kMfma, int kGroups, class F, class Issue, class Read, class Mma>
+__device__ __forceinline__ void pipeline(char* smem, int nk, F (&f)[2], Issue issue, Read read,
+                                         Mma mma) {
+    static_assert(kGroups <= kMfma, "one fragment group per MFMA at most");
     if (nk <= 0)
         return;
-    issue(smem, 0);
-    wait_vm0();
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-        char* cur = smem + (kt & 1) * C::kStage;
-        char* nxt = smem + ((kt + 1) & 1) * C::kStage;
-        begin(kt);
-        if (kt + 1 < nk)
-            issue(nxt, kt + 1);
-        compute(cur, kt);
-        wait_vm0();
-        __syncthreads();
+    const int nu = (nk + 1) >> 1;                        // load units
+    const uint32_t lds0 = lds_addr(smem);
+    auto buf = [&](int u) { return smem + (u & 1) * C::kUnit; };
+    auto lds = [&](int u) { return lds0 + (uint32_t)((u & 1) * C::kUnit); };
+#pragma unroll
+    for (int i = 0; i < VM; i++)
+        issue(lds(0), 0, i);
+#pragma unroll
+    for (int i = 0; i < VM; i++)
+        issue(lds(1), 1, i);
+    vm_wait<VM>();                                       // all of unit 0
+    unit_barrier();
+#pragma unroll
+    for (int g = 0; g < kGroups; g++)
+        read(buf(0), 0, f[0], g);
+    // stage 2u, reading stage 2u+1 from the same unit
+    auto even = [&](int u) {
+#pragma unroll
+        for (int m = 0; m < kMfma; m++) {
+            mma(f[0], m, m + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < kGroups)
+                read(buf(u), 2 * u + 1, f[1], m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    int u = 0;
+    for (; u + 1 < nu; u++) {
+        even(u);
+        // stage 2u+1: hand over unit u+1, refill unit u's buffer with u+2
+        wait_all();
+        unit_barrier();
+#pragma unroll
+        for (int m = 0; m < kMfma; m++) {
+            mma(f[1], m, m + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < VM; i++)
+                if (i * kMfma / VM == m)
+                    issue(lds(u), u + 2, i);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < kGroups)
+                read(buf(u + 1), 2 * u + 2, f[0], m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    even(u);
+    mma(f[1], 0, kMfma);
+    wait_all();
+    unit_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -403,39 +524,113 @@ __device__ __forceinline__ void store8(void* base, int dtype, int64_t i, const f
 }
 
 // ---------------------------------------------------------------------------
-// Row walk of a wave's accumulators (MB == 2: 64 rows x 32 NB columns).  The
-// MFMA layout gives a lane one column and 16 rows of a block; stores want a
-// lane to own consecutive columns of one row.  The walk stages 64 columns at
-// a time through the wave's private LDS region and calls
-//   fn(t, r, c, v)  for the 8 columns [c, c+8) of wave-tile row r, v fp32,
-// where lane l visits rows (l >> 3) + 8 t, t = 0..7, at c = 8 (l & 7) + 64 h.
+// Raw loads of 8 consecutive elements (16 bytes for bf16 / fp16; W32: 32 for
+// fp32), converted to fp32 only when used, so that a caller can have many in
+// flight.  The element index is a multiple of 8.
+// ---------------------------------------------------------------------------
+template <bool W32>
+struct Raw8 {
+    u32x4 w[W32 ? 2 : 1];
+};
+
+template <bool W32>
+__device__ __forceinline__ Raw8<W32> raw8_load(const void* base, int64_t i) {
+    Raw8<W32> r;
+    if constexpr (W32) {
+        r.w[0] = *reinterpret_cast<const u32x4*>((const float*)base + i);
+        r.w[1] = *reinterpret_cast<const u32x4*>((const float*)base + i + 4);
+    } else {
+        r.w[0] = *reinterpret_cast<const u32x4*>((const uint16_t*)base + i);
+    }
+    return r;
+}
+
+// dtype: kF32 when W32, else kBF16 or kF16.
+template <bool W32>
+__device__ __forceinline__ void raw8_cvt(const Raw8<W32>& r, int dtype, float (&v)[8]) {
+    if constexpr (W32) {
+        const uint32_t ws[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w,
+                                r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            v[k] = __builtin_bit_cast(float, ws[k]);
+    } else {
+        unpack8_16(r.w[0], dtype, v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row walk of a wave's accumulators (32 MB rows x 32 NB columns, MB and NB
+// even).  The MFMA layout gives a lane one column and 16 rows of a block;
+// stores want a lane to own consecutive columns of one row.  The walk stages
+// 64 x 64 quadrants through the wave's private LDS region and visits, for
+// lane l, the items (t, r, c): the 8 columns [c, c+8) of wave-tile row r,
+// r = (l >> 3) + 8 t, t = 0 .. 4 MB - 1, c = 8 (l & 7) + 64 h; for each h
+// the t values come in increasing order.  The caller's loads run kAhead
+// items ahead of their use, so that many are in flight at once:
+//   load(t, r, c)            queue the loads of an item, returning them;
+//   fn(t, r, c, v, pre)      process an item with its accumulators v (fp32)
+//                            and what load returned for it.
 // Only this wave touches `lds`; the caller separates it from the main loop
 // with a barrier.
 // ---------------------------------------------------------------------------
-template <class C, class Fn>
-__device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB], float* lds, Fn fn) {
-    static_assert(C::MB == 2 && C::NB % 2 == 0, "row walk expects 64-row wave tiles");
+template <class C, int kAhead, class Load, class Fn>
+__device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB], float* lds, Load load,
+                                              Fn fn) {
+    static_assert(C::MB % 2 == 0 && C::NB % 2 == 0, "row walk expects 64 x 64 quadrants");
+    constexpr int kItems = 8 * (C::MB / 2) * (C::NB / 2);
     const int l = threadIdx.x & 63;
+    // item i: quadrant q = i / 8 (h = q / (MB/2), mh = q % (MB/2)), t8 = i % 8
+    auto item = [&](int i, int& t, int& r, int& c) {
+        const int q = i >> 3, h = q / (C::MB / 2), mh = q % (C::MB / 2), t8 = i & 7;
+        t = 8 * mh + t8;
+        r = 64 * mh + (l >> 3) + 8 * t8;
+        c = 64 * h + 8 * (l & 7);
+    };
+    using P = decltype(load(0, 0, 0));
+    P pre[kItems];
 #pragma unroll
-    for (int h = 0; h < C::NB / 2; h++) {
+    for (int i = 0; i < kAhead && i < kItems; i++) {
+        int t, r, c;
+        item(i, t, r, c);
+        pre[i] = load(t, r, c);
+    }
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+    for (int i = 0; i < kItems; i++) {
+        if ((i & 7) == 0) {
+            const int q = i >> 3, h = q / (C::MB / 2), mh = q % (C::MB / 2);
 #pragma unroll
-            for (int jj = 0; jj < 2; jj++)
+            for (int b = 0; b < 2; b++)
 #pragma unroll
-                for (int r = 0; r < 16; r++)
-                    lds[(32 * i + acc_row(r, l)) * kEpiPitch + 32 * jj + (l & 31)] = acc[i][2 * h + jj][r];
+                for (int jj = 0; jj < 2; jj++)
 #pragma unroll
-        for (int t = 0; t < 8; t++) {
-            const int row = (l >> 3) + 8 * t, c = 8 * (l & 7);
-            typedef float f32x4 __attribute__((ext_vector_type(4)));
-            const f32x4 a = *reinterpret_cast<const f32x4*>(lds + row * kEpiPitch + c);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(lds + row * kEpiPitch + c + 4);
-            float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-            fn(t, row, 64 * h + c, v);
+                    for (int e = 0; e < 16; e++)
+                        lds[(32 * b + acc_row(e, l)) * kEpiPitch + 32 * jj + (l & 31)] =
+                            acc[2 * mh + b][2 * h + jj][e];
         }
+        if (i + kAhead < kItems) {
+            int t, r, c;
+            item(i + kAhead, t, r, c);
+            pre[i + kAhead] = load(t, r, c);
+        }
+        int t, r, c;
+        item(i, t, r, c);
+        const int rq = r & 63, cq = c & 63;
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 a = *reinterpret_cast<const f32x4*>(lds + rq * kEpiPitch + cq);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(lds + rq * kEpiPitch + cq + 4);
+        float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        fn(t, r, c, v, pre[i]);
     }
 }
+
+// Loads of one row-walk item: NC raw 8-element loads and one fp32 per-row
+// value.
+template <bool W32, int NC>
+struct Pre8 {
+    Raw8<W32> x[NC];
+    float row;
+};
 
 // Group of an M tile: the g with po[g-1] <= m < po[g] (po[-1] = 0), by binary
 // search over the cumulative ends; L if m >= po[L-1].

@@ -11,8 +11,9 @@
 // hardware dispatcher, which starts workgroups in index order as CUs free up,
 // acts as a longest-first greedy scheduler over skewed experts.  Within an
 // expert the items are remapped so each XCD owns a band of M tiles.  The
-// reduction runs over the expert's tokens in K steps of 64 through the
-// pipelined main loop of gg_tile.hpp: K-major operands are staged in the K
+// reduction runs over the expert's tokens, 32 per stage and 64 per load
+// unit, through the pipelined main loop of gg_tile.hpp: K-major operands
+// are staged in the K
 // layout, M-/N-major operands (the natural layouts of X and dY) are staged
 // untransposed in the MN layout and transposed by the LDS transpose reads.
 #include "gg_internal.hpp"
@@ -24,25 +25,52 @@ namespace gg {
 using WgradCfg = Cfg<256, 256, 4, 2>;
 
 // Output: rows of 8 consecutive columns per lane (16-byte bf16/fp16 or
-// 32-byte fp32 accesses), accumulate mode adding the old values.
+// 32-byte fp32 accesses), accumulate mode adding the old values, which are
+// loaded 28 items ahead (14 for fp32); items off the tile load element 0
+// (always present) and store nothing.
 template <class C>
 __device__ __forceinline__ void wgrad_epilogue(const f32x16 (&acc)[C::MB][C::NB], float* lds,
                                                void* out, int dtype, int hidden, int inter,
                                                int row0, int col0, int accumulate) {
-    for_each_row8<C>(acc, lds, [&](int, int r, int c, float (&v)[8]) {
-        const int row = row0 + r, col = col0 + c;
-        if (row < hidden && col < inter) {
-            const int64_t idx = (int64_t)row * inter + col;
-            if (accumulate) {
-                float o[8];
-                load8(out, dtype, idx, o);
-#pragma unroll
-                for (int k = 0; k < 8; k++)
-                    v[k] += o[k];
+    auto walk = [&](auto W32, auto ACC) {
+        constexpr bool w32 = decltype(W32)::value, add = decltype(ACC)::value;
+        using Pre = Pre8<w32, 1>;
+        auto load = [&](int, int r, int c) {
+            Pre pre;
+            if constexpr (add) {
+                const int row = row0 + r, col = col0 + c;
+                const bool ok = (row < hidden) & (col < inter);
+                pre.x[0] = raw8_load<w32>(out, ok ? (int64_t)row * inter + col : 0);
             }
-            store8(out, dtype, idx, v);
-        }
-    });
+            return pre;
+        };
+        auto fn = [&](int, int r, int c, float (&v)[8], const Pre& pre) {
+            const int row = row0 + r, col = col0 + c;
+            if (row < hidden && col < inter) {
+                const int64_t idx = (int64_t)row * inter + col;
+                if constexpr (add) {
+                    float o[8];
+                    raw8_cvt<w32>(pre.x[0], dtype, o);
+#pragma unroll
+                    for (int k = 0; k < 8; k++)
+                        v[k] += o[k];
+                }
+                store8(out, dtype, idx, v);
+            }
+        };
+        for_each_row8<C, add ? (w32 ? 14 : 28) : 1>(acc, lds, load, fn);
+    };
+    if (dtype == kF32) {
+        if (accumulate)
+            walk(std::true_type(), std::true_type());
+        else
+            walk(std::true_type(), std::false_type());
+    } else {
+        if (accumulate)
+            walk(std::false_type(), std::true_type());
+        else
+            walk(std::false_type(), std::false_type());
+    }
 }
 
 template <class C, bool A_K, bool B_K>
@@ -87,22 +115,40 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     const char* a = (const char*)p.a;
     const char* b = (const char*)p.b;
     const int64_t T2 = p.T * 2;
-    auto issue = [&](char* st, int kt) {
-        const int64_t k0 = begin + (int64_t)kt * 64;
-        if constexpr (A_K)
-            stage_k<C, TM>(st, a + (int64_t)m0 * T2, T2, p.hidden - m0, k0 * 2, end * 2);
-        else
-            stage_mn<C>(st, a + (k0 * p.hidden + m0) * 2, (int64_t)p.hidden * 2, p.hidden - m0, end - k0);
-        if constexpr (B_K)
-            stage_k<C, TN>(st + TM * kRowBytes, b + (int64_t)n0 * T2, T2, p.inter - n0, k0 * 2, end * 2);
-        else
-            stage_mn<C>(st + TM * kRowBytes, b + (k0 * p.inter + n0) * 2, (int64_t)p.inter * 2,
-                        p.inter - n0, end - k0);
+    std::conditional_t<A_K, LoadK<C, TM>, LoadMN<C>> la;
+    std::conditional_t<B_K, LoadK<C, TN>, LoadMN<C>> lb;
+    if constexpr (A_K)
+        la.init(T2, p.hidden - m0);
+    else
+        la.init((int64_t)p.hidden * 2, p.hidden - m0);
+    if constexpr (B_K)
+        lb.init(T2, p.inter - n0);
+    else
+        lb.init((int64_t)p.inter * 2, p.inter - n0);
+    using LA = std::conditional_t<A_K, LoadK<C, TM>, LoadMN<C>>;
+    using LB = std::conditional_t<B_K, LoadK<C, TN>, LoadMN<C>>;
+    auto issue = [&](uint32_t st, int u, int i) {
+        const int64_t k0 = begin + (int64_t)u * 64;
+        if (i < LA::kN) {
+            if constexpr (A_K)
+                la.template issue<true>(st, a + (int64_t)m0 * T2 + k0 * 2, (end - k0) * 2, i);
+            else
+                la.issue(st, a + (k0 * p.hidden + m0) * 2, end - k0, i);
+        } else {
+            if constexpr (B_K)
+                lb.template issue<true>(st + TM * kRowBytes, b + (int64_t)n0 * T2 + k0 * 2,
+                                        (end - k0) * 2, i - LA::kN);
+            else
+                lb.issue(st + TM * kRowBytes, b + (k0 * p.inter + n0) * 2, end - k0, i - LA::kN);
+        }
     };
-    auto compute = [&](char* st, int) {
-        mfma_stage_bf16<C, A_K, B_K>(st, st + TM * kRowBytes, am0, bn0, acc);
+    auto read = [&](const char* st, int kt, FragBf16<C>& f, int g) {
+        read_bf16<C, A_K, B_K>(st, st + TM * kRowBytes, am0, bn0, kt & 1, f, g);
     };
-    mainloop<C>(smem, (int)((cnt + 63) / 64), issue, compute);
+    auto mma = [&](const FragBf16<C>& f, int m0_, int m1_) { mma_bf16<C>(f, acc, m0_, m1_); };
+    FragBf16<C> frag[2];
+    pipeline<C, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB>(smem, (int)((cnt + 31) / 32),
+                                                                   frag, issue, read, mma);
 
     void* out = p.out_dense
         ? (void*)((char*)p.out_dense +
