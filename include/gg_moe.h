@@ -197,7 +197,7 @@ size_t gg_dglu_workspace_size(int32_t L, int32_t n, int32_t generate_dbias);
  * a          A (m_rows, k) bf16, K-major: a[m*k + kk].
  * m_rows     rows of A, C, D, prob, dprob; >= valid_m = padded_offsets[L-1].
  *            Rows at or past valid_m are neither read for output nor written.
- * k          reduction size, a multiple of 64.
+ * k          reduction size, a multiple of 64, at most 2^21.
  * b_dense    dense weights, the pages' (N, K, L) tensor with strides
  *            (K, 1, N*K): expert g's (n, k) element at b[g*n*k + n*k + kk].
  * b_ptrs     or: int64[L] device array, expert g's (n, k) bf16 matrix at
@@ -205,7 +205,8 @@ size_t gg_dglu_workspace_size(int32_t L, int32_t n, int32_t generate_dbias);
  *            GG_MAJOR_K, N-major (element at kk*n + nn) when GG_MAJOR_N.
  *            Exactly one of b_dense / b_ptrs is non-NULL; b_dense requires
  *            GG_MAJOR_K.
- * n          compact gradient width N, a multiple of 32.
+ * n          compact gradient width N, a multiple of 32, at most 2^20
+ *            (GG_ERR_UNSUPPORTED beyond either limit).
  * c          forward activation (m_rows, 2n), row-major, dtype c_dtype
  *            (GG_BF16, GG_F16 or GG_F32).
  * padded_offsets  int32[L] cumulative group ends, each group a multiple of
@@ -255,13 +256,14 @@ size_t gg_dsrelu_workspace_size(int32_t L);
  * sfa        E8M0 scales (m_rows, k/32), row-major: sfa[m*(k/32) + kk/32].
  *            (A plain row-major layout; the pages' 6-D MMA-interleaved scale
  *            layout is not used.)
- * m_rows     as for gg_dglu.  k: a multiple of 128.
+ * m_rows     as for gg_dglu.  k: a multiple of 128, at most 2^21.
  * b_fp8,sfb  dense weights (L, n, k) E4M3, element at b[g*n*k + nn*k + kk],
  *            and scales (L, n, k/32) at sfb[(g*n + nn)*(k/32) + kk/32];
  * b_ptrs, sfb_ptrs  or: int64[L] device arrays of per-expert (n, k) codes
  *            and (n, k/32) scales with the same in-matrix layout.
  *            Exactly one of the dense pair / the pointer pair is given.
- * n          a multiple of 32.
+ * n          a multiple of 32, at most 2^21 (GG_ERR_UNSUPPORTED beyond either
+ *            limit).
  * c          (m_rows, n) row-major, c_dtype GG_BF16, GG_F16 or GG_F32.
  * padded_offsets, L  as for gg_dglu.
  * alpha      float[L];  prob  float[m_rows].

@@ -255,8 +255,8 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k, const void* b_dense,
         return fail(GG_ERR_SHAPE, "k must be positive");
     if (k % 64)
         return fail(GG_ERR_UNSUPPORTED, "k must be a multiple of 64");
-    if (k > (1 << 21) || n > (1 << 21))
-        return fail(GG_ERR_UNSUPPORTED, "k and n are limited to 2^21");
+    if (k > (1 << 21) || n > (1 << 20))
+        return fail(GG_ERR_UNSUPPORTED, "k is limited to 2^21 and n to 2^20");
     if (!aligned16(a) || !aligned16(b_dense) || !aligned16(b_ptrs) || !aligned16(dbias) ||
         ((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u))
         return fail(GG_ERR_ALIGN, "a, b and dbias must be 16-byte aligned");

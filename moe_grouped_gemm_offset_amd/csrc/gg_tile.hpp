@@ -431,13 +431,9 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
     return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// fp32 -> bf16 / fp16, round to nearest even (NaN kept quiet).
+// fp32 -> bf16 / fp16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);      // v_cvt_pk_bf16_f32: RNE
 }
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {
     _Float16 h = (_Float16)f;
@@ -560,6 +556,72 @@ __device__ __forceinline__ void raw8_cvt(const Raw8<W32>& r, int dtype, float (&
 }
 
 // ---------------------------------------------------------------------------
+// Eight consecutive elements of a bf16 / fp16 / fp32 row (16 or 32 bytes)
+// through a buffer descriptor, with the element type a runtime value and no
+// branch: both 16-byte halves are always issued, the second at kInvalid
+// (load zeros / store nothing) for 16-bit types, and conversions select
+// between the formats.  An item whose offset is kInvalid is masked the same
+// way.  Branch-free item code keeps the compiler's memory-counter waits
+// exact, so that many loads can be in flight ahead of their use.
+// ---------------------------------------------------------------------------
+struct RawB8 {
+    u32x4 w[2];
+};
+
+// Bitwise select (mask all ones: a, all zeros: b): the conditions here are
+// workgroup-uniform, and a ternary would let the compiler branch.
+__device__ __forceinline__ uint32_t bsel(uint32_t mask, uint32_t a, uint32_t b) {
+    return (a & mask) | (b & ~mask);
+}
+
+// Element format of a row piece: bytes per element and, for 16-bit, fp16
+// rather than bf16 (w32, f16 as flags; m32, m16 as all-ones masks).
+struct Fmt8 {
+    uint32_t w32, f16, m32, m16;
+    __device__ __forceinline__ explicit Fmt8(int dtype)
+        : w32(dtype == kF32), f16(dtype == kF16), m32(0u - w32), m16(0u - f16) {}
+    // byte offset of element i (a multiple of 8), or kInvalid
+    __device__ __forceinline__ uint32_t off(bool ok, int64_t i) const {
+        return ok ? (uint32_t)(i << (w32 ? 2 : 1)) : kInvalid;
+    }
+};
+
+__device__ __forceinline__ RawB8 rawb8_load(__amdgpu_buffer_rsrc_t r, const Fmt8& fm, uint32_t off) {
+    RawB8 x;
+    x.w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    x.w[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          r, fm.w32 ? off + 16 : kInvalid, 0, 0));
+    return x;
+}
+
+__device__ __forceinline__ void rawb8_cvt(const RawB8& x, const Fmt8& fm, float (&v)[8]) {
+    const uint32_t ws[8] = {x.w[0].x, x.w[0].y, x.w[0].z, x.w[0].w,
+                            x.w[1].x, x.w[1].y, x.w[1].z, x.w[1].w};
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const uint32_t h = (ws[k >> 1] >> (16 * (k & 1))) & 0xffffu;   // 16-bit element k
+        const uint32_t v16 = bsel(fm.m16, __builtin_bit_cast(uint32_t, f16_to_f32((uint16_t)h)), h << 16);
+        v[k] = __builtin_bit_cast(float, bsel(fm.m32, ws[k], v16));
+    }
+}
+
+__device__ __forceinline__ void rawb8_store(__amdgpu_buffer_rsrc_t r, const Fmt8& fm, uint32_t off,
+                                           const float (&v)[8]) {
+    uint32_t a[4], b[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t lo = bsel(fm.m16, f32_to_f16(v[2 * k]), f32_to_bf16(v[2 * k]));
+        const uint32_t hi = bsel(fm.m16, f32_to_f16(v[2 * k + 1]), f32_to_bf16(v[2 * k + 1]));
+        a[k] = bsel(fm.m32, __builtin_bit_cast(uint32_t, v[k]), lo | (hi << 16));
+        b[k] = __builtin_bit_cast(uint32_t, v[4 + k]);
+    }
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)a[0], (int)a[1], (int)a[2], (int)a[3]}, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)b[0], (int)b[1], (int)b[2], (int)b[3]}, r,
+                                           fm.w32 ? off + 16 : kInvalid, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // Row walk of a wave's accumulators (32 MB rows x 32 NB columns, MB and NB
 // even).  The MFMA layout gives a lane one column and 16 rows of a block;
 // stores want a lane to own consecutive columns of one row.  The walk stages
@@ -625,10 +687,16 @@ __device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB],
 }
 
 // Loads of one row-walk item: NC raw 8-element loads and one fp32 per-row
-// value.
+// value (plain pointers, compile-time width; or buffer descriptors, runtime
+// width).
 template <bool W32, int NC>
 struct Pre8 {
     Raw8<W32> x[NC];
+    float row;
+};
+template <int NC>
+struct PreB8 {
+    RawB8 x[NC];
     float row;
 };
 

@@ -26,51 +26,33 @@ using WgradCfg = Cfg<256, 256, 4, 2>;
 
 // Output: rows of 8 consecutive columns per lane (16-byte bf16/fp16 or
 // 32-byte fp32 accesses), accumulate mode adding the old values, which are
-// loaded 28 items ahead (14 for fp32); items off the tile load element 0
-// (always present) and store nothing.
+// loaded 8 items ahead.  Items off the tile have masked loads and stores.
 template <class C>
 __device__ __forceinline__ void wgrad_epilogue(const f32x16 (&acc)[C::MB][C::NB], float* lds,
                                                void* out, int dtype, int hidden, int inter,
                                                int row0, int col0, int accumulate) {
-    auto walk = [&](auto W32, auto ACC) {
-        constexpr bool w32 = decltype(W32)::value, add = decltype(ACC)::value;
-        using Pre = Pre8<w32, 1>;
-        auto load = [&](int, int r, int c) {
-            Pre pre;
-            if constexpr (add) {
-                const int row = row0 + r, col = col0 + c;
-                const bool ok = (row < hidden) & (col < inter);
-                pre.x[0] = raw8_load<w32>(out, ok ? (int64_t)row * inter + col : 0);
-            }
-            return pre;
-        };
-        auto fn = [&](int, int r, int c, float (&v)[8], const Pre& pre) {
-            const int row = row0 + r, col = col0 + c;
-            if (row < hidden && col < inter) {
-                const int64_t idx = (int64_t)row * inter + col;
-                if constexpr (add) {
-                    float o[8];
-                    raw8_cvt<w32>(pre.x[0], dtype, o);
-#pragma unroll
-                    for (int k = 0; k < 8; k++)
-                        v[k] += o[k];
-                }
-                store8(out, dtype, idx, v);
-            }
-        };
-        for_each_row8<C, add ? (w32 ? 14 : 28) : 1>(acc, lds, load, fn);
+    const Fmt8 fo(dtype);
+    // offsets (r inter + col) bytes from the wave tile's first row: r < 128,
+    // inter <= 2^21
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)out + (int64_t)row0 * inter * (fo.w32 ? 4 : 2));
+    auto load = [&](int, int r, int c) {
+        const int row = row0 + r, col = col0 + c;
+        const bool ok = (row < hidden) & (col < inter) & (accumulate != 0);
+        PreB8<1> pre;
+        pre.x[0] = rawb8_load(ro, fo, fo.off(ok, (int64_t)r * inter + col));
+        return pre;
     };
-    if (dtype == kF32) {
-        if (accumulate)
-            walk(std::true_type(), std::true_type());
-        else
-            walk(std::true_type(), std::false_type());
-    } else {
-        if (accumulate)
-            walk(std::false_type(), std::true_type());
-        else
-            walk(std::false_type(), std::false_type());
-    }
+    auto fn = [&](int, int r, int c, float (&v)[8], const PreB8<1>& pre) {
+        const int row = row0 + r, col = col0 + c;
+        const bool ok = (row < hidden) & (col < inter);
+        float o[8];
+        rawb8_cvt(pre.x[0], fo, o);          // zeros unless accumulating
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            v[k] += o[k];
+        rawb8_store(ro, fo, fo.off(ok, (int64_t)r * inter + col), v);
+    };
+    for_each_row8<C, 8>(acc, lds, load, fn);
 }
 
 template <class C, bool A_K, bool B_K>
@@ -103,7 +85,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     const int w = threadIdx.x >> 6;
     const int wm = w / C::WN, wn = w % C::WN;
     const int m0 = mt * TM, n0 = nt * TN;
-    const int am0 = wm * (TM / C::WM), bn0 = wn * (TN / C::WN);   // wave offsets in the tile
+    const int am0 = uniform(wm * (TM / C::WM)), bn0 = uniform(wn * (TN / C::WN));   // wave offsets in the tile
 
     f32x16 acc[C::MB][C::NB];
 #pragma unroll
