@@ -222,6 +222,53 @@ def dsrelu_inputs(L, K, N, counts, c_dtype=torch.bfloat16, m_extra=0, seed=0,
                 counts=counts, L=L, K=K, N=N, M=M, valid_m=valid_m)
 
 
+
+def dglu_mx_inputs(L, K, N, counts, c_std=2.0, c_dtype=torch.bfloat16, m_extra=0,
+                   seed=0, device="cpu", discrete=True, scale_spread=0, ints=False):
+    """Inputs of the grouped block-scaled dgrad + dGLU.
+
+    A (M, K) and B (N, K) per expert are N(0,1) values (integers in [-2, 2]
+    with ints=True, which E4M3 and bf16 both hold exactly) MXFP8-encoded by
+    mx_encode; scale_spread > 0 multiplies each row by 2^j, j uniform in
+    [-scale_spread, scale_spread], before encoding.  C (M, 2N) N(0, c_std),
+    prob U(0,1), alpha and beta U(0.5,1.5)."""
+    counts = np.asarray(counts, np.int64)
+    valid_m = int(counts.sum())
+    M = valid_m + m_extra
+    g = _gen(seed, device)
+
+    def draw(rows):
+        if ints:
+            x = torch.randint(-2, 3, (rows, K), generator=g, device=device).float()
+        else:
+            x = torch.randn((rows, K), generator=g, device=device, dtype=torch.float32)
+        if scale_spread:
+            j = torch.randint(-scale_spread, scale_spread + 1, (rows, 1), generator=g,
+                              device=device).float()
+            x = x * torch.exp2(j)
+        return mx_encode(x)
+
+    a, sfa = draw(M)
+    bl, sl = [], []
+    for _ in range(L):
+        q, s = draw(N)
+        bl.append(q)
+        sl.append(s)
+    b_dense = sfb_dense = None
+    if not discrete:
+        b_dense = torch.stack(bl).contiguous()
+        sfb_dense = torch.stack(sl).contiguous()
+        bl = [b_dense[i] for i in range(L)]
+        sl = [sfb_dense[i] for i in range(L)]
+    c = normal((M, 2 * N), c_std, g, device, c_dtype)
+    prob = uniform((M,), 0.0, 1.0, g, device)
+    alpha = uniform((L,), 0.5, 1.5, g, device)
+    beta = uniform((L,), 0.5, 1.5, g, device)
+    return dict(a=a, sfa=sfa, b_dense=b_dense, sfb_dense=sfb_dense, b_list=bl,
+                sfb_list=sl, c=c, prob=prob, alpha=alpha, beta=beta,
+                padded_offsets=torch.from_numpy(cumulative(counts)).to(device),
+                counts=counts, L=L, K=K, N=N, M=M, valid_m=valid_m)
+
 # The five named workloads (sizes and recipes; seeds 1000 + index).
 WORKLOADS = {
     "wgrad_small": dict(kind="wgrad", hidden=256, inter=256,

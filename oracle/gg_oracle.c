@@ -13,7 +13,8 @@
  *   [G] "Grouped GEMM + dGLU (SM100)": "BF16 contract / Tensors, layouts, and
  *       equation" (R_g = alpha_g^2 A_g B_g^T, X_g = beta_g C_g, the dSwiGLU and
  *       dGeGLU formulas, dprob and dbias), and "Block-scaled contract /
- *       Equations", steps 1 and 2 (interleave order, dprob reduction).
+ *       Equations", steps 1 and 2 (the dequantized GEMM, interleave order,
+ *       dprob reduction) and "Shapes" (per-group amax of shape (L, 2, 1)).
  *   [S] "Grouped GEMM + dsReLU (SM100)": "Equations" (G, D_row, dprob), and
  *       "Shapes" (per-expert Amax).
  *
@@ -28,6 +29,7 @@
 #include <math.h>
 #include <omp.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* Threads the OpenMP loops of this file use (reported with its timings). */
@@ -273,6 +275,70 @@ static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
  *   D[r*2N + c]     the interleaved gradient for listed row r;
  *   dprob_sum[r]    sum over n of R * (unscaled activation);
  *   dbias_sum[g*2N + c]  (if non-NULL) sum over the listed rows of group g. */
+/* The dGLU epilogue of [G] for one row m of group g, given that row's R
+ * values R[n], n < N: writes the interleaved gradient D[0 .. 2N) and returns
+ * the dprob sum.  Arguments as for orc_dglu. */
+static double dglu_row(const double* R, int64_t m, int g, int N,
+                       const void* C, int c_dtype, const float* beta, const float* prob,
+                       int act, double ga, double clamp_lo, double clamp_hi, double lo,
+                       int gate_first, int mask_filter, double* D) {
+    int64_t N2 = 2 * (int64_t)N;
+    double pr = (double)prob[m];
+    double dp = 0.0;
+    for (int n = 0; n < N; n++) {
+        /* 32-wide blocks: compact column n sits in pair p at offset j. */
+        int p = n / 32, j = n % 32;
+        int64_t c_in = 64 * (int64_t)p + (gate_first ? 32 : 0) + j;
+        int64_t c_gt = 64 * (int64_t)p + (gate_first ? 0 : 32) + j;
+        /* X = beta_g * C as one fp32 product (see the file header). */
+        float xin = beta[g] * (float)orc_decode(C, c_dtype, m * N2 + c_in);
+        float xgt = beta[g] * (float)orc_decode(C, c_dtype, m * N2 + c_gt);
+        double u = xin, gt = xgt, d_in, d_gt, a;
+        if (act == 0) {
+            /* dSwiGLU with s = sigmoid(gate):
+             *   dinput = R prob gate s
+             *   dgate  = R prob input s (1 + gate (1 - s))
+             * and the unscaled activation is swish(gate) * input. */
+            double s = sigmoid(gt);
+            d_in = R[n] * pr * gt * s;
+            d_gt = R[n] * pr * u * s * (1.0 + gt * (1.0 - s));
+            a = gt * s * u;
+        } else {
+            /* dGeGLU: clamped values feed the activation, the filters
+             * carry the raw value where it lies inside the clamp. */
+            double gc = gt < clamp_hi ? gt : clamp_hi;
+            double uc = u < clamp_lo ? clamp_lo : (u > clamp_hi ? clamp_hi : u);
+            int g_in = gt <= clamp_hi;
+            int u_in = u >= clamp_lo && u <= clamp_hi;
+            double gf = g_in ? (mask_filter ? 1.0 : gt) : 0.0;
+            double uf = u_in ? (mask_filter ? 1.0 : u) : 0.0;
+            double s = sigmoid(ga * gc);
+            d_gt = R[n] * pr * (uc + lo) * s * (1.0 + ga * gc * (1.0 - s)) * gf;
+            d_in = R[n] * pr * gc * s * uf;
+            a = gc * s * (uc + lo);
+        }
+        dp += R[n] * a;
+        D[c_in] = d_in;
+        D[c_gt] = d_gt;
+    }
+    return dp;
+}
+
+/* dbias of [G]: per-expert row reduction of the interleaved output over the
+ * listed rows. */
+static void dglu_dbias(const double* D, const int32_t* po, int L, int N, const int64_t* rows,
+                       int64_t nrows, double* dbias_sum) {
+    int64_t N2 = 2 * (int64_t)N;
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t m = rows ? rows[r] : r;
+        int g = group_of_row(po, L, m);
+        if (g < 0)
+            continue;
+        for (int64_t c = 0; c < N2; c++)
+            dbias_sum[g * N2 + c] += D[r * N2 + c];
+    }
+}
+
 void orc_dglu(const uint16_t* A, int64_t M, int K,
               const uint16_t* const* Bp, int b_major, int N,
               const void* C, int c_dtype, const int32_t* po, int L,
@@ -284,70 +350,100 @@ void orc_dglu(const uint16_t* A, int64_t M, int K,
     if (!rows)
         nrows = M;
     int64_t N2 = 2 * (int64_t)N;
-#pragma omp parallel for schedule(dynamic, 4)
-    for (int64_t r = 0; r < nrows; r++) {
-        int64_t m = rows ? rows[r] : r;
-        int g = group_of_row(po, L, m);
-        if (g < 0)
-            continue;
-        const uint16_t* Bg = Bp[g];
-        double a2 = (double)alpha[g] * (double)alpha[g];
-        double pr = (double)prob[m];
-        double dp = 0.0;
-        for (int n = 0; n < N; n++) {
-            /* R_g[m, n] = alpha_g^2 * sum_k A[m,k] * B_g[n,k] */
-            double acc = 0.0;
-            for (int k = 0; k < K; k++) {
-                int64_t ib = b_major == 0 ? (int64_t)n * K + k : (int64_t)k * N + n;
-                acc += orc_bf16_to_double(A[m * K + k]) * orc_bf16_to_double(Bg[ib]);
-            }
-            double R = a2 * acc;
-            /* 32-wide blocks: compact column n sits in pair p at offset j. */
-            int p = n / 32, j = n % 32;
-            int64_t c_in = 64 * (int64_t)p + (gate_first ? 32 : 0) + j;
-            int64_t c_gt = 64 * (int64_t)p + (gate_first ? 0 : 32) + j;
-            /* X = beta_g * C as one fp32 product (see the file header). */
-            float xin = beta[g] * (float)orc_decode(C, c_dtype, m * N2 + c_in);
-            float xgt = beta[g] * (float)orc_decode(C, c_dtype, m * N2 + c_gt);
-            double u = xin, gt = xgt, d_in, d_gt, a;
-            if (act == 0) {
-                /* dSwiGLU with s = sigmoid(gate):
-                 *   dinput = R prob gate s
-                 *   dgate  = R prob input s (1 + gate (1 - s))
-                 * and the unscaled activation is swish(gate) * input. */
-                double s = sigmoid(gt);
-                d_in = R * pr * gt * s;
-                d_gt = R * pr * u * s * (1.0 + gt * (1.0 - s));
-                a = gt * s * u;
-            } else {
-                /* dGeGLU: clamped values feed the activation, the filters
-                 * carry the raw value where it lies inside the clamp. */
-                double gc = gt < clamp_hi ? gt : clamp_hi;
-                double uc = u < clamp_lo ? clamp_lo : (u > clamp_hi ? clamp_hi : u);
-                int g_in = gt <= clamp_hi;
-                int u_in = u >= clamp_lo && u <= clamp_hi;
-                double gf = g_in ? (mask_filter ? 1.0 : gt) : 0.0;
-                double uf = u_in ? (mask_filter ? 1.0 : u) : 0.0;
-                double s = sigmoid(ga * gc);
-                d_gt = R * pr * (uc + lo) * s * (1.0 + ga * gc * (1.0 - s)) * gf;
-                d_in = R * pr * gc * s * uf;
-                a = gc * s * (uc + lo);
-            }
-            dp += R * a;
-            D[r * N2 + c_in] = d_in;
-            D[r * N2 + c_gt] = d_gt;
-        }
-        dprob_sum[r] = dp;
-    }
-    /* dbias: per-expert row reduction of the interleaved output. */
-    if (dbias_sum) {
+#pragma omp parallel
+    {
+        double* R = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 4)
         for (int64_t r = 0; r < nrows; r++) {
             int64_t m = rows ? rows[r] : r;
             int g = group_of_row(po, L, m);
             if (g < 0)
                 continue;
-            for (int64_t c = 0; c < N2; c++)
-                dbias_sum[g * N2 + c] += D[r * N2 + c];
+            const uint16_t* Bg = Bp[g];
+            double a2 = (double)alpha[g] * (double)alpha[g];
+            for (int n = 0; n < N; n++) {
+                /* R_g[m, n] = alpha_g^2 * sum_k A[m,k] * B_g[n,k] */
+                double acc = 0.0;
+                for (int k = 0; k < K; k++) {
+                    int64_t ib = b_major == 0 ? (int64_t)n * K + k : (int64_t)k * N + n;
+                    acc += orc_bf16_to_double(A[m * K + k]) * orc_bf16_to_double(Bg[ib]);
+                }
+                R[n] = a2 * acc;
+            }
+            dprob_sum[r] = dglu_row(R, m, g, N, C, c_dtype, beta, prob, act, ga, clamp_lo,
+                                    clamp_hi, lo, gate_first, mask_filter, D + r * N2);
+        }
+        free(R);
+    }
+    if (dbias_sum)
+        dglu_dbias(D, po, L, N, rows, nrows, dbias_sum);
+}
+
+/* [G] "Block-scaled contract / Equations", steps 1 and 2, on MXFP8 operands:
+ * R_g = alpha_g^2 * sum_k deq(A[m,k]) deq(B_g[n,k]), with deq(q) = e4m3(q) *
+ * 2^(e8m0 - 127) and one E8M0 scale per 32 K values of a row, then the dGLU
+ * epilogue of orc_dglu.
+ *   A (M, K) E4M3, K-major; SFA (M, K/32) E8M0: SFA[m*(K/32) + k/32].
+ *   Bp[g] -> expert g's (N, K) E4M3, K-major; SFBp[g] -> its (N, K/32).
+ * Other arguments and outputs as for orc_dglu, plus
+ *   amax[2g + h] (h 0: the input-gradient columns, 1: the gate-gradient
+ *   columns) raised to max |D| over the listed rows of group g (the caller
+ *   initialises it). */
+void orc_dglu_mx(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
+                 const uint8_t* const* Bp, const uint8_t* const* SFBp, int N,
+                 const void* C, int c_dtype, const int32_t* po, int L,
+                 const float* alpha, const float* beta, const float* prob,
+                 int act, double ga, double clamp_lo, double clamp_hi, double lo,
+                 int gate_first, int mask_filter,
+                 const int64_t* rows, int64_t nrows,
+                 double* D, double* dprob_sum, double* dbias_sum, double* amax) {
+    if (!rows)
+        nrows = M;
+    int64_t N2 = 2 * (int64_t)N;
+    int KB = K / 32;
+#pragma omp parallel
+    {
+        double* R = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; r++) {
+            int64_t m = rows ? rows[r] : r;
+            int g = group_of_row(po, L, m);
+            if (g < 0)
+                continue;
+            const uint8_t* Bg = Bp[g];
+            const uint8_t* Sg = SFBp[g];
+            double a2 = (double)alpha[g] * (double)alpha[g];
+            for (int n = 0; n < N; n++) {
+                double acc = 0.0;
+                for (int k = 0; k < K; k++) {
+                    double da = orc_e4m3_to_double(A[m * K + k]) *
+                                orc_e8m0_to_double(SFA[m * KB + k / 32]);
+                    double db = orc_e4m3_to_double(Bg[(int64_t)n * K + k]) *
+                                orc_e8m0_to_double(Sg[(int64_t)n * KB + k / 32]);
+                    acc += da * db;
+                }
+                R[n] = a2 * acc;
+            }
+            dprob_sum[r] = dglu_row(R, m, g, N, C, c_dtype, beta, prob, act, ga, clamp_lo,
+                                    clamp_hi, lo, gate_first, mask_filter, D + r * N2);
+        }
+        free(R);
+    }
+    if (dbias_sum)
+        dglu_dbias(D, po, L, N, rows, nrows, dbias_sum);
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t m = rows ? rows[r] : r;
+        int g = group_of_row(po, L, m);
+        if (g < 0)
+            continue;
+        for (int64_t c = 0; c < N2; c++) {
+            /* column c is an input-gradient column when its 32-block within
+             * the 64-column pair is the input block */
+            int in_block = ((c % 64) < 32) != (gate_first != 0);
+            double v = fabs(D[r * N2 + c]);
+            double* slot = &amax[2 * g + (in_block ? 0 : 1)];
+            if (v > *slot)
+                *slot = v;
         }
     }
 }

@@ -65,6 +65,9 @@ def lib():
         L.orc_dsrelu.argtypes = [P, P, I64, I, P, P, I, P, I, P, I, P, P,
                                  P, I64, P, P, P]
         L.orc_dsrelu.restype = None
+        L.orc_dglu_mx.argtypes = [P, P, I64, I, P, P, I, P, I, P, I, P, P, P,
+                                  I, D, D, D, D, I, I, P, I64, P, P, P, P]
+        L.orc_dglu_mx.restype = None
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = I
         _lib = L
@@ -223,6 +226,55 @@ def _valid_rows(po, m_rows, rr):
     valid_m = int(po[-1]) if po.size else 0
     idx = np.arange(m_rows) if rr is None else rr
     return idx < valid_m
+
+
+# --------------------------------------------------------------------------
+# block-scaled grouped dgrad + dGLU (MXFP8)
+# --------------------------------------------------------------------------
+
+def dglu_mx(a, sfa, m_rows, k, b_list, sfb_list, n, c, c_dtype, padded_offsets,
+            alpha, beta, prob, act=DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0,
+            clamp_max=7.0, linear_offset=1.0, gate_first=False, mask_filter=False,
+            d_dtype=BF16, dprob_in=None, dbias_in=None, rows=None):
+    """Block-scaled (MXFP8) grouped dgrad fused with dSwiGLU / dGeGLU.
+
+    a: uint8 e4m3 codes (m_rows, k); sfa: uint8 e8m0 (m_rows, k/32);
+    b_list / sfb_list: per expert K-major (n, k) codes and (n, k/32) scales;
+    c: (m_rows, 2n) in c_dtype bits.  Returns what dglu returns, plus amax
+    (float64 (L, 2): max |D| of the input-gradient and the gate-gradient
+    columns of each expert's listed rows, from 0)."""
+    po = _c(padded_offsets, np.int32)
+    L = po.size
+    a = _c(a, np.uint8).ravel()
+    sfa = _c(sfa, np.uint8).ravel()
+    bl = [_c(x, np.uint8).ravel() for x in b_list]
+    sl = [_c(x, np.uint8).ravel() for x in sfb_list]
+    assert len(bl) == L and len(sl) == L
+    bptr = (ctypes.c_void_p * L)(*[x.ctypes.data for x in bl])
+    sptr = (ctypes.c_void_p * L)(*[x.ctypes.data for x in sl])
+    c = _c(c, _DT_NP[c_dtype]).ravel()
+    rr = None if rows is None else _c(rows, np.int64)
+    nrows = m_rows if rr is None else rr.size
+    D = np.zeros((nrows, 2 * n), np.float64)
+    dps = np.zeros(nrows, np.float64)
+    want_bias = dbias_in is not None
+    dbs = np.zeros((L, 2 * n), np.float64) if want_bias else None
+    amax = np.zeros((L, 2), np.float64)
+    lib().orc_dglu_mx(_p(a), _p(sfa), m_rows, k, ctypes.cast(bptr, ctypes.c_void_p),
+                      ctypes.cast(sptr, ctypes.c_void_p), n, _p(c), c_dtype, _p(po), L,
+                      _p(_c(alpha, np.float32)), _p(_c(beta, np.float32)),
+                      _p(_c(prob, np.float32)), act, geglu_alpha, clamp_min, clamp_max,
+                      linear_offset, int(bool(gate_first)), int(bool(mask_filter)),
+                      _p(rr), nrows, _p(D), _p(dps), _p(dbs), _p(amax))
+    valid = _valid_rows(po, m_rows, rr)
+    out = {"D": D, "D_q": round_to(D, d_dtype), "valid": valid, "amax": amax}
+    dp_in = np.zeros(m_rows, np.float32) if dprob_in is None else np.asarray(dprob_in, np.float32)
+    dp_in = dp_in if rr is None else dp_in[rr]
+    out["dprob"] = dp_in.astype(np.float64) + dps
+    if want_bias:
+        out["dbias"] = decode_array(_c(dbias_in, np.uint16), BF16).reshape(L, 2 * n) + dbs
+        out["dbias_q"] = round_to(out["dbias"], BF16)
+    return out
 
 
 # --------------------------------------------------------------------------
