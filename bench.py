@@ -12,6 +12,12 @@ inputs already resident in HBM:
                            discrete K-major B, dbias
   dsrelu_mxfp8  gg_dsrelu, MXFP8, L 16, K 7168, N 2048, M 65536, dense B
 
+and, as single-op workloads outside the default step:
+
+  dglu_mxfp8    gg_dglu_mx, MXFP8 dSwiGLU with amax, L 32, K 4096, N 1536,
+                M 32768, discrete B (b_ptrs / sfb_ptrs)
+  wgrad_moe_kmajor  the wgrad workload with A K-major
+
 value = algorithmic FLOPs of the step (2 sum_e M_e N_e K_e per GEMM) over the
 measured wall time of K steps.  Every call is also bracketed by HIP events on
 the stream it runs on, which gives each kernel's average duration; the kernel
@@ -33,14 +39,23 @@ if ROOT not in sys.path:
 
 PEAK = {"bf16": 2500.0, "fp8": 5000.0}        # MI355X dense MFMA, TFLOP/s
 HBM_PEAK = 8000.0                              # GB/s
-KERNEL_SOURCES = ["gg_tile.hpp", "gg_wgrad.hip", "gg_dglu.hip", "gg_dsrelu.hip",
-                  "gg_prologue.hip", "gg_api.cpp"]
+# The sources each kernel's code is compiled from (with the build flags of
+# build.py): the HBM traffic recorded for a kernel is reported only while
+# their hash is unchanged.
+KERNEL_SOURCES = {
+    "wgrad_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_wgrad.hip"],
+    "dglu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_dglu_epi.hpp", "gg_dglu.hip"],
+    "dglu_mx_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_dglu_epi.hpp",
+                       "gg_dglu_mx.hip"],
+    "dsrelu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_dsrelu.hip"],
+}
 
 
-def source_hash():
+def source_hash(kernel):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "moe_grouped_gemm_offset_amd", "csrc", f), "rb") as fh:
+    pkg = os.path.join(ROOT, "moe_grouped_gemm_offset_amd")
+    for f in [os.path.join("csrc", x) for x in KERNEL_SOURCES[kernel]] + ["build.py"]:
+        with open(os.path.join(pkg, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -171,6 +186,46 @@ def make_dsrelu(dev):
     return Op("dsrelu_mxfp8", "dsrelu_kernel", synth.flops_dgrad(vm, N, K), "fp8", run, alg, sample)
 
 
+def make_dglu_mx(dev):
+    import numpy as np
+    import torch
+    from moe_grouped_gemm_offset_amd import binding as B, synth
+    from oracle import oracle as orc
+    w = synth.WORKLOADS["dglu_mxfp8"]
+    counts = synth.workload_counts("dglu_mxfp8")
+    inp = synth.dglu_mx_inputs(w["L"], w["K"], w["N"], counts, c_std=w["c_std"], seed=w["seed"],
+                               device=dev, discrete=w["discrete"])
+    M, N, K, L = inp["M"], inp["N"], inp["K"], inp["L"]
+    d = torch.empty(M, 2 * N, dtype=torch.bfloat16, device=dev)
+    dprob = torch.zeros(M, dtype=torch.float32, device=dev)
+    amax = torch.zeros(L, 2, dtype=torch.float32, device=dev)
+    ws = torch.empty(B.gg_dglu_workspace_size(L, N, 0), dtype=torch.uint8, device=dev)
+    a8 = inp["a"].view(torch.uint8)
+    bp = torch.tensor([x.data_ptr() for x in inp["b_list"]], dtype=torch.int64, device=dev)
+    sp = torch.tensor([x.data_ptr() for x in inp["sfb_list"]], dtype=torch.int64, device=dev)
+
+    def run():
+        B.gg_dglu_mx(a8, inp["sfa"], None, None, bp, sp, N, inp["c"], inp["padded_offsets"],
+                     inp["alpha"], inp["beta"], inp["prob"], d, dprob, amax=amax, workspace=ws)
+
+    vm = inp["valid_m"]
+    # A, B and their scales once, C read and D written (bf16, 2N wide), prob
+    # read and dprob written
+    alg = M * K + L * N * K + (M + L * N) * K // 32 + 2 * (M * 2 * N * 2) + 8 * M
+
+    def sample(nrows):
+        cpu = _cpu(inp)
+        rows = np.linspace(0, vm - 1, nrows).astype(np.int64)
+        t0 = time.perf_counter()
+        orc.dglu_mx(synth.bits(cpu["a"]), synth.bits(cpu["sfa"]), M, K,
+                    [synth.bits(x) for x in cpu["b_list"]], [synth.bits(x) for x in cpu["sfb_list"]],
+                    N, synth.bits(cpu["c"]), orc.BF16, cpu["padded_offsets"].numpy(),
+                    cpu["alpha"].numpy(), cpu["beta"].numpy(), cpu["prob"].numpy(), rows=rows)
+        return time.perf_counter() - t0, 2.0 * nrows * N * K
+
+    return Op("dglu_mxfp8", "dglu_mx_kernel", synth.flops_dgrad(vm, N, K), "fp8", run, alg, sample)
+
+
 WORKLOAD_OPS = {
     "moe_backward": ["dswiglu", "wgrad_moe", "dgeglu", "dsrelu_mxfp8"],
     "dswiglu": ["dswiglu"],
@@ -178,6 +233,7 @@ WORKLOAD_OPS = {
     "wgrad_moe_kmajor": ["wgrad_moe_kmajor"],
     "dgeglu": ["dgeglu"],
     "dsrelu_mxfp8": ["dsrelu_mxfp8"],
+    "dglu_mxfp8": ["dglu_mxfp8"],
 }
 
 
@@ -190,6 +246,8 @@ def build_op(name, dev):
         op = make_wgrad(dev, "k")
         op.name = name
         return op
+    if name == "dglu_mxfp8":
+        return make_dglu_mx(dev)
     return make_dsrelu(dev)
 
 
@@ -228,7 +286,7 @@ def calibrate_copy(dev, reps=3):
     del src, dst
 
 
-def summarize_pmc(fetch_csv, write_csv, workload_kernels, src_hash, out_path):
+def summarize_pmc(fetch_csv, write_csv, workload_kernels, out_path):
     """Per-launch HBM traffic of our kernels from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled
     by COPY_BYTES over what it reads for the calibration copy."""
@@ -263,7 +321,7 @@ def summarize_pmc(fetch_csv, write_csv, workload_kernels, src_hash, out_path):
             samples = [x for v in hits for x in v]
             key = f"{kernel}:{workload}"
             if counter == "FETCH_SIZE" or key not in out:
-                out[key] = {"source_hash": src_hash}
+                out[key] = {"source_hash": source_hash(kernel)}
             out[key][counter.lower() + "_bytes"] = sum(samples) / len(samples) * scale
             out[key][counter.lower() + "_scale"] = scale
     for ent in out.values():
@@ -275,14 +333,14 @@ def summarize_pmc(fetch_csv, write_csv, workload_kernels, src_hash, out_path):
     return out
 
 
-def traffic_for(kernel, workload, src_hash):
+def traffic_for(kernel, workload):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
     ent = data.get(f"{kernel}:{workload}")
-    if not ent or ent.get("source_hash") != src_hash:
+    if not ent or ent.get("source_hash") != source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -306,10 +364,11 @@ def main():
         if len(names) != 1:
             sys.exit("--summarize-pmc needs a single-op --workload")
         kernel = {"dswiglu": "dglu_kernel", "dgeglu": "dglu_kernel", "wgrad_moe": "wgrad_kernel",
-                  "wgrad_moe_kmajor": "wgrad_kernel", "dsrelu_mxfp8": "dsrelu_kernel"}[names[0]]
+                  "wgrad_moe_kmajor": "wgrad_kernel", "dsrelu_mxfp8": "dsrelu_kernel",
+                  "dglu_mxfp8": "dglu_mx_kernel"}[names[0]]
         path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
         res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
-                            {names[0]: (kernel, names[0])}, source_hash(), path)
+                            {names[0]: (kernel, names[0])}, path)
         print(json.dumps(res, indent=1))
         return
     if args.gpus != 1:
@@ -359,15 +418,17 @@ def main():
         kernels[op.name] = {"kernel": op.kernel, "ms": round(ms, 4), "gflop": round(op.flops / 1e9, 2),
                             "tflops": round(tf, 1), "peak_frac": round(tf / PEAK[op.dtype], 4),
                             "dtype": op.dtype, "alg_gb_s": round(op.alg_bytes / (ms * 1e-3) / 1e9, 1)}
+        tr = traffic_for(op.kernel, op.name)
+        kernels[op.name]["hbm_gb_per_launch"] = None if tr is None else round(tr / 1e9, 3)
     total_flops = sum(op.flops for op in ops)
     value = total_flops / (ms_step * 1e-3) / 1e12
     dom = max(ops, key=lambda o: kernels[o.name]["ms"])
     kd = kernels[dom.name]
     achieved = dom.flops / (kd["ms"] * 1e-3) / 1e12
-    src = source_hash()
+    src = source_hash(dom.kernel)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK[dom.dtype],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK[dom.dtype], 4),
-                "traffic": traffic_for(dom.kernel, dom.name, src), "kernel": dom.kernel,
+                "traffic": traffic_for(dom.kernel, dom.name), "kernel": dom.kernel,
                 "workload": dom.name, "source_hash": src}
     cpu = None
     if not args.no_cpu_baseline:

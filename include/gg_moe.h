@@ -14,6 +14,10 @@
  *              fused with the dSwiGLU / dGeGLU backward over 32-wide
  *              interleaved blocks of X_g = beta_g C_g, a dprob row reduction
  *              and an optional per-expert dbias.
+ *   gg_dglu_mx "Grouped GEMM + dGLU (SM100)", section "Block-scaled
+ *              contract / Equations": the same fused op on MXFP8 operands,
+ *              R_g = alpha_g^2 deq(A_g) deq(B_g)^T, with the per-expert amax
+ *              of the input and gate halves of D ("Shapes": (L, 2, 1)).
  *   gg_dsrelu  "Grouped GEMM + dsReLU (SM100)", section "Equations":
  *              G = alpha_g deq(A) deq(B)^T on MXFP8 operands,
  *              D_row = prob * 2 * C * relu(G), dprob = sum_n C relu(G)^2,
@@ -234,6 +238,55 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k,
                   gg_act act, float geglu_alpha, float clamp_min, float clamp_max,
                   float linear_offset, uint32_t flags,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Grouped dgrad + dSwiGLU / dGeGLU on MXFP8 operands                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For the rows m of group g ("Grouped GEMM + dGLU (SM100)", "Block-scaled
+ * contract / Equations"):
+ *   R[m,n] = alpha_g^2 * sum_k deq(A[m,k]) deq(B_g[n,k])   (fp32 accumulation)
+ * with deq(q, s) = e4m3(q) * 2^(s - 127), one E8M0 scale byte per 32
+ * consecutive K values of a row (MXFP8: "sf_vec_size 32" in the page's
+ * data-type table), followed by exactly the dSwiGLU / dGeGLU, dprob and dbias
+ * steps documented for gg_dglu.  In addition ("Shapes": amax (L, 2, 1) for
+ * a bf16 / fp16 D):
+ *   amax[2g + 0] = max |D| over the group's input-gradient columns,
+ *   amax[2g + 1] = max |D| over its gate-gradient columns,
+ * taken before rounding (0 for an empty group).
+ *
+ * a_fp8      A (m_rows, k) E4M3 codes, K-major: a[m*k + kk].
+ * sfa        E8M0 scales (m_rows, k/32), row-major: sfa[m*(k/32) + kk/32]
+ *            (a plain layout; the pages' MMA-interleaved scale layout is not
+ *            used).
+ * m_rows     as for gg_dglu.  k: a multiple of 128, at most 2^21.
+ * b_fp8,sfb  dense weights (L, n, k) E4M3, element at b[g*n*k + nn*k + kk],
+ *            and scales (L, n, k/32) at sfb[(g*n + nn)*(k/32) + kk/32];
+ * b_ptrs, sfb_ptrs  or: int64[L] device arrays of per-expert (n, k) codes
+ *            and (n, k/32) scales with the same in-matrix layout (the page's
+ *            discrete b_ptrs / sfb_ptrs).  Exactly one of the dense pair /
+ *            the pointer pair is given.
+ * n          compact width, a multiple of 32, at most 2^20
+ *            (GG_ERR_UNSUPPORTED beyond either limit).
+ * c, c_dtype, padded_offsets, L, alpha, beta, prob, d_row, d_dtype, dprob,
+ * dbias, act, geglu_alpha, clamp_min, clamp_max, linear_offset
+ *            as for gg_dglu.
+ * amax       float[2L] ((L, 2) row-major), written by the call (the library
+ *            clears it first), or NULL.
+ * flags      as for gg_dglu.
+ * workspace  >= gg_dglu_workspace_size(L, n, dbias != NULL), 256-B aligned.
+ */
+gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
+                     const void* b_fp8, const uint8_t* sfb,
+                     const int64_t* b_ptrs, const int64_t* sfb_ptrs, int32_t n,
+                     const void* c, gg_dtype c_dtype,
+                     const int32_t* padded_offsets, int32_t L,
+                     const float* alpha, const float* beta, const float* prob,
+                     void* d_row, gg_dtype d_dtype, float* dprob, void* dbias, float* amax,
+                     gg_act act, float geglu_alpha, float clamp_min, float clamp_max,
+                     float linear_offset, uint32_t flags,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Grouped dgrad + dsReLU on MXFP8 operands                                  */

@@ -24,8 +24,8 @@ STATUS_NAMES = ["GG_OK", "GG_ERR_NULL", "GG_ERR_SHAPE", "GG_ERR_DTYPE", "GG_ERR_
                 "GG_ERR_ALIGN", "GG_ERR_MODE", "GG_ERR_WORKSPACE", "GG_ERR_UNSUPPORTED",
                 "GG_ERR_DEVICE", "GG_ERR_HIP", "GG_ERR_OFFSETS"]
 EXPORTS = ["gg_abi_version", "gg_last_error", "gg_device_error", "gg_wgrad_workspace_size",
-           "gg_wgrad", "gg_dglu_workspace_size", "gg_dglu", "gg_dsrelu_workspace_size",
-           "gg_dsrelu"]
+           "gg_wgrad", "gg_dglu_workspace_size", "gg_dglu", "gg_dglu_mx",
+           "gg_dsrelu_workspace_size", "gg_dsrelu"]
 
 _TORCH_DTYPE = {torch.bfloat16: GG_BF16, torch.float16: GG_F16, torch.float32: GG_F32,
                 torch.float8_e4m3fn: GG_F8E4M3}
@@ -69,6 +69,9 @@ def load_library(path=LIB_PATH):
     L.gg_dglu.restype = ctypes.c_int
     L.gg_dglu.argtypes = [P, I64, I32, P, P, I32, I32, P, I32, P, I32, P, P, P, P, I32, P, P,
                           I32, F, F, F, F, U32, P, SZ, P]
+    L.gg_dglu_mx.restype = ctypes.c_int
+    L.gg_dglu_mx.argtypes = [P, P, I64, I32, P, P, P, P, I32, P, I32, P, I32, P, P, P, P, I32, P,
+                             P, P, I32, F, F, F, F, U32, P, SZ, P]
     L.gg_dsrelu.restype = ctypes.c_int
     L.gg_dsrelu.argtypes = [P, P, I64, I32, P, P, P, P, I32, P, I32, P, I32, P, P, P, I32, P, P,
                             U32, P, SZ, P]
@@ -159,6 +162,23 @@ def gg_dglu(a, b_dense, b_ptrs, b_major, n, c, padded_offsets, alpha, beta, prob
                      _ptr(beta), _ptr(prob), _ptr(d_row), _TORCH_DTYPE[d_row.dtype], _ptr(dprob),
                      _ptr(dbias), act, geglu_alpha, clamp_min, clamp_max, linear_offset, flags,
                      _ptr(ws), nbytes, _stream(stream)))
+    return ws
+
+
+def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, beta, prob, d_row,
+               dprob, dbias=None, amax=None, act=GG_DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0,
+               clamp_max=7.0, linear_offset=1.0, flags=0, workspace=None, stream=None):
+    """Grouped MXFP8 dgrad + dSwiGLU/dGeGLU (gg_dglu_mx of gg_moe.h): a is an
+    (m_rows, k) uint8 tensor of E4M3 codes.  Returns the workspace used."""
+    L = load_library()
+    nl = padded_offsets.numel()
+    ws, nbytes = _workspace(workspace, L.gg_dglu_workspace_size(nl, n, dbias is not None), a)
+    _check(L.gg_dglu_mx(_ptr(a), _ptr(sfa), a.shape[0], a.shape[1], _ptr(b), _ptr(sfb),
+                        _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
+                        _ptr(padded_offsets), nl, _ptr(alpha), _ptr(beta), _ptr(prob),
+                        _ptr(d_row), _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(dbias),
+                        _ptr(amax), act, geglu_alpha, clamp_min, clamp_max, linear_offset, flags,
+                        _ptr(ws), nbytes, _stream(stream)))
     return ws
 
 

@@ -186,7 +186,7 @@ gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_ma
     }
     int32_t* ws = (int32_t*)workspace;
     hipError_t e = gg::launch_prologue(offsets, num_experts, tokens_sum, 0, ws,
-                                       ws + gg::kWsHeader / 4, nullptr, 0, s);
+                                       ws + gg::kWsHeader / 4, nullptr, 0, nullptr, 0, s);
     if (e != hipSuccess)
         return hip_fail(e, "launching the wgrad prologue");
     gg::WgradArgs p;
@@ -227,6 +227,82 @@ static gg_status check_rows(const int32_t* po, int32_t L, int64_t m_rows, const 
     return GG_OK;
 }
 
+// Checks of the activation, output and flag arguments shared by gg_dglu and
+// gg_dglu_mx.
+static gg_status check_dglu_common(gg_dtype c_dtype, gg_dtype d_dtype, gg_act act,
+                                   const float* alpha, const float* beta, const void* dbias,
+                                   uint32_t flags, const char* name) {
+    if (!alpha || !beta)
+        return fail(GG_ERR_NULL, "alpha and beta must be non-NULL");
+    if (!is_out_dtype(c_dtype) || !is_out_dtype(d_dtype))
+        return fail(GG_ERR_DTYPE, "c_dtype and d_dtype must be GG_BF16, GG_F16 or GG_F32");
+    if (act != GG_DSWIGLU && act != GG_DGEGLU)
+        return fail(GG_ERR_MODE, "act must be GG_DSWIGLU or GG_DGEGLU");
+    if (!aligned16(dbias) || ((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u))
+        return fail(GG_ERR_ALIGN, "dbias must be 16-byte aligned, alpha and beta 4-byte");
+    if (flags & ~(uint32_t)(GG_FLAG_GATE_FIRST | GG_FLAG_GEGLU_MASK_FILTER | GG_FLAG_VALIDATE_OFFSETS))
+        return fail(GG_ERR_MODE, "unsupported flags 0x%x for %s", flags, name);
+    return GG_OK;
+}
+
+// Fills the epilogue fields of the dGLU parameter block and queues prologue,
+// kernel and dbias finalize (the operand fields are set by the caller).
+static gg_status run_dglu(gg::DgluArgs& p, bool mx, const void* c, gg_dtype c_dtype,
+                          const int32_t* padded_offsets, int32_t L, const float* alpha,
+                          const float* beta, const float* prob, void* d_row, gg_dtype d_dtype,
+                          float* dprob, void* dbias, float* amax, gg_act act, float geglu_alpha,
+                          float clamp_min, float clamp_max, float linear_offset, uint32_t flags,
+                          void* workspace, size_t workspace_bytes, void* stream, const char* name) {
+    size_t need = gg_dglu_workspace_size(L, p.N, dbias != nullptr);
+    if (workspace_bytes < need)
+        return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    gg_status st = check_device();
+    if (st != GG_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (flags & GG_FLAG_VALIDATE_OFFSETS) {
+        st = validate_offsets_host(padded_offsets, L, p.m_rows, true, s);
+        if (st != GG_OK)
+            return st;
+    }
+    int32_t* ws = (int32_t*)workspace;
+    float* acc = dbias ? (float*)((char*)workspace + gg::kWsHeader) : nullptr;
+    const int64_t nacc = dbias ? (int64_t)L * 2 * p.N : 0;
+    hipError_t e = gg::launch_prologue(padded_offsets, L, p.m_rows, 1, ws, nullptr, acc, nacc,
+                                       amax, amax ? 2 * (int64_t)L : 0, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "launching the dglu prologue");
+    p.c = c;
+    p.po = padded_offsets;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.prob = prob;
+    p.d = d_row;
+    p.dprob = dprob;
+    p.dbias = dbias;
+    p.amax = amax;
+    p.ws = ws;
+    p.L = L;
+    p.c_dtype = (int)c_dtype;
+    p.d_dtype = (int)d_dtype;
+    p.act = act == GG_DGEGLU;
+    p.gate_first = (flags & GG_FLAG_GATE_FIRST) != 0;
+    p.mask_filter = (flags & GG_FLAG_GEGLU_MASK_FILTER) != 0;
+    p.geglu_alpha = geglu_alpha;
+    p.clamp_min = clamp_min;
+    p.clamp_max = clamp_max;
+    p.linear_offset = linear_offset;
+    e = mx ? gg::launch_dglu_mx(p, s) : gg::launch_dglu(p, s);
+    if (e != hipSuccess)
+        return hip_fail(e, mx ? "launching gg_dglu_mx" : "launching gg_dglu");
+    if (dbias) {
+        e = gg::launch_dbias_finalize((uint16_t*)dbias, acc, nacc, s);
+        if (e != hipSuccess)
+            return hip_fail(e, "launching the dbias finalize");
+    }
+    return ok();
+}
+
 gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k, const void* b_dense,
                   const int64_t* b_ptrs, gg_major b_major, int32_t n, const void* c,
                   gg_dtype c_dtype, const int32_t* padded_offsets, int32_t L, const float* alpha,
@@ -237,18 +313,17 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k, const void* b_dense,
     gg_status st = check_rows(padded_offsets, L, m_rows, c, prob, d_row, dprob, workspace);
     if (st != GG_OK)
         return st;
-    if (!a || !alpha || !beta)
-        return fail(GG_ERR_NULL, "a, alpha and beta must be non-NULL");
+    if (!a)
+        return fail(GG_ERR_NULL, "a must be non-NULL");
     if ((b_dense != nullptr) == (b_ptrs != nullptr))
         return fail(GG_ERR_MODE, "exactly one of b_dense and b_ptrs must be given");
     if (b_major != GG_MAJOR_K && b_major != GG_MAJOR_N)
         return fail(GG_ERR_LAYOUT, "b_major must be GG_MAJOR_K or GG_MAJOR_N");
     if (b_dense && b_major != GG_MAJOR_K)
         return fail(GG_ERR_LAYOUT, "dense B must be K-major");
-    if (!is_out_dtype(c_dtype) || !is_out_dtype(d_dtype))
-        return fail(GG_ERR_DTYPE, "c_dtype and d_dtype must be GG_BF16, GG_F16 or GG_F32");
-    if (act != GG_DSWIGLU && act != GG_DGEGLU)
-        return fail(GG_ERR_MODE, "act must be GG_DSWIGLU or GG_DGEGLU");
+    st = check_dglu_common(c_dtype, d_dtype, act, alpha, beta, dbias, flags, "gg_dglu");
+    if (st != GG_OK)
+        return st;
     if (n <= 0 || n % 32)
         return fail(GG_ERR_SHAPE, "n must be a positive multiple of 32 (got %d)", n);
     if (k <= 0)
@@ -257,65 +332,66 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k, const void* b_dense,
         return fail(GG_ERR_UNSUPPORTED, "k must be a multiple of 64");
     if (k > (1 << 21) || n > (1 << 20))
         return fail(GG_ERR_UNSUPPORTED, "k is limited to 2^21 and n to 2^20");
-    if (!aligned16(a) || !aligned16(b_dense) || !aligned16(b_ptrs) || !aligned16(dbias) ||
-        ((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u))
-        return fail(GG_ERR_ALIGN, "a, b and dbias must be 16-byte aligned");
-    if (flags & ~(uint32_t)(GG_FLAG_GATE_FIRST | GG_FLAG_GEGLU_MASK_FILTER | GG_FLAG_VALIDATE_OFFSETS))
-        return fail(GG_ERR_MODE, "unsupported flags 0x%x for gg_dglu", flags);
-    size_t need = gg_dglu_workspace_size(L, n, dbias != nullptr);
-    if (workspace_bytes < need)
-        return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
-    st = check_device();
-    if (st != GG_OK)
-        return st;
-    hipStream_t s = (hipStream_t)stream;
-    if (flags & GG_FLAG_VALIDATE_OFFSETS) {
-        st = validate_offsets_host(padded_offsets, L, m_rows, true, s);
-        if (st != GG_OK)
-            return st;
-    }
-    int32_t* ws = (int32_t*)workspace;
-    float* acc = dbias ? (float*)((char*)workspace + gg::kWsHeader) : nullptr;
-    const int64_t nacc = dbias ? (int64_t)L * 2 * n : 0;
-    hipError_t e = gg::launch_prologue(padded_offsets, L, m_rows, 1, ws, nullptr, acc, nacc, s);
-    if (e != hipSuccess)
-        return hip_fail(e, "launching the dglu prologue");
-    gg::DgluArgs p;
+    if (!aligned16(a) || !aligned16(b_dense) || !aligned16(b_ptrs))
+        return fail(GG_ERR_ALIGN, "a and b must be 16-byte aligned");
+    gg::DgluArgs p = {};
     p.a = a;
     p.b_dense = b_dense;
     p.b_ptrs = b_ptrs;
-    p.c = c;
-    p.po = padded_offsets;
-    p.alpha = alpha;
-    p.beta = beta;
-    p.prob = prob;
-    p.d = d_row;
-    p.dprob = dprob;
-    p.dbias = dbias;
-    p.ws = ws;
     p.m_rows = m_rows;
     p.K = k;
     p.N = n;
-    p.L = L;
     p.b_kmajor = b_major == GG_MAJOR_K;
-    p.c_dtype = (int)c_dtype;
-    p.d_dtype = (int)d_dtype;
-    p.act = act == GG_DGEGLU;
-    p.gate_first = (flags & GG_FLAG_GATE_FIRST) != 0;
-    p.mask_filter = (flags & GG_FLAG_GEGLU_MASK_FILTER) != 0;
-    p.geglu_alpha = geglu_alpha;
-    p.clamp_min = clamp_min;
-    p.clamp_max = clamp_max;
-    p.linear_offset = linear_offset;
-    e = gg::launch_dglu(p, s);
-    if (e != hipSuccess)
-        return hip_fail(e, "launching gg_dglu");
-    if (dbias) {
-        e = gg::launch_dbias_finalize((uint16_t*)dbias, acc, nacc, s);
-        if (e != hipSuccess)
-            return hip_fail(e, "launching the dbias finalize");
-    }
-    return ok();
+    return run_dglu(p, false, c, c_dtype, padded_offsets, L, alpha, beta, prob, d_row, d_dtype,
+                    dprob, dbias, nullptr, act, geglu_alpha, clamp_min, clamp_max, linear_offset,
+                    flags, workspace, workspace_bytes, stream, "gg_dglu");
+}
+
+gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
+                     const void* b_fp8, const uint8_t* sfb, const int64_t* b_ptrs,
+                     const int64_t* sfb_ptrs, int32_t n, const void* c, gg_dtype c_dtype,
+                     const int32_t* padded_offsets, int32_t L, const float* alpha,
+                     const float* beta, const float* prob, void* d_row, gg_dtype d_dtype,
+                     float* dprob, void* dbias, float* amax, gg_act act, float geglu_alpha,
+                     float clamp_min, float clamp_max, float linear_offset, uint32_t flags,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    gg_status st = check_rows(padded_offsets, L, m_rows, c, prob, d_row, dprob, workspace);
+    if (st != GG_OK)
+        return st;
+    if (!a_fp8 || !sfa)
+        return fail(GG_ERR_NULL, "a_fp8 and sfa must be non-NULL");
+    const bool dense = b_fp8 || sfb;
+    const bool discrete = b_ptrs || sfb_ptrs;
+    if (dense == discrete || (dense && (!b_fp8 || !sfb)) || (discrete && (!b_ptrs || !sfb_ptrs)))
+        return fail(GG_ERR_MODE, "give exactly one of (b_fp8, sfb) and (b_ptrs, sfb_ptrs)");
+    st = check_dglu_common(c_dtype, d_dtype, act, alpha, beta, dbias, flags, "gg_dglu_mx");
+    if (st != GG_OK)
+        return st;
+    if (n <= 0 || n % 32)
+        return fail(GG_ERR_SHAPE, "n must be a positive multiple of 32 (got %d)", n);
+    if (k <= 0)
+        return fail(GG_ERR_SHAPE, "k must be positive");
+    if (k % 128)
+        return fail(GG_ERR_UNSUPPORTED, "k must be a multiple of 128");
+    if (k > (1 << 21) || n > (1 << 20))
+        return fail(GG_ERR_UNSUPPORTED, "k is limited to 2^21 and n to 2^20");
+    if (!aligned16(a_fp8) || !aligned16(b_fp8) || !aligned16(b_ptrs) || !aligned16(sfb_ptrs) ||
+        ((uintptr_t)sfa & 3u) || ((uintptr_t)sfb & 3u) || ((uintptr_t)amax & 3u))
+        return fail(GG_ERR_ALIGN, "operands must be 16-byte aligned, scales and amax 4-byte aligned");
+    gg::DgluArgs p = {};
+    p.a = a_fp8;
+    p.sfa = sfa;
+    p.b_dense = b_fp8;
+    p.sfb_dense = sfb;
+    p.b_ptrs = b_ptrs;
+    p.sfb_ptrs = sfb_ptrs;
+    p.m_rows = m_rows;
+    p.K = k;
+    p.N = n;
+    p.b_kmajor = 1;
+    return run_dglu(p, true, c, c_dtype, padded_offsets, L, alpha, beta, prob, d_row, d_dtype,
+                    dprob, dbias, amax, act, geglu_alpha, clamp_min, clamp_max, linear_offset,
+                    flags, workspace, workspace_bytes, stream, "gg_dglu_mx");
 }
 
 gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
@@ -363,7 +439,7 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
     }
     int32_t* ws = (int32_t*)workspace;
     hipError_t e = gg::launch_prologue(padded_offsets, L, m_rows, 1, ws, nullptr, amax,
-                                       amax ? L : 0, s);
+                                       amax ? L : 0, nullptr, 0, s);
     if (e != hipSuccess)
         return hip_fail(e, "launching the dsrelu prologue");
     gg::DsreluArgs p;

@@ -24,9 +24,13 @@ struct WgradArgs {
 };
 
 struct DgluArgs {
-    const void* a;
+    const void* a;            // bf16, or E4M3 codes (block-scaled)
     const void* b_dense;
     const int64_t* b_ptrs;
+    const uint8_t* sfa;       // block-scaled only: E8M0 scales of A and B
+    const uint8_t* sfb_dense;
+    const int64_t* sfb_ptrs;
+    float* amax;              // block-scaled only: [L][2] or NULL
     const void* c;
     const int32_t* po;
     const float* alpha;
@@ -68,14 +72,16 @@ struct DsreluArgs {
 // Launchers (return the HIP status of the launch).
 hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s);
 hipError_t launch_dglu(const DgluArgs& p, hipStream_t s);
+hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s);
 hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s);
 
-// Prologue: clears the error word and `nclear` floats at `clear`, checks the
-// offsets (wgrad: last == total; dgrad: last <= total) and, when order is
-// non-NULL, writes the experts sorted by count, largest first.
+// Prologue: clears the error word, `nclear` floats at `clear` and `nclear2`
+// floats at `clear2`, checks the offsets (wgrad: last == total; dgrad: last
+// <= total) and, when order is non-NULL, writes the experts sorted by count,
+// largest first.
 hipError_t launch_prologue(const int32_t* offsets, int n, int64_t total, int dgrad,
                            int32_t* err, int32_t* order, float* clear, int64_t nclear,
-                           hipStream_t s);
+                           float* clear2, int64_t nclear2, hipStream_t s);
 // dbias[i] = bf16(float(dbias[i]) + acc[i]) for i < n.
 hipError_t launch_dbias_finalize(uint16_t* dbias, const float* acc, int64_t n, hipStream_t s);
 

@@ -1,0 +1,121 @@
+// gg_mx.hpp -- the block-scaled (MXFP8) main loop of the M-grouped dgrad
+// kernels on gfx950: A (M, K) and the expert's B (N, K), both K-major E4M3
+// codes with one E8M0 scale byte per 32 consecutive K values of a row
+// (row-major (rows, K/32) scale arrays), contracted by
+// v_mfma_scale_f32_32x32x64_f8f6f4 with 64 values of K per stage and 128 per
+// load unit.
+//
+// The scales of 8 stages at a time (16 bytes of each of the tile's operand
+// rows) are staged in LDS by dword LDS-writing loads, four row-contiguous
+// words per 4 lanes, in two alternating buffers: the next group's words
+// arrive with the load units of the current group.  A per-lane scale fetch
+// per stage would instead send one cache request per row and stage through
+// the vector memory path, more requests than the operand data itself.  With
+// the fragments of a stage a lane reads the scale word of each of its
+// fragment rows and shifts it so that the byte of the K block it feeds to the
+// MFMA sits in byte 0.
+#pragma once
+#include "gg_tile.hpp"
+
+namespace gg {
+
+// Scale staging: two buffers, each holding the scale words of a group of 8
+// stages (4 load units; 4 words per row: one word covers 128 K values) for
+// the tile's A rows (slots 0 .. TM-1) and B rows (slots TM .. TM+TN-1), 16
+// bytes per slot, word w at byte 4 w.  (A stage's word of 32 consecutive
+// slots is then read with 2-way bank conflicts, 8 such reads per stage and
+// wave.)  Group g lives in buffer g & 1.  Group g+1 comes with units 4g+1 ..
+// 4g+4, one slice of 128 slots per unit: the last slice lands with the unit
+// group g+1 starts in, and the first is issued only after the barrier that
+// follows the last read of group g-1.  Past the last group the slices load
+// words no stage reads, which keeps the count of loads per unit fixed.
+constexpr int kScaleUnits = 4;
+template <class C>
+struct ScaleLds {
+    static constexpr int kSlots = C::TM + C::TN;
+    static constexpr int kBuf = kSlots * 16;                           // bytes per buffer
+    static constexpr int kBase = 2 * C::kUnit;                         // after the unit buffers
+    static constexpr int kSmem = kBase + 2 * kBuf > C::kLds ? kBase + 2 * kBuf : C::kLds;
+    static constexpr int kPerUnit = kSlots / kScaleUnits / 16 / C::kWaves;   // loads per wave
+    static_assert(C::TM == C::TN && kPerUnit * 16 * C::kWaves * kScaleUnits == kSlots,
+                  "scale slices must split evenly over waves and units");
+};
+
+// acc[i][j] += the wave's (32 i, 32 j) blocks of deq(A) deq(B)^T over all of
+// K for the tile whose A rows start at `a` (scales `sfa`) and whose B rows
+// start at `b` (scales `sfb`).  Rows at or past rows_valid / cols_valid load
+// zeros.  K is a multiple of 128; smem holds ScaleLds<C>::kSmem bytes.
+template <class C>
+__device__ __forceinline__ void mx_mainloop(char* smem, const char* a, const char* sfa,
+                                            const char* b, const char* sfb, int64_t K,
+                                            int rows_valid, int cols_valid, int am0, int bn0,
+                                            f32x16 (&acc)[C::MB][C::NB]) {
+    constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
+    using S = ScaleLds<C>;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int lr = l & 31, lq = l >> 5;
+    const int64_t KB = K / 32;                   // scale bytes per row
+    const int nk = (int)(K / 64);                // stages; K % 128 == 0, so nk is even
+    // Scale records end at the last valid row, so rows past the tile edge
+    // load zeros.  Words past the end of K are never read: they belong to no
+    // stage.
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sfa, (uint32_t)(rows_valid * KB));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sfb, (uint32_t)(cols_valid * KB));
+    char* const sbuf = smem + S::kBase;
+    const uint32_t sbuf32 = lds_addr(sbuf);
+    const int wu = uniform(w);
+    // Slice s (0 .. 3) of a group: slots 128 (s & 1) + 16 (kPerUnit w + t) +
+    // (l >> 2) of A (s < 2) or B (s >= 2), t < kPerUnit, lane l taking word
+    // l & 3 of its slot.
+    constexpr int kSliceSlots = TM / 2;
+    const uint32_t sc_off = (uint32_t)((16 * S::kPerUnit * w + (l >> 2)) * KB + 4 * (l & 3));
+    // load t (0 .. kPerUnit-1) of slice `slice` of scale group grp
+    auto scale_load = [&](int grp, int slice, int t) {
+        const int half = slice & 1;
+        const bool is_a = slice < 2;
+        const int slot0 = kSliceSlots * half + 16 * (S::kPerUnit * wu + t);
+        const uint32_t lds = sbuf32 + (grp & 1) * S::kBuf + (is_a ? 0 : TM * 16) + slot0 * 16;
+        dma4(is_a ? rsa : rsb, lds, sc_off + (uint32_t)((kSliceSlots * half + 16 * t) * KB + 16 * grp));
+    };
+    LoadK<C, TM> la;
+    LoadK<C, TN> lb;
+    la.init(K, rows_valid);
+    lb.init(K, cols_valid);
+    constexpr int kLA = LoadK<C, TM>::kN, kLB = LoadK<C, TN>::kN;
+    auto issue = [&](uint32_t st, int u, int i) {
+        const int64_t kb = (int64_t)u * 128;
+        if (i < kLA) {
+            la.template issue<false>(st, a + kb, K - kb, i);
+        } else if (i < kLA + kLB) {
+            lb.template issue<false>(st + TM * kRowBytes, b + kb, K - kb, i - kLA);
+        } else {
+            // units 1 .. 4 carry group 1, 5 .. 8 group 2, ...; unit 0
+            // carries a slice of group 0 again (identical words)
+            const int v = u > 0 ? u - 1 : 0;
+            scale_load(u > 0 ? v / kScaleUnits + 1 : 0, v % kScaleUnits, i - kLA - kLB);
+        }
+    };
+    const int lsh = 8 * lq;
+    auto read = [&](const char* st, int kt, FragMx8<C>& f, int g) {
+        read_mx8<C>(st, st + TM * kRowBytes, am0, bn0, kt & 1, f, g);
+        // this stage's scale word of the group's row, shifted so byte 0 is
+        // this lane's K block
+        const char* buf = sbuf + ((kt / 8) & 1) * S::kBuf + 4 * ((kt % 8) >> 1);
+        const int sh = lsh + 16 * (kt & 1);
+        if (g < MB)
+            f.sa[g] = *reinterpret_cast<const uint32_t*>(buf + (am0 + 32 * g + lr) * 16) >> sh;
+        else
+            f.sb[g - MB] = *reinterpret_cast<const uint32_t*>(buf + (TM + bn0 + 32 * (g - MB) + lr) * 16) >> sh;
+    };
+    auto mma = [&](const FragMx8<C>& f, int m0_, int m1_) { mma_mx8<C>(f, acc, m0_, m1_); };
+    FragMx8<C> frag[2];
+    // Group 0 ahead of unit 0: complete whenever unit 0 is.
+#pragma unroll
+    for (int s4 = 0; s4 < kScaleUnits; s4++)
+#pragma unroll
+        for (int t = 0; t < S::kPerUnit; t++)
+            scale_load(0, s4, t);
+    pipeline<C, kLA + kLB + S::kPerUnit, MB * NB, MB + NB>(smem, nk, frag, issue, read, mma);
+}
+
+}  // namespace gg

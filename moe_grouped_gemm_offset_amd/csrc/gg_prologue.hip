@@ -17,11 +17,16 @@ constexpr int kPrologueThreads = 1024;
 __global__ void __launch_bounds__(kPrologueThreads)
 prologue_kernel(const int32_t* __restrict__ offsets, int n, int64_t total, int dgrad,
                 int32_t* __restrict__ err, int32_t* __restrict__ order,
-                float* __restrict__ clear, int64_t nclear) {
+                float* __restrict__ clear, int64_t nclear, float* __restrict__ clear2,
+                int64_t nclear2) {
     const int t = threadIdx.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + t; i < nclear;
-         i += (int64_t)gridDim.x * blockDim.x)
-        clear[i] = 0.0f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + t; i < nclear + nclear2;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < nclear)
+            clear[i] = 0.0f;
+        else
+            clear2[i - nclear] = 0.0f;
+    }
     if (blockIdx.x != 0)
         return;
     __shared__ int32_t cnt[1024];
@@ -60,14 +65,14 @@ prologue_kernel(const int32_t* __restrict__ offsets, int n, int64_t total, int d
 
 hipError_t launch_prologue(const int32_t* offsets, int n, int64_t total, int dgrad,
                            int32_t* err, int32_t* order, float* clear, int64_t nclear,
-                           hipStream_t s) {
-    int64_t blocks = (nclear + kPrologueThreads * 4 - 1) / (kPrologueThreads * 4);
+                           float* clear2, int64_t nclear2, hipStream_t s) {
+    int64_t blocks = (nclear + nclear2 + kPrologueThreads * 4 - 1) / (kPrologueThreads * 4);
     if (blocks < 1)
         blocks = 1;
     if (blocks > 256)
         blocks = 256;
     hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)blocks), dim3(kPrologueThreads), 0, s,
-                       offsets, n, total, dgrad, err, order, clear, nclear);
+                       offsets, n, total, dgrad, err, order, clear, nclear, clear2, nclear2);
     return hipGetLastError();
 }
 

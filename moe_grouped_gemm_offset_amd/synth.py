@@ -4,8 +4,8 @@ This module only draws inputs (random values, group sizes, MXFP8 encodings of
 random values).  It holds none of the method's arithmetic, and both the CPU
 oracle and the HIP path take their inputs from it.
 
-Shapes and distributions follow the five workloads the library is measured
-on (tokens grouped in multiples of 256, as the pages require of offsets and
+Shapes and distributions follow the workloads the library is measured on
+(tokens grouped in multiples of 256, as the pages require of offsets and
 padded_offsets):
 
   wgrad_small   hidden 256, inter 256, 4 experts, counts [256, 0, 512, 256]
@@ -13,6 +13,9 @@ padded_offsets):
   wgrad_moe     hidden 4096, inter 2048, 64 experts, 65536 tokens, Zipf(1.2)
   dgeglu        L 32, K 4096, N 1536, M 32768, discrete B, dbias
   dsrelu_mxfp8  L 16, K 7168, N 2048, M 65536, MXFP8 A and B
+  dglu_mxfp8    L 32, K 4096, N 1536, M 32768, MXFP8 A and discrete B,
+                dSwiGLU with amax (the dGeGLU workload's shape on the
+                block-scaled path)
 
 Every generator takes a seed and a torch device; tensors are created on that
 device from a torch.Generator seeded with it, so a run that needs the same
@@ -269,7 +272,7 @@ def dglu_mx_inputs(L, K, N, counts, c_std=2.0, c_dtype=torch.bfloat16, m_extra=0
                 padded_offsets=torch.from_numpy(cumulative(counts)).to(device),
                 counts=counts, L=L, K=K, N=N, M=M, valid_m=valid_m)
 
-# The five named workloads (sizes and recipes; seeds 1000 + index).
+# The named workloads (sizes and recipes; seeds 1000 + index).
 WORKLOADS = {
     "wgrad_small": dict(kind="wgrad", hidden=256, inter=256,
                         counts=[256, 0, 512, 256], a_major="k", b_major="n", seed=1001),
@@ -280,6 +283,8 @@ WORKLOADS = {
     "dgeglu": dict(kind="dglu", act="dgeglu", L=32, K=4096, N=1536, M=32768,
                    c_std=4.0, discrete=True, dbias=True, seed=1004),
     "dsrelu_mxfp8": dict(kind="dsrelu", L=16, K=7168, N=2048, M=65536, seed=1005),
+    "dglu_mxfp8": dict(kind="dglu_mx", act="dswiglu", L=32, K=4096, N=1536, M=32768,
+                       c_std=2.0, discrete=True, dbias=False, seed=1006),
 }
 
 

@@ -137,8 +137,42 @@ def test_dsrelu_rejects(kw, status):
     assert dsrelu(**kw) == status
 
 
+def dglu_mx(**kw):
+    args = dict(a=P, sfa=P, M=1024, k=512, b=P, sfb=P, bp=None, sp=None, n=256, c=P, cdt=0, po=P,
+                L=4, alpha=P, beta=P, prob=P, d=P, ddt=0, dprob=P, dbias=None, amax=P, act=0,
+                flags=0, ws=WS, wsb=1 << 20)
+    args.update(kw)
+    lib = B.load_library()
+    return lib.gg_dglu_mx(args["a"], args["sfa"], args["M"], args["k"], args["b"], args["sfb"],
+                          args["bp"], args["sp"], args["n"], args["c"], args["cdt"], args["po"],
+                          args["L"], args["alpha"], args["beta"], args["prob"], args["d"],
+                          args["ddt"], args["dprob"], args["dbias"], args["amax"], args["act"],
+                          1.702, -7.0, 7.0, 1.0, args["flags"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sfa=None), NULL),
+    (dict(beta=None), NULL),
+    (dict(b=None, sfb=None), MODE),
+    (dict(bp=P, sp=P), MODE),
+    (dict(b=None, sfb=None, bp=P), MODE),
+    (dict(act=2), MODE),
+    (dict(flags=8), MODE),
+    (dict(k=192), UNSUPPORTED),
+    (dict(n=1 << 21), UNSUPPORTED),
+    (dict(n=40), SHAPE),
+    (dict(cdt=3), DTYPE),
+    (dict(amax=P + 2), ALIGN),
+    (dict(a=P + 8), ALIGN),
+    (dict(dbias=P, wsb=256), WORKSPACE),
+])
+def test_dglu_mx_rejects(kw, status):
+    assert dglu_mx(**kw) == status
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
 def test_valid_call_without_a_gpu_reports_device():
     assert wgrad() == DEVICE
     assert dglu() == DEVICE
     assert dsrelu() == DEVICE
+    assert dglu_mx() == DEVICE
