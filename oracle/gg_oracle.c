@@ -14,7 +14,8 @@
  *       equation" (R_g = alpha_g^2 A_g B_g^T, X_g = beta_g C_g, the dSwiGLU and
  *       dGeGLU formulas, dprob and dbias), and "Block-scaled contract /
  *       Equations", steps 1 and 2 (the dequantized GEMM, interleave order,
- *       dprob reduction) and "Shapes" (per-group amax of shape (L, 2, 1)).
+ *       dprob reduction), "Equations" for dSiTU-GLU (T_g, T_u and their
+ *       derivatives) and "Shapes" (per-group amax of shape (L, 2, 1)).
  *   [S] "Grouped GEMM + dsReLU (SM100)": "Equations" (G, D_row, dprob), and
  *       "Shapes" (per-expert Amax).
  *
@@ -263,7 +264,8 @@ static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
  *            case Bp[g] = B + g*N*K with b_major 0.)
  *   C (M, 2N), row-major, c_dtype; alpha, beta (L) fp32; prob (M) fp32.
  *   act 0 = dSwiGLU, 1 = dGeGLU with constants ga (1.702), clamp_lo (-7),
- *   clamp_hi (7) and linear offset lo (1).
+ *   clamp_hi (7) and linear offset lo (1); 2 = dSiTU-GLU with tanh scales
+ *   situ_b1 (4) and situ_b2 (25), block-scaled only (orc_dglu_mx).
  *   gate_first 0: in every 64-column pair of C and D the first 32 columns are
  *   the input block and the next 32 the gate block ("interleaved input/gate",
  *   and the step that interleaves [ab, dswiglu]); 1 swaps the two.
@@ -281,7 +283,8 @@ static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 static double dglu_row(const double* R, int64_t m, int g, int N,
                        const void* C, int c_dtype, const float* beta, const float* prob,
                        int act, double ga, double clamp_lo, double clamp_hi, double lo,
-                       int gate_first, int mask_filter, double* D) {
+                       double situ_b1, double situ_b2, int gate_first, int mask_filter,
+                       double* D) {
     int64_t N2 = 2 * (int64_t)N;
     double pr = (double)prob[m];
     double dp = 0.0;
@@ -303,6 +306,22 @@ static double dglu_row(const double* R, int64_t m, int g, int N,
             d_in = R[n] * pr * gt * s;
             d_gt = R[n] * pr * u * s * (1.0 + gt * (1.0 - s));
             a = gt * s * u;
+        } else if (act == 2) {
+            /* dSiTU-GLU: T_g = b1 tanh(gate/b1) s, T_u = b2 tanh(input/b2),
+             * s = sigmoid(gate);
+             *   dT_g/dgate  = (1 - tanh^2(gate/b1)) s + b1 tanh(gate/b1) s (1 - s)
+             *   dT_u/dinput = 1 - tanh^2(input/b2)
+             *   dgate  = R prob T_u dT_g/dgate
+             *   dinput = R prob T_g dT_u/dinput
+             * and the unscaled activation is T_g T_u. */
+            double s = sigmoid(gt);
+            double tg = tanh(gt / situ_b1), tu = tanh(u / situ_b2);
+            double Tg = situ_b1 * tg * s, Tu = situ_b2 * tu;
+            double dTg = (1.0 - tg * tg) * s + situ_b1 * tg * s * (1.0 - s);
+            double dTu = 1.0 - tu * tu;
+            d_gt = R[n] * pr * Tu * dTg;
+            d_in = R[n] * pr * Tg * dTu;
+            a = Tg * Tu;
         } else {
             /* dGeGLU: clamped values feed the activation, the filters
              * carry the raw value where it lies inside the clamp. */
@@ -371,7 +390,8 @@ void orc_dglu(const uint16_t* A, int64_t M, int K,
                 R[n] = a2 * acc;
             }
             dprob_sum[r] = dglu_row(R, m, g, N, C, c_dtype, beta, prob, act, ga, clamp_lo,
-                                    clamp_hi, lo, gate_first, mask_filter, D + r * N2);
+                                    clamp_hi, lo, 0.0, 0.0, gate_first, mask_filter,
+                                    D + r * N2);
         }
         free(R);
     }
@@ -382,7 +402,7 @@ void orc_dglu(const uint16_t* A, int64_t M, int K,
 /* [G] "Block-scaled contract / Equations", steps 1 and 2, on MXFP8 operands:
  * R_g = alpha_g^2 * sum_k deq(A[m,k]) deq(B_g[n,k]), with deq(q) = e4m3(q) *
  * 2^(e8m0 - 127) and one E8M0 scale per 32 K values of a row, then the dGLU
- * epilogue of orc_dglu.
+ * epilogue of orc_dglu (and dSiTU-GLU, act 2, of the same section).
  *   A (M, K) E4M3, K-major; SFA (M, K/32) E8M0: SFA[m*(K/32) + k/32].
  *   Bp[g] -> expert g's (N, K) E4M3, K-major; SFBp[g] -> its (N, K/32).
  * Other arguments and outputs as for orc_dglu, plus
@@ -394,7 +414,7 @@ void orc_dglu_mx(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
                  const void* C, int c_dtype, const int32_t* po, int L,
                  const float* alpha, const float* beta, const float* prob,
                  int act, double ga, double clamp_lo, double clamp_hi, double lo,
-                 int gate_first, int mask_filter,
+                 double situ_b1, double situ_b2, int gate_first, int mask_filter,
                  const int64_t* rows, int64_t nrows,
                  double* D, double* dprob_sum, double* dbias_sum, double* amax) {
     if (!rows)
@@ -425,7 +445,8 @@ void orc_dglu_mx(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
                 R[n] = a2 * acc;
             }
             dprob_sum[r] = dglu_row(R, m, g, N, C, c_dtype, beta, prob, act, ga, clamp_lo,
-                                    clamp_hi, lo, gate_first, mask_filter, D + r * N2);
+                                    clamp_hi, lo, situ_b1, situ_b2, gate_first, mask_filter,
+                                    D + r * N2);
         }
         free(R);
     }

@@ -66,7 +66,7 @@ def lib():
                                  P, I64, P, P, P]
         L.orc_dsrelu.restype = None
         L.orc_dglu_mx.argtypes = [P, P, I64, I, P, P, I, P, I, P, I, P, P, P,
-                                  I, D, D, D, D, I, I, P, I64, P, P, P, P]
+                                  I, D, D, D, D, D, D, I, I, P, I64, P, P, P, P]
         L.orc_dglu_mx.restype = None
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = I
@@ -177,7 +177,7 @@ def decode_array(bits, dtype):
 # grouped dgrad + dGLU
 # --------------------------------------------------------------------------
 
-DSWIGLU, DGEGLU = 0, 1
+DSWIGLU, DGEGLU, DSITUGLU = 0, 1, 2   # dSiTU-GLU: block-scaled only
 
 
 def dglu(a, m_rows, k, b_list, b_major, n, c, c_dtype, padded_offsets,
@@ -192,6 +192,7 @@ def dglu(a, m_rows, k, b_list, b_major, n, c, c_dtype, padded_offsets,
     Returns a dict with D (float64, listed rows), D_q (rounded), dprob
     (float64: dprob_in + row sum), and, when dbias_in is given, dbias
     (float64: dbias_in + column sums) and dbias_q (bf16 bits)."""
+    assert act in (DSWIGLU, DGEGLU), "dSiTU-GLU is defined for the block-scaled contract only"
     po = _c(padded_offsets, np.int32)
     L = po.size
     a = _c(a, np.uint16).ravel()
@@ -234,9 +235,11 @@ def _valid_rows(po, m_rows, rr):
 
 def dglu_mx(a, sfa, m_rows, k, b_list, sfb_list, n, c, c_dtype, padded_offsets,
             alpha, beta, prob, act=DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0,
-            clamp_max=7.0, linear_offset=1.0, gate_first=False, mask_filter=False,
-            d_dtype=BF16, dprob_in=None, dbias_in=None, rows=None):
-    """Block-scaled (MXFP8) grouped dgrad fused with dSwiGLU / dGeGLU.
+            clamp_max=7.0, linear_offset=1.0, situ_beta1=4.0, situ_beta2=25.0,
+            gate_first=False, mask_filter=False, d_dtype=BF16, dprob_in=None,
+            dbias_in=None, rows=None):
+    """Block-scaled (MXFP8) grouped dgrad fused with dSwiGLU / dGeGLU /
+    dSiTU-GLU (act DSITUGLU, tanh scales situ_beta1 and situ_beta2).
 
     a: uint8 e4m3 codes (m_rows, k); sfa: uint8 e8m0 (m_rows, k/32);
     b_list / sfb_list: per expert K-major (n, k) codes and (n, k/32) scales;
@@ -264,7 +267,8 @@ def dglu_mx(a, sfa, m_rows, k, b_list, sfb_list, n, c, c_dtype, padded_offsets,
                       ctypes.cast(sptr, ctypes.c_void_p), n, _p(c), c_dtype, _p(po), L,
                       _p(_c(alpha, np.float32)), _p(_c(beta, np.float32)),
                       _p(_c(prob, np.float32)), act, geglu_alpha, clamp_min, clamp_max,
-                      linear_offset, int(bool(gate_first)), int(bool(mask_filter)),
+                      linear_offset, situ_beta1, situ_beta2, int(bool(gate_first)),
+                      int(bool(mask_filter)),
                       _p(rr), nrows, _p(D), _p(dps), _p(dbs), _p(amax))
     valid = _valid_rows(po, m_rows, rr)
     out = {"D": D, "D_q": round_to(D, d_dtype), "valid": valid, "amax": amax}

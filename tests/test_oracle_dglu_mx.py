@@ -17,6 +17,13 @@ Pinned by:
   A multiplies that row of D, and its dprob, by 2^j;
 * amax equal to the maxima of |D| over the two column sets of each group,
   with the sets swapping under gate-first, and over the listed rows only.
+
+dSiTU-GLU (the page's "Equations": T_g = b1 tanh(G/b1) sigmoid(G),
+T_u = b2 tanh(U/b2); gradients R prob T_u dT_g/dG and R prob T_g dT_u/dU,
+dprob the row sum of R T_g T_u) is pinned by finite differences of
+f = sum prob R T_g T_u, by its limit b1, b2 -> infinity, where T_g -> SiLU(G)
+and T_u -> U make it dSwiGLU, and by the oddness of T_u (negating every
+input negates the gate gradient and dprob and leaves the input gradient).
 """
 import numpy as np
 import pytest
@@ -199,3 +206,58 @@ def test_amax_over_listed_rows():
         blk = np.abs(full["D"][sel])
         assert part["amax"][g, 0] == blk[:, cin].max()
         assert part["amax"][g, 1] == blk[:, cgt].max()
+
+
+def act_situ(g, u, b1=4.0, b2=25.0):
+    return b1 * np.tanh(g / b1) * sig(g) * (b2 * np.tanh(u / b2))
+
+
+def test_situ_finite_differences():
+    inp = small(76, c_std=4.0)
+    out = run(inp, act=orc.DSITUGLU)
+    R = library_R(inp)
+    X = inp["c"].double().numpy()
+    prob = inp["prob"].double().numpy()
+    N = inp["N"]
+    cin, cgt = column_maps(N)
+    checked = 0
+    for m in range(inp["valid_m"]):
+        for n in range(N):
+            g, u = X[m, cgt[n]], X[m, cin[n]]
+            for which, x0, col in (("g", g, cgt[n]), ("u", u, cin[n])):
+                h = 1e-5 * max(1.0, abs(x0))
+                if which == "g":
+                    fd = (act_situ(g + h, u) - act_situ(g - h, u)) / (2 * h)
+                else:
+                    fd = (act_situ(g, u + h) - act_situ(g, u - h)) / (2 * h)
+                want = prob[m] * R[m, n] * fd
+                got = out["D"][m, col]
+                assert abs(got - want) <= 1e-6 * max(abs(want), abs(prob[m] * R[m, n]), 1e-12), \
+                    (m, n, which, got, want)
+                checked += 1
+        want_dp = np.sum(R[m] * act_situ(X[m, cgt], X[m, cin]))
+        assert abs(out["dprob"][m] - want_dp) <= 1e-9 * max(1.0, np.sum(np.abs(R[m]))), m
+    assert checked > 1000
+
+
+def test_situ_large_scales_reduce_to_dswiglu():
+    inp = small(77)
+    situ = run(inp, act=orc.DSITUGLU, situ_beta1=1e7, situ_beta2=1e7)
+    swi = run(inp, act=orc.DSWIGLU)
+    vm = inp["valid_m"]
+    np.testing.assert_allclose(situ["D"][:vm], swi["D"][:vm], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(situ["dprob"][:vm], swi["dprob"][:vm], rtol=1e-9, atol=1e-12)
+
+
+def test_situ_input_oddness():
+    inp = small(78)
+    N = inp["N"]
+    cin, cgt = column_maps(N)
+    base = run(inp, act=orc.DSITUGLU)
+    c = inp["c"].clone()
+    c[:, cin] = -c[:, cin]
+    flip = run(dict(inp, c=c), act=orc.DSITUGLU)
+    vm = inp["valid_m"]
+    assert np.array_equal(flip["D"][:vm][:, cgt], -base["D"][:vm][:, cgt])
+    assert np.array_equal(flip["D"][:vm][:, cin], base["D"][:vm][:, cin])
+    assert np.array_equal(flip["dprob"][:vm], -base["dprob"][:vm])
