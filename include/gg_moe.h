@@ -70,7 +70,8 @@ typedef enum {
     GG_ERR_UNSUPPORTED = 8,  /* valid per the pages but outside this build       */
     GG_ERR_DEVICE = 9,       /* no gfx950 device current                         */
     GG_ERR_HIP = 10,         /* a HIP runtime call failed                        */
-    GG_ERR_OFFSETS = 11      /* offsets rejected by GG_FLAG_VALIDATE_OFFSETS     */
+    GG_ERR_OFFSETS = 11,     /* offsets rejected by GG_FLAG_VALIDATE_OFFSETS     */
+    GG_ERR_VALUE = 12        /* a scalar parameter is outside its domain         */
 } gg_status;
 
 typedef enum {
@@ -86,7 +87,8 @@ typedef enum {
     GG_MAJOR_N = 2           /* the N axis (columns of the product) is contiguous */
 } gg_major;
 
-typedef enum { GG_DSWIGLU = 0, GG_DGEGLU = 1 } gg_act;
+/* GG_DSITUGLU is defined for the block-scaled contract only (gg_dglu_mx). */
+typedef enum { GG_DSWIGLU = 0, GG_DGEGLU = 1, GG_DSITUGLU = 2 } gg_act;
 
 enum {
     /* dGLU: in each 64-column pair of C and D the gate block comes first.
@@ -270,8 +272,18 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k,
  * n          compact width, a multiple of 32, at most 2^20
  *            (GG_ERR_UNSUPPORTED beyond either limit).
  * c, c_dtype, padded_offsets, L, alpha, beta, prob, d_row, d_dtype, dprob,
- * dbias, act, geglu_alpha, clamp_min, clamp_max, linear_offset
+ * dbias, geglu_alpha, clamp_min, clamp_max, linear_offset
  *            as for gg_dglu.
+ * act        GG_DSWIGLU, GG_DGEGLU, or GG_DSITUGLU: the page's dSiTU-GLU
+ *            ("Block-scaled contract / Equations") on gate G and input U of
+ *            X = beta_g C, b1 = situ_beta1, b2 = situ_beta2 (the page's
+ *            defaults: 4 and 25; both positive and finite, else
+ *            GG_ERR_VALUE; ignored for the other activations):
+ *              T_g = b1 tanh(G/b1) sigmoid(G),   T_u = b2 tanh(U/b2)
+ *              D[gate]  = R prob T_u ((1 - tanh^2(G/b1)) sigmoid(G)
+ *                         + b1 tanh(G/b1) sigmoid(G) (1 - sigmoid(G)))
+ *              D[input] = R prob T_g (1 - tanh^2(U/b2))
+ *              dprob   += R T_g T_u
  * amax       float[2L] ((L, 2) row-major), written by the call (the library
  *            clears it first), or NULL.
  * flags      as for gg_dglu.
@@ -285,7 +297,7 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
                      const float* alpha, const float* beta, const float* prob,
                      void* d_row, gg_dtype d_dtype, float* dprob, void* dbias, float* amax,
                      gg_act act, float geglu_alpha, float clamp_min, float clamp_max,
-                     float linear_offset, uint32_t flags,
+                     float linear_offset, float situ_beta1, float situ_beta2, uint32_t flags,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */

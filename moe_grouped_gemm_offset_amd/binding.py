@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libgg_moe.so")
 # enums of gg_moe.h
 GG_BF16, GG_F16, GG_F32, GG_F8E4M3 = 0, 1, 2, 3
 GG_MAJOR_K, GG_MAJOR_M, GG_MAJOR_N = 0, 1, 2
-GG_DSWIGLU, GG_DGEGLU = 0, 1
+GG_DSWIGLU, GG_DGEGLU, GG_DSITUGLU = 0, 1, 2
 GG_FLAG_GATE_FIRST, GG_FLAG_GEGLU_MASK_FILTER, GG_FLAG_VALIDATE_OFFSETS = 1, 2, 4
 GG_DEVERR_DECREASING, GG_DEVERR_GRANULE, GG_DEVERR_LAST, GG_DEVERR_SKIPPED = 1, 2, 4, 8
 STATUS_NAMES = ["GG_OK", "GG_ERR_NULL", "GG_ERR_SHAPE", "GG_ERR_DTYPE", "GG_ERR_LAYOUT",
@@ -71,7 +71,7 @@ def load_library(path=LIB_PATH):
                           I32, F, F, F, F, U32, P, SZ, P]
     L.gg_dglu_mx.restype = ctypes.c_int
     L.gg_dglu_mx.argtypes = [P, P, I64, I32, P, P, P, P, I32, P, I32, P, I32, P, P, P, P, I32, P,
-                             P, P, I32, F, F, F, F, U32, P, SZ, P]
+                             P, P, I32, F, F, F, F, F, F, U32, P, SZ, P]
     L.gg_dsrelu.restype = ctypes.c_int
     L.gg_dsrelu.argtypes = [P, P, I64, I32, P, P, P, P, I32, P, I32, P, I32, P, P, P, I32, P, P,
                             U32, P, SZ, P]
@@ -167,7 +167,8 @@ def gg_dglu(a, b_dense, b_ptrs, b_major, n, c, padded_offsets, alpha, beta, prob
 
 def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, beta, prob, d_row,
                dprob, dbias=None, amax=None, act=GG_DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0,
-               clamp_max=7.0, linear_offset=1.0, flags=0, workspace=None, stream=None):
+               clamp_max=7.0, linear_offset=1.0, situ_beta1=4.0, situ_beta2=25.0, flags=0,
+               workspace=None, stream=None):
     """Grouped MXFP8 dgrad + dSwiGLU/dGeGLU (gg_dglu_mx of gg_moe.h): a is an
     (m_rows, k) uint8 tensor of E4M3 codes.  Returns the workspace used."""
     L = load_library()
@@ -177,8 +178,8 @@ def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, be
                         _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
                         _ptr(padded_offsets), nl, _ptr(alpha), _ptr(beta), _ptr(prob),
                         _ptr(d_row), _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(dbias),
-                        _ptr(amax), act, geglu_alpha, clamp_min, clamp_max, linear_offset, flags,
-                        _ptr(ws), nbytes, _stream(stream)))
+                        _ptr(amax), act, geglu_alpha, clamp_min, clamp_max, linear_offset,
+                        situ_beta1, situ_beta2, flags, _ptr(ws), nbytes, _stream(stream)))
     return ws
 
 

@@ -8,6 +8,7 @@
 // dGLU with dbias a finalize kernel -- all on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -229,15 +230,17 @@ static gg_status check_rows(const int32_t* po, int32_t L, int64_t m_rows, const 
 
 // Checks of the activation, output and flag arguments shared by gg_dglu and
 // gg_dglu_mx.
-static gg_status check_dglu_common(gg_dtype c_dtype, gg_dtype d_dtype, gg_act act,
+static gg_status check_dglu_common(gg_dtype c_dtype, gg_dtype d_dtype, gg_act act, bool mx,
                                    const float* alpha, const float* beta, const void* dbias,
                                    uint32_t flags, const char* name) {
     if (!alpha || !beta)
         return fail(GG_ERR_NULL, "alpha and beta must be non-NULL");
     if (!is_out_dtype(c_dtype) || !is_out_dtype(d_dtype))
         return fail(GG_ERR_DTYPE, "c_dtype and d_dtype must be GG_BF16, GG_F16 or GG_F32");
-    if (act != GG_DSWIGLU && act != GG_DGEGLU)
-        return fail(GG_ERR_MODE, "act must be GG_DSWIGLU or GG_DGEGLU");
+    if (act == GG_DSITUGLU && !mx)
+        return fail(GG_ERR_MODE, "GG_DSITUGLU is defined for the block-scaled gg_dglu_mx only");
+    if (act != GG_DSWIGLU && act != GG_DGEGLU && act != GG_DSITUGLU)
+        return fail(GG_ERR_MODE, "act must be GG_DSWIGLU, GG_DGEGLU or GG_DSITUGLU");
     if (!aligned16(dbias) || ((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u))
         return fail(GG_ERR_ALIGN, "dbias must be 16-byte aligned, alpha and beta 4-byte");
     if (flags & ~(uint32_t)(GG_FLAG_GATE_FIRST | GG_FLAG_GEGLU_MASK_FILTER | GG_FLAG_VALIDATE_OFFSETS))
@@ -251,8 +254,9 @@ static gg_status run_dglu(gg::DgluArgs& p, bool mx, const void* c, gg_dtype c_dt
                           const int32_t* padded_offsets, int32_t L, const float* alpha,
                           const float* beta, const float* prob, void* d_row, gg_dtype d_dtype,
                           float* dprob, void* dbias, float* amax, gg_act act, float geglu_alpha,
-                          float clamp_min, float clamp_max, float linear_offset, uint32_t flags,
-                          void* workspace, size_t workspace_bytes, void* stream, const char* name) {
+                          float clamp_min, float clamp_max, float linear_offset, float situ_b1,
+                          float situ_b2, uint32_t flags, void* workspace, size_t workspace_bytes,
+                          void* stream) {
     size_t need = gg_dglu_workspace_size(L, p.N, dbias != nullptr);
     if (workspace_bytes < need)
         return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
@@ -285,13 +289,15 @@ static gg_status run_dglu(gg::DgluArgs& p, bool mx, const void* c, gg_dtype c_dt
     p.L = L;
     p.c_dtype = (int)c_dtype;
     p.d_dtype = (int)d_dtype;
-    p.act = act == GG_DGEGLU;
+    p.act = (int)act;
     p.gate_first = (flags & GG_FLAG_GATE_FIRST) != 0;
     p.mask_filter = (flags & GG_FLAG_GEGLU_MASK_FILTER) != 0;
     p.geglu_alpha = geglu_alpha;
     p.clamp_min = clamp_min;
     p.clamp_max = clamp_max;
     p.linear_offset = linear_offset;
+    p.situ_b1 = situ_b1;
+    p.situ_b2 = situ_b2;
     e = mx ? gg::launch_dglu_mx(p, s) : gg::launch_dglu(p, s);
     if (e != hipSuccess)
         return hip_fail(e, mx ? "launching gg_dglu_mx" : "launching gg_dglu");
@@ -321,7 +327,7 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k, const void* b_dense,
         return fail(GG_ERR_LAYOUT, "b_major must be GG_MAJOR_K or GG_MAJOR_N");
     if (b_dense && b_major != GG_MAJOR_K)
         return fail(GG_ERR_LAYOUT, "dense B must be K-major");
-    st = check_dglu_common(c_dtype, d_dtype, act, alpha, beta, dbias, flags, "gg_dglu");
+    st = check_dglu_common(c_dtype, d_dtype, act, false, alpha, beta, dbias, flags, "gg_dglu");
     if (st != GG_OK)
         return st;
     if (n <= 0 || n % 32)
@@ -344,7 +350,7 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k, const void* b_dense,
     p.b_kmajor = b_major == GG_MAJOR_K;
     return run_dglu(p, false, c, c_dtype, padded_offsets, L, alpha, beta, prob, d_row, d_dtype,
                     dprob, dbias, nullptr, act, geglu_alpha, clamp_min, clamp_max, linear_offset,
-                    flags, workspace, workspace_bytes, stream, "gg_dglu");
+                    1.0f, 1.0f, flags, workspace, workspace_bytes, stream);
 }
 
 gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
@@ -353,8 +359,9 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
                      const int32_t* padded_offsets, int32_t L, const float* alpha,
                      const float* beta, const float* prob, void* d_row, gg_dtype d_dtype,
                      float* dprob, void* dbias, float* amax, gg_act act, float geglu_alpha,
-                     float clamp_min, float clamp_max, float linear_offset, uint32_t flags,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     float clamp_min, float clamp_max, float linear_offset, float situ_beta1,
+                     float situ_beta2, uint32_t flags, void* workspace, size_t workspace_bytes,
+                     void* stream) {
     gg_status st = check_rows(padded_offsets, L, m_rows, c, prob, d_row, dprob, workspace);
     if (st != GG_OK)
         return st;
@@ -364,9 +371,12 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
     const bool discrete = b_ptrs || sfb_ptrs;
     if (dense == discrete || (dense && (!b_fp8 || !sfb)) || (discrete && (!b_ptrs || !sfb_ptrs)))
         return fail(GG_ERR_MODE, "give exactly one of (b_fp8, sfb) and (b_ptrs, sfb_ptrs)");
-    st = check_dglu_common(c_dtype, d_dtype, act, alpha, beta, dbias, flags, "gg_dglu_mx");
+    st = check_dglu_common(c_dtype, d_dtype, act, true, alpha, beta, dbias, flags, "gg_dglu_mx");
     if (st != GG_OK)
         return st;
+    if (act == GG_DSITUGLU && !(situ_beta1 > 0.0f && situ_beta1 <= FLT_MAX &&
+                                situ_beta2 > 0.0f && situ_beta2 <= FLT_MAX))
+        return fail(GG_ERR_VALUE, "situ_beta1 and situ_beta2 must be positive and finite");
     if (n <= 0 || n % 32)
         return fail(GG_ERR_SHAPE, "n must be a positive multiple of 32 (got %d)", n);
     if (k <= 0)
@@ -391,7 +401,8 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
     p.b_kmajor = 1;
     return run_dglu(p, true, c, c_dtype, padded_offsets, L, alpha, beta, prob, d_row, d_dtype,
                     dprob, dbias, amax, act, geglu_alpha, clamp_min, clamp_max, linear_offset,
-                    flags, workspace, workspace_bytes, stream, "gg_dglu_mx");
+                    act == GG_DSITUGLU ? situ_beta1 : 1.0f, act == GG_DSITUGLU ? situ_beta2 : 1.0f,
+                    flags, workspace, workspace_bytes, stream);
 }
 
 gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,

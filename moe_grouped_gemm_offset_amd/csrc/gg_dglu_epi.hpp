@@ -1,4 +1,4 @@
-// gg_dglu_epi.hpp -- the fused dSwiGLU / dGeGLU epilogue of the M-grouped
+// gg_dglu_epi.hpp -- the fused dSwiGLU / dGeGLU / dSiTU-GLU epilogue of the M-grouped
 // dgrad kernels (bf16 and block-scaled main loops alike).
 //
 // For a tile of rows of group g and compact columns n ("Grouped GEMM + dGLU
@@ -26,6 +26,9 @@ namespace gg {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// tanh(x) = 2 sigmoid(2x) - 1 (exact at +-inf: +-1).
+__device__ __forceinline__ float tanhf_(float x) { return 2.0f * sigmoidf_(2.0f * x) - 1.0f; }
+
 // X = beta * C as a single fp32 product: no contraction into a later FMA, so
 // the clamp / filter comparisons see exactly the rounded product.
 __device__ __forceinline__ float scaled_x(float beta, float c) {
@@ -33,7 +36,10 @@ __device__ __forceinline__ float scaled_x(float beta, float c) {
     return beta * c;
 }
 
-// W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU; AMAX: raise
+// W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU, 2 dSiTU-GLU
+// (the block-scaled contract's "Equations": T_g = b1 tanh(G/b1) sigmoid(G),
+// T_u = b2 tanh(U/b2), gradients R prob T_u dT_g/dG and R prob T_g dT_u/dU,
+// activation T_g T_u); AMAX: raise
 // p.amax[2 g + {0: input, 1: gate}]; kAhead: row-walk items whose C loads are
 // in flight while one is processed.  The caller has passed the barrier that
 // ends the main loop's use of smem.
@@ -46,6 +52,7 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
     const float a2 = al * al;
     const float bet = p.beta[g];
     const int64_t N2 = 2 * (int64_t)p.N;
+    const float rb1 = 1.0f / p.situ_b1, rb2 = 1.0f / p.situ_b2;
     float* dbias_ws = p.dbias ? (float*)((char*)p.ws + kWsHeader) + (int64_t)g * N2 : nullptr;
     constexpr int kT = 4 * C::MB;                  // row walk steps per lane
     float rowsum[kT], bs_in[8], bs_gt[8];
@@ -101,6 +108,14 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
                     din[k] = Rp * gt * sg;
                     dgt[k] = Rp * u * sg * (1.0f + gt * (1.0f - sg));
                     act = gt * sg * u;
+                } else if constexpr (ACT == 2) {
+                    const float sg = sigmoidf_(gt);
+                    const float tg = tanhf_(gt * rb1), tu = tanhf_(u * rb2);
+                    const float Tg = p.situ_b1 * tg * sg, Tu = p.situ_b2 * tu;
+                    const float dTg = (1.0f - tg * tg) * sg + p.situ_b1 * tg * sg * (1.0f - sg);
+                    dgt[k] = Rp * Tu * dTg;
+                    din[k] = Rp * Tg * (1.0f - tu * tu);
+                    act = Tg * Tu;
                 } else {
                     const float gc = fminf(gt, p.clamp_max);
                     const float uc = fminf(fmaxf(u, p.clamp_min), p.clamp_max);

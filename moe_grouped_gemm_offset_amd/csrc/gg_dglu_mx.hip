@@ -1,13 +1,14 @@
 // gg_dglu_mx.hip -- M-grouped block-scaled (MXFP8) dgrad fused with the
-// dSwiGLU / dGeGLU backward on gfx950.
+// dSwiGLU / dGeGLU / dSiTU-GLU backward on gfx950.
 //
 // For the rows of group g ("Grouped GEMM + dGLU (SM100)", "Block-scaled
 // contract / Equations"):
 //   R = alpha_g^2 * sum_k deq(A) deq(B_g)   (E4M3 values, one E8M0 scale per
 //                                            32 K values of a row)
-// followed by the activation backward of the BF16 contract on X = beta_g C
-// (D, dprob, optional dbias) and the per-expert amax of the input-gradient
-// and gate-gradient halves of D ("Shapes": (L, 2, 1)).  Each expert's codes
+// followed by the activation backward on X = beta_g C (the BF16 contract's
+// dSwiGLU and dGeGLU, or the block-scaled contract's dSiTU-GLU), which
+// yields D, dprob and the optional dbias, and by the per-expert amax of the
+// input-gradient and gate-gradient halves of D ("Shapes": (L, 2, 1)).  Each expert's codes
 // and scales may sit at their own addresses (pointer arrays), as well as in
 // one dense (L, N, K) tensor.
 //
@@ -22,7 +23,7 @@ namespace gg {
 
 using DgluMxCfg = Cfg<256, 256, 2, 2>;
 
-// W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU.
+// W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU, 2 dSiTU-GLU.
 template <class C, bool W32, int ACT>
 __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
@@ -80,8 +81,10 @@ hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s) {
         constexpr bool w32 = decltype(W32)::value;
         if (p.act == 0)
             hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 0>), grid, block, 0, s, p);
-        else
+        else if (p.act == 1)
             hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 1>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 2>), grid, block, 0, s, p);
     };
     if (p.c_dtype == kF32)
         go(std::true_type());

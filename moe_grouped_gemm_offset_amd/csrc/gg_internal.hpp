@@ -44,9 +44,10 @@ struct DgluArgs {
     int K, N, L;
     int b_kmajor;
     int c_dtype, d_dtype;
-    int act;                  // 0 dSwiGLU, 1 dGeGLU
+    int act;                  // 0 dSwiGLU, 1 dGeGLU, 2 dSiTU-GLU (block-scaled)
     int gate_first, mask_filter;
     float geglu_alpha, clamp_min, clamp_max, linear_offset;
+    float situ_b1, situ_b2;   // dSiTU-GLU tanh scales
 };
 
 struct DsreluArgs {

@@ -14,7 +14,8 @@ from moe_grouped_gemm_offset_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gg_moe.h")
 
-OK, NULL, SHAPE, DTYPE, LAYOUT, ALIGN, MODE, WORKSPACE, UNSUPPORTED, DEVICE, HIP, OFFSETS = range(12)
+OK, NULL, SHAPE, DTYPE, LAYOUT, ALIGN, MODE, WORKSPACE, UNSUPPORTED, DEVICE, HIP, OFFSETS, VALUE = \
+    range(13)
 
 P = 1 << 20          # a fake 256-byte aligned device address
 WS = 1 << 24
@@ -99,6 +100,7 @@ def dglu(**kw):
     (dict(bm=1, bd=None, bp=P), LAYOUT),
     (dict(cdt=3), DTYPE),
     (dict(act=2), MODE),
+    (dict(act=3), MODE),
     (dict(n=48), SHAPE),
     (dict(k=96), UNSUPPORTED),
     (dict(L=0), SHAPE),
@@ -140,14 +142,15 @@ def test_dsrelu_rejects(kw, status):
 def dglu_mx(**kw):
     args = dict(a=P, sfa=P, M=1024, k=512, b=P, sfb=P, bp=None, sp=None, n=256, c=P, cdt=0, po=P,
                 L=4, alpha=P, beta=P, prob=P, d=P, ddt=0, dprob=P, dbias=None, amax=P, act=0,
-                flags=0, ws=WS, wsb=1 << 20)
+                flags=0, ws=WS, wsb=1 << 20, b1=4.0, b2=25.0)
     args.update(kw)
     lib = B.load_library()
     return lib.gg_dglu_mx(args["a"], args["sfa"], args["M"], args["k"], args["b"], args["sfb"],
                           args["bp"], args["sp"], args["n"], args["c"], args["cdt"], args["po"],
                           args["L"], args["alpha"], args["beta"], args["prob"], args["d"],
                           args["ddt"], args["dprob"], args["dbias"], args["amax"], args["act"],
-                          1.702, -7.0, 7.0, 1.0, args["flags"], args["ws"], args["wsb"], None)
+                          1.702, -7.0, 7.0, 1.0, args["b1"], args["b2"], args["flags"], args["ws"],
+                          args["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -156,8 +159,12 @@ def dglu_mx(**kw):
     (dict(b=None, sfb=None), MODE),
     (dict(bp=P, sp=P), MODE),
     (dict(b=None, sfb=None, bp=P), MODE),
-    (dict(act=2), MODE),
+    (dict(act=3), MODE),
     (dict(flags=8), MODE),
+    (dict(act=2, b1=0.0), VALUE),
+    (dict(act=2, b2=-1.0), VALUE),
+    (dict(act=2, b1=float("inf")), VALUE),
+    (dict(act=2, b2=float("nan")), VALUE),
     (dict(k=192), UNSUPPORTED),
     (dict(n=1 << 21), UNSUPPORTED),
     (dict(n=40), SHAPE),
@@ -176,3 +183,5 @@ def test_valid_call_without_a_gpu_reports_device():
     assert dglu() == DEVICE
     assert dsrelu() == DEVICE
     assert dglu_mx() == DEVICE
+    assert dglu_mx(act=2) == DEVICE
+    assert dglu_mx(act=0, b1=0.0) == DEVICE, "the dSiTU scales are ignored for other activations"

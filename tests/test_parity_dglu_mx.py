@@ -2,10 +2,11 @@
 
 Small cases span several tiles, a partial N tile, an empty group, rows past
 valid_m, per-row scale spreads, dense and discrete (b_ptrs / sfb_ptrs) B,
-both activations, the gate-first and mask-filter flags, dbias, and C/D
-dtypes; the MoE-scale workload (L 32, K 4096, N 1536, M 32768, discrete B)
-runs at full size in the bench's launch configuration and is checked on
-sampled rows, the amax halves against the maxima of the kernel's own D.
+all three activations (dSiTU-GLU with default and small tanh scales), the
+gate-first and mask-filter flags, dbias, and C/D dtypes; the MoE-scale
+workload (L 32, K 4096, N 1536, M 32768, discrete B) runs at full size in
+the bench's launch configuration and is checked on sampled rows, the amax
+halves against the maxima of the kernel's own D.
 """
 import numpy as np
 import pytest
@@ -32,7 +33,8 @@ def column_maps(N, gate_first=False):
     return cin, cgt
 
 
-def run_gpu(inp, d_dtype=torch.bfloat16, with_amax=True, dbias=False, act=orc.DSWIGLU, flags=0):
+def run_gpu(inp, d_dtype=torch.bfloat16, with_amax=True, dbias=False, act=orc.DSWIGLU, flags=0,
+            situ=(4.0, 25.0)):
     b = gg()
     dev = lambda x: x.cuda()
     M, N, L = inp["M"], inp["N"], inp["L"]
@@ -54,21 +56,24 @@ def run_gpu(inp, d_dtype=torch.bfloat16, with_amax=True, dbias=False, act=orc.DS
     db = torch.zeros(L, 2 * N, dtype=torch.bfloat16, device="cuda") if dbias else None
     ws = b.gg_dglu_mx(a, dev(inp["sfa"]), bd, sd, bp, sp, N, dev(inp["c"]),
                       dev(inp["padded_offsets"]), dev(inp["alpha"]), dev(inp["beta"]),
-                      dev(inp["prob"]), d, dprob, dbias=db, amax=amax, act=act, flags=flags)
+                      dev(inp["prob"]), d, dprob, dbias=db, amax=amax, act=act, flags=flags,
+                      situ_beta1=situ[0], situ_beta2=situ[1])
     torch.cuda.synchronize()
     err = b.gg_device_error(ws)
     return dict(d=d.cpu(), dprob=dprob.cpu(), amax=(amax.cpu() if with_amax else None),
                 dbias=(db.cpu() if dbias else None), err=err)
 
 
-def run_oracle(inp, d_dtype=torch.bfloat16, rows=None, dbias=False, act=orc.DSWIGLU, flags=0):
+def run_oracle(inp, d_dtype=torch.bfloat16, rows=None, dbias=False, act=orc.DSWIGLU, flags=0,
+               situ=(4.0, 25.0)):
     L, N = inp["L"], inp["N"]
     return orc.dglu_mx(synth.bits(inp["a"]), synth.bits(inp["sfa"]), inp["M"], inp["K"],
                        [synth.bits(x) for x in inp["b_list"]],
                        [synth.bits(x) for x in inp["sfb_list"]], N, synth.bits(inp["c"]),
                        ORC_DT[inp["c"].dtype], inp["padded_offsets"].numpy(),
                        inp["alpha"].numpy(), inp["beta"].numpy(), inp["prob"].numpy(), act=act,
-                       gate_first=bool(flags & 1), mask_filter=bool(flags & 2),
+                       situ_beta1=situ[0], situ_beta2=situ[1], gate_first=bool(flags & 1),
+                       mask_filter=bool(flags & 2),
                        d_dtype=ORC_DT[d_dtype], rows=rows,
                        dbias_in=np.zeros((L, 2 * N), np.uint16) if dbias else None)
 
@@ -94,11 +99,11 @@ def check(inp, got, ref, d_dtype=orc.BF16):
         start += c
 
 
-@pytest.mark.parametrize("act", [orc.DSWIGLU, orc.DGEGLU])
+@pytest.mark.parametrize("act", [orc.DSWIGLU, orc.DGEGLU, orc.DSITUGLU])
 @pytest.mark.parametrize("discrete", [False, True])
 def test_small(discrete, act):
     inp = small(81, discrete, c_std=4.0 if act == orc.DGEGLU else 2.0)
-    say("dglu_mx small", "discrete" if discrete else "dense", "dgeglu" if act else "dswiglu")
+    say("dglu_mx small", "discrete" if discrete else "dense", ["dswiglu", "dgeglu", "dsituglu"][act])
     got = run_gpu(inp, act=act)
     ref = run_oracle(inp, act=act)
     check(inp, got, ref)
@@ -135,6 +140,19 @@ def test_dtypes(c_dtype, d_dtype):
     got = run_gpu(inp, d_dtype, act=orc.DGEGLU)
     ref = run_oracle(inp, d_dtype, act=orc.DGEGLU)
     check(inp, got, ref, ORC_DT[d_dtype])
+
+
+@pytest.mark.parametrize("situ", [(4.0, 25.0), (1.0, 2.0)])
+@pytest.mark.parametrize("c_dtype", [torch.bfloat16, torch.float32])
+def test_situ(c_dtype, situ):
+    """dSiTU-GLU with the page's default scales and with small ones (tanh
+    saturates), C drawn N(0, 4); fp32 D so the 1e-3 tolerance applies."""
+    inp = small(86, True, c_dtype=c_dtype, c_std=4.0)
+    got = run_gpu(inp, torch.float32, act=orc.DSITUGLU, situ=situ, dbias=True)
+    ref = run_oracle(inp, torch.float32, act=orc.DSITUGLU, situ=situ, dbias=True)
+    check(inp, got, ref, orc.F32)
+    assert_close(values(got["dbias"]), ref["dbias"], orc.BF16, "dbias")
+    assert_close(got["amax"].numpy().ravel(), ref["amax"].ravel(), orc.F32, "amax")
 
 
 def test_unit_scales_no_amax():
