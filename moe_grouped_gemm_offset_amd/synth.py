@@ -139,6 +139,53 @@ def wgrad_inputs(hidden, inter, counts, a_major="k", b_major="n", seed=0,
                 counts=counts, hidden=hidden, inter=inter, tokens_sum=T)
 
 
+def wgrad_mx_inputs(hidden, inter, counts, seed=0, device="cpu", scale_spread=0, ints=False):
+    """Inputs of the block-scaled (MXFP8) grouped wgrad.
+
+    A is the logical (hidden, T) matrix, stored K-major; B the logical
+    (T, inter) matrix, stored K-major as an (inter, T) array.  Both are N(0,1)
+    values (integers in [-2, 2] with ints=True) MXFP8-encoded along T by
+    mx_encode (one E8M0 scale per 32 tokens of a row); scale_spread > 0
+    multiplies each row by 2^j, j uniform in [-scale_spread, scale_spread],
+    before encoding.  Returns the codes `a` (hidden, T), `b` (inter, T), the
+    scales `sfa` (hidden, T/32), `sfb` (inter, T/32), the offsets and sizes."""
+    counts = np.asarray(counts, np.int64)
+    T = int(counts.sum())
+    g = _gen(seed, device)
+
+    def draw(rows):
+        if ints:
+            x = torch.randint(-2, 3, (rows, T), generator=g, device=device).float()
+        else:
+            x = torch.randn((rows, T), generator=g, device=device, dtype=torch.float32)
+        if scale_spread:
+            j = torch.randint(-scale_spread, scale_spread + 1, (rows, 1), generator=g,
+                              device=device).float()
+            x = x * torch.exp2(j)
+        return mx_encode(x)
+
+    a, sfa = draw(hidden)
+    b, sfb = draw(inter)
+    return dict(a=a, sfa=sfa, b=b, sfb=sfb,
+                offsets=torch.from_numpy(cumulative(counts)).to(device),
+                counts=counts, hidden=hidden, inter=inter, tokens_sum=T)
+
+
+def to_ragged(x, counts, per=1):
+    """The "tensor_ragged" storage of a K-major (rows, K) tensor whose K axis
+    is split into consecutive per-expert slices of counts[e] // per columns:
+    the per-expert (rows, count) blocks, each K-contiguous, concatenated in
+    expert order (a flat tensor).  Pure data movement: per = 32 relays out a
+    scale array whose columns cover 32 tokens each."""
+    cols = [int(c) // per for c in counts]
+    parts, start = [], 0
+    for c in cols:
+        parts.append(x[:, start:start + c].reshape(-1))
+        start += c
+    assert start == x.shape[1]
+    return torch.cat(parts) if parts else x.reshape(-1)[:0]
+
+
 def wgrad_initial(num_experts, hidden, inter, dtype, seed, device="cpu"):
     """Initial outputs for accumulate mode: N(0,1) in the output dtype."""
     g = _gen(seed, device)

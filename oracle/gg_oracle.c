@@ -9,7 +9,9 @@
  * What it follows (NVIDIA cuDNN frontend documentation pages):
  *   [W] "Grouped GEMM + WGrad (Unified)": section "Operation" (the per-expert
  *       token slice and the accumulate/overwrite rule), section "BF16
- *       contract" (shapes, strides and majors of A, B, offsets and outputs).
+ *       contract" (shapes, strides and majors of A, B, offsets and outputs),
+ *       section "Block-scaled contract" (the same operation on block-scaled
+ *       operands; MXFP8 here).
  *   [G] "Grouped GEMM + dGLU (SM100)": "BF16 contract / Tensors, layouts, and
  *       equation" (R_g = alpha_g^2 A_g B_g^T, X_g = beta_g C_g, the dSwiGLU and
  *       dGeGLU formulas, dprob and dbias), and "Block-scaled contract /
@@ -212,6 +214,43 @@ void orc_wgrad(const uint16_t* A, int a_major, const uint16_t* B, int b_major,
                 for (int i = 0; i < inter; i++) {
                     int64_t ib = b_major == 0 ? (int64_t)i * T + t : t * inter + i;
                     o[i] += av * orc_bf16_to_double(B[ib]);
+                }
+            }
+        }
+    }
+}
+
+/* [W] "Block-scaled contract" on MXFP8 operands: the "Operation" of the page
+ * with every operand value dequantized, deq(q) = e4m3(q) * 2^(e8m0 - 127),
+ * one E8M0 scale per 32 consecutive tokens (the K axis) of a row.
+ *   A (hidden, T) K-major codes: (h,t) at h*T + t; SFA (hidden, T/32):
+ *     SFA[h*(T/32) + t/32].
+ *   B (T, inter) stored K-major, i.e. as an (inter, T) array of codes:
+ *     (t,i) at i*T + t; SFB (inter, T/32): SFB[i*(T/32) + t/32].
+ * Outputs as for orc_wgrad (exact products, in double, per listed row); the
+ * accumulate rule and the rounding are orc_wgrad_finish's. */
+void orc_wgrad_mx(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                  const int32_t* offsets, int E, int64_t T, int hidden, int inter,
+                  const int32_t* hrows, int nrows, double* out) {
+    if (!hrows)
+        nrows = hidden;
+    int64_t TB = T / 32;
+    for (int e = 0; e < E; e++) {
+        int64_t begin = e ? offsets[e - 1] : 0;
+        int64_t end = offsets[e];
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; r++) {
+            int h = hrows ? hrows[r] : r;
+            double* o = out + ((int64_t)e * nrows + r) * inter;
+            for (int i = 0; i < inter; i++)
+                o[i] = 0.0;
+            for (int64_t t = begin; t < end; t++) {
+                double av = orc_e4m3_to_double(A[(int64_t)h * T + t]) *
+                            orc_e8m0_to_double(SFA[(int64_t)h * TB + t / 32]);
+                for (int i = 0; i < inter; i++) {
+                    double bv = orc_e4m3_to_double(B[(int64_t)i * T + t]) *
+                                orc_e8m0_to_double(SFB[(int64_t)i * TB + t / 32]);
+                    o[i] += av * bv;
                 }
             }
         }

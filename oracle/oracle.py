@@ -58,6 +58,8 @@ def lib():
         L.orc_wgrad.argtypes = [P, I, P, I, P, I, I64, I, I, P, I, P]
         L.orc_wgrad.restype = None
         L.orc_wgrad_finish.argtypes = [P, I64, I, P, I, P]
+        L.orc_wgrad_mx.argtypes = [P, P, P, P, P, I, I64, I, I, P, I, P]
+        L.orc_wgrad_mx.restype = None
         L.orc_wgrad_finish.restype = None
         L.orc_dglu.argtypes = [P, I64, I, P, I, I, P, I, P, I, P, P, P,
                                I, D, D, D, D, I, I, P, I64, P, P, P]
@@ -149,6 +151,39 @@ def wgrad(a, a_major, b, b_major, offsets, hidden, inter, tokens_sum,
     prod = np.zeros((E, nrows, inter), np.float64)
     lib().orc_wgrad(_p(a), a_major, _p(b), b_major, _p(offsets), E, tokens_sum,
                     hidden, inter, _p(hr), nrows, _p(prod))
+    if accumulate:
+        old = _c(old, _DT_NP[out_dtype])
+        if hr is not None:
+            old = np.ascontiguousarray(old[:, hr, :])
+        assert old.shape == prod.shape
+    else:
+        old = np.zeros(prod.shape, _DT_NP[out_dtype])
+    res = np.empty(prod.shape, _DT_NP[out_dtype])
+    lib().orc_wgrad_finish(_p(prod), prod.size, int(bool(accumulate)), _p(old),
+                           out_dtype, _p(res))
+    exact = prod + (decode_array(old, out_dtype) if accumulate else 0.0)
+    return exact, res
+
+
+def wgrad_mx(a, sfa, b, sfb, offsets, hidden, inter, tokens_sum, out_dtype=F32,
+             accumulate=False, old=None, hrows=None):
+    """Block-scaled (MXFP8) Wgrad[e] = deq(A)[:, begin:end] @ deq(B)[begin:end, :].
+
+    a: uint8 E4M3 codes of A (hidden, tokens_sum), K-major; sfa: uint8 E8M0
+    (hidden, tokens_sum/32).  b: codes of B stored K-major, i.e. an
+    (inter, tokens_sum) array; sfb: (inter, tokens_sum/32).  Other arguments
+    and the return value as for wgrad."""
+    offsets = _c(offsets, np.int32)
+    E = offsets.size
+    a, sfa = _c(a, np.uint8).ravel(), _c(sfa, np.uint8).ravel()
+    b, sfb = _c(b, np.uint8).ravel(), _c(sfb, np.uint8).ravel()
+    assert a.size == hidden * tokens_sum and b.size == tokens_sum * inter
+    assert sfa.size == hidden * (tokens_sum // 32) and sfb.size == inter * (tokens_sum // 32)
+    hr = None if hrows is None else _c(hrows, np.int32)
+    nrows = hidden if hr is None else hr.size
+    prod = np.zeros((E, nrows, inter), np.float64)
+    lib().orc_wgrad_mx(_p(a), _p(sfa), _p(b), _p(sfb), _p(offsets), E, tokens_sum, hidden,
+                       inter, _p(hr), nrows, _p(prod))
     if accumulate:
         old = _c(old, _DT_NP[out_dtype])
         if hr is not None:
