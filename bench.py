@@ -16,6 +16,8 @@ and, as single-op workloads outside the default step:
 
   dglu_mxfp8    gg_dglu_mx, MXFP8 dSwiGLU with amax, L 32, K 4096, N 1536,
                 M 32768, discrete B (b_ptrs / sfb_ptrs)
+  wgrad_mxfp8   gg_wgrad_mx, the wgrad_moe shape on MXFP8 K-major operands,
+                bf16 dense output, overwrite
   wgrad_moe_kmajor  the wgrad workload with A K-major
 
 value = algorithmic FLOPs of the step (2 sum_e M_e N_e K_e per GEMM) over the
@@ -43,11 +45,13 @@ HBM_PEAK = 8000.0                              # GB/s
 # build.py): the HBM traffic recorded for a kernel is reported only while
 # their hash is unchanged.
 KERNEL_SOURCES = {
-    "wgrad_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_wgrad.hip"],
+    "wgrad_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_wgrad_epi.hpp", "gg_wgrad.hip"],
     "dglu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_dglu_epi.hpp", "gg_dglu.hip"],
     "dglu_mx_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_dglu_epi.hpp",
                        "gg_dglu_mx.hip"],
     "dsrelu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_dsrelu.hip"],
+    "wgrad_mx_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_wgrad_epi.hpp",
+                        "gg_wgrad_mx.hip"],
 }
 
 
@@ -150,6 +154,39 @@ def make_wgrad(dev, a_major="m"):
     return Op("wgrad_moe", "wgrad_kernel", synth.flops_wgrad(h, i, counts), "bf16", run, alg, sample)
 
 
+def make_wgrad_mx(dev):
+    import numpy as np
+    import torch
+    from moe_grouped_gemm_offset_amd import binding as B, synth
+    from oracle import oracle as orc
+    w = synth.WORKLOADS["wgrad_mxfp8"]
+    counts = synth.workload_counts("wgrad_mxfp8")
+    inp = synth.wgrad_mx_inputs(w["hidden"], w["inter"], counts, seed=w["seed"], device=dev)
+    E, h, i, T = len(counts), inp["hidden"], inp["inter"], inp["tokens_sum"]
+    out = torch.empty(E, h, i, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(B.gg_wgrad_workspace_size(E), dtype=torch.uint8, device=dev)
+    a8, b8 = inp["a"].view(torch.uint8), inp["b"].view(torch.uint8)
+
+    def run():
+        B.gg_wgrad_mx(a8, inp["sfa"], b8, inp["sfb"], inp["offsets"], T, h, i, wgrad_dense=out,
+                      workspace=ws)
+
+    # codes and scales once, bf16 output written once
+    alg = (h + i) * T + (h + i) * T // 32 + 2 * E * h * i
+
+    def sample(nrows):
+        cpu = _cpu(inp)
+        rows = np.linspace(0, h - 1, nrows).astype(np.int32)
+        t0 = time.perf_counter()
+        orc.wgrad_mx(synth.bits(cpu["a"]), synth.bits(cpu["sfa"]), synth.bits(cpu["b"]),
+                     synth.bits(cpu["sfb"]), cpu["offsets"].numpy(), h, i, T, out_dtype=orc.BF16,
+                     hrows=rows)
+        return time.perf_counter() - t0, 2.0 * nrows * i * T
+
+    return Op("wgrad_mxfp8", "wgrad_mx_kernel", synth.flops_wgrad(h, i, counts), "fp8", run, alg,
+              sample)
+
+
 def make_dsrelu(dev):
     import numpy as np
     import torch
@@ -234,6 +271,7 @@ WORKLOAD_OPS = {
     "dgeglu": ["dgeglu"],
     "dsrelu_mxfp8": ["dsrelu_mxfp8"],
     "dglu_mxfp8": ["dglu_mxfp8"],
+    "wgrad_mxfp8": ["wgrad_mxfp8"],
 }
 
 
@@ -248,6 +286,8 @@ def build_op(name, dev):
         return op
     if name == "dglu_mxfp8":
         return make_dglu_mx(dev)
+    if name == "wgrad_mxfp8":
+        return make_wgrad_mx(dev)
     return make_dsrelu(dev)
 
 
@@ -365,7 +405,7 @@ def main():
             sys.exit("--summarize-pmc needs a single-op --workload")
         kernel = {"dswiglu": "dglu_kernel", "dgeglu": "dglu_kernel", "wgrad_moe": "wgrad_kernel",
                   "wgrad_moe_kmajor": "wgrad_kernel", "dsrelu_mxfp8": "dsrelu_kernel",
-                  "dglu_mxfp8": "dglu_mx_kernel"}[names[0]]
+                  "dglu_mxfp8": "dglu_mx_kernel", "wgrad_mxfp8": "wgrad_mx_kernel"}[names[0]]
         path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
         res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
                             {names[0]: (kernel, names[0])}, path)

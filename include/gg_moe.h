@@ -2,13 +2,15 @@
  * gg_moe.h -- C ABI of libgg_moe: grouped GEMMs of the MoE expert backward
  * pass on AMD Instinct MI355X (gfx950).
  *
- * Three operations, each defined on an NVIDIA cuDNN frontend documentation
+ * The entry points, each defined on an NVIDIA cuDNN frontend documentation
  * page (the pages describe the method; this library is an independent
  * implementation for CDNA4):
  *
  *   gg_wgrad   "Grouped GEMM + WGrad (Unified)", section "Operation":
  *              Wgrad[e] = A[:, begin:end] @ B[begin:end, :] over the token
  *              slice of expert e, accumulate or overwrite.
+ *   gg_wgrad_mx  the same, section "Block-scaled contract", on MXFP8
+ *              operands.
  *   gg_dglu    "Grouped GEMM + dGLU (SM100)", section "BF16 contract /
  *              Tensors, layouts, and equation": R_g = alpha_g^2 A_g B_g^T
  *              fused with the dSwiGLU / dGeGLU backward over 32-wide
@@ -103,7 +105,14 @@ enum {
      * return GG_ERR_OFFSETS unless they are non-decreasing, every group is a
      * multiple of 256, and the last value equals tokens_sum (wgrad) or is at
      * most m_rows (dgrad).  Off by default: it synchronises the stream. */
-    GG_FLAG_VALIDATE_OFFSETS = 4u
+    GG_FLAG_VALIDATE_OFFSETS = 4u,
+    /* wgrad: K-major operands are stored "tensor_ragged" (the wgrad page's
+     * input_order): expert e's (rows, count_e) block is K-contiguous, with
+     * row pitch count_e, and the blocks are concatenated in expert order, so
+     * that block e starts at element rows * offsets[e-1] (0 for e = 0).
+     * M-/N-major operands hold each token contiguously either way, so the
+     * flag leaves them as they are. */
+    GG_FLAG_TENSOR_RAGGED = 8u
 };
 
 /* Bits of the device error word (see gg_device_error). */
@@ -161,7 +170,8 @@ size_t gg_wgrad_workspace_size(int32_t num_experts);
  * accumulate   nonzero: out = round(old + result) (the caller initialises
  *              every output); zero: out = round(result), an empty expert
  *              gives exact zeros.  Rounding is to nearest even.
- * flags        0 or GG_FLAG_VALIDATE_OFFSETS.
+ * flags        OR of GG_FLAG_VALIDATE_OFFSETS and GG_FLAG_TENSOR_RAGGED
+ *              ("input_order": the K-major operands' storage, see the flag).
  * workspace    >= gg_wgrad_workspace_size(num_experts) bytes, 256-B aligned.
  */
 gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_major,
@@ -170,6 +180,35 @@ gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_ma
                    void* wgrad_dense, const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype,
                    int32_t accumulate, uint32_t flags,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same operation on block-scaled operands ("Grouped GEMM + WGrad
+ * (Unified)", "Block-scaled contract"), MXFP8: E4M3 codes with one E8M0
+ * scale per 32 consecutive tokens of a row, deq(q, s) = e4m3(q) * 2^(s-127),
+ * fp32 accumulation.  The reduction axis is contiguous in both operands:
+ * a_fp8      A (hidden, tokens_sum) K-major: (h,t) at a[h*tokens_sum + t];
+ * sfa        (hidden, tokens_sum/32): sfa[h*(tokens_sum/32) + t/32];
+ * b_fp8      B (tokens_sum, intermediate) stored K-major, as an
+ *            (intermediate, tokens_sum) array: (t,i) at b[i*tokens_sum + t];
+ * sfb        (intermediate, tokens_sum/32): sfb[i*(tokens_sum/32) + t/32].
+ *            With GG_FLAG_TENSOR_RAGGED all four hold per-expert blocks
+ *            instead: expert e's codes at a[hidden*begin + h*count + t-begin]
+ *            and scales at sfa[(hidden*begin + h*count + t-begin)/32]
+ *            (likewise b, sfb with intermediate).
+ * tokens_sum a multiple of 128, as is every expert's count (the pages ask
+ *            for 256; a count that is not a multiple of 128 is skipped and
+ *            flagged GG_DEVERR_SKIPPED, one of 128 but not 256 computed and
+ *            flagged GG_DEVERR_GRANULE).
+ * Codes 16-byte, scales 4-byte aligned.  Every other argument as for
+ * gg_wgrad; the pages' global scales belong to formats other than MXFP8 and
+ * are not taken.
+ */
+gg_status gg_wgrad_mx(const void* a_fp8, const uint8_t* sfa, const void* b_fp8, const uint8_t* sfb,
+                      const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                      int32_t hidden, int32_t intermediate,
+                      void* wgrad_dense, const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype,
+                      int32_t accumulate, uint32_t flags,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Grouped dgrad + dSwiGLU / dGeGLU                                          */

@@ -19,12 +19,13 @@ GG_BF16, GG_F16, GG_F32, GG_F8E4M3 = 0, 1, 2, 3
 GG_MAJOR_K, GG_MAJOR_M, GG_MAJOR_N = 0, 1, 2
 GG_DSWIGLU, GG_DGEGLU, GG_DSITUGLU = 0, 1, 2
 GG_FLAG_GATE_FIRST, GG_FLAG_GEGLU_MASK_FILTER, GG_FLAG_VALIDATE_OFFSETS = 1, 2, 4
+GG_FLAG_TENSOR_RAGGED = 8
 GG_DEVERR_DECREASING, GG_DEVERR_GRANULE, GG_DEVERR_LAST, GG_DEVERR_SKIPPED = 1, 2, 4, 8
 STATUS_NAMES = ["GG_OK", "GG_ERR_NULL", "GG_ERR_SHAPE", "GG_ERR_DTYPE", "GG_ERR_LAYOUT",
                 "GG_ERR_ALIGN", "GG_ERR_MODE", "GG_ERR_WORKSPACE", "GG_ERR_UNSUPPORTED",
-                "GG_ERR_DEVICE", "GG_ERR_HIP", "GG_ERR_OFFSETS"]
+                "GG_ERR_DEVICE", "GG_ERR_HIP", "GG_ERR_OFFSETS", "GG_ERR_VALUE"]
 EXPORTS = ["gg_abi_version", "gg_last_error", "gg_device_error", "gg_wgrad_workspace_size",
-           "gg_wgrad", "gg_dglu_workspace_size", "gg_dglu", "gg_dglu_mx",
+           "gg_wgrad", "gg_wgrad_mx", "gg_dglu_workspace_size", "gg_dglu", "gg_dglu_mx",
            "gg_dsrelu_workspace_size", "gg_dsrelu"]
 
 _TORCH_DTYPE = {torch.bfloat16: GG_BF16, torch.float16: GG_F16, torch.float32: GG_F32,
@@ -66,6 +67,8 @@ def load_library(path=LIB_PATH):
     L.gg_dsrelu_workspace_size.argtypes = [I32]
     L.gg_wgrad.restype = ctypes.c_int
     L.gg_wgrad.argtypes = [P, I32, P, I32, P, I32, I64, I32, I32, P, P, I32, I32, U32, P, SZ, P]
+    L.gg_wgrad_mx.restype = ctypes.c_int
+    L.gg_wgrad_mx.argtypes = [P, P, P, P, P, I32, I64, I32, I32, P, P, I32, I32, U32, P, SZ, P]
     L.gg_dglu.restype = ctypes.c_int
     L.gg_dglu.argtypes = [P, I64, I32, P, P, I32, I32, P, I32, P, I32, P, P, P, P, I32, P, P,
                           I32, F, F, F, F, U32, P, SZ, P]
@@ -146,6 +149,22 @@ def gg_wgrad(a, a_major, b, b_major, offsets, tokens_sum, hidden, intermediate,
     _check(L.gg_wgrad(_ptr(a), a_major, _ptr(b), b_major, _ptr(offsets), E, tokens_sum, hidden,
                       intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
                       int(bool(accumulate)), flags, _ptr(ws), nbytes, _stream(stream)))
+    return ws
+
+
+def gg_wgrad_mx(a, sfa, b, sfb, offsets, tokens_sum, hidden, intermediate, wgrad_dense=None,
+                wgrad_ptrs=None, wgrad_dtype=None, accumulate=False, flags=0, workspace=None,
+                stream=None):
+    """Grouped MXFP8 wgrad (gg_wgrad_mx of gg_moe.h): uint8 codes and E8M0
+    scales, both operands K-major.  Returns the workspace used."""
+    L = load_library()
+    E = offsets.numel()
+    if wgrad_dtype is None:
+        wgrad_dtype = _TORCH_DTYPE[wgrad_dense.dtype]
+    ws, nbytes = _workspace(workspace, L.gg_wgrad_workspace_size(E), offsets)
+    _check(L.gg_wgrad_mx(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(offsets), E, tokens_sum,
+                         hidden, intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
+                         int(bool(accumulate)), flags, _ptr(ws), nbytes, _stream(stream)))
     return ws
 
 

@@ -136,19 +136,14 @@ size_t gg_dsrelu_workspace_size(int32_t L) {
     return round256(gg::kWsHeader);
 }
 
-gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_major,
-                   const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
-                   int32_t hidden, int32_t intermediate, void* wgrad_dense,
-                   const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype, int32_t accumulate,
-                   uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
-    if (!offsets || !workspace)
-        return fail(GG_ERR_NULL, "offsets and workspace must be non-NULL");
-    if ((!a || !b) && tokens_sum > 0)
-        return fail(GG_ERR_NULL, "a and b must be non-NULL");
-    if (a_major != GG_MAJOR_K && a_major != GG_MAJOR_M)
-        return fail(GG_ERR_LAYOUT, "a_major must be GG_MAJOR_K or GG_MAJOR_M");
-    if (b_major != GG_MAJOR_K && b_major != GG_MAJOR_N)
-        return fail(GG_ERR_LAYOUT, "b_major must be GG_MAJOR_K or GG_MAJOR_N");
+// Checks shared by gg_wgrad and gg_wgrad_mx (all but the operand pointers,
+// majors and scales), then the prologue and the launch.
+static gg_status run_wgrad(gg::WgradArgs& p, bool mx, const int32_t* offsets, int32_t num_experts,
+                           int64_t tokens_sum, int32_t hidden, int32_t intermediate,
+                           void* wgrad_dense, const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype,
+                           int32_t accumulate, uint32_t flags, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    const char* name = mx ? "gg_wgrad_mx" : "gg_wgrad";
     if (!is_out_dtype(wgrad_dtype))
         return fail(GG_ERR_DTYPE, "wgrad_dtype must be GG_BF16, GG_F16 or GG_F32");
     if ((wgrad_dense != nullptr) == (wgrad_ptrs != nullptr))
@@ -161,21 +156,21 @@ gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_ma
         return fail(GG_ERR_SHAPE, "hidden and intermediate must be positive");
     if (hidden % 64 || intermediate % 64)
         return fail(GG_ERR_UNSUPPORTED, "hidden and intermediate must be multiples of 64");
-    if (tokens_sum % 8)
-        return fail(GG_ERR_ALIGN, "tokens_sum must be a multiple of 8 (16-byte rows)");
+    if (mx ? tokens_sum % 128 : tokens_sum % 8)
+        return fail(GG_ERR_ALIGN, mx ? "tokens_sum must be a multiple of 128"
+                                     : "tokens_sum must be a multiple of 8 (16-byte rows)");
     // tile-relative 32-bit buffer offsets: 256 rows of the largest pitch
     if (tokens_sum > (1 << 21) || hidden > (1 << 21) || intermediate > (1 << 21))
         return fail(GG_ERR_UNSUPPORTED, "tokens_sum, hidden and intermediate are limited to 2^21");
-    if (!aligned16(a) || !aligned16(b) || !aligned16(wgrad_dense) || !aligned16(wgrad_ptrs) ||
-        ((uintptr_t)offsets & 3u))
-        return fail(GG_ERR_ALIGN, "a, b and the output must be 16-byte aligned");
+    if (!aligned16(wgrad_dense) || !aligned16(wgrad_ptrs) || ((uintptr_t)offsets & 3u))
+        return fail(GG_ERR_ALIGN, "the output must be 16-byte aligned, offsets 4-byte");
     if ((uintptr_t)workspace & 255u)
         return fail(GG_ERR_ALIGN, "workspace must be 256-byte aligned");
     if (workspace_bytes < gg_wgrad_workspace_size(num_experts))
         return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
                     gg_wgrad_workspace_size(num_experts));
-    if (flags & ~(uint32_t)GG_FLAG_VALIDATE_OFFSETS)
-        return fail(GG_ERR_MODE, "unsupported flags 0x%x for gg_wgrad", flags);
+    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_TENSOR_RAGGED))
+        return fail(GG_ERR_MODE, "unsupported flags 0x%x for %s", flags, name);
     gg_status st = check_device();
     if (st != GG_OK)
         return st;
@@ -190,9 +185,6 @@ gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_ma
                                        ws + gg::kWsHeader / 4, nullptr, 0, nullptr, 0, s);
     if (e != hipSuccess)
         return hip_fail(e, "launching the wgrad prologue");
-    gg::WgradArgs p;
-    p.a = a;
-    p.b = b;
     p.offsets = offsets;
     p.ws = ws;
     p.out_dense = wgrad_dense;
@@ -201,14 +193,58 @@ gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_ma
     p.hidden = hidden;
     p.inter = intermediate;
     p.E = num_experts;
-    p.a_kmajor = a_major == GG_MAJOR_K;
-    p.b_kmajor = b_major == GG_MAJOR_K;
+    p.ragged = (flags & GG_FLAG_TENSOR_RAGGED) != 0;
     p.out_dtype = (int)wgrad_dtype;
     p.accumulate = accumulate ? 1 : 0;
-    e = gg::launch_wgrad(p, s);
+    e = mx ? gg::launch_wgrad_mx(p, s) : gg::launch_wgrad(p, s);
     if (e != hipSuccess)
-        return hip_fail(e, "launching gg_wgrad");
+        return hip_fail(e, mx ? "launching gg_wgrad_mx" : "launching gg_wgrad");
     return ok();
+}
+
+gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_major,
+                   const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                   int32_t hidden, int32_t intermediate, void* wgrad_dense,
+                   const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype, int32_t accumulate,
+                   uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!offsets || !workspace)
+        return fail(GG_ERR_NULL, "offsets and workspace must be non-NULL");
+    if ((!a || !b) && tokens_sum > 0)
+        return fail(GG_ERR_NULL, "a and b must be non-NULL");
+    if (a_major != GG_MAJOR_K && a_major != GG_MAJOR_M)
+        return fail(GG_ERR_LAYOUT, "a_major must be GG_MAJOR_K or GG_MAJOR_M");
+    if (b_major != GG_MAJOR_K && b_major != GG_MAJOR_N)
+        return fail(GG_ERR_LAYOUT, "b_major must be GG_MAJOR_K or GG_MAJOR_N");
+    if (!aligned16(a) || !aligned16(b))
+        return fail(GG_ERR_ALIGN, "a, b and the output must be 16-byte aligned");
+    gg::WgradArgs p = {};
+    p.a = a;
+    p.b = b;
+    p.a_kmajor = a_major == GG_MAJOR_K;
+    p.b_kmajor = b_major == GG_MAJOR_K;
+    return run_wgrad(p, false, offsets, num_experts, tokens_sum, hidden, intermediate, wgrad_dense,
+                     wgrad_ptrs, wgrad_dtype, accumulate, flags, workspace, workspace_bytes, stream);
+}
+
+gg_status gg_wgrad_mx(const void* a_fp8, const uint8_t* sfa, const void* b_fp8, const uint8_t* sfb,
+                      const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                      int32_t hidden, int32_t intermediate, void* wgrad_dense,
+                      const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype, int32_t accumulate,
+                      uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!offsets || !workspace)
+        return fail(GG_ERR_NULL, "offsets and workspace must be non-NULL");
+    if ((!a_fp8 || !b_fp8 || !sfa || !sfb) && tokens_sum > 0)
+        return fail(GG_ERR_NULL, "a_fp8, sfa, b_fp8 and sfb must be non-NULL");
+    if (!aligned16(a_fp8) || !aligned16(b_fp8) || ((uintptr_t)sfa & 3u) || ((uintptr_t)sfb & 3u))
+        return fail(GG_ERR_ALIGN, "codes must be 16-byte aligned, scales 4-byte aligned");
+    gg::WgradArgs p = {};
+    p.a = a_fp8;
+    p.b = b_fp8;
+    p.sfa = sfa;
+    p.sfb = sfb;
+    p.a_kmajor = p.b_kmajor = 1;
+    return run_wgrad(p, true, offsets, num_experts, tokens_sum, hidden, intermediate, wgrad_dense,
+                     wgrad_ptrs, wgrad_dtype, accumulate, flags, workspace, workspace_bytes, stream);
 }
 
 static gg_status check_rows(const int32_t* po, int32_t L, int64_t m_rows, const void* c,

@@ -65,7 +65,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
                                : (const char*)p.b_ptrs[g] + (int64_t)n0 * K;
     const char* sfb = p.sfb_dense ? (const char*)p.sfb_dense + ((int64_t)g * p.N + n0) * KB
                                   : (const char*)p.sfb_ptrs[g] + (int64_t)n0 * KB;
-    mx_mainloop<C>(smem, a, sfa, bg, sfb, K, rows_valid, cols_valid, am0, bn0, acc);
+    mx_mainloop<C>(smem, a, sfa, bg, sfb, K, K, rows_valid, cols_valid, am0, bn0, acc);
 
     // C of the items 12 ahead (6 for fp32 C) in flight in the epilogue
     dglu_epilogue<C, W32, ACT, true, W32 ? 6 : 12>(p, acc, smem, m0, n0, g, rows_valid, am0, bn0);

@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                                : (const char*)p.b_ptrs[g] + (int64_t)n0 * K;
     const char* sfb = p.sfb_dense ? (const char*)p.sfb_dense + ((int64_t)g * p.N + n0) * KB
                                   : (const char*)p.sfb_ptrs[g] + (int64_t)n0 * KB;
-    mx_mainloop<C>(smem, a, sfa, bg, sfb, K, rows_valid, cols_valid, am0, bn0, acc);
+    mx_mainloop<C>(smem, a, sfa, bg, sfb, K, K, rows_valid, cols_valid, am0, bn0, acc);
 
     // ---------------- epilogue ----------------
     // Rows of 8 columns per lane: C and D are 16-byte accesses (32 for fp32).

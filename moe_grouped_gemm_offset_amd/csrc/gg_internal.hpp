@@ -11,8 +11,10 @@ namespace gg {
 constexpr size_t kWsHeader = 256;
 
 struct WgradArgs {
-    const void* a;
+    const void* a;            // bf16, or E4M3 codes (block-scaled)
     const void* b;
+    const uint8_t* sfa;       // block-scaled only: E8M0 scales of A and B
+    const uint8_t* sfb;
     const int32_t* offsets;
     int32_t* ws;              // header + int32 order[E]
     void* out_dense;
@@ -20,6 +22,7 @@ struct WgradArgs {
     int64_t T;
     int hidden, inter, E;
     int a_kmajor, b_kmajor;
+    int ragged;               // K-major operands stored tensor_ragged
     int out_dtype, accumulate;
 };
 
@@ -72,6 +75,7 @@ struct DsreluArgs {
 
 // Launchers (return the HIP status of the launch).
 hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s);
+hipError_t launch_wgrad_mx(const WgradArgs& p, hipStream_t s);
 hipError_t launch_dglu(const DgluArgs& p, hipStream_t s);
 hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s);
 hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s);

@@ -41,26 +41,34 @@ struct ScaleLds {
                   "scale slices must split evenly over waves and units");
 };
 
-// acc[i][j] += the wave's (32 i, 32 j) blocks of deq(A) deq(B)^T over all of
-// K for the tile whose A rows start at `a` (scales `sfa`) and whose B rows
-// start at `b` (scales `sfb`).  Rows at or past rows_valid / cols_valid load
-// zeros.  K is a multiple of 128; smem holds ScaleLds<C>::kSmem bytes.
+// acc[i][j] += the wave's (32 i, 32 j) blocks of deq(A) deq(B)^T over the
+// first K values of each row, for the tile whose A rows start at `a` (scales
+// `sfa`) and whose B rows start at `b` (scales `sfb`).  Rows are `ld` bytes
+// apart (codes) and ld / 32 bytes apart (scales); K and ld are multiples of
+// 128 (whole load units, 4-byte scale words), and rows at or past rows_valid
+// / cols_valid contribute zero.  smem holds ScaleLds<C>::kSmem bytes.
 template <class C>
 __device__ __forceinline__ void mx_mainloop(char* smem, const char* a, const char* sfa,
-                                            const char* b, const char* sfb, int64_t K,
+                                            const char* b, const char* sfb, int64_t ld, int64_t K,
                                             int rows_valid, int cols_valid, int am0, int bn0,
                                             f32x16 (&acc)[C::MB][C::NB]) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
     using S = ScaleLds<C>;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int lr = l & 31, lq = l >> 5;
-    const int64_t KB = K / 32;                   // scale bytes per row
+    const int64_t KB = ld / 32;                  // scale bytes per row
     const int nk = (int)(K / 64);                // stages; K % 128 == 0, so nk is even
-    // Scale records end at the last valid row, so rows past the tile edge
-    // load zeros.  Words past the end of K are never read: they belong to no
+    // Scale records end with the K/32 bytes of the tile's last valid row, so
+    // rows past the tile edge load zeros and no load passes the end of the
+    // last row's K range (when ld > K the next bytes may lie past the
+    // array).  Words past K inside other rows are loaded but belong to no
     // stage.
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sfa, (uint32_t)(rows_valid * KB));
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sfb, (uint32_t)(cols_valid * KB));
+    auto scale_records = [&](int valid, int rows) {
+        const int v = valid < rows ? valid : rows;
+        return (uint32_t)(v > 0 ? (int64_t)(v - 1) * KB + K / 32 : 0);
+    };
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sfa, scale_records(rows_valid, TM));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sfb, scale_records(cols_valid, TN));
     char* const sbuf = smem + S::kBase;
     const uint32_t sbuf32 = lds_addr(sbuf);
     const int wu = uniform(w);
@@ -79,8 +87,8 @@ __device__ __forceinline__ void mx_mainloop(char* smem, const char* a, const cha
     };
     LoadK<C, TM> la;
     LoadK<C, TN> lb;
-    la.init(K, rows_valid);
-    lb.init(K, cols_valid);
+    la.init(ld, rows_valid);
+    lb.init(ld, cols_valid);
     constexpr int kLA = LoadK<C, TM>::kN, kLB = LoadK<C, TN>::kN;
     auto issue = [&](uint32_t st, int u, int i) {
         const int64_t kb = (int64_t)u * 128;

@@ -16,44 +16,12 @@
 // are staged in the K
 // layout, M-/N-major operands (the natural layouts of X and dY) are staged
 // untransposed in the MN layout and transposed by the LDS transpose reads.
-#include "gg_internal.hpp"
-#include "gg_tile.hpp"
+#include "gg_wgrad_epi.hpp"
 #include "gg_moe.h"
 
 namespace gg {
 
 using WgradCfg = Cfg<256, 256, 4, 2>;
-
-// Output: rows of 8 consecutive columns per lane (16-byte bf16/fp16 or
-// 32-byte fp32 accesses), accumulate mode adding the old values, which are
-// loaded 8 items ahead.  Items off the tile have masked loads and stores.
-template <class C>
-__device__ __forceinline__ void wgrad_epilogue(const f32x16 (&acc)[C::MB][C::NB], float* lds,
-                                               void* out, int dtype, int hidden, int inter,
-                                               int row0, int col0, int accumulate) {
-    const Fmt8 fo(dtype);
-    // offsets (r inter + col) bytes from the wave tile's first row: r < 128,
-    // inter <= 2^21
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)out + (int64_t)row0 * inter * (fo.w32 ? 4 : 2));
-    auto load = [&](int, int r, int c) {
-        const int row = row0 + r, col = col0 + c;
-        const bool ok = (row < hidden) & (col < inter) & (accumulate != 0);
-        PreB8<1> pre;
-        pre.x[0] = rawb8_load(ro, fo, fo.off(ok, (int64_t)r * inter + col));
-        return pre;
-    };
-    auto fn = [&](int, int r, int c, float (&v)[8], const PreB8<1>& pre) {
-        const int row = row0 + r, col = col0 + c;
-        const bool ok = (row < hidden) & (col < inter);
-        float o[8];
-        rawb8_cvt(pre.x[0], fo, o);          // zeros unless accumulating
-#pragma unroll
-        for (int k = 0; k < 8; k++)
-            v[k] += o[k];
-        rawb8_store(ro, fo, fo.off(ok, (int64_t)r * inter + col), v);
-    };
-    for_each_row8<C, 8>(acc, lds, load, fn);
-}
 
 template <class C, bool A_K, bool B_K>
 __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
@@ -94,17 +62,23 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         for (int j = 0; j < C::NB; j++)
             acc[i][j] = f32x16{0};
 
+    // K-major operands: the expert's slice starts at token `begin` of rows T
+    // tokens apart (tensor2d), or is its own (rows, cnt) block stored at
+    // element rows * begin (tensor_ragged).  M-/N-major operands hold each
+    // token's row contiguously either way.
+    const int64_t ldk = (p.ragged ? cnt : p.T) * 2;
     const char* a = (const char*)p.a;
     const char* b = (const char*)p.b;
-    const int64_t T2 = p.T * 2;
+    const char* ak = a + (p.ragged ? (int64_t)p.hidden * begin : begin) * 2;
+    const char* bk = b + (p.ragged ? (int64_t)p.inter * begin : begin) * 2;
     std::conditional_t<A_K, LoadK<C, TM>, LoadMN<C>> la;
     std::conditional_t<B_K, LoadK<C, TN>, LoadMN<C>> lb;
     if constexpr (A_K)
-        la.init(T2, p.hidden - m0);
+        la.init(ldk, p.hidden - m0);
     else
         la.init((int64_t)p.hidden * 2, p.hidden - m0);
     if constexpr (B_K)
-        lb.init(T2, p.inter - n0);
+        lb.init(ldk, p.inter - n0);
     else
         lb.init((int64_t)p.inter * 2, p.inter - n0);
     using LA = std::conditional_t<A_K, LoadK<C, TM>, LoadMN<C>>;
@@ -113,12 +87,12 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         const int64_t k0 = begin + (int64_t)u * 64;
         if (i < LA::kN) {
             if constexpr (A_K)
-                la.template issue<true>(st, a + (int64_t)m0 * T2 + k0 * 2, (end - k0) * 2, i);
+                la.template issue<true>(st, ak + (int64_t)m0 * ldk + (int64_t)u * 128, (end - k0) * 2, i);
             else
                 la.issue(st, a + (k0 * p.hidden + m0) * 2, end - k0, i);
         } else {
             if constexpr (B_K)
-                lb.template issue<true>(st + TM * kRowBytes, b + (int64_t)n0 * T2 + k0 * 2,
+                lb.template issue<true>(st + TM * kRowBytes, bk + (int64_t)n0 * ldk + (int64_t)u * 128,
                                         (end - k0) * 2, i - LA::kN);
             else
                 lb.issue(st + TM * kRowBytes, b + (k0 * p.inter + n0) * 2, end - k0, i - LA::kN);

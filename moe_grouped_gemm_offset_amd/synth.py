@@ -16,6 +16,8 @@ padded_offsets):
   dglu_mxfp8    L 32, K 4096, N 1536, M 32768, MXFP8 A and discrete B,
                 dSwiGLU with amax (the dGeGLU workload's shape on the
                 block-scaled path)
+  wgrad_mxfp8   the wgrad_moe shape (hidden 4096, inter 2048, 64 experts,
+                65536 Zipf(1.2) tokens) on MXFP8 K-major operands
 
 Every generator takes a seed and a torch device; tensors are created on that
 device from a torch.Generator seeded with it, so a run that needs the same
@@ -332,12 +334,14 @@ WORKLOADS = {
     "dsrelu_mxfp8": dict(kind="dsrelu", L=16, K=7168, N=2048, M=65536, seed=1005),
     "dglu_mxfp8": dict(kind="dglu_mx", act="dswiglu", L=32, K=4096, N=1536, M=32768,
                        c_std=2.0, discrete=True, dbias=False, seed=1006),
+    "wgrad_mxfp8": dict(kind="wgrad_mx", hidden=4096, inter=2048, E=64, T=65536, zipf=1.2,
+                        seed=1007),
 }
 
 
 def workload_counts(name):
     w = WORKLOADS[name]
-    if w["kind"] == "wgrad":
+    if w["kind"] in ("wgrad", "wgrad_mx"):
         if "counts" in w:
             return np.asarray(w["counts"], np.int64)
         return zipf_groups(w["T"], w["E"], w["zipf"], w["seed"])

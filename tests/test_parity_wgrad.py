@@ -26,10 +26,19 @@ def gg():
     return binding
 
 
-def run_gpu(inp, out_dtype, accumulate=False, old=None, discrete=False):
+def run_gpu(inp, out_dtype, accumulate=False, old=None, discrete=False, ragged=False):
     b = gg()
     E = len(inp["counts"])
     a, bb = inp["a"].cuda(), inp["b"].cuda()
+    flags = 0
+    if ragged:
+        # tensor_ragged storage of the K-major operands (the others are
+        # per-token rows either way)
+        flags = b.GG_FLAG_TENSOR_RAGGED
+        if inp["a_major"] == "k":
+            a = synth.to_ragged(a, inp["counts"])
+        if inp["b_major"] == "k":
+            bb = synth.to_ragged(bb, inp["counts"])
     off = inp["offsets"].cuda()
     h, i = inp["hidden"], inp["inter"]
     if discrete:
@@ -39,14 +48,15 @@ def run_gpu(inp, out_dtype, accumulate=False, old=None, discrete=False):
                 outs[e].copy_(old[e])
         ptrs = torch.tensor([o.data_ptr() for o in outs], dtype=torch.int64, device="cuda")
         ws = b.gg_wgrad(a, MAJ[inp["a_major"]], bb, MAJ[inp["b_major"]], off, inp["tokens_sum"], h, i,
-                        wgrad_ptrs=ptrs, wgrad_dtype=b._TORCH_DTYPE[out_dtype], accumulate=accumulate)
+                        wgrad_ptrs=ptrs, wgrad_dtype=b._TORCH_DTYPE[out_dtype], accumulate=accumulate,
+                        flags=flags)
         torch.cuda.synchronize()
         res = torch.stack(outs)
     else:
         res = old.clone().cuda() if accumulate else torch.full((E, h, i), float("nan"), dtype=out_dtype,
                                                                device="cuda")
         ws = b.gg_wgrad(a, MAJ[inp["a_major"]], bb, MAJ[inp["b_major"]], off, inp["tokens_sum"], h, i,
-                        wgrad_dense=res, accumulate=accumulate)
+                        wgrad_dense=res, accumulate=accumulate, flags=flags)
         torch.cuda.synchronize()
     return res.cpu(), b.gg_device_error(ws)
 
@@ -95,6 +105,19 @@ def test_majors_ragged(a_major, b_major):
     got, err = run_gpu(inp, torch.float32)
     assert err == 2  # GG_DEVERR_GRANULE: counts not multiples of 256 (still computed)
     compare(got, inp, torch.float32, name=f"{a_major}{b_major}")
+
+
+@pytest.mark.parametrize("a_major", ["k", "m"])
+@pytest.mark.parametrize("b_major", ["k", "n"])
+def test_tensor_ragged(a_major, b_major):
+    """GG_FLAG_TENSOR_RAGGED: K-major operands stored as per-expert
+    K-contiguous blocks; the result is that of the tensor2d storage."""
+    counts = [520, 0, 256, 72, 8, 320]
+    inp = synth.wgrad_inputs(512, 384, counts, a_major, b_major, seed=46)
+    say("tensor_ragged", a_major, b_major, counts)
+    got, err = run_gpu(inp, torch.float32, ragged=True)
+    assert err == 2  # GG_DEVERR_GRANULE only
+    compare(got, inp, torch.float32, name=f"ragged {a_major}{b_major}")
 
 
 def test_exact_integers_bit_exact():
