@@ -19,13 +19,16 @@
  *       dprob reduction), "Equations" for dSiTU-GLU (T_g, T_u and their
  *       derivatives) and "Shapes" (per-group amax of shape (L, 2, 1)).
  *   [S] "Grouped GEMM + dsReLU (SM100)": "Equations" (G, D_row, dprob), and
- *       "Shapes" (per-expert Amax).
+ *       "Shapes" (per-expert Amax; FP8 D_row / D_col with SFD_row / SFD_col).
+ *   [G] step 3 (optional quantized output): orc_quant_fp8.
  *
  * Arithmetic: every input is decoded exactly into double; every sum is taken
  * in double in the plain index order; outputs are rounded once, to nearest
- * even, by the encoders below.  The one deliberate fp32 step is X = beta*C of
+ * even, by the encoders below.  The deliberate fp32 steps are X = beta*C of
  * [G], formed as a single fp32 product, because the clamp and filter tests of
- * dGeGLU compare X with +-7 and the product is what the method feeds them.
+ * dGeGLU compare X with +-7 and the product is what the method feeds them;
+ * and the FP8 output quantization of step 3, whose integer scale exponent is
+ * decided in the fp32 arithmetic of the kernels' epilogue.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  */
@@ -158,6 +161,93 @@ float orc_double_to_f32(double x) {
     double y = round_format(fabs(x), 24, -126, ldexp(16777215.0, 104));
     float f = (float)y;            /* exact */
     return signbit(x) ? -f : f;
+}
+
+/* OCP E4M3 ("float8_e4m3fn": 4 significand bits, minimum normal exponent
+ * -6, largest finite 448, no infinity) by round-to-nearest-even, with
+ * magnitudes above 448 clamped to 448 first (the quantizer below never
+ * produces them but for rounding in its scale computation). */
+uint8_t orc_double_to_e4m3(double x) {
+    if (isnan(x))
+        return 0x7f;
+    uint8_t s = signbit(x) ? 0x80u : 0u;
+    double ax = fabs(x);
+    double y = round_format(ax > 448.0 ? 448.0 : ax, 4, -6, 448.0);
+    if (y == 0.0)
+        return s;
+    int E;
+    frexp(y, &E);
+    int e = E - 1;
+    if (e < -6)                                    /* subnormal: y = m * 2^-9 */
+        return s | (uint8_t)(int)ldexp(y, 9);
+    int m = (int)(ldexp(y, -e) * 8.0) - 8;         /* exact: 3 fraction bits */
+    return s | (uint8_t)(((e + 7) << 3) | m);
+}
+
+/* [G] "Block-scaled contract / Equations", step 3 (and the FP8 D_row / D_col
+ * with SFD_row / SFD_col of [S] "Shapes"): blocks of 32 values (32 columns of
+ * a row for D_row, 32 rows of a column for D_col) share one E8M0 scale
+ *   SFD = norm_const * max|D| * rcp_max,   D_q = D * norm_const / SFD,
+ * with rcp_max = 1/448 (E4M3).  E8M0 holds powers of two only: SFD is taken
+ * as the smallest power of two 2^e not below the product (so |D_q| <= 448),
+ * e clamped to [-127, 127], e = -127 for an all-zero block.  The scale
+ * exponent is an integer decided by floating point, so it is decided in the
+ * precision of the kernel's epilogue: D rounded to fp32, the product formed
+ * as fp32(fp32(norm_const * amax) * fp32(1/448)); D_q = e4m3(fp32(D * nc)
+ * * 2^-e).  Returns e. */
+static int fp8_block_exponent(float amax, float norm_const) {
+    const float rcp_max = 1.0f / 448.0f;
+    volatile float t = norm_const * amax;      /* one fp32 rounding each */
+    volatile float x = t * rcp_max;
+    if (!(x > 0.0f))
+        return -127;
+    if (isinf(x))
+        return 127;
+    int E;
+    float f = frexpf(x, &E);                   /* x = f * 2^E, f in [0.5, 1) */
+    int e = (f == 0.5f) ? E - 1 : E;           /* smallest e with 2^e >= x */
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+static uint8_t fp8_quantize(double d, float norm_const, int e) {
+    volatile float v = (float)d * norm_const;  /* fp32(D) * nc, one rounding */
+    return orc_double_to_e4m3((double)ldexpf(v, -e));
+}
+
+/* D (nrows, W) doubles, W a multiple of 32.  q_row (nrows, W) E4M3 and
+ * sfd_row (nrows, W/32) E8M0: row blocks; if q_col is non-NULL (nrows a
+ * multiple of 32, consecutive rows): q_col (nrows, W) and sfd_col
+ * (W, nrows/32), column blocks of rows 32j .. 32j+31. */
+void orc_quant_fp8(const double* D, int64_t nrows, int W, float norm_const,
+                   uint8_t* q_row, uint8_t* sfd_row, uint8_t* q_col, uint8_t* sfd_col) {
+    int WB = W / 32;
+    for (int64_t r = 0; r < nrows; r++)
+        for (int b = 0; b < WB; b++) {
+            float amax = 0.0f;
+            for (int k = 0; k < 32; k++) {
+                float v = fabsf((float)D[r * W + 32 * b + k]);
+                amax = v > amax ? v : amax;
+            }
+            int e = fp8_block_exponent(amax, norm_const);
+            sfd_row[r * WB + b] = (uint8_t)(e + 127);
+            for (int k = 0; k < 32; k++)
+                q_row[r * W + 32 * b + k] = fp8_quantize(D[r * W + 32 * b + k], norm_const, e);
+        }
+    if (!q_col)
+        return;
+    int64_t RB = nrows / 32;
+    for (int c = 0; c < W; c++)
+        for (int64_t j = 0; j < RB; j++) {
+            float amax = 0.0f;
+            for (int k = 0; k < 32; k++) {
+                float v = fabsf((float)D[(32 * j + k) * W + c]);
+                amax = v > amax ? v : amax;
+            }
+            int e = fp8_block_exponent(amax, norm_const);
+            sfd_col[(int64_t)c * RB + j] = (uint8_t)(e + 127);
+            for (int k = 0; k < 32; k++)
+                q_col[(32 * j + k) * W + c] = fp8_quantize(D[(32 * j + k) * W + c], norm_const, e);
+        }
 }
 
 /* Round n doubles to dtype and store them into out (uint16 or float). */

@@ -59,6 +59,10 @@ def lib():
         L.orc_wgrad.restype = None
         L.orc_wgrad_finish.argtypes = [P, I64, I, P, I, P]
         L.orc_wgrad_mx.argtypes = [P, P, P, P, P, I, I64, I, I, P, I, P]
+        L.orc_double_to_e4m3.argtypes = [D]
+        L.orc_double_to_e4m3.restype = ctypes.c_uint8
+        L.orc_quant_fp8.argtypes = [P, I64, I, ctypes.c_float, P, P, P, P]
+        L.orc_quant_fp8.restype = None
         L.orc_wgrad_mx.restype = None
         L.orc_wgrad_finish.restype = None
         L.orc_dglu.argtypes = [P, I64, I, P, I, I, P, I, P, I, P, P, P,
@@ -121,6 +125,28 @@ def round_to(x, dtype):
     out = np.empty(x.shape, _DT_NP[dtype])
     lib().orc_round_array(_p(x), x.size, dtype, _p(out))
     return out
+
+
+def encode_e4m3(x):
+    """OCP E4M3 codes (uint8) of float64 values, RNE, magnitudes clamped to 448."""
+    x = np.asarray(x, np.float64).ravel()
+    return np.array([lib().orc_double_to_e4m3(float(v)) for v in x], np.uint8)
+
+
+def quant_fp8(D, norm_const, with_col=True):
+    """Step 3 of the block-scaled dGLU contract (and the FP8 outputs of the
+    dsReLU page) on a float64 (nrows, W) D: row-quantized E4M3 codes and
+    E8M0 scales per 32 columns, and (with_col, nrows a multiple of 32) the
+    column-quantized codes with scales per 32 rows, laid out (W, nrows/32)."""
+    D = np.ascontiguousarray(D, np.float64)
+    nrows, W = D.shape
+    q_row = np.zeros((nrows, W), np.uint8)
+    sfd_row = np.zeros((nrows, W // 32), np.uint8)
+    q_col = np.zeros((nrows, W), np.uint8) if with_col else None
+    sfd_col = np.zeros((W, nrows // 32), np.uint8) if with_col else None
+    lib().orc_quant_fp8(_p(D), nrows, W, float(norm_const), _p(q_row), _p(sfd_row), _p(q_col),
+                        _p(sfd_col))
+    return {"q_row": q_row, "sfd_row": sfd_row, "q_col": q_col, "sfd_col": sfd_col}
 
 
 # --------------------------------------------------------------------------
