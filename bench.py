@@ -18,6 +18,9 @@ and, as single-op workloads outside the default step:
                 M 32768, discrete B (b_ptrs / sfb_ptrs)
   wgrad_mxfp8   gg_wgrad_mx, the wgrad_moe shape on MXFP8 K-major operands,
                 bf16 dense output, overwrite
+  dsrelu_mxfp8_fp8out, dglu_mxfp8_fp8out
+                the two block-scaled dgrad workloads with FP8 (E4M3) D_row
+                and D_col and their E8M0 scales instead of a bf16 D
   wgrad_moe_kmajor  the wgrad workload with A K-major
 
 value = algorithmic FLOPs of the step (2 sum_e M_e N_e K_e per GEMM) over the
@@ -46,10 +49,12 @@ HBM_PEAK = 8000.0                              # GB/s
 # their hash is unchanged.
 KERNEL_SOURCES = {
     "wgrad_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_wgrad_epi.hpp", "gg_wgrad.hip"],
-    "dglu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_dglu_epi.hpp", "gg_dglu.hip"],
-    "dglu_mx_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_dglu_epi.hpp",
-                       "gg_dglu_mx.hip"],
-    "dsrelu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_dsrelu.hip"],
+    "dglu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_fp8out.hpp", "gg_dglu_epi.hpp",
+                    "gg_dglu.hip"],
+    "dglu_mx_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_fp8out.hpp",
+                       "gg_dglu_epi.hpp", "gg_dglu_mx.hip"],
+    "dsrelu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_fp8out.hpp",
+                      "gg_dsrelu.hip"],
     "wgrad_mx_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_wgrad_epi.hpp",
                         "gg_wgrad_mx.hip"],
 }
@@ -187,7 +192,7 @@ def make_wgrad_mx(dev):
               sample)
 
 
-def make_dsrelu(dev):
+def make_dsrelu(dev, fp8out=False):
     import numpy as np
     import torch
     from moe_grouped_gemm_offset_amd import binding as B, synth
@@ -197,6 +202,9 @@ def make_dsrelu(dev):
     inp = synth.dsrelu_inputs(w["L"], w["K"], w["N"], counts, seed=w["seed"], device=dev)
     M, N, K, L = inp["M"], inp["N"], inp["K"], inp["L"]
     d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    q = None
+    if fp8out:
+        d, q = _fp8_outputs(M, N, dev)
     dprob = torch.zeros(M, dtype=torch.float32, device=dev)
     amax = torch.zeros(L, dtype=torch.float32, device=dev)
     ws = torch.empty(B.gg_dsrelu_workspace_size(L), dtype=torch.uint8, device=dev)
@@ -205,10 +213,11 @@ def make_dsrelu(dev):
 
     def run():
         B.gg_dsrelu(a8, inp["sfa"], b8, inp["sfb_dense"], None, None, N, inp["c"], inp["padded_offsets"],
-                    inp["alpha"], inp["prob"], d, dprob, amax, workspace=ws)
+                    inp["alpha"], inp["prob"], d, dprob, amax, fp8_out=q, workspace=ws)
 
     vm = inp["valid_m"]
-    alg = M * K + L * N * K + (M + L * N) * K // 32 + 2 * M * N * 2 + 8 * M
+    d_bytes = M * N * 2 if not fp8out else 2 * M * N + 2 * M * N // 32
+    alg = M * K + L * N * K + (M + L * N) * K // 32 + M * N * 2 + d_bytes + 8 * M
 
     def sample(nrows):
         cpu = _cpu(inp)
@@ -220,10 +229,24 @@ def make_dsrelu(dev):
                    cpu["alpha"].numpy(), cpu["prob"].numpy(), rows=rows)
         return time.perf_counter() - t0, 2.0 * nrows * N * K
 
-    return Op("dsrelu_mxfp8", "dsrelu_kernel", synth.flops_dgrad(vm, N, K), "fp8", run, alg, sample)
+    return Op("dsrelu_mxfp8_fp8out" if fp8out else "dsrelu_mxfp8", "dsrelu_kernel",
+              synth.flops_dgrad(vm, N, K), "fp8", run, alg, sample)
 
 
-def make_dglu_mx(dev):
+def _fp8_outputs(M, W, dev):
+    """E4M3 D_row with the rest of the FP8 output (D_col, both scale arrays,
+    norm_const 1)."""
+    import torch
+    P = (M + 31) // 32
+    d = torch.empty(M, W, dtype=torch.float8_e4m3fn, device=dev)
+    q = dict(d_col=torch.empty(M, W, dtype=torch.uint8, device=dev),
+             sfd_row=torch.empty(M, W // 32, dtype=torch.uint8, device=dev),
+             sfd_col=torch.empty(W, P, dtype=torch.uint8, device=dev),
+             norm_const=torch.ones(1, dtype=torch.float32, device=dev))
+    return d, q
+
+
+def make_dglu_mx(dev, fp8out=False):
     import numpy as np
     import torch
     from moe_grouped_gemm_offset_amd import binding as B, synth
@@ -234,6 +257,9 @@ def make_dglu_mx(dev):
                                device=dev, discrete=w["discrete"])
     M, N, K, L = inp["M"], inp["N"], inp["K"], inp["L"]
     d = torch.empty(M, 2 * N, dtype=torch.bfloat16, device=dev)
+    q = None
+    if fp8out:
+        d, q = _fp8_outputs(M, 2 * N, dev)
     dprob = torch.zeros(M, dtype=torch.float32, device=dev)
     amax = torch.zeros(L, 2, dtype=torch.float32, device=dev)
     ws = torch.empty(B.gg_dglu_workspace_size(L, N, 0), dtype=torch.uint8, device=dev)
@@ -243,12 +269,14 @@ def make_dglu_mx(dev):
 
     def run():
         B.gg_dglu_mx(a8, inp["sfa"], None, None, bp, sp, N, inp["c"], inp["padded_offsets"],
-                     inp["alpha"], inp["beta"], inp["prob"], d, dprob, amax=amax, workspace=ws)
+                     inp["alpha"], inp["beta"], inp["prob"], d, dprob, amax=amax, fp8_out=q,
+                     workspace=ws)
 
     vm = inp["valid_m"]
-    # A, B and their scales once, C read and D written (bf16, 2N wide), prob
-    # read and dprob written
-    alg = M * K + L * N * K + (M + L * N) * K // 32 + 2 * (M * 2 * N * 2) + 8 * M
+    # A, B and their scales once, C read (bf16, 2N wide), D written (bf16;
+    # or E4M3 D_row and D_col with their scales), prob read, dprob written
+    d_bytes = M * 2 * N * 2 if not fp8out else 2 * M * 2 * N + 2 * M * 2 * N // 32
+    alg = M * K + L * N * K + (M + L * N) * K // 32 + M * 2 * N * 2 + d_bytes + 8 * M
 
     def sample(nrows):
         cpu = _cpu(inp)
@@ -260,7 +288,8 @@ def make_dglu_mx(dev):
                     cpu["alpha"].numpy(), cpu["beta"].numpy(), cpu["prob"].numpy(), rows=rows)
         return time.perf_counter() - t0, 2.0 * nrows * N * K
 
-    return Op("dglu_mxfp8", "dglu_mx_kernel", synth.flops_dgrad(vm, N, K), "fp8", run, alg, sample)
+    return Op("dglu_mxfp8_fp8out" if fp8out else "dglu_mxfp8", "dglu_mx_kernel",
+              synth.flops_dgrad(vm, N, K), "fp8", run, alg, sample)
 
 
 WORKLOAD_OPS = {
@@ -272,6 +301,8 @@ WORKLOAD_OPS = {
     "dsrelu_mxfp8": ["dsrelu_mxfp8"],
     "dglu_mxfp8": ["dglu_mxfp8"],
     "wgrad_mxfp8": ["wgrad_mxfp8"],
+    "dsrelu_mxfp8_fp8out": ["dsrelu_mxfp8_fp8out"],
+    "dglu_mxfp8_fp8out": ["dglu_mxfp8_fp8out"],
 }
 
 
@@ -288,6 +319,10 @@ def build_op(name, dev):
         return make_dglu_mx(dev)
     if name == "wgrad_mxfp8":
         return make_wgrad_mx(dev)
+    if name == "dglu_mxfp8_fp8out":
+        return make_dglu_mx(dev, fp8out=True)
+    if name == "dsrelu_mxfp8_fp8out":
+        return make_dsrelu(dev, fp8out=True)
     return make_dsrelu(dev)
 
 
@@ -405,7 +440,9 @@ def main():
             sys.exit("--summarize-pmc needs a single-op --workload")
         kernel = {"dswiglu": "dglu_kernel", "dgeglu": "dglu_kernel", "wgrad_moe": "wgrad_kernel",
                   "wgrad_moe_kmajor": "wgrad_kernel", "dsrelu_mxfp8": "dsrelu_kernel",
-                  "dglu_mxfp8": "dglu_mx_kernel", "wgrad_mxfp8": "wgrad_mx_kernel"}[names[0]]
+                  "dglu_mxfp8": "dglu_mx_kernel", "wgrad_mxfp8": "wgrad_mx_kernel",
+                  "dsrelu_mxfp8_fp8out": "dsrelu_kernel",
+                  "dglu_mxfp8_fp8out": "dglu_mx_kernel"}[names[0]]
         path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
         res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
                             {names[0]: (kernel, names[0])}, path)

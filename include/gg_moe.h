@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define GG_ABI_VERSION 1
+#define GG_ABI_VERSION 2
 
 typedef enum {
     GG_OK = 0,
@@ -114,6 +114,31 @@ enum {
      * flag leaves them as they are. */
     GG_FLAG_TENSOR_RAGGED = 8u
 };
+
+/*
+ * FP8 outputs of the block-scaled dgrad entries (gg_dglu_mx, gg_dsrelu) when
+ * d_dtype is GG_F8E4M3 ("Grouped GEMM + dGLU (SM100)", "Block-scaled
+ * contract / Equations", step 3; the dsReLU page's FP8 D_row / D_col with
+ * SFD_row / SFD_col).  W is the width of D (2n for dGLU, n for dsReLU).
+ * Blocks of 32 values -- 32 columns of a row for d_row, 32 rows of a column
+ * for d_col -- share one E8M0 scale SFD = 2^e, e the smallest integer with
+ *   2^e >= fp32(fp32(norm_const * max|D|) * fp32(1/448))
+ * (the page's norm_const * max|D| * rcp_max, rounded up to a power of two,
+ * which keeps every code within E4M3's 448; e in [-127, 127], -127 for an
+ * all-zero block), and each value is stored as E4M3(D * norm_const / 2^e),
+ * round to nearest even.  D here is the fp32 result before any rounding.
+ * A plain layout replaces the pages' MMA-interleaved scale tensors; the
+ * column scales of one group occupy its own row-block range of every column
+ * (groups are multiples of 256 rows, so no block straddles two).
+ */
+typedef struct {
+    void* d_col;               /* (m_rows, W) E4M3 column-quantized D, row-major, 16-B
+                                  aligned; or NULL for no column output             */
+    uint8_t* sfd_row;          /* (m_rows, W/32): row m, block b at m*(W/32) + b      */
+    uint8_t* sfd_col;          /* (W, P), P = ceil(m_rows/32): column c, rows 32j ..
+                                  32j+31 at c*P + j; NULL exactly when d_col is NULL */
+    const float* norm_const;   /* float[1], device memory                              */
+} gg_fp8_out;
 
 /* Bits of the device error word (see gg_device_error). */
 enum {
@@ -325,6 +350,10 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k,
  *              dprob   += R T_g T_u
  * amax       float[2L] ((L, 2) row-major), written by the call (the library
  *            clears it first), or NULL.
+ * d_dtype    as for gg_dglu, or GG_F8E4M3: d_row then holds the
+ *            row-quantized E4M3 D ((m_rows, 2n), 16-B aligned) and fp8_out
+ *            [host] the rest of the FP8 output (see gg_fp8_out); fp8_out is
+ *            ignored for the other dtypes.
  * flags      as for gg_dglu.
  * workspace  >= gg_dglu_workspace_size(L, n, dbias != NULL), 256-B aligned.
  */
@@ -335,7 +364,7 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
                      const int32_t* padded_offsets, int32_t L,
                      const float* alpha, const float* beta, const float* prob,
                      void* d_row, gg_dtype d_dtype, float* dprob, void* dbias, float* amax,
-                     gg_act act, float geglu_alpha, float clamp_min, float clamp_max,
+                     const gg_fp8_out* fp8_out, gg_act act, float geglu_alpha, float clamp_min, float clamp_max,
                      float linear_offset, float situ_beta1, float situ_beta2, uint32_t flags,
                      void* workspace, size_t workspace_bytes, void* stream);
 
@@ -371,7 +400,9 @@ size_t gg_dsrelu_workspace_size(int32_t L);
  * c          (m_rows, n) row-major, c_dtype GG_BF16, GG_F16 or GG_F32.
  * padded_offsets, L  as for gg_dglu.
  * alpha      float[L];  prob  float[m_rows].
- * d_row      (m_rows, n) row-major, d_dtype GG_BF16, GG_F16 or GG_F32.
+ * d_row      (m_rows, n) row-major, d_dtype GG_BF16, GG_F16 or GG_F32; or
+ *            GG_F8E4M3, the row-quantized D, with fp8_out [host] giving the
+ *            rest of the FP8 output (see gg_fp8_out; ignored otherwise).
  * dprob      float[m_rows], caller-zeroed, accumulated into.
  * amax       float[L], written by the call (the library clears it first), or
  *            NULL.
@@ -385,7 +416,8 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
                     const int32_t* padded_offsets, int32_t L,
                     const float* alpha, const float* prob,
                     void* d_row, gg_dtype d_dtype, float* dprob, float* amax,
-                    uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
+                    const gg_fp8_out* fp8_out, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -74,10 +74,10 @@ def load_library(path=LIB_PATH):
                           I32, F, F, F, F, U32, P, SZ, P]
     L.gg_dglu_mx.restype = ctypes.c_int
     L.gg_dglu_mx.argtypes = [P, P, I64, I32, P, P, P, P, I32, P, I32, P, I32, P, P, P, P, I32, P,
-                             P, P, I32, F, F, F, F, F, F, U32, P, SZ, P]
+                             P, P, P, I32, F, F, F, F, F, F, U32, P, SZ, P]
     L.gg_dsrelu.restype = ctypes.c_int
     L.gg_dsrelu.argtypes = [P, P, I64, I32, P, P, P, P, I32, P, I32, P, I32, P, P, P, I32, P, P,
-                            U32, P, SZ, P]
+                            P, U32, P, SZ, P]
     _lib = L
     return L
 
@@ -96,6 +96,25 @@ def _stream(stream):
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+class Fp8Out(ctypes.Structure):
+    """gg_fp8_out of gg_moe.h (device pointers)."""
+    _fields_ = [("d_col", ctypes.c_void_p), ("sfd_row", ctypes.c_void_p),
+                ("sfd_col", ctypes.c_void_p), ("norm_const", ctypes.c_void_p)]
+
+
+def _fp8_out(f):
+    """A dict of tensors (sfd_row, norm_const and optionally d_col, sfd_col)
+    as a gg_fp8_out, or None."""
+    if f is None:
+        return None
+    return Fp8Out(_ptr(f.get("d_col")), _ptr(f.get("sfd_row")), _ptr(f.get("sfd_col")),
+                  _ptr(f.get("norm_const")))
+
+
+def _ref(s):
+    return None if s is None else ctypes.addressof(s)
 
 
 def _check(status):
@@ -185,11 +204,14 @@ def gg_dglu(a, b_dense, b_ptrs, b_major, n, c, padded_offsets, alpha, beta, prob
 
 
 def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, beta, prob, d_row,
-               dprob, dbias=None, amax=None, act=GG_DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0,
+               dprob, dbias=None, amax=None, fp8_out=None, act=GG_DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0,
                clamp_max=7.0, linear_offset=1.0, situ_beta1=4.0, situ_beta2=25.0, flags=0,
                workspace=None, stream=None):
     """Grouped MXFP8 dgrad + dSwiGLU/dGeGLU (gg_dglu_mx of gg_moe.h): a is an
-    (m_rows, k) uint8 tensor of E4M3 codes.  Returns the workspace used."""
+    (m_rows, k) uint8 tensor of E4M3 codes.  With a uint8 d_row (E4M3 codes)
+    fp8_out is a dict of the other FP8 outputs (sfd_row, norm_const and
+    optionally d_col, sfd_col).  Returns the workspace used."""
+    q = _fp8_out(fp8_out)
     L = load_library()
     nl = padded_offsets.numel()
     ws, nbytes = _workspace(workspace, L.gg_dglu_workspace_size(nl, n, dbias is not None), a)
@@ -197,21 +219,22 @@ def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, be
                         _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
                         _ptr(padded_offsets), nl, _ptr(alpha), _ptr(beta), _ptr(prob),
                         _ptr(d_row), _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(dbias),
-                        _ptr(amax), act, geglu_alpha, clamp_min, clamp_max, linear_offset,
+                        _ptr(amax), _ref(q), act, geglu_alpha, clamp_min, clamp_max, linear_offset,
                         situ_beta1, situ_beta2, flags, _ptr(ws), nbytes, _stream(stream)))
     return ws
 
 
 def gg_dsrelu(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, prob, d_row, dprob,
-              amax=None, flags=0, workspace=None, stream=None):
-    """Grouped MXFP8 dgrad + dsReLU (gg_dsrelu of gg_moe.h).  Returns the
-    workspace used."""
+              amax=None, fp8_out=None, flags=0, workspace=None, stream=None):
+    """Grouped MXFP8 dgrad + dsReLU (gg_dsrelu of gg_moe.h); fp8_out as for
+    gg_dglu_mx.  Returns the workspace used."""
+    q = _fp8_out(fp8_out)
     L = load_library()
     nl = padded_offsets.numel()
     ws, nbytes = _workspace(workspace, L.gg_dsrelu_workspace_size(nl), a)
     _check(L.gg_dsrelu(_ptr(a), _ptr(sfa), a.shape[0], a.shape[1], _ptr(b), _ptr(sfb),
                        _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
                        _ptr(padded_offsets), nl, _ptr(alpha), _ptr(prob), _ptr(d_row),
-                       _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(amax), flags, _ptr(ws),
+                       _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(amax), _ref(q), flags, _ptr(ws),
                        nbytes, _stream(stream)))
     return ws

@@ -271,8 +271,10 @@ static gg_status check_dglu_common(gg_dtype c_dtype, gg_dtype d_dtype, gg_act ac
                                    uint32_t flags, const char* name) {
     if (!alpha || !beta)
         return fail(GG_ERR_NULL, "alpha and beta must be non-NULL");
-    if (!is_out_dtype(c_dtype) || !is_out_dtype(d_dtype))
-        return fail(GG_ERR_DTYPE, "c_dtype and d_dtype must be GG_BF16, GG_F16 or GG_F32");
+    if (!is_out_dtype(c_dtype) || !(is_out_dtype(d_dtype) || (mx && d_dtype == GG_F8E4M3)))
+        return fail(GG_ERR_DTYPE, mx ? "c_dtype must be GG_BF16, GG_F16 or GG_F32, d_dtype one of "
+                                       "those or GG_F8E4M3"
+                                     : "c_dtype and d_dtype must be GG_BF16, GG_F16 or GG_F32");
     if (act == GG_DSITUGLU && !mx)
         return fail(GG_ERR_MODE, "GG_DSITUGLU is defined for the block-scaled gg_dglu_mx only");
     if (act != GG_DSWIGLU && act != GG_DGEGLU && act != GG_DSITUGLU)
@@ -345,6 +347,26 @@ static gg_status run_dglu(gg::DgluArgs& p, bool mx, const void* c, gg_dtype c_dt
     return ok();
 }
 
+// FP8 outputs (d_dtype GG_F8E4M3 of the block-scaled dgrad entries): checks
+// them and fills q; width is W, the columns of D.
+static gg_status check_fp8_out(const gg_fp8_out* f, const void* d_row, int64_t m_rows, int64_t width,
+                               gg::Fp8Out& q) {
+    if (!f || !f->sfd_row || !f->norm_const)
+        return fail(GG_ERR_NULL, "GG_F8E4M3 output needs fp8_out with sfd_row and norm_const");
+    if ((f->d_col != nullptr) != (f->sfd_col != nullptr))
+        return fail(GG_ERR_MODE, "give both of fp8_out->d_col and fp8_out->sfd_col, or neither");
+    if (!aligned16(f->d_col) || ((uintptr_t)f->norm_const & 3u))
+        return fail(GG_ERR_ALIGN, "fp8_out->d_col must be 16-byte aligned, norm_const 4-byte");
+    q.d_row = (uint8_t*)d_row;
+    q.d_col = (uint8_t*)f->d_col;
+    q.sfd_row = f->sfd_row;
+    q.sfd_col = f->sfd_col;
+    q.norm_const = f->norm_const;
+    q.W = width;
+    q.pitch = (m_rows + 31) / 32;
+    return GG_OK;
+}
+
 gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k, const void* b_dense,
                   const int64_t* b_ptrs, gg_major b_major, int32_t n, const void* c,
                   gg_dtype c_dtype, const int32_t* padded_offsets, int32_t L, const float* alpha,
@@ -394,8 +416,9 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
                      const int64_t* sfb_ptrs, int32_t n, const void* c, gg_dtype c_dtype,
                      const int32_t* padded_offsets, int32_t L, const float* alpha,
                      const float* beta, const float* prob, void* d_row, gg_dtype d_dtype,
-                     float* dprob, void* dbias, float* amax, gg_act act, float geglu_alpha,
-                     float clamp_min, float clamp_max, float linear_offset, float situ_beta1,
+                     float* dprob, void* dbias, float* amax, const gg_fp8_out* fp8_out, gg_act act,
+                     float geglu_alpha, float clamp_min, float clamp_max, float linear_offset,
+                     float situ_beta1,
                      float situ_beta2, uint32_t flags, void* workspace, size_t workspace_bytes,
                      void* stream) {
     gg_status st = check_rows(padded_offsets, L, m_rows, c, prob, d_row, dprob, workspace);
@@ -425,6 +448,11 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
         ((uintptr_t)sfa & 3u) || ((uintptr_t)sfb & 3u) || ((uintptr_t)amax & 3u))
         return fail(GG_ERR_ALIGN, "operands must be 16-byte aligned, scales and amax 4-byte aligned");
     gg::DgluArgs p = {};
+    if (d_dtype == GG_F8E4M3) {
+        st = check_fp8_out(fp8_out, d_row, m_rows, 2 * (int64_t)n, p.q);
+        if (st != GG_OK)
+            return st;
+    }
     p.a = a_fp8;
     p.sfa = sfa;
     p.b_dense = b_fp8;
@@ -446,7 +474,8 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
                     const int64_t* sfb_ptrs, int32_t n, const void* c, gg_dtype c_dtype,
                     const int32_t* padded_offsets, int32_t L, const float* alpha,
                     const float* prob, void* d_row, gg_dtype d_dtype, float* dprob, float* amax,
-                    uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+                    const gg_fp8_out* fp8_out, uint32_t flags, void* workspace,
+                    size_t workspace_bytes, void* stream) {
     gg_status st = check_rows(padded_offsets, L, m_rows, c, prob, d_row, dprob, workspace);
     if (st != GG_OK)
         return st;
@@ -456,8 +485,9 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
     const bool discrete = b_ptrs || sfb_ptrs;
     if (dense == discrete || (dense && (!b_fp8 || !sfb)) || (discrete && (!b_ptrs || !sfb_ptrs)))
         return fail(GG_ERR_MODE, "give exactly one of (b_fp8, sfb) and (b_ptrs, sfb_ptrs)");
-    if (!is_out_dtype(c_dtype) || !is_out_dtype(d_dtype))
-        return fail(GG_ERR_DTYPE, "c_dtype and d_dtype must be GG_BF16, GG_F16 or GG_F32");
+    if (!is_out_dtype(c_dtype) || !(is_out_dtype(d_dtype) || d_dtype == GG_F8E4M3))
+        return fail(GG_ERR_DTYPE, "c_dtype must be GG_BF16, GG_F16 or GG_F32, d_dtype one of those "
+                                  "or GG_F8E4M3");
     if (n <= 0 || n % 32)
         return fail(GG_ERR_SHAPE, "n must be a positive multiple of 32 (got %d)", n);
     if (k <= 0)
@@ -475,6 +505,12 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
     size_t need = gg_dsrelu_workspace_size(L);
     if (workspace_bytes < need)
         return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    gg::DsreluArgs p = {};
+    if (d_dtype == GG_F8E4M3) {
+        st = check_fp8_out(fp8_out, d_row, m_rows, n, p.q);
+        if (st != GG_OK)
+            return st;
+    }
     st = check_device();
     if (st != GG_OK)
         return st;
@@ -489,7 +525,6 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
                                        amax ? L : 0, nullptr, 0, s);
     if (e != hipSuccess)
         return hip_fail(e, "launching the dsrelu prologue");
-    gg::DsreluArgs p;
     p.a = (const uint8_t*)a_fp8;
     p.sfa = sfa;
     p.b_dense = (const uint8_t*)b_fp8;

@@ -19,6 +19,7 @@
 // raised with one atomicMax per half on the fp32 bit pattern (which orders
 // like the value because |D| >= 0).
 #pragma once
+#include "gg_fp8out.hpp"
 #include "gg_internal.hpp"
 #include "gg_tile.hpp"
 
@@ -40,10 +41,11 @@ __device__ __forceinline__ float scaled_x(float beta, float c) {
 // (the block-scaled contract's "Equations": T_g = b1 tanh(G/b1) sigmoid(G),
 // T_u = b2 tanh(U/b2), gradients R prob T_u dT_g/dG and R prob T_g dT_u/dU,
 // activation T_g T_u); AMAX: raise
-// p.amax[2 g + {0: input, 1: gate}]; kAhead: row-walk items whose C loads are
-// in flight while one is processed.  The caller has passed the barrier that
-// ends the main loop's use of smem.
-template <class C, bool W32, int ACT, bool AMAX, int kAhead>
+// p.amax[2 g + {0: input, 1: gate}]; Q: D as FP8 (E4M3) D_row / D_col with
+// E8M0 scales (gg_fp8out.hpp) instead of a 16/32-bit D; kAhead: row-walk
+// items whose C loads are in flight while one is processed.  The caller has
+// passed the barrier that ends the main loop's use of smem.
+template <class C, bool W32, int ACT, bool AMAX, int kAhead, bool Q = false>
 __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&acc)[C::MB][C::NB],
                                               char* smem, int64_t m0, int n0, int g,
                                               int rows_valid, int am0, int bn0) {
@@ -67,6 +69,8 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
     // flight while an item is processed; items off the tile load row 0 /
     // column 0 (always present) and store nothing.
     float* const elds = (float*)(smem + w * kEpiWaveBytes);
+    const float nc = Q ? *p.q.norm_const : 1.0f;
+    float dcol_in[4][8], dcol_gt[4][8];            // Q: a column block's 4 items
     using Pre = Pre8<W32, 2>;
     auto cols = [&](int c, int64_t& c_in, int64_t& c_gt) {
         const int n = n0 + bn0 + c;                 // first compact column
@@ -90,9 +94,16 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
         const int n = n0 + bn0 + c;
         int64_t c_in, c_gt;
         cols(c, c_in, c_gt);
+        const bool ok = (rr < rows_valid) & (n < p.N);
+        float din[8], dgt[8];
+        if constexpr (Q) {
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                din[k] = dgt[k] = 0.0f;
+        }
         if (rr < rows_valid && n < p.N) {
             const int64_t row = m0 + rr;
-            float xin[8], xgt[8], din[8], dgt[8];
+            float xin[8], xgt[8];
             raw8_cvt<W32>(pre.x[0], p.c_dtype, xin);
             raw8_cvt<W32>(pre.x[1], p.c_dtype, xgt);
             const float pr = pre.row;
@@ -137,8 +148,33 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
                     amax_gt = fmaxf(amax_gt, fabsf(dgt[k]));
                 }
             }
-            store8(p.d, p.d_dtype, row * N2 + c_in, din);
-            store8(p.d, p.d_dtype, row * N2 + c_gt, dgt);
+            if constexpr (!Q) {
+                store8(p.d, p.d_dtype, row * N2 + c_in, din);
+                store8(p.d, p.d_dtype, row * N2 + c_gt, dgt);
+            }
+        }
+        if constexpr (Q) {
+            // every lane takes part in the block reductions; lanes off the
+            // tile hold zeros and store nothing
+            int ein, egt;
+            const uint2 qin = fp8_row8(din, nc, ein);
+            const uint2 qgt = fp8_row8(dgt, nc, egt);
+            if (ok) {
+                fp8_store_row(p.q, m0 + rr, c_in, qin, ein);
+                fp8_store_row(p.q, m0 + rr, c_gt, qgt, egt);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                dcol_in[t & 3][k] = din[k];
+                dcol_gt[t & 3][k] = dgt[k];
+            }
+            if ((t & 3) == 3 && p.q.d_col) {
+                const int r0 = r - 24;                 // this lane's row of item t-3
+                const int64_t rb0 = m0 + am0 + (r0 & ~31), row0 = m0 + am0 + r0;
+                const int left = rows_valid - (am0 + r0);
+                fp8_col_block(p.q, nc, dcol_in, rb0, row0, c_in, n < p.N, left);
+                fp8_col_block(p.q, nc, dcol_gt, rb0, row0, c_gt, n < p.N, left);
+            }
         }
         if (t == kT - 1 && dbias_ws) {
             // column sums over the wave's rows: lanes sharing l & 7 hold

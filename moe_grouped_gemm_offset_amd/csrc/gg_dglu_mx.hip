@@ -23,8 +23,9 @@ namespace gg {
 
 using DgluMxCfg = Cfg<256, 256, 2, 2>;
 
-// W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU, 2 dSiTU-GLU.
-template <class C, bool W32, int ACT>
+// W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU, 2 dSiTU-GLU;
+// Q: FP8 D_row / D_col with E8M0 scales.
+template <class C, bool W32, int ACT, bool Q>
 __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
     __shared__ __attribute__((aligned(1024))) char smem[ScaleLds<C>::kSmem];
@@ -68,7 +69,8 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
     mx_mainloop<C>(smem, a, sfa, bg, sfb, K, K, rows_valid, cols_valid, am0, bn0, acc);
 
     // C of the items 12 ahead (6 for fp32 C) in flight in the epilogue
-    dglu_epilogue<C, W32, ACT, true, W32 ? 6 : 12>(p, acc, smem, m0, n0, g, rows_valid, am0, bn0);
+    dglu_epilogue<C, W32, ACT, true, Q ? (W32 ? 4 : 8) : (W32 ? 6 : 12), Q>(p, acc, smem, m0, n0, g,
+                                                                          rows_valid, am0, bn0);
 }
 
 hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s) {
@@ -77,19 +79,20 @@ hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s) {
     if (tiles == 0)
         return hipSuccess;
     const dim3 grid((unsigned)tiles), block(C::kThreads);
-    auto go = [&](auto W32) {
-        constexpr bool w32 = decltype(W32)::value;
+    auto go = [&](auto W32, auto Q) {
+        constexpr bool w32 = decltype(W32)::value, q = decltype(Q)::value;
         if (p.act == 0)
-            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 0>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 0, q>), grid, block, 0, s, p);
         else if (p.act == 1)
-            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 1>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 1, q>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 2>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 2, q>), grid, block, 0, s, p);
     };
-    if (p.c_dtype == kF32)
-        go(std::true_type());
+    const bool w32 = p.c_dtype == kF32;
+    if (p.d_dtype == kF8)
+        w32 ? go(std::true_type(), std::true_type()) : go(std::false_type(), std::true_type());
     else
-        go(std::false_type());
+        w32 ? go(std::true_type(), std::false_type()) : go(std::false_type(), std::false_type());
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@
 // row and wave) and Amax across the wave (one atomicMax on the fp32 bit
 // pattern, which orders like the value because |D| >= 0).
 #include "gg_internal.hpp"
+#include "gg_fp8out.hpp"
 #include "gg_mx.hpp"
 #include "gg_moe.h"
 
@@ -22,7 +23,8 @@ namespace gg {
 
 using DsreluCfg = Cfg<256, 256, 2, 2>;
 
-template <class C>
+// Q: FP8 (E4M3) D_row / D_col with E8M0 scales (else a 16/32-bit D_row).
+template <class C, bool Q>
 __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
     __shared__ __attribute__((aligned(1024))) char smem[ScaleLds<C>::kSmem];
@@ -79,6 +81,8 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     for (int t = 0; t < kT; t++)
         rowsum[t] = 0.0f;
     float* const elds = (float*)(smem + w * kEpiWaveBytes);
+    const float nc = Q ? *p.q.norm_const : 1.0f;
+    float dcol[4][8];                              // Q: a column block's 4 items
     auto epilogue = [&](auto W32) {
         constexpr bool w32 = decltype(W32)::value;
         using Pre = Pre8<w32, 1>;
@@ -94,7 +98,36 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
         auto fn = [&](int t, int r, int c, float (&v)[8], const Pre& pre) {
             const int rr = am0 + r;
             const int col = n0 + bn0 + c;
-            if (rr < rows_valid && col < p.N) {
+            if constexpr (Q) {
+                // every lane computes (the block reductions shuffle across
+                // lanes); lanes off the tile contribute zeros
+                const bool ok = (rr < rows_valid) & (col < p.N);
+                float d[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+                if (ok) {
+                    float cv[8];
+                    raw8_cvt<w32>(pre.x[0], p.c_dtype, cv);
+                    const float pr2 = pre.row * 2.0f;
+#pragma unroll
+                    for (int k = 0; k < 8; k++) {
+                        const float rl = fmaxf(al * v[k], 0.0f);
+                        d[k] = pr2 * cv[k] * rl;
+                        rowsum[t] += cv[k] * rl * rl;
+                        amax = fmaxf(amax, fabsf(d[k]));
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 8; k++)
+                    dcol[t & 3][k] = d[k];
+                int e;
+                const uint2 codes = fp8_row8(d, nc, e);
+                if (ok)
+                    fp8_store_row(p.q, m0 + rr, col, codes, e);
+                if ((t & 3) == 3 && p.q.d_col) {
+                    const int r0 = r - 24;             // this lane's row of item t-3
+                    fp8_col_block(p.q, nc, dcol, m0 + am0 + (r0 & ~31), m0 + am0 + r0, col,
+                                  col < p.N, rows_valid - (am0 + r0));
+                }
+            } else if (rr < rows_valid && col < p.N) {
                 const int64_t row = m0 + rr;
                 float cv[8], d[8];
                 raw8_cvt<w32>(pre.x[0], p.c_dtype, cv);
@@ -109,7 +142,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                 store8(p.d, p.d_dtype, row * N + col, d);
             }
         };
-        for_each_row8<C, w32 ? 12 : 24>(acc, elds, load, fn);
+        for_each_row8<C, Q ? (w32 ? 6 : 12) : (w32 ? 12 : 24)>(acc, elds, load, fn);
     };
     if (p.c_dtype == kF32)
         epilogue(std::true_type());
@@ -139,7 +172,10 @@ hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s) {
     const int64_t tiles = ((p.m_rows + C::TM - 1) / C::TM) * ((p.N + C::TN - 1) / C::TN);
     if (tiles == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((dsrelu_kernel<C>), dim3((unsigned)tiles), dim3(C::kThreads), 0, s, p);
+    if (p.d_dtype == kF8)
+        hipLaunchKernelGGL((dsrelu_kernel<C, true>), dim3((unsigned)tiles), dim3(C::kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((dsrelu_kernel<C, false>), dim3((unsigned)tiles), dim3(C::kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -10,6 +10,16 @@ namespace gg {
 // device error word, followed by the op's own region.
 constexpr size_t kWsHeader = 256;
 
+// FP8 outputs of the block-scaled dgrad epilogues (d_dtype E4M3).
+struct Fp8Out {
+    uint8_t* d_row;           // (rows, W) codes
+    uint8_t* d_col;           // (rows, W) codes, or null
+    uint8_t* sfd_row;         // (rows, W/32)
+    uint8_t* sfd_col;         // (W, pitch): column c, row block j at c * pitch + j
+    const float* norm_const;  // [1]
+    int64_t W, pitch;
+};
+
 struct WgradArgs {
     const void* a;            // bf16, or E4M3 codes (block-scaled)
     const void* b;
@@ -51,6 +61,7 @@ struct DgluArgs {
     int gate_first, mask_filter;
     float geglu_alpha, clamp_min, clamp_max, linear_offset;
     float situ_b1, situ_b2;   // dSiTU-GLU tanh scales
+    Fp8Out q;                 // block-scaled only, with d_dtype E4M3
 };
 
 struct DsreluArgs {
@@ -71,6 +82,7 @@ struct DsreluArgs {
     int64_t m_rows;
     int K, N, L;
     int c_dtype, d_dtype;
+    Fp8Out q;                 // with d_dtype E4M3
 };
 
 // Launchers (return the HIP status of the launch).

@@ -447,7 +447,7 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 }
 
 // dtype codes (the gg_dtype values of the ABI)
-constexpr int kBF16 = 0, kF16 = 1, kF32 = 2;
+constexpr int kBF16 = 0, kF16 = 1, kF32 = 2, kF8 = 3;   // gg_dtype codes
 
 __device__ __forceinline__ float load_elem(const void* base, int dtype, int64_t i) {
     if (dtype == kBF16)

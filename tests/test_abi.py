@@ -32,7 +32,7 @@ def test_loads_and_exports_every_declared_symbol():
     assert set(names) == set(B.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert B.gg_abi_version() == 1
+    assert B.gg_abi_version() == 2
 
 
 def test_workspace_sizes():
@@ -115,13 +115,13 @@ def test_dglu_rejects(kw, status):
 
 def dsrelu(**kw):
     args = dict(a=P, sfa=P, M=1024, k=512, b=P, sfb=P, bp=None, sp=None, n=256, c=P, cdt=0, po=P,
-                L=4, alpha=P, prob=P, d=P, ddt=0, dprob=P, amax=P, flags=0, ws=WS, wsb=256)
+                L=4, alpha=P, prob=P, d=P, ddt=0, dprob=P, amax=P, fp8=None, flags=0, ws=WS, wsb=256)
     args.update(kw)
     lib = B.load_library()
     return lib.gg_dsrelu(args["a"], args["sfa"], args["M"], args["k"], args["b"], args["sfb"],
                          args["bp"], args["sp"], args["n"], args["c"], args["cdt"], args["po"],
                          args["L"], args["alpha"], args["prob"], args["d"], args["ddt"], args["dprob"],
-                         args["amax"], args["flags"], args["ws"], args["wsb"], None)
+                         args["amax"], args["fp8"], args["flags"], args["ws"], args["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -131,7 +131,7 @@ def dsrelu(**kw):
     (dict(sfb=None), MODE),
     (dict(k=192), UNSUPPORTED),
     (dict(n=40), SHAPE),
-    (dict(ddt=3), DTYPE),
+    (dict(ddt=4), DTYPE),
     (dict(sfa=P + 1), ALIGN),
     (dict(wsb=16), WORKSPACE),
 ])
@@ -139,16 +139,47 @@ def test_dsrelu_rejects(kw, status):
     assert dsrelu(**kw) == status
 
 
+def fp8_out(**kw):
+    f = dict(d_col=P, sfd_row=P, sfd_col=P, norm_const=P)
+    f.update(kw)
+    return B.Fp8Out(f["d_col"], f["sfd_row"], f["sfd_col"], f["norm_const"])
+
+
+@pytest.mark.parametrize("entry", ["dsrelu", "dglu_mx"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(), None),
+    (dict(d_col=None), MODE),
+    (dict(sfd_col=None), MODE),
+    (dict(d_col=None, sfd_col=None), None),
+    (dict(sfd_row=None), NULL),
+    (dict(norm_const=None), NULL),
+    (dict(d_col=P + 8), ALIGN),
+    (dict(norm_const=P + 2), ALIGN),
+])
+def test_fp8_out_checks(entry, kw, status):
+    """GG_F8E4M3 outputs: fp8_out is required and checked; valid ones reach
+    the device check (GG_ERR_DEVICE here, where there is no GPU)."""
+    f = fp8_out(**kw)                  # kept alive across the calls below
+    call = dsrelu if entry == "dsrelu" else dglu_mx
+    got = call(ddt=3, fp8=ctypes.addressof(f))
+    want = status if status is not None else (DEVICE if not torch.cuda.is_available() else OK)
+    if status is None and torch.cuda.is_available():
+        pytest.skip("checks the no-device path")
+    assert got == want
+    assert call(ddt=3, fp8=None) == NULL
+    assert call(ddt=4, fp8=ctypes.addressof(f)) == DTYPE
+
+
 def dglu_mx(**kw):
     args = dict(a=P, sfa=P, M=1024, k=512, b=P, sfb=P, bp=None, sp=None, n=256, c=P, cdt=0, po=P,
-                L=4, alpha=P, beta=P, prob=P, d=P, ddt=0, dprob=P, dbias=None, amax=P, act=0,
+                L=4, alpha=P, beta=P, prob=P, d=P, ddt=0, dprob=P, dbias=None, amax=P, fp8=None, act=0,
                 flags=0, ws=WS, wsb=1 << 20, b1=4.0, b2=25.0)
     args.update(kw)
     lib = B.load_library()
     return lib.gg_dglu_mx(args["a"], args["sfa"], args["M"], args["k"], args["b"], args["sfb"],
                           args["bp"], args["sp"], args["n"], args["c"], args["cdt"], args["po"],
                           args["L"], args["alpha"], args["beta"], args["prob"], args["d"],
-                          args["ddt"], args["dprob"], args["dbias"], args["amax"], args["act"],
+                          args["ddt"], args["dprob"], args["dbias"], args["amax"], args["fp8"], args["act"],
                           1.702, -7.0, 7.0, 1.0, args["b1"], args["b2"], args["flags"], args["ws"],
                           args["wsb"], None)
 
