@@ -194,6 +194,22 @@ static gg_status run_wgrad(gg::WgradArgs& p, bool mx, const int32_t* offsets, in
     p.inter = intermediate;
     p.E = num_experts;
     p.ragged = (flags & GG_FLAG_TENSOR_RAGGED) != 0;
+    // XCD blocks of an expert's tiles: the gm x (8/gm) grid that reads the
+    // fewest operand panels (an A panel per M tile by 8/gm XCDs, a B panel
+    // per N tile by gm), among those that divide the tile grid
+    {
+        const int tm = (hidden + 255) / 256, tn = (intermediate + 255) / 256;
+        int best = 0, best_cost = 0;
+        for (int gm = 1; gm <= 8; gm *= 2) {
+            const int gn = 8 / gm;
+            if (tm % gm || tn % gn)
+                continue;
+            const int cost = tm * gn + tn * gm;
+            if (best == 0 || cost < best_cost)
+                best = gm, best_cost = cost;
+        }
+        p.xcd_gm = best;
+    }
     p.out_dtype = (int)wgrad_dtype;
     p.accumulate = accumulate ? 1 : 0;
     e = mx ? gg::launch_wgrad_mx(p, s) : gg::launch_wgrad(p, s);

@@ -19,6 +19,7 @@
 namespace gg {
 
 using DgluCfg = Cfg<256, 256, 4, 2>;
+constexpr bool kDgluSlots5 = true;      // the five-slot pipeline of gg_tile.hpp
 
 // W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU.  Each
 // combination is its own kernel so the register allocation of one epilogue
@@ -26,7 +27,7 @@ using DgluCfg = Cfg<256, 256, 4, 2>;
 template <class C, bool B_K, bool W32, int ACT>
 __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
-    __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
+    __shared__ __attribute__((aligned(1024))) char smem[kDgluSlots5 ? Slots5<C>::kLds : C::kLds];
 
     const int tiles_n = (p.N + TN - 1) / TN;
     const int tiles_m = (int)((p.m_rows + TM - 1) / TM);
@@ -69,25 +70,31 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
         lb.init((int64_t)p.N * 2, p.N - n0);
     using LB = std::conditional_t<B_K, LoadK<C, TN>, LoadMN<C>>;
     constexpr int kLA = LoadK<C, TM>::kN;
-    auto issue = [&](uint32_t st, int u, int i) {
+    auto issue2 = [&](uint32_t sa, uint32_t sb, int u, int i) {
         const int64_t kb = (int64_t)u * 128;
         if (i < kLA) {
-            la.template issue<false>(st, a + kb, lda - kb, i);
+            la.template issue<false>(sa, a + kb, lda - kb, i);
         } else {
             if constexpr (B_K)
-                lb.template issue<false>(st + TM * kRowBytes, bg + (int64_t)n0 * lda + kb, lda - kb,
-                                         i - kLA);
+                lb.template issue<false>(sb, bg + (int64_t)n0 * lda + kb, lda - kb, i - kLA);
             else
-                lb.issue(st + TM * kRowBytes, bg + ((int64_t)u * 64 * p.N + n0) * 2,
-                         (int64_t)p.K - u * 64, i - kLA);
+                lb.issue(sb, bg + ((int64_t)u * 64 * p.N + n0) * 2, (int64_t)p.K - u * 64, i - kLA);
         }
     };
-    auto read = [&](const char* st, int kt, FragBf16<C>& f, int g) {
-        read_bf16<C, true, B_K>(st, st + TM * kRowBytes, am0, bn0, kt & 1, f, g);
+    auto read2 = [&](const char* sa, const char* sb, int kt, FragBf16<C>& f, int g) {
+        read_bf16<C, true, B_K>(sa, sb, am0, bn0, kt & 1, f, g);
     };
     auto mma = [&](const FragBf16<C>& f, int m0_, int m1_) { mma_bf16<C>(f, acc, m0_, m1_); };
     FragBf16<C> frag[2];
-    pipeline<C, kLA + LB::kN, 2 * MB * NB, MB + NB>(smem, p.K / 32, frag, issue, read, mma);
+    if constexpr (kDgluSlots5) {
+        pipeline5<C, kLA, kLA + LB::kN, 2 * MB * NB, MB + NB>(smem, p.K / 32, frag, issue2, read2, mma);
+    } else {
+        auto issue = [&](uint32_t st, int u, int i) { issue2(st, st + TM * kRowBytes, u, i); };
+        auto read = [&](const char* st, int kt, FragBf16<C>& f, int g) {
+            read2(st, st + TM * kRowBytes, kt, f, g);
+        };
+        pipeline<C, kLA + LB::kN, 2 * MB * NB, MB + NB>(smem, p.K / 32, frag, issue, read, mma);
+    }
 
     // C of the items 12 ahead (6 for fp32 C) in flight in the epilogue
     dglu_epilogue<C, W32, ACT, false, W32 ? 6 : 12>(p, acc, smem, m0, n0, g, rows_valid, am0, bn0);

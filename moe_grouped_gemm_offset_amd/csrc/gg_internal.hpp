@@ -33,6 +33,7 @@ struct WgradArgs {
     int hidden, inter, E;
     int a_kmajor, b_kmajor;
     int ragged;               // K-major operands stored tensor_ragged
+    int xcd_gm;               // XCD block grid rows for xcd_remap2d (0: 1-D remap)
     int out_dtype, accumulate;
 };
 

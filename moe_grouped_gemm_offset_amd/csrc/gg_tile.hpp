@@ -414,6 +414,120 @@ __device__ __forceinline__ void pipeline(char* smem, int nk, F (&f)[2], Issue is
 }
 
 // ---------------------------------------------------------------------------
+// Five-slot variant for tiles with TM == TN (bf16: 5 x 32 KiB = 160 KiB of
+// LDS).  Each operand half of a unit (its A rows or its B rows) occupies one
+// of five slots, so besides units u and u+1 one slot is always spare.  Unit
+// u+2's A half is loaded into the spare slot during the even half of
+// iteration u -- no barrier is needed, the slot's last reader passed the
+// barrier of iteration u-1 -- and its B half into unit u's A slot during
+// the odd half, after the barrier; unit u's B slot becomes the next spare.
+// The load path thus works through both halves of every iteration instead
+// of the odd half alone, and the A half gets one and a half iterations to
+// land.  The wait before each barrier leaves the A half just issued in
+// flight.
+//   issue(lds_a, lds_b, u, i)  queues load i of unit u: i < VMA are A loads
+//                              (into lds_a), VMA <= i < VM B loads (lds_b);
+//   read(buf_a, buf_b, kt, f, g), mma(f, m0, m1) as for pipeline.
+// ---------------------------------------------------------------------------
+template <class C>
+struct Slots5 {
+    static constexpr int kSlot = C::TM * kRowBytes;
+    static constexpr int kLds = 5 * kSlot > C::kWaves * kEpiWaveBytes ? 5 * kSlot
+                                                                     : C::kWaves * kEpiWaveBytes;
+    static_assert(C::TM == C::TN, "five equal slots");
+};
+
+template <class C, int VMA, int VM, int kMfma, int kGroups, class F, class Issue, class Read,
+          class Mma>
+__device__ __forceinline__ void pipeline5(char* smem, int nk, F (&f)[2], Issue issue, Read read,
+                                          Mma mma) {
+    static_assert(kGroups <= kMfma && VMA <= VM, "one fragment group per MFMA at most");
+    constexpr int kSlot = Slots5<C>::kSlot;
+    if (nk <= 0)
+        return;
+    const int nu = (nk + 1) >> 1;                        // load units
+    const uint32_t lds0 = lds_addr(smem);
+    auto sl = [&](int k) { return lds0 + (uint32_t)(k * kSlot); };
+    auto sb = [&](int k) { return smem + k * kSlot; };
+    // slots of unit u (a, b) and u+1 (a1, b1), and the spare one
+    int a = 0, b = 1, a1 = 2, b1 = 3, sp = 4;
+#pragma unroll
+    for (int i = 0; i < VM; i++)
+        issue(sl(0), sl(1), 0, i);
+#pragma unroll
+    for (int i = 0; i < VM; i++)
+        issue(sl(2), sl(3), 1, i);
+    vm_wait<VM>();                                       // all of unit 0
+    unit_barrier();
+#pragma unroll
+    for (int g = 0; g < kGroups; g++)
+        read(sb(0), sb(1), 0, f[0], g);
+    int u = 0;
+    for (; u + 1 < nu; u++) {
+        // stage 2u, reading stage 2u+1 of unit u; unit u+2's A half into
+        // the spare slot
+        const uint32_t la = sl(sp);
+        const char* ra = sb(a);
+        const char* rb = sb(b);
+#pragma unroll
+        for (int m = 0; m < kMfma; m++) {
+            mma(f[0], m, m + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < VMA; i++)
+                if (i * kMfma / VMA == m)
+                    issue(la, 0u, u + 2, i);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < kGroups)
+                read(ra, rb, 2 * u + 1, f[1], m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // unit u+1 has landed once only the A half just issued is in flight
+        vm_wait<VMA>();
+        unit_barrier();
+        // stage 2u+1, reading stage 2u+2 of unit u+1; unit u+2's B half
+        // into unit u's A slot
+        const uint32_t lb = sl(a);
+        const char* qa = sb(a1);
+        const char* qb = sb(b1);
+#pragma unroll
+        for (int m = 0; m < kMfma; m++) {
+            mma(f[1], m, m + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = VMA; i < VM; i++)
+                if ((i - VMA) * kMfma / (VM - VMA) == m)
+                    issue(0u, lb, u + 2, i);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < kGroups)
+                read(qa, qb, 2 * u + 2, f[0], m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int na = sp, nb = a, ns = b;
+        a = a1;
+        b = b1;
+        a1 = na;
+        b1 = nb;
+        sp = ns;
+    }
+    {
+        const char* ra = sb(a);
+        const char* rb = sb(b);
+#pragma unroll
+        for (int m = 0; m < kMfma; m++) {
+            mma(f[0], m, m + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < kGroups)
+                read(ra, rb, 2 * u + 1, f[1], m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    mma(f[1], 0, kMfma);
+    wait_all();
+    unit_barrier();
+}
+
+// ---------------------------------------------------------------------------
 // Work-item remap: workgroups are dispatched to the 8 XCDs round-robin
 // (XCD = blockIdx % 8).  Within a chunk of P consecutive items (P % 8 == 0)
 // the remap gives XCD x the contiguous items [x P/8, (x+1) P/8), so tiles that
@@ -423,6 +537,26 @@ __device__ __forceinline__ int xcd_remap(int q, int P) {
     if (P % 8 != 0)
         return q;
     return (q & 7) * (P >> 3) + (q >> 3);
+}
+
+// Two-dimensional variant for a tiles_m x tiles_n chunk: the chunk is cut into
+// a gm x (8/gm) grid of equal blocks of tiles, and XCD x takes block
+// (x / (8/gm), x % (8/gm)), so that an M-tile row's A panel is read by 8/gm
+// XCDs and an N-tile column's B panel by gm, instead of 1 and 8.  gm divides
+// 8 and tiles_m, 8/gm divides tiles_n (the caller checks); gm = 0 falls back
+// to xcd_remap.
+__device__ __forceinline__ void xcd_remap2d(int q, int tiles_m, int tiles_n, int gm, int& mt,
+                                            int& nt) {
+    if (gm == 0) {
+        const int r = xcd_remap(q, tiles_m * tiles_n);
+        mt = r / tiles_n;
+        nt = r % tiles_n;
+        return;
+    }
+    const int gn = 8 / gm, bm = tiles_m / gm, bn = tiles_n / gn;
+    const int x = q & 7, j = q >> 3;
+    mt = (x / gn) * bm + j / bn;
+    nt = (x % gn) * bn + j % bn;
 }
 
 // Element (block i, block j, register r) of an MFMA 32x32 accumulator is row

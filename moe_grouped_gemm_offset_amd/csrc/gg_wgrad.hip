@@ -22,18 +22,20 @@
 namespace gg {
 
 using WgradCfg = Cfg<256, 256, 4, 2>;
+constexpr bool kWgradSlots5 = true;     // the five-slot pipeline of gg_tile.hpp
 
 template <class C, bool A_K, bool B_K>
 __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     constexpr int TM = C::TM, TN = C::TN;
-    __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
+    __shared__ __attribute__((aligned(1024))) char smem[kWgradSlots5 ? Slots5<C>::kLds : C::kLds];
 
     const int tiles_m = (p.hidden + TM - 1) / TM;
     const int tiles_n = (p.inter + TN - 1) / TN;
     const int P = tiles_m * tiles_n;
     const int rank = uniform(blockIdx.x / P);
-    const int q = uniform(xcd_remap(blockIdx.x % P, P));
-    const int mt = uniform(q / tiles_n), nt = uniform(q % tiles_n);
+    int mt_, nt_;
+    xcd_remap2d(blockIdx.x % P, tiles_m, tiles_n, p.xcd_gm, mt_, nt_);
+    const int mt = uniform(mt_), nt = uniform(nt_);
     const int32_t* order = p.ws + kWsHeader / 4;
     const int e = uniform(order[rank]);
 
@@ -83,28 +85,37 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         lb.init((int64_t)p.inter * 2, p.inter - n0);
     using LA = std::conditional_t<A_K, LoadK<C, TM>, LoadMN<C>>;
     using LB = std::conditional_t<B_K, LoadK<C, TN>, LoadMN<C>>;
-    auto issue = [&](uint32_t st, int u, int i) {
+    auto issue2 = [&](uint32_t sa, uint32_t sb, int u, int i) {
         const int64_t k0 = begin + (int64_t)u * 64;
         if (i < LA::kN) {
             if constexpr (A_K)
-                la.template issue<true>(st, ak + (int64_t)m0 * ldk + (int64_t)u * 128, (end - k0) * 2, i);
+                la.template issue<true>(sa, ak + (int64_t)m0 * ldk + (int64_t)u * 128, (end - k0) * 2, i);
             else
-                la.issue(st, a + (k0 * p.hidden + m0) * 2, end - k0, i);
+                la.issue(sa, a + (k0 * p.hidden + m0) * 2, end - k0, i);
         } else {
             if constexpr (B_K)
-                lb.template issue<true>(st + TM * kRowBytes, bk + (int64_t)n0 * ldk + (int64_t)u * 128,
+                lb.template issue<true>(sb, bk + (int64_t)n0 * ldk + (int64_t)u * 128,
                                         (end - k0) * 2, i - LA::kN);
             else
-                lb.issue(st + TM * kRowBytes, b + (k0 * p.inter + n0) * 2, end - k0, i - LA::kN);
+                lb.issue(sb, b + (k0 * p.inter + n0) * 2, end - k0, i - LA::kN);
         }
     };
-    auto read = [&](const char* st, int kt, FragBf16<C>& f, int g) {
-        read_bf16<C, A_K, B_K>(st, st + TM * kRowBytes, am0, bn0, kt & 1, f, g);
+    auto read2 = [&](const char* sa, const char* sb, int kt, FragBf16<C>& f, int g) {
+        read_bf16<C, A_K, B_K>(sa, sb, am0, bn0, kt & 1, f, g);
     };
     auto mma = [&](const FragBf16<C>& f, int m0_, int m1_) { mma_bf16<C>(f, acc, m0_, m1_); };
     FragBf16<C> frag[2];
-    pipeline<C, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB>(smem, (int)((cnt + 31) / 32),
-                                                                   frag, issue, read, mma);
+    const int nk = (int)((cnt + 31) / 32);
+    if constexpr (kWgradSlots5) {
+        pipeline5<C, LA::kN, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB>(smem, nk, frag, issue2,
+                                                                                read2, mma);
+    } else {
+        auto issue = [&](uint32_t st, int u, int i) { issue2(st, st + TM * kRowBytes, u, i); };
+        auto read = [&](const char* st, int kt, FragBf16<C>& f, int g) {
+            read2(st, st + TM * kRowBytes, kt, f, g);
+        };
+        pipeline<C, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB>(smem, nk, frag, issue, read, mma);
+    }
 
     void* out = p.out_dense
         ? (void*)((char*)p.out_dense +

@@ -32,8 +32,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_mx_kernel(WgradArgs p) {
     const int tiles_n = (p.inter + TN - 1) / TN;
     const int P = tiles_m * tiles_n;
     const int rank = uniform(blockIdx.x / P);
-    const int q = uniform(xcd_remap(blockIdx.x % P, P));
-    const int mt = uniform(q / tiles_n), nt = uniform(q % tiles_n);
+    int mt_, nt_;
+    xcd_remap2d(blockIdx.x % P, tiles_m, tiles_n, p.xcd_gm, mt_, nt_);
+    const int mt = uniform(mt_), nt = uniform(nt_);
     const int32_t* order = p.ws + kWsHeader / 4;
     const int e = uniform(order[rank]);
 
