@@ -96,8 +96,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
         pipeline<C, kLA + LB::kN, 2 * MB * NB, MB + NB>(smem, p.K / 32, frag, issue, read, mma);
     }
 
-    // C of the items 12 ahead (6 for fp32 C) in flight in the epilogue
-    dglu_epilogue<C, W32, ACT, false, W32 ? 6 : 12>(p, acc, smem, m0, n0, g, rows_valid, am0, bn0);
+    // C of the items 6 ahead (3 for fp32 C) in flight in the epilogue: deeper
+    // prefetch spilled registers and measured slower
+    dglu_epilogue<C, W32, ACT, false, W32 ? 3 : 6>(p, acc, smem, m0, n0, g, rows_valid, am0, bn0);
 }
 
 hipError_t launch_dglu(const DgluArgs& p, hipStream_t s) {
