@@ -21,10 +21,10 @@ namespace gg {
 using DgluCfg = Cfg<256, 256, 4, 2>;
 constexpr bool kDgluSlots5 = true;      // the five-slot pipeline of gg_tile.hpp
 
-// W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU.  Each
-// combination is its own kernel so the register allocation of one epilogue
-// does not burden the others.
-template <class C, bool B_K, bool W32, int ACT>
+// W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU; BF: C and D
+// both bf16.  Each combination is its own kernel so the register allocation
+// of one epilogue does not burden the others.
+template <class C, bool B_K, bool W32, int ACT, bool BF>
 __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
     __shared__ __attribute__((aligned(1024))) char smem[kDgluSlots5 ? Slots5<C>::kLds : C::kLds];
@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
 
     // C of the items 6 ahead (3 for fp32 C) in flight in the epilogue: deeper
     // prefetch spilled registers and measured slower
-    dglu_epilogue<C, W32, ACT, false, W32 ? 3 : 6>(p, acc, smem, m0, n0, g, rows_valid, am0, bn0);
+    dglu_epilogue<C, W32, ACT, false, W32 ? 3 : 6, false, BF>(p, acc, smem, m0, n0, g, rows_valid, am0, bn0);
 }
 
 hipError_t launch_dglu(const DgluArgs& p, hipStream_t s) {
@@ -107,18 +107,26 @@ hipError_t launch_dglu(const DgluArgs& p, hipStream_t s) {
     if (tiles == 0)
         return hipSuccess;
     const dim3 grid((unsigned)tiles), block(C::kThreads);
-    auto go = [&](auto BK, auto W32) {
+    auto go = [&](auto BK, auto W32, auto BF) {
         constexpr bool bk = decltype(BK)::value, w32 = decltype(W32)::value;
+        constexpr bool bf = decltype(BF)::value;
         if (p.act == 0)
-            hipLaunchKernelGGL((dglu_kernel<C, bk, w32, 0>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_kernel<C, bk, w32, 0, bf>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((dglu_kernel<C, bk, w32, 1>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_kernel<C, bk, w32, 1, bf>), grid, block, 0, s, p);
     };
-    const bool w32 = p.c_dtype == kF32;
+    auto go_bk = [&](auto BK) {
+        if (p.c_dtype == kF32)
+            go(BK, std::true_type(), std::false_type());
+        else if (p.c_dtype == kBF16 && p.d_dtype == kBF16)
+            go(BK, std::false_type(), std::true_type());
+        else
+            go(BK, std::false_type(), std::false_type());
+    };
     if (p.b_kmajor)
-        w32 ? go(std::true_type(), std::true_type()) : go(std::true_type(), std::false_type());
+        go_bk(std::true_type());
     else
-        w32 ? go(std::false_type(), std::true_type()) : go(std::false_type(), std::false_type());
+        go_bk(std::false_type());
     return hipGetLastError();
 }
 

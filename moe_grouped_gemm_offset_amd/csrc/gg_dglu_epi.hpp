@@ -25,7 +25,9 @@
 
 namespace gg {
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// The hardware reciprocal (1 ulp) instead of an IEEE division: the epilogue's
+// arithmetic is a good share of the dGLU kernels' time.
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // tanh(x) = 2 sigmoid(2x) - 1 (exact at +-inf: +-1).
 __device__ __forceinline__ float tanhf_(float x) { return 2.0f * sigmoidf_(2.0f * x) - 1.0f; }
@@ -42,10 +44,12 @@ __device__ __forceinline__ float scaled_x(float beta, float c) {
 // T_u = b2 tanh(U/b2), gradients R prob T_u dT_g/dG and R prob T_g dT_u/dU,
 // activation T_g T_u); AMAX: raise
 // p.amax[2 g + {0: input, 1: gate}]; Q: D as FP8 (E4M3) D_row / D_col with
-// E8M0 scales (gg_fp8out.hpp) instead of a 16/32-bit D; kAhead: row-walk
+// E8M0 scales (gg_fp8out.hpp) instead of a 16/32-bit D; BF: C and D are
+// both bf16, known at compile time (no per-element format branches, which
+// also keeps the compiler's memory-counter waits exact); kAhead: row-walk
 // items whose C loads are in flight while one is processed.  The caller has
 // passed the barrier that ends the main loop's use of smem.
-template <class C, bool W32, int ACT, bool AMAX, int kAhead, bool Q = false>
+template <class C, bool W32, int ACT, bool AMAX, int kAhead, bool Q = false, bool BF = false>
 __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&acc)[C::MB][C::NB],
                                               char* smem, int64_t m0, int n0, int g,
                                               int rows_valid, int am0, int bn0) {
@@ -55,6 +59,7 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
     const float bet = p.beta[g];
     const int64_t N2 = 2 * (int64_t)p.N;
     const float rb1 = 1.0f / p.situ_b1, rb2 = 1.0f / p.situ_b2;
+    const int cdt = BF ? kBF16 : p.c_dtype, ddt = BF ? kBF16 : p.d_dtype;
     float* dbias_ws = p.dbias ? (float*)((char*)p.ws + kWsHeader) + (int64_t)g * N2 : nullptr;
     constexpr int kT = 4 * C::MB;                  // row walk steps per lane
     float rowsum[kT], bs_in[8], bs_gt[8];
@@ -104,8 +109,8 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
         if (rr < rows_valid && n < p.N) {
             const int64_t row = m0 + rr;
             float xin[8], xgt[8];
-            raw8_cvt<W32>(pre.x[0], p.c_dtype, xin);
-            raw8_cvt<W32>(pre.x[1], p.c_dtype, xgt);
+            raw8_cvt<W32>(pre.x[0], cdt, xin);
+            raw8_cvt<W32>(pre.x[1], cdt, xgt);
             const float pr = pre.row;
 #pragma unroll
             for (int k = 0; k < 8; k++) {
@@ -149,8 +154,8 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
                 }
             }
             if constexpr (!Q) {
-                store8(p.d, p.d_dtype, row * N2 + c_in, din);
-                store8(p.d, p.d_dtype, row * N2 + c_gt, dgt);
+                store8(p.d, ddt, row * N2 + c_in, din);
+                store8(p.d, ddt, row * N2 + c_gt, dgt);
             }
         }
         if constexpr (Q) {

@@ -24,8 +24,8 @@ namespace gg {
 using DgluMxCfg = Cfg<256, 256, 2, 2>;
 
 // W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU, 2 dSiTU-GLU;
-// Q: FP8 D_row / D_col with E8M0 scales.
-template <class C, bool W32, int ACT, bool Q>
+// Q: FP8 D_row / D_col with E8M0 scales; BF: C and D both bf16.
+template <class C, bool W32, int ACT, bool Q, bool BF>
 __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
     __shared__ __attribute__((aligned(1024))) char smem[ScaleLds<C>::kSmem];
@@ -69,8 +69,8 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
     mx_mainloop<C>(smem, a, sfa, bg, sfb, K, K, rows_valid, cols_valid, am0, bn0, acc);
 
     // C of the items 12 ahead (6 for fp32 C) in flight in the epilogue
-    dglu_epilogue<C, W32, ACT, true, Q ? (W32 ? 4 : 8) : (W32 ? 6 : 12), Q>(p, acc, smem, m0, n0, g,
-                                                                          rows_valid, am0, bn0);
+    dglu_epilogue<C, W32, ACT, true, Q ? (W32 ? 4 : 8) : (W32 ? 6 : 12), Q, BF>(
+        p, acc, smem, m0, n0, g, rows_valid, am0, bn0);
 }
 
 hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s) {
@@ -79,20 +79,27 @@ hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s) {
     if (tiles == 0)
         return hipSuccess;
     const dim3 grid((unsigned)tiles), block(C::kThreads);
-    auto go = [&](auto W32, auto Q) {
+    auto go = [&](auto W32, auto Q, auto BF) {
         constexpr bool w32 = decltype(W32)::value, q = decltype(Q)::value;
+        constexpr bool bf = decltype(BF)::value;
         if (p.act == 0)
-            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 0, q>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 0, q, bf>), grid, block, 0, s, p);
         else if (p.act == 1)
-            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 1, q>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 1, q, bf>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 2, q>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_mx_kernel<C, w32, 2, q, bf>), grid, block, 0, s, p);
     };
+    const std::false_type no;
+    const std::true_type yes;
     const bool w32 = p.c_dtype == kF32;
     if (p.d_dtype == kF8)
-        w32 ? go(std::true_type(), std::true_type()) : go(std::false_type(), std::true_type());
+        w32 ? go(yes, yes, no) : go(no, yes, no);
+    else if (w32)
+        go(yes, no, no);
+    else if (p.c_dtype == kBF16 && p.d_dtype == kBF16)
+        go(no, no, yes);
     else
-        w32 ? go(std::true_type(), std::false_type()) : go(std::false_type(), std::false_type());
+        go(no, no, no);
     return hipGetLastError();
 }
 

@@ -23,8 +23,9 @@ namespace gg {
 
 using DsreluCfg = Cfg<256, 256, 2, 2>;
 
-// Q: FP8 (E4M3) D_row / D_col with E8M0 scales (else a 16/32-bit D_row).
-template <class C, bool Q>
+// Q: FP8 (E4M3) D_row / D_col with E8M0 scales (else a 16/32-bit D_row);
+// BF: C and D both bf16, known at compile time.
+template <class C, bool Q, bool BF>
 __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
     __shared__ __attribute__((aligned(1024))) char smem[ScaleLds<C>::kSmem];
@@ -82,6 +83,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
         rowsum[t] = 0.0f;
     float* const elds = (float*)(smem + w * kEpiWaveBytes);
     const float nc = Q ? *p.q.norm_const : 1.0f;
+    const int cdt = BF ? kBF16 : p.c_dtype, ddt = BF ? kBF16 : p.d_dtype;
     float dcol[4][8];                              // Q: a column block's 4 items
     auto epilogue = [&](auto W32) {
         constexpr bool w32 = decltype(W32)::value;
@@ -105,7 +107,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                 float d[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
                 if (ok) {
                     float cv[8];
-                    raw8_cvt<w32>(pre.x[0], p.c_dtype, cv);
+                    raw8_cvt<w32>(pre.x[0], cdt, cv);
                     const float pr2 = pre.row * 2.0f;
 #pragma unroll
                     for (int k = 0; k < 8; k++) {
@@ -130,7 +132,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
             } else if (rr < rows_valid && col < p.N) {
                 const int64_t row = m0 + rr;
                 float cv[8], d[8];
-                raw8_cvt<w32>(pre.x[0], p.c_dtype, cv);
+                raw8_cvt<w32>(pre.x[0], cdt, cv);
                 const float pr2 = pre.row * 2.0f;
 #pragma unroll
                 for (int k = 0; k < 8; k++) {
@@ -139,7 +141,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                     rowsum[t] += cv[k] * rl * rl;
                     amax = fmaxf(amax, fabsf(d[k]));
                 }
-                store8(p.d, p.d_dtype, row * N + col, d);
+                store8(p.d, ddt, row * N + col, d);
             }
         };
         for_each_row8<C, Q ? (w32 ? 6 : 12) : (w32 ? 12 : 24)>(acc, elds, load, fn);
@@ -172,10 +174,13 @@ hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s) {
     const int64_t tiles = ((p.m_rows + C::TM - 1) / C::TM) * ((p.N + C::TN - 1) / C::TN);
     if (tiles == 0)
         return hipSuccess;
+    const dim3 grid((unsigned)tiles), block(C::kThreads);
     if (p.d_dtype == kF8)
-        hipLaunchKernelGGL((dsrelu_kernel<C, true>), dim3((unsigned)tiles), dim3(C::kThreads), 0, s, p);
+        hipLaunchKernelGGL((dsrelu_kernel<C, true, false>), grid, block, 0, s, p);
+    else if (p.c_dtype == kBF16 && p.d_dtype == kBF16)
+        hipLaunchKernelGGL((dsrelu_kernel<C, false, true>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL((dsrelu_kernel<C, false>), dim3((unsigned)tiles), dim3(C::kThreads), 0, s, p);
+        hipLaunchKernelGGL((dsrelu_kernel<C, false, false>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
