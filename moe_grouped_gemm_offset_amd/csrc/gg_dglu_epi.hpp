@@ -44,8 +44,8 @@ __device__ __forceinline__ float scaled_x(float beta, float c) {
 // T_u = b2 tanh(U/b2), gradients R prob T_u dT_g/dG and R prob T_g dT_u/dU,
 // activation T_g T_u); AMAX: raise
 // p.amax[2 g + {0: input, 1: gate}]; Q: D as FP8 (E4M3) D_row / D_col with
-// E8M0 scales (gg_fp8out.hpp) instead of a 16/32-bit D; BF: C and D are
-// both bf16, known at compile time (no per-element format branches, which
+// E8M0 scales (gg_fp8out.hpp) instead of a 16/32-bit D; BF: C is bf16 and,
+// unless Q, so is D, known at compile time (no per-element format branches, which
 // also keeps the compiler's memory-counter waits exact); kAhead: row-walk
 // items whose C loads are in flight while one is processed.  The caller has
 // passed the barrier that ends the main loop's use of smem.

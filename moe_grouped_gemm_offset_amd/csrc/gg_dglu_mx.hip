@@ -24,7 +24,7 @@ namespace gg {
 using DgluMxCfg = Cfg<256, 256, 2, 2>;
 
 // W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU, 2 dSiTU-GLU;
-// Q: FP8 D_row / D_col with E8M0 scales; BF: C and D both bf16.
+// Q: FP8 D_row / D_col with E8M0 scales; BF: C bf16 and, unless Q, D bf16.
 template <class C, bool W32, int ACT, bool Q, bool BF>
 __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
@@ -93,7 +93,7 @@ hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s) {
     const std::true_type yes;
     const bool w32 = p.c_dtype == kF32;
     if (p.d_dtype == kF8)
-        w32 ? go(yes, yes, no) : go(no, yes, no);
+        w32 ? go(yes, yes, no) : (p.c_dtype == kBF16 ? go(no, yes, yes) : go(no, yes, no));
     else if (w32)
         go(yes, no, no);
     else if (p.c_dtype == kBF16 && p.d_dtype == kBF16)

@@ -24,7 +24,7 @@ namespace gg {
 using DsreluCfg = Cfg<256, 256, 2, 2>;
 
 // Q: FP8 (E4M3) D_row / D_col with E8M0 scales (else a 16/32-bit D_row);
-// BF: C and D both bf16, known at compile time.
+// BF: C bf16 and, unless Q, D bf16, known at compile time.
 template <class C, bool Q, bool BF>
 __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
@@ -175,7 +175,9 @@ hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s) {
     if (tiles == 0)
         return hipSuccess;
     const dim3 grid((unsigned)tiles), block(C::kThreads);
-    if (p.d_dtype == kF8)
+    if (p.d_dtype == kF8 && p.c_dtype == kBF16)
+        hipLaunchKernelGGL((dsrelu_kernel<C, true, true>), grid, block, 0, s, p);
+    else if (p.d_dtype == kF8)
         hipLaunchKernelGGL((dsrelu_kernel<C, true, false>), grid, block, 0, s, p);
     else if (p.c_dtype == kBF16 && p.d_dtype == kBF16)
         hipLaunchKernelGGL((dsrelu_kernel<C, false, true>), grid, block, 0, s, p);
