@@ -19,7 +19,9 @@
 namespace gg {
 
 using DgluCfg = Cfg<256, 256, 4, 2>;
-constexpr bool kDgluSlots5 = true;      // the five-slot pipeline of gg_tile.hpp
+// main loop of gg_tile.hpp: 0 two unit buffers, 1 five slots, 2 five slots
+// with the two wave groups in ping-pong
+constexpr int kDgluPipe = 2;
 
 // W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU; BF: C and D
 // both bf16.  Each combination is its own kernel so the register allocation
@@ -27,7 +29,7 @@ constexpr bool kDgluSlots5 = true;      // the five-slot pipeline of gg_tile.hpp
 template <class C, bool B_K, bool W32, int ACT, bool BF>
 __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
-    __shared__ __attribute__((aligned(1024))) char smem[kDgluSlots5 ? Slots5<C>::kLds : C::kLds];
+    __shared__ __attribute__((aligned(1024))) char smem[kDgluPipe ? Slots5<C>::kLds : C::kLds];
 
     const int tiles_n = (p.N + TN - 1) / TN;
     const int tiles_m = (int)((p.m_rows + TM - 1) / TM);
@@ -86,7 +88,10 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
     };
     auto mma = [&](const FragBf16<C>& f, int m0_, int m1_) { mma_bf16<C>(f, acc, m0_, m1_); };
     FragBf16<C> frag[2];
-    if constexpr (kDgluSlots5) {
+    if constexpr (kDgluPipe == 2) {
+        pipeline_pp<C, kLA, kLA + LB::kN, 2 * MB * NB, MB + NB>(smem, p.K / 32, frag[0], issue2, read2,
+                                                                mma);
+    } else if constexpr (kDgluPipe == 1) {
         pipeline5<C, kLA, kLA + LB::kN, 2 * MB * NB, MB + NB>(smem, p.K / 32, frag, issue2, read2, mma);
     } else {
         auto issue = [&](uint32_t st, int u, int i) { issue2(st, st + TM * kRowBytes, u, i); };

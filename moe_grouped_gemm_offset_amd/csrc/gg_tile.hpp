@@ -79,6 +79,16 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // descriptors built from it stay scalar.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// The same for a pointer (e.g. one loaded from a pointer array): buffer
+// descriptors built from a pointer the compiler takes for divergent would be
+// wrapped in a loop over the lanes' distinct values.
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * kRowBytes + ((chunk ^ swz(row)) << 4);
 }
@@ -527,6 +537,110 @@ __device__ __forceinline__ void pipeline5(char* smem, int nk, F (&f)[2], Issue i
     unit_barrier();
 }
 
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS reads have completed; vector
+// memory operations may still be in flight.
+__device__ __forceinline__ void lds_wait() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong variant of the five-slot loop, for 8 waves (TM == TN).  Waves
+// 0-3 and 4-7 form two groups with one wave of each on every SIMD.  Each
+// wave alternates a memory phase (its fragment reads of one stage and its
+// share of one half-unit's loads) and a compute phase (that stage's MFMAs,
+// at raised issue priority), and the second group runs one phase behind the
+// first: in every phase one wave per SIMD feeds the MFMA pipe while the
+// other waits on the LDS and the load path, so a load that stalls at issue
+// never holds up an MFMA.  One barrier separates consecutive phases; one
+// fragment set per wave suffices, since a wave never reads while it
+// computes.
+//
+// Slots (32 KiB each) at the start of window u (stages 2u, 2u+1): A(u) and
+// B(u) are read, A(u+1) has landed or is landing, and two are free (unit
+// u-1's, whose last reads ended before the window's first barrier).  In
+// window u each wave issues B(u+1) into the first free slot in its first
+// memory phase and A(u+2) into the second in its second memory phase.
+// B(u+1) must land before window u+1: the first group waits for it at the
+// end of its second compute phase, the second at the end of its second
+// memory phase -- in both cases with only A(u+2) left in flight, one to two
+// phases after issue.
+//   issue, read, mma as for pipeline5; f is a single fragment set.
+// ---------------------------------------------------------------------------
+template <class C, int VMA, int VM, int kMfma, int kGroups, class F, class Issue, class Read,
+          class Mma>
+__device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issue, Read read,
+                                            Mma mma) {
+    static_assert(C::kWaves == 8 && VMA <= VM, "two groups of four waves");
+    constexpr int kSlot = Slots5<C>::kSlot;
+    if (nk <= 0)
+        return;
+    const int nu = (nk + 1) >> 1;                        // load units
+    const bool second = uniform(threadIdx.x >> 6) >= 4;
+    const uint32_t lds0 = lds_addr(smem);
+    auto sl = [&](int k) { return lds0 + (uint32_t)(k * kSlot); };
+    auto sb = [&](int k) { return smem + k * kSlot; };
+    int a = 0, b = 1, a1 = 2, f1 = 3, f2 = 4;
+#pragma unroll
+    for (int i = 0; i < VM; i++)
+        issue(sl(0), sl(1), 0, i);
+#pragma unroll
+    for (int i = 0; i < VMA; i++)
+        issue(sl(2), 0u, 1, i);
+    vm_wait<VMA>();                                      // A(0), B(0)
+    unit_barrier();
+    if (second)
+        unit_barrier();                                  // one phase behind
+    auto compute = [&]() {
+        __builtin_amdgcn_s_setprio(1);
+        mma(f, 0, kMfma);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int u = 0; u < nu; u++) {
+        const char* ra = sb(a);
+        const char* rb = sb(b);
+        // memory: stage 2u, B(u+1)
+#pragma unroll
+        for (int g = 0; g < kGroups; g++)
+            read(ra, rb, 2 * u, f, g);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = VMA; i < VM; i++)
+            issue(0u, sl(f1), u + 1, i);
+        lds_wait();
+        unit_barrier();
+        compute();
+        unit_barrier();
+        // memory: stage 2u+1, A(u+2)
+#pragma unroll
+        for (int g = 0; g < kGroups; g++)
+            read(ra, rb, 2 * u + 1, f, g);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < VMA; i++)
+            issue(sl(f2), 0u, u + 2, i);
+        if (second)
+            vm_wait<VMA>();                              // B(u+1) has landed
+        else
+            lds_wait();
+        unit_barrier();
+        compute();
+        if (!second)
+            vm_wait<VMA>();                              // B(u+1) has landed
+        unit_barrier();
+        const int na = a1, nb = f1, na1 = f2;
+        f1 = a;
+        f2 = b;
+        a = na;
+        b = nb;
+        a1 = na1;
+    }
+    if (!second)
+        unit_barrier();                                  // the second group's last phase
+    wait_all();
+    unit_barrier();
+}
+
 // ---------------------------------------------------------------------------
 // Work-item remap: workgroups are dispatched to the 8 XCDs round-robin
 // (XCD = blockIdx % 8).  Within a chunk of P consecutive items (P % 8 == 0)
@@ -632,6 +746,7 @@ __device__ __forceinline__ void load8(const void* base, int dtype, int64_t i, fl
     }
 }
 
+// Stores of results the kernel does not read again are non-temporal.
 __device__ __forceinline__ void store8(void* base, int dtype, int64_t i, const float (&v)[8]) {
     if (dtype == kF32) {
         u32x4 a, b;
@@ -639,8 +754,8 @@ __device__ __forceinline__ void store8(void* base, int dtype, int64_t i, const f
         a.z = __builtin_bit_cast(uint32_t, v[2]); a.w = __builtin_bit_cast(uint32_t, v[3]);
         b.x = __builtin_bit_cast(uint32_t, v[4]); b.y = __builtin_bit_cast(uint32_t, v[5]);
         b.z = __builtin_bit_cast(uint32_t, v[6]); b.w = __builtin_bit_cast(uint32_t, v[7]);
-        *reinterpret_cast<u32x4*>((float*)base + i) = a;
-        *reinterpret_cast<u32x4*>((float*)base + i + 4) = b;
+        __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>((float*)base + i));
+        __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>((float*)base + i + 4));
     } else {
         uint32_t ws[4];
 #pragma unroll
@@ -649,7 +764,8 @@ __device__ __forceinline__ void store8(void* base, int dtype, int64_t i, const f
             const uint32_t hi = dtype == kBF16 ? f32_to_bf16(v[2 * k + 1]) : f32_to_f16(v[2 * k + 1]);
             ws[k] = lo | (hi << 16);
         }
-        *reinterpret_cast<u32x4*>((uint16_t*)base + i) = u32x4{ws[0], ws[1], ws[2], ws[3]};
+        __builtin_nontemporal_store(u32x4{ws[0], ws[1], ws[2], ws[3]},
+                                    reinterpret_cast<u32x4*>((uint16_t*)base + i));
     }
 }
 

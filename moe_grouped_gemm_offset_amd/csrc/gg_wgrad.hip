@@ -22,12 +22,14 @@
 namespace gg {
 
 using WgradCfg = Cfg<256, 256, 4, 2>;
-constexpr bool kWgradSlots5 = true;     // the five-slot pipeline of gg_tile.hpp
+// main loop of gg_tile.hpp: 0 two unit buffers, 1 five slots, 2 five slots
+// with the two wave groups in ping-pong
+constexpr int kWgradPipe = 2;
 
 template <class C, bool A_K, bool B_K>
 __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     constexpr int TM = C::TM, TN = C::TN;
-    __shared__ __attribute__((aligned(1024))) char smem[kWgradSlots5 ? Slots5<C>::kLds : C::kLds];
+    __shared__ __attribute__((aligned(1024))) char smem[kWgradPipe ? Slots5<C>::kLds : C::kLds];
 
     const int tiles_m = (p.hidden + TM - 1) / TM;
     const int tiles_n = (p.inter + TN - 1) / TN;
@@ -106,7 +108,10 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     auto mma = [&](const FragBf16<C>& f, int m0_, int m1_) { mma_bf16<C>(f, acc, m0_, m1_); };
     FragBf16<C> frag[2];
     const int nk = (int)((cnt + 31) / 32);
-    if constexpr (kWgradSlots5) {
+    if constexpr (kWgradPipe == 2) {
+        pipeline_pp<C, LA::kN, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB>(smem, nk, frag[0],
+                                                                                  issue2, read2, mma);
+    } else if constexpr (kWgradPipe == 1) {
         pipeline5<C, LA::kN, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB>(smem, nk, frag, issue2,
                                                                                 read2, mma);
     } else {
@@ -121,6 +126,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         ? (void*)((char*)p.out_dense +
                   (int64_t)e * p.hidden * p.inter * (p.out_dtype == kF32 ? 4 : 2))
         : (void*)p.out_ptrs[e];
+    out = uniform_ptr(out);
     const int accumulate = cnt > 0 ? p.accumulate : 0;
     wgrad_epilogue<C>(acc, (float*)(smem + w * kEpiWaveBytes), out, p.out_dtype, p.hidden,
                       p.inter, m0 + am0, n0 + bn0, accumulate);

@@ -79,6 +79,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_mx_kernel(WgradArgs p) {
         ? (void*)((char*)p.out_dense +
                   (int64_t)e * p.hidden * p.inter * (p.out_dtype == kF32 ? 4 : 2))
         : (void*)p.out_ptrs[e];
+    out = uniform_ptr(out);
     const int accumulate = cnt > 0 ? p.accumulate : 0;
     wgrad_epilogue<C>(acc, (float*)(smem + w * kEpiWaveBytes), out, p.out_dtype, p.hidden,
                       p.inter, m0 + am0, n0 + bn0, accumulate);
