@@ -9,6 +9,9 @@ namespace gg {
 // Workspace layout (every op): a 256-byte header whose first int32 is the
 // device error word, followed by the op's own region.
 constexpr size_t kWsHeader = 256;
+// int32 index, in the header, of the 8 work-queue counters of the persistent
+// wgrad kernel (one per XCD), cleared by the set-up kernel
+constexpr int kWsQueue = 16;
 
 // FP8 outputs of the block-scaled dgrad epilogues (d_dtype E4M3).
 struct Fp8Out {

@@ -6,7 +6,7 @@
 // the group offsets against the pages' rules (non-decreasing cumulative
 // ends, every group a multiple of 256, last end == total / <= rows), and for
 // wgrad ranks the experts by token count, largest first, so that the longest
-// reductions are dispatched first.
+// reductions are dispatched first, and clears the work-queue counters.
 #include "gg_internal.hpp"
 #include "gg_moe.h"
 
@@ -51,6 +51,8 @@ prologue_kernel(const int32_t* __restrict__ offsets, int n, int64_t total, int d
     __syncthreads();
     if (t == 0)
         err[0] = flags;
+    if (t < 8)
+        err[kWsQueue + t] = 0;
     if (order) {
         for (int i = t; i < n; i += blockDim.x) {
             int ci = cnt[i], rank = 0;

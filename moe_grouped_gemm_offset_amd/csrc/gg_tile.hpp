@@ -186,7 +186,8 @@ struct LoadK {
     template <bool RAGGED>
     __device__ __forceinline__ void issue(uint32_t lds, const char* tile, int64_t kleft, int i) const {
         const int w = uniform(threadIdx.x >> 6);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, kleft > 0 ? 0x7ffffff0u : 0u);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(uniform_ptr(tile), (uint32_t)uniform(kleft > 0 ? 0x7ffffff0 : 0));
         const uint32_t kl = (uint32_t)(kleft < 128 ? (kleft < 0 ? 0 : kleft) : 128);
         dma16(rs, lds + (w * kN + i) * 1024, !RAGGED || c16[i] < kl ? off[i] : kInvalid);
     }
@@ -219,7 +220,7 @@ struct LoadMN {
     __device__ __forceinline__ void issue(uint32_t lds, const char* tile, int64_t krows, int i) const {
         const int w = uniform(threadIdx.x >> 6);
         const uint32_t kr = (uint32_t)(krows < 64 ? (krows < 0 ? 0 : krows) : 64);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, kr * ld);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(tile), (uint32_t)uniform((int)(kr * ld)));
         dma16(rs, lds + (w * kN + i) * 1024, off[i]);
     }
 };
@@ -565,24 +566,31 @@ __device__ __forceinline__ void lds_wait() {
 // memory phase -- in both cases with only A(u+2) left in flight, one to two
 // phases after issue.
 //   issue, read, mma as for pipeline5; f is a single fragment set.
+// With kPre, the caller has already issued unit 0 into slots 0 and 1 (other
+// vector memory operations may have followed; they are awaited with it).
 // ---------------------------------------------------------------------------
-template <class C, int VMA, int VM, int kMfma, int kGroups, class F, class Issue, class Read,
-          class Mma>
+template <class C, int VMA, int VM, int kMfma, int kGroups, bool kPre = false, class F, class Issue,
+          class Read, class Mma>
 __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issue, Read read,
                                             Mma mma) {
     static_assert(C::kWaves == 8 && VMA <= VM, "two groups of four waves");
     constexpr int kSlot = Slots5<C>::kSlot;
-    if (nk <= 0)
+    if (nk <= 0) {
+        if constexpr (kPre)
+            wait_all();                                  // the prefetched unit has landed
         return;
+    }
     const int nu = (nk + 1) >> 1;                        // load units
     const bool second = uniform(threadIdx.x >> 6) >= 4;
     const uint32_t lds0 = lds_addr(smem);
     auto sl = [&](int k) { return lds0 + (uint32_t)(k * kSlot); };
     auto sb = [&](int k) { return smem + k * kSlot; };
     int a = 0, b = 1, a1 = 2, f1 = 3, f2 = 4;
+    if constexpr (!kPre) {
 #pragma unroll
-    for (int i = 0; i < VM; i++)
-        issue(sl(0), sl(1), 0, i);
+        for (int i = 0; i < VM; i++)
+            issue(sl(0), sl(1), 0, i);
+    }
 #pragma unroll
     for (int i = 0; i < VMA; i++)
         issue(sl(2), 0u, 1, i);
@@ -875,28 +883,35 @@ __device__ __forceinline__ void rawb8_store(__amdgpu_buffer_rsrc_t r, const Fmt8
 // Row walk of a wave's accumulators (32 MB rows x 32 NB columns, MB and NB
 // even).  The MFMA layout gives a lane one column and 16 rows of a block;
 // stores want a lane to own consecutive columns of one row.  The walk stages
-// 64 x 64 quadrants through the wave's private LDS region and visits, for
-// lane l, the items (t, r, c): the 8 columns [c, c+8) of wave-tile row r,
-// r = (l >> 3) + 8 t, t = 0 .. 4 MB - 1, c = 8 (l & 7) + 64 h; for each h
-// the t values come in increasing order.  The caller's loads run kAhead
-// items ahead of their use, so that many are in flight at once:
+// kQR x 64 pieces (kQR = 64: quadrants of 2 x 2 blocks, the wave's LDS
+// region kEpiWaveBytes; kQR = 32: 1 x 2 blocks, kEpiHalfBytes) through the
+// wave's private LDS region and visits, for lane l, the items (t, r, c): the
+// 8 columns [c, c+8) of wave-tile row r, r = (l >> 3) + 8 t,
+// t = 0 .. 4 MB - 1, c = 8 (l & 7) + 64 h; for each h the t values come in
+// increasing order.  The caller's loads run kAhead items ahead of their use,
+// so that many are in flight at once:
 //   load(t, r, c)            queue the loads of an item, returning them;
 //   fn(t, r, c, v, pre)      process an item with its accumulators v (fp32)
 //                            and what load returned for it.
 // Only this wave touches `lds`; the caller separates it from the main loop
 // with a barrier.
 // ---------------------------------------------------------------------------
-template <class C, int kAhead, class Load, class Fn>
+constexpr int kEpiHalfBytes = 32 * kEpiPitch * 4;
+
+template <class C, int kAhead, int kQR = 64, class Load, class Fn>
 __device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB], float* lds, Load load,
                                               Fn fn) {
     static_assert(C::MB % 2 == 0 && C::NB % 2 == 0, "row walk expects 64 x 64 quadrants");
+    static_assert(kQR == 64 || kQR == 32, "staged pieces of 64 or 32 rows");
+    constexpr int kBR = kQR / 32;                        // block rows per piece
+    constexpr int kPer = kQR / 8;                        // items per piece
     constexpr int kItems = 8 * (C::MB / 2) * (C::NB / 2);
     const int l = threadIdx.x & 63;
-    // item i: quadrant q = i / 8 (h = q / (MB/2), mh = q % (MB/2)), t8 = i % 8
+    // item i: piece q = i / kPer (h = q / (MB/kBR), mh = q % (MB/kBR)), ti = i % kPer
     auto item = [&](int i, int& t, int& r, int& c) {
-        const int q = i >> 3, h = q / (C::MB / 2), mh = q % (C::MB / 2), t8 = i & 7;
-        t = 8 * mh + t8;
-        r = 64 * mh + (l >> 3) + 8 * t8;
+        const int q = i / kPer, h = q / (C::MB / kBR), mh = q % (C::MB / kBR), ti = i % kPer;
+        t = kPer * mh + ti;
+        r = kQR * mh + (l >> 3) + 8 * ti;
         c = 64 * h + 8 * (l & 7);
     };
     using P = decltype(load(0, 0, 0));
@@ -909,16 +924,16 @@ __device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB],
     }
 #pragma unroll
     for (int i = 0; i < kItems; i++) {
-        if ((i & 7) == 0) {
-            const int q = i >> 3, h = q / (C::MB / 2), mh = q % (C::MB / 2);
+        if (i % kPer == 0) {
+            const int q = i / kPer, h = q / (C::MB / kBR), mh = q % (C::MB / kBR);
 #pragma unroll
-            for (int b = 0; b < 2; b++)
+            for (int b = 0; b < kBR; b++)
 #pragma unroll
                 for (int jj = 0; jj < 2; jj++)
 #pragma unroll
                     for (int e = 0; e < 16; e++)
                         lds[(32 * b + acc_row(e, l)) * kEpiPitch + 32 * jj + (l & 31)] =
-                            acc[2 * mh + b][2 * h + jj][e];
+                            acc[kBR * mh + b][2 * h + jj][e];
         }
         if (i + kAhead < kItems) {
             int t, r, c;
@@ -927,7 +942,7 @@ __device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB],
         }
         int t, r, c;
         item(i, t, r, c);
-        const int rq = r & 63, cq = c & 63;
+        const int rq = r % kQR, cq = c & 63;
         typedef float f32x4 __attribute__((ext_vector_type(4)));
         const f32x4 a = *reinterpret_cast<const f32x4*>(lds + rq * kEpiPitch + cq);
         const f32x4 b = *reinterpret_cast<const f32x4*>(lds + rq * kEpiPitch + cq + 4);
