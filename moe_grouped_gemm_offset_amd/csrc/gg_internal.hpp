@@ -13,6 +13,33 @@ constexpr size_t kWsHeader = 256;
 // wgrad kernel (one per XCD), cleared by the set-up kernel
 constexpr int kWsQueue = 16;
 
+// Compute units of the current device (cached per device), and the grid of a
+// persistent kernel over `items` work items: one workgroup per CU, a multiple
+// of 8 so that every XCD gets the same number, and at least 8 (or one per
+// item) so that every XCD's queue is served.
+inline int cu_count() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+inline int64_t persistent_grid(int64_t items) {
+    int64_t g = cu_count() & ~7;
+    if (g > items)
+        g = items >= 8 ? (items & ~7) : items;
+    if (g < 8 && items >= 8)
+        g = 8;
+    return g;
+}
+
 // FP8 outputs of the block-scaled dgrad epilogues (d_dtype E4M3).
 struct Fp8Out {
     uint8_t* d_row;           // (rows, W) codes

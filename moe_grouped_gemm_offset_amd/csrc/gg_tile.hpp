@@ -145,6 +145,12 @@ __device__ __forceinline__ void vm_wait() {
 }
 __device__ __forceinline__ void wait_all() { vm_wait<0>(); }
 
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS reads have completed; vector
+// memory operations may still be in flight.
+__device__ __forceinline__ void lds_wait() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+}
+
 // Workgroup barrier that lets the compiler move neither memory accesses nor,
 // through the scheduling barriers, any other instruction across it.  (The
 // fence of __syncthreads would add waits of its own.)
@@ -536,12 +542,6 @@ __device__ __forceinline__ void pipeline5(char* smem, int nk, F (&f)[2], Issue i
     mma(f[1], 0, kMfma);
     wait_all();
     unit_barrier();
-}
-
-// s_waitcnt lgkmcnt(0) alone: this wave's LDS reads have completed; vector
-// memory operations may still be in flight.
-__device__ __forceinline__ void lds_wait() {
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
 }
 
 // ---------------------------------------------------------------------------

@@ -189,22 +189,6 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     }
 }
 
-// Compute units of the current device (cached per device).
-static int cu_count() {
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
-
 hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s) {
     using C = WgradCfg;
     const int64_t total = (int64_t)((p.hidden + C::TM - 1) / C::TM) *
@@ -213,14 +197,7 @@ hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s) {
         return hipSuccess;
     if (total > (1 << 28))              // item numbers and queue positions stay in int32
         return hipErrorInvalidConfiguration;
-    // one workgroup per CU, a multiple of 8 so that every XCD gets the same
-    // number; at least 8 (or one per item) so that every queue is served
-    int64_t g = cu_count() & ~7;
-    if (g > total)
-        g = total >= 8 ? (total & ~7) : total;
-    if (g < 8 && total >= 8)
-        g = 8;
-    const dim3 grid((unsigned)g), block(C::kThreads);
+    const dim3 grid((unsigned)persistent_grid(total)), block(C::kThreads);
     if (p.a_kmajor && p.b_kmajor)
         hipLaunchKernelGGL((wgrad_kernel<C, true, true>), grid, block, 0, s, p);
     else if (p.a_kmajor)
