@@ -161,3 +161,29 @@ def test_moe_scale_sampled(a_major):
     inp_cpu = dict(inp, a=inp["a"].cpu(), b=inp["b"].cpu(), offsets=inp["offsets"].cpu())
     rows = np.array([0, 1, 255, 256, 2047, 2048, 4000, 4095], np.int32)
     compare(got, inp_cpu, torch.bfloat16, hrows=rows, name="wgrad_moe")
+
+
+def test_work_queues_many_items():
+    """More work items than compute units, in a count that is no multiple
+    of 8: 100 experts (some empty) on a 2 x 3 tile grid (hidden 512,
+    intermediate 768: partial N tiles) give 600 items over the per-XCD
+    queues of the persistent kernel.  A second call on the same workspace
+    must give the same output (the set-up kernel resets the queues)."""
+    rng = np.random.default_rng(47)
+    counts = (rng.integers(0, 3, size=100) * 256).astype(np.int64)
+    counts[[3, 50, 99]] = 0
+    inp = synth.wgrad_inputs(512, 768, counts, "m", "n", seed=47)
+    say("work queues", "experts", len(counts), "tokens", int(counts.sum()))
+    b = gg()
+    a, bb, off = inp["a"].cuda(), inp["b"].cuda(), inp["offsets"].cuda()
+    ws = torch.empty(b.gg_wgrad_workspace_size(len(counts)), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        res = torch.full((len(counts), 512, 768), float("nan"), dtype=torch.bfloat16, device="cuda")
+        b.gg_wgrad(a, MAJ["m"], bb, MAJ["n"], off, inp["tokens_sum"], 512, 768, wgrad_dense=res,
+                   workspace=ws)
+        torch.cuda.synchronize()
+        assert b.gg_device_error(ws) == 0
+        outs.append(res.cpu())
+    assert torch.equal(outs[0], outs[1]), "second call on the same workspace differs"
+    compare(outs[0], inp, torch.bfloat16, name="work queues")
