@@ -187,3 +187,45 @@ def test_work_queues_many_items():
         outs.append(res.cpu())
     assert torch.equal(outs[0], outs[1]), "second call on the same workspace differs"
     compare(outs[0], inp, torch.bfloat16, name="work queues")
+
+
+@pytest.mark.parametrize("a_major", ["k", "m"])
+@pytest.mark.parametrize("out", ["bf16_dense", "f32_discrete"])
+def test_moe_scale_output_modes(a_major, out):
+    """The MoE-scale workload into bf16 dense outputs or discrete per-expert
+    fp32 outputs (separate allocations reached through the int64 pointer
+    array): accumulate onto seeded N(0,1) values, then overwrite the same
+    buffers.  Sampled hidden rows of every expert against the oracle; empty
+    experts keep their old values bit for bit when accumulating and are
+    exactly zero after the overwrite."""
+    w = synth.WORKLOADS["wgrad_moe"]
+    counts = synth.workload_counts("wgrad_moe")
+    inp = synth.wgrad_inputs(w["hidden"], w["inter"], counts, a_major, w["b_major"],
+                             seed=w["seed"], device="cuda")
+    E, h, i = len(counts), w["hidden"], w["inter"]
+    dt = torch.bfloat16 if out == "bf16_dense" else torch.float32
+    init = synth.wgrad_initial(E, h, i, dt, seed=1003, device="cuda")
+    say("wgrad_moe", a_major, out, "experts", E, "empty", int(np.sum(counts == 0)))
+    b = gg()
+    rows = np.array([0, 1, 255, 256, 2047, 2048, 4000, 4095], np.int32)
+    inp_cpu = dict(inp, a=inp["a"].cpu(), b=inp["b"].cpu(), offsets=inp["offsets"].cpu())
+    old = init.cpu()
+    if out == "bf16_dense":
+        res = init.clone()
+        outs = None
+    else:
+        outs = [init[e].clone() for e in range(E)]
+        ptrs = torch.tensor([o.data_ptr() for o in outs], dtype=torch.int64, device="cuda")
+    for accumulate in (True, False):
+        if outs is None:
+            ws = b.gg_wgrad(inp["a"], MAJ[a_major], inp["b"], MAJ["n"], inp["offsets"],
+                            inp["tokens_sum"], h, i, wgrad_dense=res, accumulate=accumulate)
+        else:
+            ws = b.gg_wgrad(inp["a"], MAJ[a_major], inp["b"], MAJ["n"], inp["offsets"],
+                            inp["tokens_sum"], h, i, wgrad_ptrs=ptrs,
+                            wgrad_dtype=b._TORCH_DTYPE[dt], accumulate=accumulate)
+        torch.cuda.synchronize()
+        assert b.gg_device_error(ws) == 0
+        got = (res if outs is None else torch.stack(outs)).cpu()
+        compare(got, inp_cpu, dt, accumulate, old if accumulate else None, hrows=rows,
+                name=f"wgrad_moe {out} {'accumulate' if accumulate else 'overwrite'}")
