@@ -22,12 +22,18 @@ and, as single-op workloads outside the default step:
                 the two block-scaled dgrad workloads with FP8 (E4M3) D_row
                 and D_col and their E8M0 scales instead of a bf16 D
   wgrad_moe_kmajor  the wgrad workload with A K-major
+  wgrad_moe_f32acc  the wgrad workload into discrete per-expert fp32
+                outputs (int64 pointer array), accumulate mode: the
+                variant whose roofline is HBM (old outputs read and
+                written back), reported in GB/s against the HBM peak
 
 value = algorithmic FLOPs of the step (2 sum_e M_e N_e K_e per GEMM) over the
 measured wall time of K steps.  Every call is also bracketed by HIP events on
 the stream it runs on, which gives each kernel's average duration; the kernel
-with the largest share is reported against its MFMA roofline.  The CPU oracle
-is timed on a bounded sample of rows of the same workloads (cpu_baseline).
+with the largest share is reported against its roofline: MFMA, or HBM when
+its algorithmic bytes at 8 TB/s take longer than its FLOPs at the MFMA
+peak.  The CPU oracle is timed on a bounded sample of rows of the same
+workloads (cpu_baseline).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -128,7 +134,7 @@ def make_dglu(name, dev):
     return Op(name, "dglu_kernel", synth.flops_dgrad(vm, N, K), "bf16", run, alg, sample)
 
 
-def make_wgrad(dev, a_major="m"):
+def make_wgrad(dev, a_major="m", f32acc=False):
     import numpy as np
     import torch
     from moe_grouped_gemm_offset_amd import binding as B, synth
@@ -138,15 +144,32 @@ def make_wgrad(dev, a_major="m"):
     inp = synth.wgrad_inputs(w["hidden"], w["inter"], counts, a_major, w["b_major"], seed=w["seed"],
                              device=dev)
     E, h, i, T = len(counts), inp["hidden"], inp["inter"], inp["tokens_sum"]
-    out = torch.empty(E, h, i, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(B.gg_wgrad_workspace_size(E), dtype=torch.uint8, device=dev)
     am = B.GG_MAJOR_K if a_major == "k" else B.GG_MAJOR_M
+    if f32acc:
+        # discrete per-expert fp32 outputs, separate allocations, accumulated
+        # into from seeded N(0,1) values
+        init = synth.wgrad_initial(E, h, i, torch.float32, seed=1003, device=dev)
+        outs = [init[e].clone() for e in range(E)]
+        del init
+        ptrs = torch.tensor([o.data_ptr() for o in outs], dtype=torch.int64, device=dev)
 
-    def run():
-        B.gg_wgrad(inp["a"], am, inp["b"], B.GG_MAJOR_N, inp["offsets"], T, h, i,
-                   wgrad_dense=out, workspace=ws)
+        def run():
+            B.gg_wgrad(inp["a"], am, inp["b"], B.GG_MAJOR_N, inp["offsets"], T, h, i,
+                       wgrad_ptrs=ptrs, wgrad_dtype=B.GG_F32, accumulate=True, workspace=ws)
 
-    alg = 2 * (h * T + T * i) + 2 * E * h * i
+        # operands once; old outputs read and written back on the non-empty
+        # experts (empty ones are left untouched)
+        alg = 2 * (h * T + T * i) + 2 * 4 * int(np.sum(counts > 0)) * h * i
+        run.keep = outs
+    else:
+        out = torch.empty(E, h, i, dtype=torch.bfloat16, device=dev)
+
+        def run():
+            B.gg_wgrad(inp["a"], am, inp["b"], B.GG_MAJOR_N, inp["offsets"], T, h, i,
+                       wgrad_dense=out, workspace=ws)
+
+        alg = 2 * (h * T + T * i) + 2 * E * h * i
 
     def sample(nrows):
         cpu = _cpu(inp)
@@ -297,6 +320,7 @@ WORKLOAD_OPS = {
     "dswiglu": ["dswiglu"],
     "wgrad_moe": ["wgrad_moe"],
     "wgrad_moe_kmajor": ["wgrad_moe_kmajor"],
+    "wgrad_moe_f32acc": ["wgrad_moe_f32acc"],
     "dgeglu": ["dgeglu"],
     "dsrelu_mxfp8": ["dsrelu_mxfp8"],
     "dglu_mxfp8": ["dglu_mxfp8"],
@@ -313,6 +337,10 @@ def build_op(name, dev):
         return make_wgrad(dev, "m")
     if name == "wgrad_moe_kmajor":
         op = make_wgrad(dev, "k")
+        op.name = name
+        return op
+    if name == "wgrad_moe_f32acc":
+        op = make_wgrad(dev, "m", f32acc=True)
         op.name = name
         return op
     if name == "dglu_mxfp8":
@@ -408,6 +436,14 @@ def summarize_pmc(fetch_csv, write_csv, workload_kernels, out_path):
     return out
 
 
+def bound_of(op):
+    """The roofline that bounds an op: "hbm" when its algorithmic bytes at
+    the HBM peak take longer than its FLOPs at the MFMA peak, else "mfma"."""
+    t_hbm = op.alg_bytes / (HBM_PEAK * 1e9)
+    t_mfma = op.flops / (PEAK[op.dtype] * 1e12)
+    return "hbm" if t_hbm > t_mfma else "mfma"
+
+
 def traffic_for(kernel, workload):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
@@ -439,7 +475,8 @@ def main():
         if len(names) != 1:
             sys.exit("--summarize-pmc needs a single-op --workload")
         kernel = {"dswiglu": "dglu_kernel", "dgeglu": "dglu_kernel", "wgrad_moe": "wgrad_kernel",
-                  "wgrad_moe_kmajor": "wgrad_kernel", "dsrelu_mxfp8": "dsrelu_kernel",
+                  "wgrad_moe_kmajor": "wgrad_kernel", "wgrad_moe_f32acc": "wgrad_kernel",
+                  "dsrelu_mxfp8": "dsrelu_kernel",
                   "dglu_mxfp8": "dglu_mx_kernel", "wgrad_mxfp8": "wgrad_mx_kernel",
                   "dsrelu_mxfp8_fp8out": "dsrelu_kernel",
                   "dglu_mxfp8_fp8out": "dglu_mx_kernel"}[names[0]]
@@ -497,14 +534,18 @@ def main():
                             "dtype": op.dtype, "alg_gb_s": round(op.alg_bytes / (ms * 1e-3) / 1e9, 1)}
         tr = traffic_for(op.kernel, op.name)
         kernels[op.name]["hbm_gb_per_launch"] = None if tr is None else round(tr / 1e9, 3)
+        kernels[op.name]["bound"] = bound_of(op)
     total_flops = sum(op.flops for op in ops)
     value = total_flops / (ms_step * 1e-3) / 1e12
     dom = max(ops, key=lambda o: kernels[o.name]["ms"])
     kd = kernels[dom.name]
-    achieved = dom.flops / (kd["ms"] * 1e-3) / 1e12
     src = source_hash(dom.kernel)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK[dom.dtype],
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK[dom.dtype], 4),
+    if bound_of(dom) == "hbm":
+        achieved, peak, unit = dom.alg_bytes / (kd["ms"] * 1e-3) / 1e9, HBM_PEAK, "GB/s"
+    else:
+        achieved, peak, unit = dom.flops / (kd["ms"] * 1e-3) / 1e12, PEAK[dom.dtype], "TFLOP/s"
+    roofline = {"bound": bound_of(dom), "achieved": round(achieved, 1), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": traffic_for(dom.kernel, dom.name), "kernel": dom.kernel,
                 "workload": dom.name, "source_hash": src}
     cpu = None
