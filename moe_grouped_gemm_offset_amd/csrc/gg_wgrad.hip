@@ -139,10 +139,10 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     if (threadIdx.x == 0)
         *bcast = atomicAdd(queue, 1);
     __syncthreads();
-    int t = 8 * uniform(*bcast) + x;
-    if (t >= total)
+    const int t0 = 8 * uniform(*bcast) + x;
+    if (t0 >= total)
         return;
-    decode(t);
+    decode(t0);
     prefetch();
     for (;;) {
         const bool skip = cnt == 0 && p.accumulate;     // nothing to add: output untouched
@@ -186,7 +186,6 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         // the stores and the prefetch stay in flight
         lds_wait();
         unit_barrier();
-        t = tn;
     }
 }
 
