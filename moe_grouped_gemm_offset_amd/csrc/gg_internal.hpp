@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace gg {
 
 // Workspace layout (every op): a 256-byte header whose first int32 is the
@@ -18,18 +20,19 @@ constexpr int kWsQueue = 16;
 // of 8 so that every XCD gets the same number, and at least 8 (or one per
 // item) so that every XCD's queue is served.
 inline int cu_count() {
-    static int cache[64];
+    // host threads may race to fill an entry; they all store the same value
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 inline int64_t persistent_grid(int64_t items) {
     int64_t g = cu_count() & ~7;
