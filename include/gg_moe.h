@@ -185,7 +185,8 @@ size_t gg_wgrad_workspace_size(int32_t num_experts);
  *            computed exactly and flagged (GG_DEVERR_GRANULE); a group whose
  *            bounds are not multiples of 8 is skipped (GG_DEVERR_SKIPPED).
  * num_experts 1..1024.  tokens_sum >= 0, a multiple of 8.
- * hidden, intermediate  multiples of 64, >= 64.
+ * hidden, intermediate  multiples of 64, >= 64; at most 2^28 output tiles
+ *            of 256 x 256 over all experts (GG_ERR_UNSUPPORTED beyond).
  * Output, exactly one of ("Output modes"):
  * wgrad_dense  (num_experts, hidden, intermediate) row-major, or NULL;
  * wgrad_ptrs   int64[num_experts] device array of 16-B-aligned, non-NULL
@@ -198,6 +199,9 @@ size_t gg_wgrad_workspace_size(int32_t num_experts);
  * flags        OR of GG_FLAG_VALIDATE_OFFSETS and GG_FLAG_TENSOR_RAGGED
  *              ("input_order": the K-major operands' storage, see the flag).
  * workspace    >= gg_wgrad_workspace_size(num_experts) bytes, 256-B aligned.
+ *              Besides the error word and the expert order it holds the
+ *              work-queue counters of the kernel's scheduler, reset by every
+ *              call; calls that may overlap must not share it.
  */
 gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_major,
                    const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,

@@ -162,6 +162,10 @@ static gg_status run_wgrad(gg::WgradArgs& p, bool mx, const int32_t* offsets, in
     // tile-relative 32-bit buffer offsets: 256 rows of the largest pitch
     if (tokens_sum > (1 << 21) || hidden > (1 << 21) || intermediate > (1 << 21))
         return fail(GG_ERR_UNSUPPORTED, "tokens_sum, hidden and intermediate are limited to 2^21");
+    // the work items (256 x 256 output tiles of every expert) are numbered in
+    // int32 by the kernels' schedulers
+    if ((int64_t)((hidden + 255) / 256) * ((intermediate + 255) / 256) * num_experts > (1 << 28))
+        return fail(GG_ERR_UNSUPPORTED, "more than 2^28 output tiles (256 x 256, all experts)");
     if (!aligned16(wgrad_dense) || !aligned16(wgrad_ptrs) || ((uintptr_t)offsets & 3u))
         return fail(GG_ERR_ALIGN, "the output must be 16-byte aligned, offsets 4-byte");
     if ((uintptr_t)workspace & 255u)

@@ -74,6 +74,7 @@ def wgrad(**kw):
     (dict(wsb=100), WORKSPACE),
     (dict(flags=1), MODE),
     (dict(T=1 << 22), UNSUPPORTED),
+    (dict(hidden=1 << 20, inter=1 << 20, E=1024), UNSUPPORTED),
 ])
 def test_wgrad_rejects(kw, status):
     assert wgrad(**kw) == status
