@@ -527,9 +527,13 @@ def main():
 
     kernels = {}
     for op in ops:
-        ms = sum(s.elapsed_time(e) for s, e in ev[op.name]) / len(ev[op.name])
+        times = sorted(s.elapsed_time(e) for s, e in ev[op.name])
+        ms = sum(times) / len(times)
+        pct = lambda q: times[min(len(times) - 1, int(q * (len(times) - 1) + 0.5))]
         tf = op.flops / (ms * 1e-3) / 1e12
-        kernels[op.name] = {"kernel": op.kernel, "ms": round(ms, 4), "gflop": round(op.flops / 1e9, 2),
+        kernels[op.name] = {"kernel": op.kernel, "ms": round(ms, 4),
+                            "ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
+                            "gflop": round(op.flops / 1e9, 2),
                             "tflops": round(tf, 1), "peak_frac": round(tf / PEAK[op.dtype], 4),
                             "dtype": op.dtype, "alg_gb_s": round(op.alg_bytes / (ms * 1e-3) / 1e9, 1)}
         tr = traffic_for(op.kernel, op.name)
