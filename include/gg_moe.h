@@ -69,7 +69,7 @@ typedef enum {
     GG_ERR_ALIGN = 5,        /* a base pointer or row pitch is not 16-B aligned  */
     GG_ERR_MODE = 6,         /* not exactly one output (wgrad) / weight mode     */
     GG_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than required          */
-    GG_ERR_UNSUPPORTED = 8,  /* valid per the pages but outside this build       */
+    GG_ERR_UNSUPPORTED = 8,  /* valid per the pages but outside this library     */
     GG_ERR_DEVICE = 9,       /* no gfx950 device current                         */
     GG_ERR_HIP = 10,         /* a HIP runtime call failed                        */
     GG_ERR_OFFSETS = 11,     /* offsets rejected by GG_FLAG_VALIDATE_OFFSETS     */
