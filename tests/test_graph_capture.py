@@ -164,3 +164,38 @@ def test_wgrad_mx_graph_replays():
         torch.cuda.synchronize()
         say("wgrad_mx replay", r)
         assert torch.equal(out, want), f"replay {r} differs from the eager call"
+
+
+def test_dglu_mx_graph_replays():
+    b = lib()
+    x = synth.dglu_mx_inputs(2, 256, 64, [256, 512], seed=65, discrete=True, device="cuda")
+    M = x["padded_offsets"][-1].item()
+    bl = [t.view(torch.uint8) for t in x["b_list"]]
+    bp = torch.tensor([t.data_ptr() for t in bl], dtype=torch.int64, device="cuda")
+    sp = torch.tensor([t.data_ptr() for t in x["sfb_list"]], dtype=torch.int64, device="cuda")
+    dr = torch.empty(M, 128, dtype=torch.bfloat16, device="cuda")
+    dp = torch.zeros(M, dtype=torch.float32, device="cuda")
+    am = torch.empty(2, 2, dtype=torch.float32, device="cuda")
+    ws = torch.empty(b.gg_dglu_workspace_size(2, 64, 0), dtype=torch.uint8, device="cuda")
+
+    def call():
+        b.gg_dglu_mx(x["a"].view(torch.uint8), x["sfa"], None, None, bp, sp, 64, x["c"],
+                     x["padded_offsets"], x["alpha"], x["beta"], x["prob"], dr, dp, amax=am,
+                     workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    want_d, want_p, want_a = dr.clone(), dp.clone(), am.clone()
+    g = capture(call)
+    for r in range(REPLAYS):
+        dr.fill_(float("nan"))
+        dp.zero_()
+        am.fill_(-1.0)
+        eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        say("dglu_mx replay", r)
+        assert torch.equal(dr, want_d), f"replay {r}: D_row differs"
+        assert torch.equal(am, want_a), f"replay {r}: amax differs"
+        assert normwise(dp.double().cpu().numpy(), want_p.double().cpu().numpy()) <= 1e-6
+        assert b.gg_device_error(ws) == 0
