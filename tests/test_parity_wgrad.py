@@ -229,3 +229,30 @@ def test_moe_scale_output_modes(a_major, out):
         got = (res if outs is None else torch.stack(outs)).cpu()
         compare(got, inp_cpu, dt, accumulate, old if accumulate else None, hrows=rows,
                 name=f"wgrad_moe {out} {'accumulate' if accumulate else 'overwrite'}")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_shapes(case):
+    """Seeded random shapes through the persistent scheduler: hidden and
+    intermediate multiples of 64 up to 1024 (partial tiles; expert grids of
+    3-12 tiles, mostly not a multiple of 8, so the 1-D XCD remap, and one
+    of 8 tiles on the 4 x 2 XCD blocks; 63-420 items), 1-40 experts with
+    256-multiple counts (some empty), all majors and output dtypes, both
+    modes; every element against the oracle.  (A grid of fewer than 8
+    items is the 256 x 256, 4-expert workload above.)"""
+    rng = np.random.default_rng(900 + case)
+    h = int(rng.integers(1, 17)) * 64
+    i = int(rng.integers(1, 17)) * 64
+    E = int(rng.integers(1, 41))
+    counts = (rng.integers(0, 4, size=E) * 256).astype(np.int64)
+    if counts.sum() == 0:
+        counts[0] = 256
+    am, bm = ["k", "m"][case % 2], ["k", "n"][(case // 2) % 2]
+    dt = [torch.bfloat16, torch.float16, torch.float32][case % 3]
+    accumulate = bool(case % 4 == 3)
+    inp = synth.wgrad_inputs(h, i, counts, am, bm, seed=900 + case)
+    say("random shape", h, i, "experts", E, "tokens", int(counts.sum()), am, bm, dt, accumulate)
+    old = synth.wgrad_initial(E, h, i, dt, seed=950 + case) if accumulate else None
+    got, err = run_gpu(inp, dt, accumulate, old)
+    assert err == 0
+    compare(got, inp, dt, accumulate, old, name=f"random {case}")
