@@ -140,3 +140,26 @@ def test_workload_sampled(name):
         for g, (s, c) in enumerate(zip(starts, inp["counts"])):
             want[g] = dv[s:s + c].sum(0)
         assert_close(values(db), want, orc.BF16, f"{name} dbias vs sum of D")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_shapes(case):
+    """Seeded random shapes through the ping-pong main loop: K a multiple of
+    64 from 64 (a single load unit) to 1024, compact N a multiple of 32 up
+    to 640 (partial N tiles), 1-6 groups of 256-multiple rows (some empty),
+    rows past valid_m, dense or discrete K-/N-major B, both activations,
+    with or without dbias; every row against the oracle."""
+    rng = np.random.default_rng(800 + case)
+    K = int(rng.integers(1, 17)) * 64
+    N = int(rng.integers(1, 21)) * 32
+    L = int(rng.integers(1, 7))
+    counts = [int(c) * 256 for c in rng.integers(0, 3, size=L)]
+    if sum(counts) == 0:
+        counts[0] = 256
+    discrete = bool(case % 2)
+    b_major = "n" if (discrete and case % 4 == 3) else "k"
+    act = orc.DGEGLU if case % 3 == 0 else orc.DSWIGLU
+    inp = synth.dglu_inputs(L, K, N, counts, a_std=0.05, b_std=0.05, c_std=4.0, m_extra=64 * (case % 2),
+                            seed=800 + case, discrete=discrete, b_major=b_major)
+    check(inp, act, dbias=bool(case % 3 == 1), name=f"random {case}: K {K} N {N} L {L} {counts} "
+          f"{'discrete ' + b_major if discrete else 'dense'}")
