@@ -130,3 +130,34 @@ def test_workload_sampled():
     for g, (s, c) in enumerate(zip(starts, counts)):
         want = dv[s:s + c].max() if c else 0.0
         assert abs(amax[g].item() - want) <= 2.0 ** -8 * max(want, 1e-30), (g, amax[g].item(), want)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_shapes(case):
+    """Seeded random shapes: K a multiple of 128 from 128 to 2048 (1-16 load
+    units, scale groups cut short), compact N a multiple of 32 up to 640
+    (partial N tiles), 1-6 groups of 256-multiple rows (some empty), rows
+    past valid_m, dense or discrete B, spread scales; every row, dprob and
+    amax against the oracle."""
+    rng = np.random.default_rng(700 + case)
+    K = int(rng.integers(1, 17)) * 128
+    N = int(rng.integers(1, 21)) * 32
+    L = int(rng.integers(1, 7))
+    counts = [int(c) * 256 for c in rng.integers(0, 3, size=L)]
+    if sum(counts) == 0:
+        counts[0] = 256
+    inp = synth.dsrelu_inputs(L, K, N, counts, m_extra=64 * (case % 2), seed=700 + case,
+                              discrete=bool(case % 2), scale_spread=3)
+    say("dsrelu random", case, "K", K, "N", N, "L", L, counts)
+    d, dprob, amax, err = run_gpu(inp)
+    assert err == 0
+    ref = run_oracle(inp)
+    vm = inp["valid_m"]
+    assert_close(values(d[:vm]), ref["D"][:vm], orc.BF16, "D_row")
+    assert torch.all(torch.isnan(d[vm:]))
+    assert_close(values(dprob[:vm]), ref["dprob"][:vm], orc.F32, "dprob")
+    for g, c in enumerate(counts):
+        if c == 0:
+            assert amax[g] == 0.0, "an empty expert's amax is 0"
+        else:
+            assert abs(amax[g].item() - ref["amax"][g]) <= 1e-3 * ref["amax"][g]
