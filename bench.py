@@ -539,6 +539,10 @@ def main():
         tr = traffic_for(op.kernel, op.name)
         kernels[op.name]["hbm_gb_per_launch"] = None if tr is None else round(tr / 1e9, 3)
         kernels[op.name]["bound"] = bound_of(op)
+        # the roofline time (the larger of the MFMA-peak and HBM-peak times)
+        # over the measured time
+        t_roof = max(op.flops / (PEAK[op.dtype] * 1e12), op.alg_bytes / (HBM_PEAK * 1e9))
+        kernels[op.name]["roofline_frac"] = round(t_roof / (ms * 1e-3), 4)
     total_flops = sum(op.flops for op in ops)
     value = total_flops / (ms_step * 1e-3) / 1e12
     dom = max(ops, key=lambda o: kernels[o.name]["ms"])
