@@ -24,11 +24,11 @@
  *
  * Arithmetic: every input is decoded exactly into double; every sum is taken
  * in double in the plain index order; outputs are rounded once, to nearest
- * even, by the encoders below.  The deliberate fp32 steps are X = beta*C of
+ * even, by the encoders below.  The one deliberate fp32 step is X = beta*C of
  * [G], formed as a single fp32 product, because the clamp and filter tests of
- * dGeGLU compare X with +-7 and the product is what the method feeds them;
- * and the FP8 output quantization of step 3, whose integer scale exponent is
- * decided in the fp32 arithmetic of the kernels' epilogue.
+ * dGeGLU compare X with +-7 and the product is what the method feeds them.
+ * The FP8 output quantization of step 3 decides its scale exponents and
+ * codes exactly, from the double D.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  */
@@ -164,15 +164,38 @@ float orc_double_to_f32(double x) {
 }
 
 /* OCP E4M3 ("float8_e4m3fn": 4 significand bits, minimum normal exponent
- * -6, largest finite 448, no infinity) by round-to-nearest-even, with
- * magnitudes above 448 clamped to 448 first (the quantizer below never
- * produces them but for rounding in its scale computation). */
-uint8_t orc_double_to_e4m3(double x) {
-    if (isnan(x))
+ * -6, largest finite 448, no infinity) of the exact value hi + lo, where lo
+ * is the rounding error of hi (|lo| <= half an ulp of hi, the same sign
+ * convention as the value), by round-to-nearest-even; magnitudes above 448
+ * are clamped to 448 first.  hi is the double nearest to the value, so the
+ * value and hi fall on the same side of every E4M3 rounding midpoint except
+ * when hi is that midpoint: then lo decides the direction. */
+static uint8_t e4m3_of_sum(double hi, double lo) {
+    if (isnan(hi))
         return 0x7f;
-    uint8_t s = signbit(x) ? 0x80u : 0u;
-    double ax = fabs(x);
-    double y = round_format(ax > 448.0 ? 448.0 : ax, 4, -6, 448.0);
+    uint8_t s = signbit(hi) ? 0x80u : 0u;
+    double ax = fabs(hi), alo = signbit(hi) ? -lo : lo;   /* value = ax + alo, >= 0 */
+    double y;
+    if (ax >= 448.0) {
+        y = 448.0;
+    } else if (ax == 0.0) {
+        y = 0.0;
+    } else {
+        int E;
+        frexp(ax, &E);
+        int e = E - 1 < -6 ? -6 : E - 1;          /* ax in [2^e, 2^(e+1)) or subnormal */
+        int ulp = e - 3;
+        double q = ldexp(ax, -ulp);               /* exact */
+        double fl = floor(q);
+        double r;
+        if (q - fl == 0.5 && alo != 0.0)
+            r = alo > 0.0 ? fl + 1.0 : fl;        /* the value lies off the midpoint */
+        else
+            r = nearbyint(q);                     /* ties to even */
+        y = ldexp(r, ulp);
+        if (y > 448.0)
+            y = 448.0;
+    }
     if (y == 0.0)
         return s;
     int E;
@@ -184,34 +207,47 @@ uint8_t orc_double_to_e4m3(double x) {
     return s | (uint8_t)(((e + 7) << 3) | m);
 }
 
+uint8_t orc_double_to_e4m3(double x) { return e4m3_of_sum(x, 0.0); }
+
 /* [G] "Block-scaled contract / Equations", step 3 (and the FP8 D_row / D_col
  * with SFD_row / SFD_col of [S] "Shapes"): blocks of 32 values (32 columns of
  * a row for D_row, 32 rows of a column for D_col) share one E8M0 scale
  *   SFD = norm_const * max|D| * rcp_max,   D_q = D * norm_const / SFD,
  * with rcp_max = 1/448 (E4M3).  E8M0 holds powers of two only: SFD is taken
  * as the smallest power of two 2^e not below the product (so |D_q| <= 448),
- * e clamped to [-127, 127], e = -127 for an all-zero block.  The scale
- * exponent is an integer decided by floating point, so it is decided in the
- * precision of the kernel's epilogue: D rounded to fp32, the product formed
- * as fp32(fp32(norm_const * amax) * fp32(1/448)); D_q = e4m3(fp32(D * nc)
- * * 2^-e).  Returns e. */
-static int fp8_block_exponent(float amax, float norm_const) {
-    const float rcp_max = 1.0f / 448.0f;
-    volatile float t = norm_const * amax;      /* one fp32 rounding each */
-    volatile float x = t * rcp_max;
-    if (!(x > 0.0f))
+ * e clamped to [-127, 127], e = -127 for an all-zero block.  Both the
+ * exponent and the codes are decided in exact arithmetic on the double D:
+ * no intermediate rounding of D, of the product or of the quotient. */
+
+/* Smallest integer e with 2^e >= norm_const * amax / 448, exactly: with
+ * amax = ia 2^(ea-53) and norm_const = in 2^(en-24) (integer significands
+ * from frexp; a float's fits 24 bits, a double's 53), the condition reads
+ * 7 * 2^(e + 83 - ea - en) >= ia * in, a comparison of integers below 2^80. */
+static int fp8_block_exponent(double amax, float norm_const) {
+    double nc = (double)norm_const;
+    if (!(amax > 0.0) || !(nc > 0.0))
         return -127;
-    if (isinf(x))
+    if (isinf(amax) || isinf(nc))
         return 127;
-    int E;
-    float f = frexpf(x, &E);                   /* x = f * 2^E, f in [0.5, 1) */
-    int e = (f == 0.5f) ? E - 1 : E;           /* smallest e with 2^e >= x */
+    int ea, en;
+    double fa = frexp(amax, &ea), fn = frexp(nc, &en);
+    unsigned __int128 prod = (unsigned __int128)(uint64_t)ldexp(fa, 53) *
+                             (unsigned __int128)(uint64_t)ldexp(fn, 24);
+    int s = 0;
+    while (((unsigned __int128)7 << s) < prod)
+        s++;
+    int e = s - 83 + ea + en;
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+/* E4M3 code of d * norm_const * 2^-e: the product is split exactly into
+ * its double rounding and that rounding's error (a fused multiply-add
+ * recovers the error exactly), and scaling by 2^-e is exact. */
 static uint8_t fp8_quantize(double d, float norm_const, int e) {
-    volatile float v = (float)d * norm_const;  /* fp32(D) * nc, one rounding */
-    return orc_double_to_e4m3((double)ldexpf(v, -e));
+    double nc = (double)norm_const;
+    double hi = d * nc;
+    double lo = fma(d, nc, -hi);
+    return e4m3_of_sum(ldexp(hi, -e), ldexp(lo, -e));
 }
 
 /* D (nrows, W) doubles, W a multiple of 32.  q_row (nrows, W) E4M3 and
@@ -223,9 +259,9 @@ void orc_quant_fp8(const double* D, int64_t nrows, int W, float norm_const,
     int WB = W / 32;
     for (int64_t r = 0; r < nrows; r++)
         for (int b = 0; b < WB; b++) {
-            float amax = 0.0f;
+            double amax = 0.0;
             for (int k = 0; k < 32; k++) {
-                float v = fabsf((float)D[r * W + 32 * b + k]);
+                double v = fabs(D[r * W + 32 * b + k]);
                 amax = v > amax ? v : amax;
             }
             int e = fp8_block_exponent(amax, norm_const);
@@ -238,9 +274,9 @@ void orc_quant_fp8(const double* D, int64_t nrows, int W, float norm_const,
     int64_t RB = nrows / 32;
     for (int c = 0; c < W; c++)
         for (int64_t j = 0; j < RB; j++) {
-            float amax = 0.0f;
+            double amax = 0.0;
             for (int k = 0; k < 32; k++) {
-                float v = fabsf((float)D[(32 * j + k) * W + c]);
+                double v = fabs(D[(32 * j + k) * W + c]);
                 amax = v > amax ? v : amax;
             }
             int e = fp8_block_exponent(amax, norm_const);
@@ -328,22 +364,30 @@ void orc_wgrad_mx(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const 
     for (int e = 0; e < E; e++) {
         int64_t begin = e ? offsets[e - 1] : 0;
         int64_t end = offsets[e];
+        int64_t cnt = end > begin ? end - begin : 0;
+        /* the expert's B values, dequantized once: Bd[(t - begin)*inter + i] */
+        double* Bd = (double*)malloc(sizeof(double) * (size_t)(cnt * inter > 0 ? cnt * inter : 1));
+#pragma omp parallel for schedule(static)
+        for (int i = 0; i < inter; i++)
+            for (int64_t t = begin; t < end; t++)
+                Bd[(t - begin) * inter + i] = orc_e4m3_to_double(B[(int64_t)i * T + t]) *
+                                              orc_e8m0_to_double(SFB[(int64_t)i * TB + t / 32]);
 #pragma omp parallel for schedule(dynamic, 1)
         for (int r = 0; r < nrows; r++) {
             int h = hrows ? hrows[r] : r;
             double* o = out + ((int64_t)e * nrows + r) * inter;
+            /* o[i] = sum over t = begin .. end-1, in that order, of A(h,t) B(t,i) */
             for (int i = 0; i < inter; i++)
                 o[i] = 0.0;
             for (int64_t t = begin; t < end; t++) {
                 double av = orc_e4m3_to_double(A[(int64_t)h * T + t]) *
                             orc_e8m0_to_double(SFA[(int64_t)h * TB + t / 32]);
-                for (int i = 0; i < inter; i++) {
-                    double bv = orc_e4m3_to_double(B[(int64_t)i * T + t]) *
-                                orc_e8m0_to_double(SFB[(int64_t)i * TB + t / 32]);
-                    o[i] += av * bv;
-                }
+                const double* bt = Bd + (t - begin) * inter;
+                for (int i = 0; i < inter; i++)
+                    o[i] += av * bt[i];
             }
         }
+        free(Bd);
     }
 }
 
@@ -487,6 +531,40 @@ static void dglu_dbias(const double* D, const int32_t* po, int L, int N, const i
     }
 }
 
+/* The listed rows (indices r into the row list) that belong to group g, in
+ * list order; returns their count.  grp[r] holds each listed row's group. */
+static int64_t rows_of_group(const int* grp, int64_t nrows, int g, int64_t* idx) {
+    int64_t n = 0;
+    for (int64_t r = 0; r < nrows; r++)
+        if (grp[r] == g)
+            idx[n++] = r;
+    return n;
+}
+
+static int* groups_of_rows(const int32_t* po, int L, const int64_t* rows, int64_t nrows) {
+    int* grp = (int*)malloc(sizeof(int) * (size_t)(nrows > 0 ? nrows : 1));
+    for (int64_t r = 0; r < nrows; r++)
+        grp[r] = group_of_row(po, L, rows ? rows[r] : r);
+    return grp;
+}
+
+/* R_g[m, n] = a2 * sum over k = 0 .. K-1, in that order, of Ad[k] * Bt[k*N + n],
+ * for one row (Ad: its K values; Bt: the group's B values as a (K, N)
+ * array).  Every R[n] adds its terms in increasing k; the k loop is outside
+ * so that Bt's rows are read in order. */
+static void row_product(const double* Ad, const double* Bt, int K, int N, double a2, double* R) {
+    for (int n = 0; n < N; n++)
+        R[n] = 0.0;
+    for (int k = 0; k < K; k++) {
+        double av = Ad[k];
+        const double* bk = Bt + (int64_t)k * N;
+        for (int n = 0; n < N; n++)
+            R[n] += av * bk[n];
+    }
+    for (int n = 0; n < N; n++)
+        R[n] *= a2;
+}
+
 void orc_dglu(const uint16_t* A, int64_t M, int K,
               const uint16_t* const* Bp, int b_major, int N,
               const void* C, int c_dtype, const int32_t* po, int L,
@@ -498,32 +576,44 @@ void orc_dglu(const uint16_t* A, int64_t M, int K,
     if (!rows)
         nrows = M;
     int64_t N2 = 2 * (int64_t)N;
+    int* grp = groups_of_rows(po, L, rows, nrows);
+    int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nrows > 0 ? nrows : 1));
+    double* Bt = (double*)malloc(sizeof(double) * (size_t)K * (size_t)N);
+    for (int g = 0; g < L; g++) {
+        int64_t cnt = rows_of_group(grp, nrows, g, idx);
+        if (cnt == 0)
+            continue;
+        /* expert g's B as a (K, N) array of exact values */
+        const uint16_t* Bg = Bp[g];
+#pragma omp parallel for schedule(static)
+        for (int k = 0; k < K; k++)
+            for (int n = 0; n < N; n++)
+                Bt[(int64_t)k * N + n] = orc_bf16_to_double(
+                    Bg[b_major == 0 ? (int64_t)n * K + k : (int64_t)k * N + n]);
+        double a2 = (double)alpha[g] * (double)alpha[g];
 #pragma omp parallel
-    {
-        double* R = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        {
+            double* R = (double*)malloc(sizeof(double) * (size_t)N);
+            double* Ad = (double*)malloc(sizeof(double) * (size_t)K);
 #pragma omp for schedule(dynamic, 4)
-        for (int64_t r = 0; r < nrows; r++) {
-            int64_t m = rows ? rows[r] : r;
-            int g = group_of_row(po, L, m);
-            if (g < 0)
-                continue;
-            const uint16_t* Bg = Bp[g];
-            double a2 = (double)alpha[g] * (double)alpha[g];
-            for (int n = 0; n < N; n++) {
+            for (int64_t j = 0; j < cnt; j++) {
+                int64_t r = idx[j];
+                int64_t m = rows ? rows[r] : r;
+                for (int k = 0; k < K; k++)
+                    Ad[k] = orc_bf16_to_double(A[m * K + k]);
                 /* R_g[m, n] = alpha_g^2 * sum_k A[m,k] * B_g[n,k] */
-                double acc = 0.0;
-                for (int k = 0; k < K; k++) {
-                    int64_t ib = b_major == 0 ? (int64_t)n * K + k : (int64_t)k * N + n;
-                    acc += orc_bf16_to_double(A[m * K + k]) * orc_bf16_to_double(Bg[ib]);
-                }
-                R[n] = a2 * acc;
+                row_product(Ad, Bt, K, N, a2, R);
+                dprob_sum[r] = dglu_row(R, m, g, N, C, c_dtype, beta, prob, act, ga, clamp_lo,
+                                        clamp_hi, lo, 0.0, 0.0, gate_first, mask_filter,
+                                        D + r * N2);
             }
-            dprob_sum[r] = dglu_row(R, m, g, N, C, c_dtype, beta, prob, act, ga, clamp_lo,
-                                    clamp_hi, lo, 0.0, 0.0, gate_first, mask_filter,
-                                    D + r * N2);
+            free(R);
+            free(Ad);
         }
-        free(R);
     }
+    free(Bt);
+    free(idx);
+    free(grp);
     if (dbias_sum)
         dglu_dbias(D, po, L, N, rows, nrows, dbias_sum);
 }
@@ -550,35 +640,45 @@ void orc_dglu_mx(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
         nrows = M;
     int64_t N2 = 2 * (int64_t)N;
     int KB = K / 32;
+    int* grp = groups_of_rows(po, L, rows, nrows);
+    int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nrows > 0 ? nrows : 1));
+    double* Bt = (double*)malloc(sizeof(double) * (size_t)K * (size_t)N);
+    for (int g = 0; g < L; g++) {
+        int64_t cnt = rows_of_group(grp, nrows, g, idx);
+        if (cnt == 0)
+            continue;
+        /* expert g's dequantized B as a (K, N) array */
+        const uint8_t* Bg = Bp[g];
+        const uint8_t* Sg = SFBp[g];
+#pragma omp parallel for schedule(static)
+        for (int k = 0; k < K; k++)
+            for (int n = 0; n < N; n++)
+                Bt[(int64_t)k * N + n] = orc_e4m3_to_double(Bg[(int64_t)n * K + k]) *
+                                         orc_e8m0_to_double(Sg[(int64_t)n * KB + k / 32]);
+        double a2 = (double)alpha[g] * (double)alpha[g];
 #pragma omp parallel
-    {
-        double* R = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        {
+            double* R = (double*)malloc(sizeof(double) * (size_t)N);
+            double* Ad = (double*)malloc(sizeof(double) * (size_t)K);
 #pragma omp for schedule(dynamic, 4)
-        for (int64_t r = 0; r < nrows; r++) {
-            int64_t m = rows ? rows[r] : r;
-            int g = group_of_row(po, L, m);
-            if (g < 0)
-                continue;
-            const uint8_t* Bg = Bp[g];
-            const uint8_t* Sg = SFBp[g];
-            double a2 = (double)alpha[g] * (double)alpha[g];
-            for (int n = 0; n < N; n++) {
-                double acc = 0.0;
-                for (int k = 0; k < K; k++) {
-                    double da = orc_e4m3_to_double(A[m * K + k]) *
-                                orc_e8m0_to_double(SFA[m * KB + k / 32]);
-                    double db = orc_e4m3_to_double(Bg[(int64_t)n * K + k]) *
-                                orc_e8m0_to_double(Sg[(int64_t)n * KB + k / 32]);
-                    acc += da * db;
-                }
-                R[n] = a2 * acc;
+            for (int64_t j = 0; j < cnt; j++) {
+                int64_t r = idx[j];
+                int64_t m = rows ? rows[r] : r;
+                for (int k = 0; k < K; k++)
+                    Ad[k] = orc_e4m3_to_double(A[m * K + k]) *
+                            orc_e8m0_to_double(SFA[m * KB + k / 32]);
+                row_product(Ad, Bt, K, N, a2, R);
+                dprob_sum[r] = dglu_row(R, m, g, N, C, c_dtype, beta, prob, act, ga, clamp_lo,
+                                        clamp_hi, lo, situ_b1, situ_b2, gate_first, mask_filter,
+                                        D + r * N2);
             }
-            dprob_sum[r] = dglu_row(R, m, g, N, C, c_dtype, beta, prob, act, ga, clamp_lo,
-                                    clamp_hi, lo, situ_b1, situ_b2, gate_first, mask_filter,
-                                    D + r * N2);
+            free(R);
+            free(Ad);
         }
-        free(R);
     }
+    free(Bt);
+    free(idx);
+    free(grp);
     if (dbias_sum)
         dglu_dbias(D, po, L, N, rows, nrows, dbias_sum);
     for (int64_t r = 0; r < nrows; r++) {
@@ -624,34 +724,51 @@ void orc_dsrelu(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
     if (!rows)
         nrows = M;
     int KB = K / 32;
-#pragma omp parallel for schedule(dynamic, 4)
-    for (int64_t r = 0; r < nrows; r++) {
-        int64_t m = rows ? rows[r] : r;
-        int g = group_of_row(po, L, m);
-        if (g < 0)
+    int* grp = groups_of_rows(po, L, rows, nrows);
+    int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nrows > 0 ? nrows : 1));
+    double* Bt = (double*)malloc(sizeof(double) * (size_t)K * (size_t)N);
+    for (int g = 0; g < L; g++) {
+        int64_t cnt = rows_of_group(grp, nrows, g, idx);
+        if (cnt == 0)
             continue;
+        /* expert g's dequantized B as a (K, N) array */
         const uint8_t* Bg = Bp[g];
         const uint8_t* Sg = SFBp[g];
-        double pr = (double)prob[m];
-        double dp = 0.0;
-        for (int n = 0; n < N; n++) {
-            double acc = 0.0;
-            for (int k = 0; k < K; k++) {
-                double da = orc_e4m3_to_double(A[m * K + k]) *
+#pragma omp parallel for schedule(static)
+        for (int k = 0; k < K; k++)
+            for (int n = 0; n < N; n++)
+                Bt[(int64_t)k * N + n] = orc_e4m3_to_double(Bg[(int64_t)n * K + k]) *
+                                         orc_e8m0_to_double(Sg[(int64_t)n * KB + k / 32]);
+#pragma omp parallel
+        {
+            double* G = (double*)malloc(sizeof(double) * (size_t)N);
+            double* Ad = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t j = 0; j < cnt; j++) {
+                int64_t r = idx[j];
+                int64_t m = rows ? rows[r] : r;
+                for (int k = 0; k < K; k++)
+                    Ad[k] = orc_e4m3_to_double(A[m * K + k]) *
                             orc_e8m0_to_double(SFA[m * KB + k / 32]);
-                double db = orc_e4m3_to_double(Bg[(int64_t)n * K + k]) *
-                            orc_e8m0_to_double(Sg[(int64_t)n * KB + k / 32]);
-                acc += da * db;
+                /* G[m, n] = alpha_g * sum_k deq(A[m,k]) * deq(B_g[n,k]) */
+                row_product(Ad, Bt, K, N, (double)alpha[g], G);
+                double pr = (double)prob[m];
+                double dp = 0.0;
+                for (int n = 0; n < N; n++) {
+                    double rl = G[n] > 0.0 ? G[n] : 0.0;
+                    double c = orc_decode(C, c_dtype, m * (int64_t)N + n);
+                    D[r * (int64_t)N + n] = pr * 2.0 * c * rl;
+                    dp += c * rl * rl;
+                }
+                dprob_sum[r] = dp;
             }
-            double G = (double)alpha[g] * acc;
-            double rl = G > 0.0 ? G : 0.0;
-            double c = orc_decode(C, c_dtype, m * (int64_t)N + n);
-            double d = pr * 2.0 * c * rl;
-            D[r * (int64_t)N + n] = d;
-            dp += c * rl * rl;
+            free(G);
+            free(Ad);
         }
-        dprob_sum[r] = dp;
     }
+    free(Bt);
+    free(idx);
+    free(grp);
     for (int64_t r = 0; r < nrows; r++) {
         int64_t m = rows ? rows[r] : r;
         int g = group_of_row(po, L, m);
