@@ -142,10 +142,25 @@ def gg_dsrelu_workspace_size(L):
     return load_library().gg_dsrelu_workspace_size(L)
 
 
-def _workspace(ws, nbytes, like):
+def _torch_stream(stream):
+    """The torch stream object of a call's stream argument (None: the current
+    stream; an int: the raw hipStream_t)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
+def _workspace(ws, nbytes, like, stream):
+    """The caller's workspace, or a new one allocated on the stream the call
+    runs on: torch's caching allocator ties a freed block to the stream it
+    was allocated on, so a workspace the caller drops is not handed to work
+    on another stream while this call's kernels may still use it."""
     if ws is not None:
         return ws, ws.numel() * ws.element_size()
-    t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=like.device)
+    with torch.cuda.stream(_torch_stream(stream)):
+        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=like.device)
     return t, t.numel()
 
 
@@ -164,7 +179,7 @@ def gg_wgrad(a, a_major, b, b_major, offsets, tokens_sum, hidden, intermediate,
     E = offsets.numel()
     if wgrad_dtype is None:
         wgrad_dtype = _TORCH_DTYPE[wgrad_dense.dtype]
-    ws, nbytes = _workspace(workspace, L.gg_wgrad_workspace_size(E), offsets)
+    ws, nbytes = _workspace(workspace, L.gg_wgrad_workspace_size(E), offsets, stream)
     _check(L.gg_wgrad(_ptr(a), a_major, _ptr(b), b_major, _ptr(offsets), E, tokens_sum, hidden,
                       intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
                       int(bool(accumulate)), flags, _ptr(ws), nbytes, _stream(stream)))
@@ -180,7 +195,7 @@ def gg_wgrad_mx(a, sfa, b, sfb, offsets, tokens_sum, hidden, intermediate, wgrad
     E = offsets.numel()
     if wgrad_dtype is None:
         wgrad_dtype = _TORCH_DTYPE[wgrad_dense.dtype]
-    ws, nbytes = _workspace(workspace, L.gg_wgrad_workspace_size(E), offsets)
+    ws, nbytes = _workspace(workspace, L.gg_wgrad_workspace_size(E), offsets, stream)
     _check(L.gg_wgrad_mx(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(offsets), E, tokens_sum,
                          hidden, intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
                          int(bool(accumulate)), flags, _ptr(ws), nbytes, _stream(stream)))
@@ -194,7 +209,7 @@ def gg_dglu(a, b_dense, b_ptrs, b_major, n, c, padded_offsets, alpha, beta, prob
     workspace used."""
     L = load_library()
     nl = padded_offsets.numel()
-    ws, nbytes = _workspace(workspace, L.gg_dglu_workspace_size(nl, n, dbias is not None), a)
+    ws, nbytes = _workspace(workspace, L.gg_dglu_workspace_size(nl, n, dbias is not None), a, stream)
     _check(L.gg_dglu(_ptr(a), a.shape[0], a.shape[1], _ptr(b_dense), _ptr(b_ptrs), b_major, n,
                      _ptr(c), _TORCH_DTYPE[c.dtype], _ptr(padded_offsets), nl, _ptr(alpha),
                      _ptr(beta), _ptr(prob), _ptr(d_row), _TORCH_DTYPE[d_row.dtype], _ptr(dprob),
@@ -214,7 +229,7 @@ def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, be
     q = _fp8_out(fp8_out)
     L = load_library()
     nl = padded_offsets.numel()
-    ws, nbytes = _workspace(workspace, L.gg_dglu_workspace_size(nl, n, dbias is not None), a)
+    ws, nbytes = _workspace(workspace, L.gg_dglu_workspace_size(nl, n, dbias is not None), a, stream)
     _check(L.gg_dglu_mx(_ptr(a), _ptr(sfa), a.shape[0], a.shape[1], _ptr(b), _ptr(sfb),
                         _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
                         _ptr(padded_offsets), nl, _ptr(alpha), _ptr(beta), _ptr(prob),
@@ -231,7 +246,7 @@ def gg_dsrelu(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, pro
     q = _fp8_out(fp8_out)
     L = load_library()
     nl = padded_offsets.numel()
-    ws, nbytes = _workspace(workspace, L.gg_dsrelu_workspace_size(nl), a)
+    ws, nbytes = _workspace(workspace, L.gg_dsrelu_workspace_size(nl), a, stream)
     _check(L.gg_dsrelu(_ptr(a), _ptr(sfa), a.shape[0], a.shape[1], _ptr(b), _ptr(sfb),
                        _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
                        _ptr(padded_offsets), nl, _ptr(alpha), _ptr(prob), _ptr(d_row),

@@ -29,8 +29,13 @@ namespace gg {
 // arithmetic is a good share of the dGLU kernels' time.
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
-// tanh(x) = 2 sigmoid(2x) - 1 (exact at +-inf: +-1).
-__device__ __forceinline__ float tanhf_(float x) { return 2.0f * sigmoidf_(2.0f * x) - 1.0f; }
+// tanh(x) from u = expm1(-2|x|) in (-1, 0]: tanh|x| = -u / (u + 2).  No
+// cancellation for small |x| (expm1 keeps u's relative accuracy where
+// exp(-2|x|) is close to 1), no overflow for large |x| (u tends to -1).
+__device__ __forceinline__ float tanhf_(float x) {
+    const float u = expm1f(-2.0f * fabsf(x));
+    return copysignf(-u * __builtin_amdgcn_rcpf(u + 2.0f), x);
+}
 
 // X = beta * C as a single fp32 product: no contraction into a later FMA, so
 // the clamp / filter comparisons see exactly the rounded product.

@@ -5,8 +5,9 @@ rows past valid_m; they cover dSwiGLU and dGeGLU (value and mask filters),
 dense / discrete K-major / discrete N-major B, the gate-first order, dbias,
 and C/D dtypes.  The two named workloads (dSwiGLU: L 8, K 2048, N 1024,
 M 16384; dGeGLU: L 32, K 4096, N 1536, M 32768, discrete B, dbias) run at
-full size in the bench's launch configuration and are checked on sampled
-rows, dbias by the per-expert column sums of the kernel's own D.
+full size in the bench's launch configuration: every row of the dSwiGLU
+workload, and for dGeGLU sampled rows of every group plus every row and the
+dbias of its small groups, all against the oracle.
 """
 import numpy as np
 import pytest
@@ -115,31 +116,58 @@ def _full(name, device="cuda"):
                              device=device, discrete=w["discrete"]), w
 
 
-@pytest.mark.parametrize("name", ["dswiglu", "dgeglu"])
-def test_workload_sampled(name):
-    inp, w = _full(name)
-    act = orc.DSWIGLU if w["act"] == "dswiglu" else orc.DGEGLU
-    say(name, "counts", inp["counts"].tolist())
-    d, dprob, db, err = run_gpu(inp, act, dbias=w["dbias"])
+def test_workload_dswiglu_every_row():
+    """The dSwiGLU workload at full size (L 8, K 2048, N 1024, M 16384): every
+    row of D and dprob against the oracle, whole and per expert."""
+    inp, w = _full("dswiglu")
+    say("dswiglu counts", inp["counts"].tolist())
+    d, dprob, _, err = run_gpu(inp, orc.DSWIGLU)
     assert err == 0
     cpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     cpu["b_list"] = [x.cpu() for x in inp["b_list"]]
-    starts = np.concatenate([[0], np.cumsum(inp["counts"])[:-1]])
-    rows = []
-    for s, c in zip(starts, inp["counts"]):
+    ref = run_oracle(cpu, orc.DSWIGLU)
+    assert_close(values(d), ref["D"], orc.BF16, "dswiglu D_row (every row)")
+    assert_close(values(dprob), ref["dprob"], orc.F32, "dswiglu dprob (every row)")
+    start = 0
+    for g, c in enumerate(inp["counts"]):
         if c:
-            rows += [s, s + 1, s + c - 1]
-    rows = np.array(sorted(set(rows)), np.int64)
-    ref = run_oracle(cpu, act, rows=rows)
-    assert_close(values(d[rows]), ref["D"], orc.BF16, f"{name} D_row (sampled rows)")
-    assert_close(values(dprob[rows]), ref["dprob"], orc.F32, f"{name} dprob (sampled rows)")
-    if w["dbias"]:
-        # dbias against the per-expert column sums of the kernel's own D
-        dv = values(d)
-        want = np.zeros((inp["L"], 2 * inp["N"]))
-        for g, (s, c) in enumerate(zip(starts, inp["counts"])):
-            want[g] = dv[s:s + c].sum(0)
-        assert_close(values(db), want, orc.BF16, f"{name} dbias vs sum of D")
+            e = normwise(values(d[start:start + c]), ref["D"][start:start + c])
+            assert e <= TOL[orc.BF16], f"group {g}: {e:.3e}"
+        start += c
+
+
+def test_workload_dgeglu():
+    """The dGeGLU workload at full size (L 32, K 4096, N 1536, M 32768,
+    discrete B, dbias): the first, second and last rows of every group, and
+    every row of the groups of at most 512 rows (its three 256-row groups
+    among them), against the oracle; those groups' dbias (the per-expert row
+    reduction of D) against the oracle's, and the empty group's dbias exactly
+    zero."""
+    inp, w = _full("dgeglu")
+    counts = inp["counts"]
+    say("dgeglu counts", counts.tolist())
+    d, dprob, db, err = run_gpu(inp, orc.DGEGLU, dbias=True)
+    assert err == 0
+    cpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    cpu["b_list"] = [x.cpu() for x in inp["b_list"]]
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    whole = [g for g, c in enumerate(counts) if 0 < c <= 512]
+    assert sum(1 for g in whole if counts[g] == 256) == 3
+    rows = set()
+    for g, (s, c) in enumerate(zip(starts, counts)):
+        if g in whole:
+            rows.update(range(s, s + c))
+        elif c:
+            rows.update([s, s + 1, s + c - 1])
+    rows = np.array(sorted(rows), np.int64)
+    ref = run_oracle(cpu, orc.DGEGLU, dbias=True, rows=rows)
+    assert_close(values(d[rows]), ref["D"], orc.BF16, "dgeglu D_row (listed rows)")
+    assert_close(values(dprob[rows]), ref["dprob"], orc.F32, "dgeglu dprob (listed rows)")
+    for g in whole:
+        assert_close(values(db[g]), ref["dbias"][g], orc.BF16, f"dgeglu dbias of group {g} ({counts[g]} rows)")
+    for g, c in enumerate(counts):
+        if c == 0:
+            assert torch.all(db[g] == 0), "an empty group's dbias must stay zero"
 
 
 @pytest.mark.parametrize("case", range(9))

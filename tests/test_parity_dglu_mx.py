@@ -5,8 +5,9 @@ valid_m, per-row scale spreads, dense and discrete (b_ptrs / sfb_ptrs) B,
 all three activations (dSiTU-GLU with default and small tanh scales), the
 gate-first and mask-filter flags, dbias, and C/D dtypes; the MoE-scale
 workload (L 32, K 4096, N 1536, M 32768, discrete B) runs at full size in
-the bench's launch configuration and is checked on sampled rows, the amax
-halves against the maxima of the kernel's own D.
+the bench's launch configuration and is checked against the oracle on
+sampled rows of every group and on every row and the amax halves of its
+256-row groups.
 """
 import numpy as np
 import pytest
@@ -164,6 +165,11 @@ def test_unit_scales_no_amax():
 
 
 def test_workload_sampled():
+    """The block-scaled dGLU workload at full size (L 32, K 4096, N 1536,
+    M 32768, discrete B and SFB): the first and last rows of every group and
+    every row of its 256-row groups against the oracle; those groups' amax
+    halves equal the oracle's, every other group's are at least the oracle's
+    |D| on its listed rows."""
     w = synth.WORKLOADS["dglu_mxfp8"]
     counts = synth.workload_counts("dglu_mxfp8")
     inp = synth.dglu_mx_inputs(w["L"], w["K"], w["N"], counts, c_std=w["c_std"], seed=w["seed"],
@@ -175,19 +181,23 @@ def test_workload_sampled():
     cpu["b_list"] = [x.cpu() for x in inp["b_list"]]
     cpu["sfb_list"] = [x.cpu() for x in inp["sfb_list"]]
     starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
-    rows = []
-    for s, c in zip(starts, counts):
-        if c:
-            rows += [s, s + c - 1]
-    rows = np.array(sorted(set(rows)), np.int64)
-    ref = run_oracle(cpu, rows=rows)
-    assert_close(values(got["d"][rows]), ref["D"], orc.BF16, "D_row (sampled rows)")
-    assert_close(values(got["dprob"][rows]), ref["dprob"], orc.F32, "dprob (sampled rows)")
-    # amax halves against the kernel's own D (bf16-rounded: within 2^-8 relative)
-    dv = np.abs(values(got["d"]))
-    cin, cgt = column_maps(w["N"])
-    amax = got["amax"].numpy()
+    whole = [g for g, c in enumerate(counts) if c == 256]
+    assert whole
+    rows = set()
     for g, (s, c) in enumerate(zip(starts, counts)):
-        for h, cols in enumerate((cin, cgt)):
-            want = dv[s:s + c][:, cols].max() if c else 0.0
-            assert abs(amax[g, h] - want) <= 2.0 ** -8 * max(want, 1e-30), (g, h, amax[g, h], want)
+        if g in whole:
+            rows.update(range(s, s + c))
+        elif c:
+            rows.update([s, s + c - 1])
+    rows = np.array(sorted(rows), np.int64)
+    ref = run_oracle(cpu, rows=rows)
+    assert_close(values(got["d"][rows]), ref["D"], orc.BF16, "D_row (listed rows)")
+    assert_close(values(got["dprob"][rows]), ref["dprob"], orc.F32, "dprob (listed rows)")
+    amax = got["amax"].numpy().astype(np.float64)
+    for g, c in enumerate(counts):
+        for h in range(2):
+            if g in whole:
+                assert abs(amax[g, h] - ref["amax"][g, h]) <= 1e-3 * ref["amax"][g, h], \
+                    (g, h, amax[g, h], ref["amax"][g, h])
+            elif c:
+                assert amax[g, h] >= ref["amax"][g, h] * (1 - 1e-3), (g, h, amax[g, h], ref["amax"][g, h])

@@ -3,8 +3,8 @@
 Small cases span several tiles, a partial N tile, an empty group, rows past
 valid_m, per-row scale spreads, dense and discrete B, and C/D dtypes; the
 MoE-scale workload (L 16, K 7168, N 2048, M 65536) runs at full size in the
-bench's launch configuration and is checked on sampled rows, Amax against
-the maximum of the kernel's own D per expert.
+bench's launch configuration and is checked against the oracle on sampled
+rows of every group and on every row and the Amax of a smallest group.
 """
 import numpy as np
 import pytest
@@ -107,6 +107,11 @@ def test_unit_scales_no_amax():
 
 
 def test_workload_sampled():
+    """The dsReLU workload at full size (L 16, K 7168, N 2048, M 65536): the
+    first and last rows of every group and every row of a smallest group
+    (2816 rows) against the oracle; that group's Amax equals the oracle's,
+    and every other group's Amax is at least the oracle's |D| on its listed
+    rows."""
     w = synth.WORKLOADS["dsrelu_mxfp8"]
     counts = synth.workload_counts("dsrelu_mxfp8")
     inp = synth.dsrelu_inputs(w["L"], w["K"], w["N"], counts, seed=w["seed"], device="cuda")
@@ -117,19 +122,25 @@ def test_workload_sampled():
     cpu["b_list"] = [x.cpu() for x in inp["b_list"]]
     cpu["sfb_list"] = [x.cpu() for x in inp["sfb_list"]]
     starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
-    rows = []
-    for s, c in zip(starts, counts):
-        if c:
-            rows += [s, s + c - 1]
-    rows = np.array(sorted(set(rows)), np.int64)
-    ref = run_oracle(cpu, rows=rows)
-    assert_close(values(d[rows]), ref["D"], orc.BF16, "D_row (sampled rows)")
-    assert_close(values(dprob[rows]), ref["dprob"], orc.F32, "dprob (sampled rows)")
-    # Amax against the kernel's own D (bf16-rounded: within 2^-8 relative)
-    dv = np.abs(values(d))
+    small_g = int(np.argmin(np.where(counts > 0, counts, np.iinfo(np.int64).max)))
+    rows = set()
     for g, (s, c) in enumerate(zip(starts, counts)):
-        want = dv[s:s + c].max() if c else 0.0
-        assert abs(amax[g].item() - want) <= 2.0 ** -8 * max(want, 1e-30), (g, amax[g].item(), want)
+        if g == small_g:
+            rows.update(range(s, s + c))
+        elif c:
+            rows.update([s, s + c - 1])
+    rows = np.array(sorted(rows), np.int64)
+    say(f"  oracle on {rows.size} rows (all {counts[small_g]} of group {small_g})")
+    ref = run_oracle(cpu, rows=rows)
+    assert_close(values(d[rows]), ref["D"], orc.BF16, "D_row (listed rows)")
+    assert_close(values(dprob[rows]), ref["dprob"], orc.F32, "dprob (listed rows)")
+    got = amax.numpy().astype(np.float64)
+    want = ref["amax"][small_g]
+    say(f"  amax of group {small_g}: {got[small_g]:.6e} vs oracle {want:.6e}")
+    assert abs(got[small_g] - want) <= 1e-3 * want
+    for g, c in enumerate(counts):
+        if c and g != small_g:
+            assert got[g] >= ref["amax"][g] * (1 - 1e-3), (g, got[g], ref["amax"][g])
 
 
 @pytest.mark.parametrize("case", range(6))
