@@ -211,6 +211,28 @@ gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_ma
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gg_wgrad without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Every argument has gg_wgrad's meaning;
+ * the scratch the kernels use (error word, work-queue counters, expert
+ * order) is a static array of 4352 bytes inside the library, one per GPU,
+ * held until the process ends, which limits num_experts to 1024 (beyond:
+ * GG_ERR_WORKSPACE; gg_wgrad's own limit is the same).  No path of the call
+ * allocates memory, host or device.
+ *   - All calls on one GPU share that GPU's scratch: calls that may overlap
+ *     on one GPU (different streams, or host threads) race and must not be
+ *     issued.  Each call clears what it needs before its kernels run.
+ *   - The device error word lives in that scratch and is not readable by
+ *     the caller; use GG_FLAG_VALIDATE_OFFSETS to have malformed offsets
+ *     rejected (GG_ERR_OFFSETS), or gg_wgrad with a workspace to read it.
+ */
+gg_status gg_wgrad_noalloc(const void* a, gg_major a_major, const void* b, gg_major b_major,
+                           const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                           int32_t hidden, int32_t intermediate,
+                           void* wgrad_dense, const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype,
+                           int32_t accumulate, uint32_t flags, void* stream);
+
+/*
  * The same operation on block-scaled operands ("Grouped GEMM + WGrad
  * (Unified)", "Block-scaled contract"), MXFP8: E4M3 codes with one E8M0
  * scale per 32 consecutive tokens of a row, deq(q, s) = e4m3(q) * 2^(s-127),

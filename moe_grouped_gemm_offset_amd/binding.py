@@ -25,7 +25,7 @@ STATUS_NAMES = ["GG_OK", "GG_ERR_NULL", "GG_ERR_SHAPE", "GG_ERR_DTYPE", "GG_ERR_
                 "GG_ERR_ALIGN", "GG_ERR_MODE", "GG_ERR_WORKSPACE", "GG_ERR_UNSUPPORTED",
                 "GG_ERR_DEVICE", "GG_ERR_HIP", "GG_ERR_OFFSETS", "GG_ERR_VALUE"]
 EXPORTS = ["gg_abi_version", "gg_last_error", "gg_device_error", "gg_wgrad_workspace_size",
-           "gg_wgrad", "gg_wgrad_mx", "gg_dglu_workspace_size", "gg_dglu", "gg_dglu_mx",
+           "gg_wgrad", "gg_wgrad_noalloc", "gg_wgrad_mx", "gg_dglu_workspace_size", "gg_dglu", "gg_dglu_mx",
            "gg_dsrelu_workspace_size", "gg_dsrelu"]
 
 _TORCH_DTYPE = {torch.bfloat16: GG_BF16, torch.float16: GG_F16, torch.float32: GG_F32,
@@ -67,6 +67,8 @@ def load_library(path=LIB_PATH):
     L.gg_dsrelu_workspace_size.argtypes = [I32]
     L.gg_wgrad.restype = ctypes.c_int
     L.gg_wgrad.argtypes = [P, I32, P, I32, P, I32, I64, I32, I32, P, P, I32, I32, U32, P, SZ, P]
+    L.gg_wgrad_noalloc.restype = ctypes.c_int
+    L.gg_wgrad_noalloc.argtypes = [P, I32, P, I32, P, I32, I64, I32, I32, P, P, I32, I32, U32, P]
     L.gg_wgrad_mx.restype = ctypes.c_int
     L.gg_wgrad_mx.argtypes = [P, P, P, P, P, I32, I64, I32, I32, P, P, I32, I32, U32, P, SZ, P]
     L.gg_dglu.restype = ctypes.c_int
@@ -184,6 +186,20 @@ def gg_wgrad(a, a_major, b, b_major, offsets, tokens_sum, hidden, intermediate,
                       intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
                       int(bool(accumulate)), flags, _ptr(ws), nbytes, _stream(stream)))
     return ws
+
+
+def gg_wgrad_noalloc(a, a_major, b, b_major, offsets, tokens_sum, hidden, intermediate,
+                     wgrad_dense=None, wgrad_ptrs=None, wgrad_dtype=None, accumulate=False, flags=0,
+                     stream=None):
+    """Grouped wgrad on the library's static scratch (gg_wgrad_noalloc of
+    gg_moe.h): no workspace is allocated or passed."""
+    L = load_library()
+    E = offsets.numel()
+    if wgrad_dtype is None:
+        wgrad_dtype = _TORCH_DTYPE[wgrad_dense.dtype]
+    _check(L.gg_wgrad_noalloc(_ptr(a), a_major, _ptr(b), b_major, _ptr(offsets), E, tokens_sum, hidden,
+                              intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
+                              int(bool(accumulate)), flags, _stream(stream)))
 
 
 def gg_wgrad_mx(a, sfa, b, sfb, offsets, tokens_sum, hidden, intermediate, wgrad_dense=None,

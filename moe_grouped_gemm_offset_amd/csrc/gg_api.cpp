@@ -13,28 +13,26 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
-#include <string>
-#include <vector>
 
 #include "gg_moe.h"
 #include "gg_internal.hpp"
 
 namespace {
 
-thread_local std::string g_err;
+// The last error message of this thread (a fixed buffer: no entry point
+// allocates memory, on any path).
+thread_local char g_err[512];
 
 gg_status fail(gg_status s, const char* fmt, ...) {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
     va_end(ap);
-    g_err = buf;
     return s;
 }
 
 gg_status ok() {
-    g_err.clear();
+    g_err[0] = '\0';
     return GG_OK;
 }
 
@@ -49,13 +47,13 @@ bool is_out_dtype(gg_dtype d) { return d == GG_BF16 || d == GG_F16 || d == GG_F3
 // Current device must be a gfx950; the answer is cached per device ordinal.
 gg_status check_device() {
     static std::mutex mu;
-    static std::vector<int> cache;   // 0 unknown, 1 gfx950, 2 other
+    static int cache[64];            // 0 unknown, 1 gfx950, 2 other
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0)
         return fail(GG_ERR_DEVICE, "no HIP device is available");
+    if (dev >= 64)
+        return fail(GG_ERR_DEVICE, "device ordinal %d is beyond the 64 this library tracks", dev);
     std::lock_guard<std::mutex> lock(mu);
-    if ((int)cache.size() <= dev)
-        cache.resize(dev + 1, 0);
     if (cache[dev] == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
@@ -78,8 +76,12 @@ gg_status hip_fail(hipError_t e, const char* what) {
 // pages' rules.  dgrad: last <= total; wgrad: last == total.
 gg_status validate_offsets_host(const int32_t* offsets, int n, int64_t total, bool dgrad,
                                 hipStream_t s) {
-    std::vector<int32_t> h(n);
-    hipError_t e = hipMemcpyAsync(h.data(), offsets, n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    // n <= 1024 (every caller checks the group count first): a stack buffer,
+    // so that no entry point allocates, not even host memory
+    int32_t h[1024];
+    if (n < 0 || n > 1024)
+        return fail(GG_ERR_SHAPE, "offsets arrays hold 1..1024 entries");
+    hipError_t e = hipMemcpyAsync(h, offsets, n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess)
         e = hipStreamSynchronize(s);
     if (e != hipSuccess)
@@ -100,13 +102,44 @@ gg_status validate_offsets_host(const int32_t* offsets, int n, int64_t total, bo
     return GG_OK;
 }
 
+// Scratch of gg_wgrad_noalloc, for callers that cannot allocate: the
+// workspace of a wgrad call with up to 1024 experts (header, then the expert
+// order).  Each GPU holds its own copy for the life of the process; host
+// code reaches it only through the address hipGetSymbolAddress returns for
+// the current device (the array's name is a host-side stand-in).
+constexpr size_t kNoallocBytes = gg::kWsHeader + sizeof(int32_t) * 1024;
+static __device__ __align__(256) int32_t scratch[kNoallocBytes / sizeof(int32_t)];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+gg_status scratch_address(void** out) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(GG_ERR_DEVICE, "no HIP device is available");
+    if (dev >= 64)
+        return fail(GG_ERR_DEVICE, "device ordinal %d is beyond the 64 this library tracks", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GG_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return GG_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int gg_abi_version(void) { return GG_ABI_VERSION; }
 
-const char* gg_last_error(void) { return g_err.c_str(); }
+const char* gg_last_error(void) { return g_err; }
 
 gg_status gg_device_error(const void* workspace, void* stream, int32_t* code) {
     if (!workspace || !code)
@@ -136,14 +169,12 @@ size_t gg_dsrelu_workspace_size(int32_t L) {
     return round256(gg::kWsHeader);
 }
 
-// Checks shared by gg_wgrad and gg_wgrad_mx (all but the operand pointers,
-// majors and scales), then the prologue and the launch.
-static gg_status run_wgrad(gg::WgradArgs& p, bool mx, const int32_t* offsets, int32_t num_experts,
-                           int64_t tokens_sum, int32_t hidden, int32_t intermediate,
-                           void* wgrad_dense, const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype,
-                           int32_t accumulate, uint32_t flags, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-    const char* name = mx ? "gg_wgrad_mx" : "gg_wgrad";
+// Host checks of the shared wgrad arguments that need neither the device nor
+// the workspace.
+static gg_status wgrad_host_checks(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                                   int32_t hidden, int32_t intermediate, void* wgrad_dense,
+                                   const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype, uint32_t flags,
+                                   bool mx, const char* name) {
     if (!is_out_dtype(wgrad_dtype))
         return fail(GG_ERR_DTYPE, "wgrad_dtype must be GG_BF16, GG_F16 or GG_F32");
     if ((wgrad_dense != nullptr) == (wgrad_ptrs != nullptr))
@@ -168,14 +199,29 @@ static gg_status run_wgrad(gg::WgradArgs& p, bool mx, const int32_t* offsets, in
         return fail(GG_ERR_UNSUPPORTED, "more than 2^28 output tiles (256 x 256, all experts)");
     if (!aligned16(wgrad_dense) || !aligned16(wgrad_ptrs) || ((uintptr_t)offsets & 3u))
         return fail(GG_ERR_ALIGN, "the output must be 16-byte aligned, offsets 4-byte");
+    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_TENSOR_RAGGED))
+        return fail(GG_ERR_MODE, "unsupported flags 0x%x for %s", flags, name);
+    return GG_OK;
+}
+
+// Checks shared by the wgrad entries (all but the operand pointers, majors
+// and scales), then the prologue and the launch.
+static gg_status run_wgrad(gg::WgradArgs& p, bool mx, const int32_t* offsets, int32_t num_experts,
+                           int64_t tokens_sum, int32_t hidden, int32_t intermediate,
+                           void* wgrad_dense, const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype,
+                           int32_t accumulate, uint32_t flags, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    gg_status st = wgrad_host_checks(offsets, num_experts, tokens_sum, hidden, intermediate,
+                                     wgrad_dense, wgrad_ptrs, wgrad_dtype, flags, mx,
+                                     mx ? "gg_wgrad_mx" : "gg_wgrad");
+    if (st != GG_OK)
+        return st;
     if ((uintptr_t)workspace & 255u)
         return fail(GG_ERR_ALIGN, "workspace must be 256-byte aligned");
     if (workspace_bytes < gg_wgrad_workspace_size(num_experts))
         return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
                     gg_wgrad_workspace_size(num_experts));
-    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_TENSOR_RAGGED))
-        return fail(GG_ERR_MODE, "unsupported flags 0x%x for %s", flags, name);
-    gg_status st = check_device();
+    st = check_device();
     if (st != GG_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
@@ -244,6 +290,49 @@ gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_ma
     p.b_kmajor = b_major == GG_MAJOR_K;
     return run_wgrad(p, false, offsets, num_experts, tokens_sum, hidden, intermediate, wgrad_dense,
                      wgrad_ptrs, wgrad_dtype, accumulate, flags, workspace, workspace_bytes, stream);
+}
+
+gg_status gg_wgrad_noalloc(const void* a, gg_major a_major, const void* b, gg_major b_major,
+                           const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                           int32_t hidden, int32_t intermediate, void* wgrad_dense,
+                           const int64_t* wgrad_ptrs, gg_dtype wgrad_dtype, int32_t accumulate,
+                           uint32_t flags, void* stream) {
+    if (num_experts > 0 && gg_wgrad_workspace_size(num_experts) > kNoallocBytes)
+        return fail(GG_ERR_WORKSPACE,
+                    "gg_wgrad_noalloc: %d experts need %zu bytes of scratch; its static scratch "
+                    "holds %zu (1024 experts)",
+                    num_experts, gg_wgrad_workspace_size(num_experts), kNoallocBytes);
+    if (!offsets)
+        return fail(GG_ERR_NULL, "offsets must be non-NULL");
+    if ((!a || !b) && tokens_sum > 0)
+        return fail(GG_ERR_NULL, "a and b must be non-NULL");
+    if (a_major != GG_MAJOR_K && a_major != GG_MAJOR_M)
+        return fail(GG_ERR_LAYOUT, "a_major must be GG_MAJOR_K or GG_MAJOR_M");
+    if (b_major != GG_MAJOR_K && b_major != GG_MAJOR_N)
+        return fail(GG_ERR_LAYOUT, "b_major must be GG_MAJOR_K or GG_MAJOR_N");
+    if (!aligned16(a) || !aligned16(b))
+        return fail(GG_ERR_ALIGN, "a, b and the output must be 16-byte aligned");
+    gg::WgradArgs p = {};
+    p.a = a;
+    p.b = b;
+    p.a_kmajor = a_major == GG_MAJOR_K;
+    p.b_kmajor = b_major == GG_MAJOR_K;
+    // the scratch address is looked up only for a call that passes every
+    // host check
+    gg_status st = wgrad_host_checks(offsets, num_experts, tokens_sum, hidden, intermediate,
+                                     wgrad_dense, wgrad_ptrs, wgrad_dtype, flags, false,
+                                     "gg_wgrad_noalloc");
+    if (st != GG_OK)
+        return st;
+    st = check_device();
+    if (st != GG_OK)
+        return st;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != GG_OK)
+        return st;
+    return run_wgrad(p, false, offsets, num_experts, tokens_sum, hidden, intermediate, wgrad_dense,
+                     wgrad_ptrs, wgrad_dtype, accumulate, flags, ws, kNoallocBytes, stream);
 }
 
 gg_status gg_wgrad_mx(const void* a_fp8, const uint8_t* sfa, const void* b_fp8, const uint8_t* sfb,

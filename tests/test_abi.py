@@ -81,6 +81,38 @@ def test_wgrad_rejects(kw, status):
     assert B.gg_last_error() != ""
 
 
+def wgrad_noalloc(**kw):
+    args = dict(a=P, a_major=0, b=P, b_major=2, offsets=P, E=4, T=1024, hidden=256, inter=256,
+                dense=P, ptrs=None, dtype=2, acc=0, flags=0, stream=None)
+    args.update(kw)
+    lib = B.load_library()
+    return lib.gg_wgrad_noalloc(args["a"], args["a_major"], args["b"], args["b_major"],
+                                args["offsets"], args["E"], args["T"], args["hidden"], args["inter"],
+                                args["dense"], args["ptrs"], args["dtype"], args["acc"], args["flags"],
+                                args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=1025), WORKSPACE),
+    (dict(E=0), SHAPE),
+    (dict(offsets=None), NULL),
+    (dict(a=None), NULL),
+    (dict(a_major=2), LAYOUT),
+    (dict(dtype=3), DTYPE),
+    (dict(ptrs=P), MODE),
+    (dict(hidden=96), UNSUPPORTED),
+    (dict(T=1020), ALIGN),
+    (dict(flags=1), MODE),
+])
+def test_wgrad_noalloc_rejects(kw, status):
+    """Host checks of the static-scratch entry, before any device call; its
+    scratch holds the workspace of at most 1024 experts."""
+    assert wgrad_noalloc(**kw) == status
+    assert B.gg_last_error() != ""
+    if kw.get("E") == 1025:
+        assert "1024 experts" in B.gg_last_error()
+
+
 def dglu(**kw):
     args = dict(a=P, M=1024, k=256, bd=P, bp=None, bm=0, n=256, c=P, cdt=0, po=P, L=4, alpha=P,
                 beta=P, prob=P, d=P, ddt=0, dprob=P, dbias=None, act=0, flags=0, ws=WS, wsb=1 << 20)
