@@ -35,7 +35,18 @@ its algorithmic bytes at 8 TB/s take longer than its FLOPs at the MFMA
 peak.  The CPU oracle is timed on a bounded sample of rows of the same
 workloads (cpu_baseline).
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+After the step, every op is launched --reps times on its own, back to back
+("warm") and with a 512 MiB read-modify-write before each launch that evicts
+the 256 MB MALL ("cold"); the median, p10 and p90 of its HIP-event durations
+and the engine clock sampled meanwhile (amdsmi GPU metrics) go into its
+`kernels` entry.  With the default workload the MoE wgrad's other modes
+(A K-major; bf16 and fp32-discrete accumulate) are timed the same way
+beside the step.  Inside the step every op reads and writes 0.2-4.7 GB
+between two launches of the same op, more than the MALL holds, so the
+step's own launches are cold as well.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--reps R]
+                  [--no-extras] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -134,7 +145,7 @@ def make_dglu(name, dev):
     return Op(name, "dglu_kernel", synth.flops_dgrad(vm, N, K), "bf16", run, alg, sample)
 
 
-def make_wgrad(dev, a_major="m", f32acc=False):
+def make_wgrad(dev, a_major="m", f32acc=False, bf16acc=False):
     import numpy as np
     import torch
     from moe_grouped_gemm_offset_amd import binding as B, synth
@@ -162,6 +173,15 @@ def make_wgrad(dev, a_major="m", f32acc=False):
         # experts (empty ones are left untouched)
         alg = 2 * (h * T + T * i) + 2 * 4 * int(np.sum(counts > 0)) * h * i
         run.keep = outs
+    elif bf16acc:
+        # the bf16 dense output accumulated into (from seeded N(0,1) values)
+        out = synth.wgrad_initial(E, h, i, torch.bfloat16, seed=1003, device=dev)
+
+        def run():
+            B.gg_wgrad(inp["a"], am, inp["b"], B.GG_MAJOR_N, inp["offsets"], T, h, i,
+                       wgrad_dense=out, accumulate=True, workspace=ws)
+
+        alg = 2 * (h * T + T * i) + 2 * 2 * int(np.sum(counts > 0)) * h * i
     else:
         out = torch.empty(E, h, i, dtype=torch.bfloat16, device=dev)
 
@@ -321,6 +341,7 @@ WORKLOAD_OPS = {
     "wgrad_moe": ["wgrad_moe"],
     "wgrad_moe_kmajor": ["wgrad_moe_kmajor"],
     "wgrad_moe_f32acc": ["wgrad_moe_f32acc"],
+    "wgrad_moe_bf16acc": ["wgrad_moe_bf16acc"],
     "dgeglu": ["dgeglu"],
     "dsrelu_mxfp8": ["dsrelu_mxfp8"],
     "dglu_mxfp8": ["dglu_mxfp8"],
@@ -343,6 +364,10 @@ def build_op(name, dev):
         op = make_wgrad(dev, "m", f32acc=True)
         op.name = name
         return op
+    if name == "wgrad_moe_bf16acc":
+        op = make_wgrad(dev, "m", bf16acc=True)
+        op.name = name
+        return op
     if name == "dglu_mxfp8":
         return make_dglu_mx(dev)
     if name == "wgrad_mxfp8":
@@ -352,6 +377,121 @@ def build_op(name, dev):
     if name == "dsrelu_mxfp8_fp8out":
         return make_dsrelu(dev, fp8out=True)
     return make_dsrelu(dev)
+
+
+# The kernel each single-op workload runs.
+KERNEL_OF = {"dswiglu": "dglu_kernel", "dgeglu": "dglu_kernel", "wgrad_moe": "wgrad_kernel",
+             "wgrad_moe_kmajor": "wgrad_kernel", "wgrad_moe_f32acc": "wgrad_kernel",
+             "wgrad_moe_bf16acc": "wgrad_kernel", "dsrelu_mxfp8": "dsrelu_kernel",
+             "dglu_mxfp8": "dglu_mx_kernel", "wgrad_mxfp8": "wgrad_mx_kernel",
+             "dsrelu_mxfp8_fp8out": "dsrelu_kernel", "dglu_mxfp8_fp8out": "dglu_mx_kernel"}
+
+# Ops timed beside a workload's step (per-op statistics only; not part of the
+# step or its value): the MoE wgrad's other output modes and A major.
+EXTRA_OPS = {"moe_backward": ["wgrad_moe_kmajor", "wgrad_moe_bf16acc", "wgrad_moe_f32acc"]}
+
+FLUSH_BYTES = 512 << 20       # > the 256 MB MALL: a read-modify-write of it evicts the cache
+
+
+class ClockSampler:
+    """Samples the GPU's current engine clock (amdsmi GPU metrics, MHz) in a
+    background thread while ops run; None where the metrics are unavailable."""
+
+    def __init__(self):
+        self.h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if hs:
+                self.amdsmi, self.h = amdsmi, hs[0]
+                if self._read() is None:
+                    self.h = None
+        except Exception:
+            self.h = None
+
+    def _read(self):
+        try:
+            m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        except Exception:
+            return None
+        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+            v = m.get(key)
+            if isinstance(v, (list, tuple)):
+                v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
+                v = sum(v) / len(v) if v else None
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                return float(v)
+        return None
+
+    def __enter__(self):
+        import threading
+        self.samples, self.stop = [], threading.Event()
+        if self.h is not None:
+            def loop():
+                while not self.stop.is_set():
+                    v = self._read()
+                    if v is not None:
+                        self.samples.append(v)
+                    self.stop.wait(0.002)
+            self.t = threading.Thread(target=loop, daemon=True)
+            self.t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.h is not None:
+            self.t.join()
+
+    def median(self):
+        v = sorted(self.samples)
+        return v[len(v) // 2] if v else None
+
+
+def per_op_stats(ops, reps, dev, clock):
+    """Median, p10 and p90 of each op's per-launch HIP-event durations over
+    `reps` launches, warm (back to back) and cold (a read-modify-write of
+    FLUSH_BYTES before each launch, outside its events, evicts the MALL),
+    and the median engine clock sampled during them."""
+    import torch
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    out = {}
+    for op in ops:
+        for _ in range(3):
+            op.run()
+        torch.cuda.synchronize()
+        st = {}
+        for mode in ("warm", "cold"):
+            evs = []
+            with clock:
+                for _ in range(reps):
+                    if mode == "cold":
+                        flush.add_(1.0)
+                    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    s.record()
+                    op.run()
+                    e.record()
+                    evs.append((s, e))
+                torch.cuda.synchronize()
+            t = sorted(s.elapsed_time(e) for s, e in evs)
+            q = lambda f: round(t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))], 4)
+            st[mode] = {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9)}
+            clk = clock.median()
+            st[mode]["clock_mhz"] = None if clk is None else round(clk)
+        out[op.name] = st
+    del flush
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(ops, budget_s):
@@ -371,6 +511,7 @@ def cpu_baseline(ops, budget_s):
         parts.append(f"{op.name}: {n} rows, {t:.1f} s, {rate / 1e9:.2f} GFLOP/s")
     total = sum(op.flops for op in ops)
     return {"value": total / proj / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "; ".join(parts) + " (rows spread over every group, extrapolated by FLOPs)"}
 
 
@@ -436,6 +577,87 @@ def summarize_pmc(fetch_csv, write_csv, workload_kernels, out_path):
     return out
 
 
+# rocprofv3 counter passes behind the utilisation summaries (each within one
+# pass's hardware limits: at most 8 SQ, 4 TCP, 2 TA, 2 TD, 2 GRBM counters).
+COUNTER_GROUPS = {
+    "sq": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_LDS",
+           "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_ANY", "SQ_BUSY_CYCLES",
+           "GRBM_GUI_ACTIVE"],
+    "mem": ["TCP_TCR_TCP_STALL_CYCLES", "TCP_PENDING_STALL_CYCLES", "TCP_TCP_TA_DATA_STALL_CYCLES",
+            "TCP_READ_TAGCONFLICT_STALL_CYCLES", "TD_TD_BUSY", "TD_TC_STALL", "TA_TA_BUSY",
+            "TA_DATA_STALLED_BY_TC_CYCLES", "GRBM_GUI_ACTIVE"],
+    "l2": ["TCC_HIT_sum", "TCC_MISS_sum", "GRBM_GUI_ACTIVE", "GRBM_COUNT"],
+}
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+def counter_command(workload, group, kernel):
+    return (f"cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc {' '.join(COUNTER_GROUPS[group])} "
+            f"--kernel-include-regex {kernel} -d $R/gpurun_out/pmc/{workload}_{group} -o out "
+            f"--output-format csv -- python3 $R/bench.py --workload {workload} --steps 3 --warmup 1 "
+            f"--reps 0 --no-extras --no-cpu-baseline")
+
+
+def summarize_counters(workload, kernel, root, out_path):
+    """Per-dispatch averages of the COUNTER_GROUPS passes of one workload
+    (root/<workload>_<group>/out_counter_collection.csv) and the
+    utilisations derived from them, written as a markdown summary."""
+    import csv
+    import collections
+    vals, durs = collections.defaultdict(list), collections.defaultdict(dict)
+    for group in COUNTER_GROUPS:
+        path = os.path.join(root, f"{workload}_{group}", "out_counter_collection.csv")
+        for r in csv.DictReader(open(path)):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            vals[(group, r["Counter_Name"])].append(float(r["Counter_Value"]))
+            durs[group][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    out = {}
+    for group in COUNTER_GROUPS:
+        d = list(durs[group].values())
+        t_us = sum(d) / len(d)
+        cyc = avg[(group, "GRBM_GUI_ACTIVE")] / N_XCD          # engine cycles per XCD
+        out[group] = {"dispatches": len(d), "us": t_us, "ghz": cyc / (t_us * 1e3), "cyc": cyc}
+    sq, mem, l2 = (out[g]["cyc"] for g in ("sq", "mem", "l2"))
+    derived = [
+        ("engine clock during the kernel (GRBM_GUI_ACTIVE / 8 XCDs / duration)",
+         f"{out['sq']['ghz']:.2f} GHz ({out['mem']['ghz']:.2f}, {out['l2']['ghz']:.2f} in the other passes)"),
+        ("MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles)",
+         f"{avg[('sq', 'SQ_VALU_MFMA_BUSY_CYCLES')] / (N_SIMD * sq):.3f}"),
+        ("MFMA busy x clock / 2.4 GHz (share of the published peak the pipe delivered)",
+         f"{avg[('sq', 'SQ_VALU_MFMA_BUSY_CYCLES')] / (N_SIMD * sq) * out['sq']['ghz'] / 2.4:.3f}"),
+        ("LDS busy: SQ_LDS_IDX_ACTIVE / (256 CUs x cycles)", f"{avg[('sq', 'SQ_LDS_IDX_ACTIVE')] / (N_CU * sq):.3f}"),
+        ("LDS bank conflicts: SQ_LDS_BANK_CONFLICT / (256 CUs x cycles)",
+         f"{avg[('sq', 'SQ_LDS_BANK_CONFLICT')] / (N_CU * sq):.3f}"),
+        ("TD busy: TD_TD_BUSY / (256 x cycles)", f"{avg[('mem', 'TD_TD_BUSY')] / (N_CU * mem):.3f}"),
+        ("TD stalled on the TC: TD_TC_STALL / (256 x cycles)", f"{avg[('mem', 'TD_TC_STALL')] / (N_CU * mem):.3f}"),
+        ("TCP waiting for L2 data: TCP_PENDING_STALL_CYCLES / (256 x cycles)",
+         f"{avg[('mem', 'TCP_PENDING_STALL_CYCLES')] / (N_CU * mem):.3f}"),
+        ("TCP stalled by the TCR (L1 -> L2 requests): TCP_TCR_TCP_STALL_CYCLES / (256 x cycles)",
+         f"{avg[('mem', 'TCP_TCR_TCP_STALL_CYCLES')] / (N_CU * mem):.3f}"),
+        ("TA busy: TA_TA_BUSY / (256 x cycles)", f"{avg[('mem', 'TA_TA_BUSY')] / (N_CU * mem):.3f}"),
+        ("L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS)",
+         f"{avg[('l2', 'TCC_HIT_sum')] / (avg[('l2', 'TCC_HIT_sum')] + avg[('l2', 'TCC_MISS_sum')]):.3f}"),
+    ]
+    lines = [f"# {kernel} on the {workload} workload — rocprofv3 counters", "",
+             "Three counter passes, each in its own run (from the repository root `$R` on the GPU box):", ""]
+    lines += ["    " + counter_command(workload, g, kernel) for g in COUNTER_GROUPS]
+    lines += ["", f"Summarised by `python3 bench.py --workload {workload} --summarize-counters "
+              f"$R/gpurun_out/pmc`.", "",
+              "| pass | dispatches | average duration µs (under counter collection) | clock GHz |",
+              "|---|---|---|---|"]
+    lines += [f"| {g} | {o['dispatches']} | {o['us']:.1f} | {o['ghz']:.2f} |" for g, o in out.items()]
+    lines += ["", "| derived (per-dispatch averages) | value |", "|---|---|"]
+    lines += [f"| {a} | {b} |" for a, b in derived]
+    lines += ["", "| counter (pass) | per-dispatch average |", "|---|---|"]
+    lines += [f"| {c} ({g}) | {v:.6g} |" for (g, c), v in sorted(avg.items())]
+    lines += ["", f"Kernel source hash at measurement: `{source_hash(kernel)}`.", ""]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    return derived
+
+
 def bound_of(op):
     """The roofline that bounds an op: "hbm" when its algorithmic bytes at
     the HBM peak take longer than its FLOPs at the MFMA peak, else "mfma"."""
@@ -463,23 +685,34 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="moe_backward", choices=sorted(WORKLOAD_OPS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reps", type=int, default=50,
+                    help="per-op launches for the warm / cold medians (0: skip that phase)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the ops timed beside the step (other wgrad modes)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="with a single-op --workload: summarise the counter passes of "
+                         "COUNTER_GROUPS found under DIR into profiles/, and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="with a single-op --workload: record its per-launch HBM traffic from "
                          "two rocprofv3 --pmc runs in profiles/hbm_traffic.json, and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        names = WORKLOAD_OPS[args.workload]
+        if len(names) != 1:
+            sys.exit("--summarize-counters needs a single-op --workload")
+        kernel = KERNEL_OF[names[0]]
+        path = os.path.join(ROOT, "profiles", f"counters-{kernel}-{names[0]}.md")
+        for a, b in summarize_counters(names[0], kernel, args.summarize_counters, path):
+            print(f"{a}: {b}")
+        return
     if args.summarize_pmc:
         names = WORKLOAD_OPS[args.workload]
         if len(names) != 1:
             sys.exit("--summarize-pmc needs a single-op --workload")
-        kernel = {"dswiglu": "dglu_kernel", "dgeglu": "dglu_kernel", "wgrad_moe": "wgrad_kernel",
-                  "wgrad_moe_kmajor": "wgrad_kernel", "wgrad_moe_f32acc": "wgrad_kernel",
-                  "dsrelu_mxfp8": "dsrelu_kernel",
-                  "dglu_mxfp8": "dglu_mx_kernel", "wgrad_mxfp8": "wgrad_mx_kernel",
-                  "dsrelu_mxfp8_fp8out": "dsrelu_kernel",
-                  "dglu_mxfp8_fp8out": "dglu_mx_kernel"}[names[0]]
+        kernel = KERNEL_OF[names[0]]
         path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
         res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
                             {names[0]: (kernel, names[0])}, path)
@@ -525,24 +758,45 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
 
-    kernels = {}
-    for op in ops:
-        times = sorted(s.elapsed_time(e) for s, e in ev[op.name])
-        ms = sum(times) / len(times)
-        pct = lambda q: times[min(len(times) - 1, int(q * (len(times) - 1) + 0.5))]
+    def entry(op, ms):
+        """An op's figures at a per-launch duration of ms."""
         tf = op.flops / (ms * 1e-3) / 1e12
-        kernels[op.name] = {"kernel": op.kernel, "ms": round(ms, 4),
-                            "ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
-                            "gflop": round(op.flops / 1e9, 2),
-                            "tflops": round(tf, 1), "peak_frac": round(tf / PEAK[op.dtype], 4),
-                            "dtype": op.dtype, "alg_gb_s": round(op.alg_bytes / (ms * 1e-3) / 1e9, 1)}
+        k = {"kernel": op.kernel, "ms": round(ms, 4), "gflop": round(op.flops / 1e9, 2),
+             "tflops": round(tf, 1), "peak_frac": round(tf / PEAK[op.dtype], 4),
+             "dtype": op.dtype, "alg_gb_s": round(op.alg_bytes / (ms * 1e-3) / 1e9, 1)}
         tr = traffic_for(op.kernel, op.name)
-        kernels[op.name]["hbm_gb_per_launch"] = None if tr is None else round(tr / 1e9, 3)
-        kernels[op.name]["bound"] = bound_of(op)
+        k["hbm_gb_per_launch"] = None if tr is None else round(tr / 1e9, 3)
+        k["bound"] = bound_of(op)
         # the roofline time (the larger of the MFMA-peak and HBM-peak times)
         # over the measured time
         t_roof = max(op.flops / (PEAK[op.dtype] * 1e12), op.alg_bytes / (HBM_PEAK * 1e9))
-        kernels[op.name]["roofline_frac"] = round(t_roof / (ms * 1e-3), 4)
+        k["roofline_frac"] = round(t_roof / (ms * 1e-3), 4)
+        return k
+
+    kernels = {}
+    for op in ops:
+        times = sorted(s.elapsed_time(e) for s, e in ev[op.name])
+        pct = lambda q: times[min(len(times) - 1, int(q * (len(times) - 1) + 0.5))]
+        # the timed region's mean duration (the step's own launches)
+        kernels[op.name] = entry(op, sum(times) / len(times))
+        kernels[op.name]["in_step"] = True
+        kernels[op.name]["step_ms_p10_p50_p90"] = [round(pct(0.1), 4), round(pct(0.5), 4),
+                                                   round(pct(0.9), 4)]
+
+    # every op again on its own: warm and cold (MALL evicted) medians over
+    # --reps launches, with the engine clock; plus the ops timed beside the
+    # step, whose figures come from their warm median
+    extras = [] if args.no_extras else [build_op(n, dev) for n in EXTRA_OPS.get(args.workload, [])]
+    if args.reps > 0:
+        print(f"[bench] per-op medians over {args.reps} launches ({len(ops) + len(extras)} ops)",
+              file=sys.stderr, flush=True)
+        stats = per_op_stats(ops + extras, args.reps, dev, ClockSampler())
+        for op in ops + extras:
+            if op in extras:
+                kernels[op.name] = entry(op, stats[op.name]["warm"]["p50"])
+                kernels[op.name]["in_step"] = False
+            kernels[op.name]["warm"] = stats[op.name]["warm"]
+            kernels[op.name]["cold"] = stats[op.name]["cold"]
     total_flops = sum(op.flops for op in ops)
     value = total_flops / (ms_step * 1e-3) / 1e12
     dom = max(ops, key=lambda o: kernels[o.name]["ms"])

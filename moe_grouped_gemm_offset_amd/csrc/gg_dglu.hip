@@ -24,9 +24,10 @@ using DgluCfg = Cfg<256, 256, 4, 2>;
 constexpr int kDgluPipe = 2;
 
 // W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU; BF: C and D
-// both bf16.  Each combination is its own kernel so the register allocation
-// of one epilogue does not burden the others.
-template <class C, bool B_K, bool W32, int ACT, bool BF>
+// both bf16; DB: dbias requested; FILT: dGeGLU's value (0) or mask (1)
+// filters.  Each combination is its own kernel so the register allocation
+// and arithmetic of one epilogue do not burden the others.
+template <class C, bool B_K, bool W32, int ACT, bool BF, bool DB, int FILT>
 __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
     __shared__ __attribute__((aligned(1024))) char smem[kDgluPipe ? Slots5<C>::kLds : C::kLds];
@@ -103,7 +104,8 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
 
     // C of the items 6 ahead (3 for fp32 C) in flight in the epilogue: deeper
     // prefetch spilled registers and measured slower
-    dglu_epilogue<C, W32, ACT, false, W32 ? 3 : 6, false, BF>(p, acc, smem, m0, n0, g, rows_valid, am0, bn0);
+    dglu_epilogue<C, W32, ACT, false, W32 ? 3 : 6, false, BF, DB, FILT>(p, acc, smem, m0, n0, g,
+                                                                       rows_valid, am0, bn0);
 }
 
 hipError_t launch_dglu(const DgluArgs& p, hipStream_t s) {
@@ -112,13 +114,21 @@ hipError_t launch_dglu(const DgluArgs& p, hipStream_t s) {
     if (tiles == 0)
         return hipSuccess;
     const dim3 grid((unsigned)tiles), block(C::kThreads);
-    auto go = [&](auto BK, auto W32, auto BF) {
+    auto go_act = [&](auto BK, auto W32, auto BF, auto DB) {
         constexpr bool bk = decltype(BK)::value, w32 = decltype(W32)::value;
-        constexpr bool bf = decltype(BF)::value;
+        constexpr bool bf = decltype(BF)::value, db = decltype(DB)::value;
         if (p.act == 0)
-            hipLaunchKernelGGL((dglu_kernel<C, bk, w32, 0, bf>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_kernel<C, bk, w32, 0, bf, db, 0>), grid, block, 0, s, p);
+        else if (p.mask_filter)
+            hipLaunchKernelGGL((dglu_kernel<C, bk, w32, 1, bf, db, 1>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((dglu_kernel<C, bk, w32, 1, bf>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((dglu_kernel<C, bk, w32, 1, bf, db, 0>), grid, block, 0, s, p);
+    };
+    auto go = [&](auto BK, auto W32, auto BF) {
+        if (p.dbias)
+            go_act(BK, W32, BF, std::true_type());
+        else
+            go_act(BK, W32, BF, std::false_type());
     };
     auto go_bk = [&](auto BK) {
         if (p.c_dtype == kF32)

@@ -68,8 +68,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
                                   : (const char*)p.sfb_ptrs[g] + (int64_t)n0 * KB;
     mx_mainloop<C>(smem, a, sfa, bg, sfb, K, K, rows_valid, cols_valid, am0, bn0, acc);
 
-    // C of the items 12 ahead (6 for fp32 C) in flight in the epilogue
-    dglu_epilogue<C, W32, ACT, true, Q ? (W32 ? 4 : 8) : (W32 ? 6 : 12), Q, BF>(
+    // C of the items 10 ahead (6 for fp32 C) in flight in the epilogue (more
+    // spilled registers in the dSwiGLU and dGeGLU kernels)
+    dglu_epilogue<C, W32, ACT, true, Q ? (W32 ? 4 : 8) : (W32 ? 6 : 10), Q, BF>(
         p, acc, smem, m0, n0, g, rows_valid, am0, bn0);
 }
 

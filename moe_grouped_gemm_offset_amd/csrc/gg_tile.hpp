@@ -628,13 +628,13 @@ __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issu
         for (int i = 0; i < VMA; i++)
             issue(sl(f2), 0u, u + 2, i);
         if (second)
-            vm_wait<VMA>();                              // B(u+1) has landed
+            vm_wait<VMA>();                         // B(u+1) has landed
         else
             lds_wait();
         unit_barrier();
         compute();
         if (!second)
-            vm_wait<VMA>();                              // B(u+1) has landed
+            vm_wait<VMA>();                         // B(u+1) has landed
         unit_barrier();
         const int na = a1, nb = f1, na1 = f2;
         f1 = a;
@@ -702,6 +702,24 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// Two fp32 values as one word of two bf16, round to nearest even (one
+// v_cvt_pk_bf16_f32; a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Eight fp32 values as eight bf16 through a buffer descriptor: one 16-byte
+// non-temporal store (the kernels never read these outputs back).
+__device__ __forceinline__ void store_bf16x8(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&v)[8]) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 w = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]),
+                     (int)pack_bf16x2(v[4], v[5]), (int)pack_bf16x2(v[6], v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 2);
+}
+
 // dtype codes (the gg_dtype values of the ABI)
 constexpr int kBF16 = 0, kF16 = 1, kF32 = 2, kF8 = 3;   // gg_dtype codes
 
@@ -767,11 +785,10 @@ __device__ __forceinline__ void store8(void* base, int dtype, int64_t i, const f
     } else {
         uint32_t ws[4];
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const uint32_t lo = dtype == kBF16 ? f32_to_bf16(v[2 * k]) : f32_to_f16(v[2 * k]);
-            const uint32_t hi = dtype == kBF16 ? f32_to_bf16(v[2 * k + 1]) : f32_to_f16(v[2 * k + 1]);
-            ws[k] = lo | (hi << 16);
-        }
+        for (int k = 0; k < 4; k++)
+            ws[k] = dtype == kBF16 ? pack_bf16x2(v[2 * k], v[2 * k + 1])
+                                   : (uint32_t)f32_to_f16(v[2 * k]) |
+                                         ((uint32_t)f32_to_f16(v[2 * k + 1]) << 16);
         __builtin_nontemporal_store(u32x4{ws[0], ws[1], ws[2], ws[3]},
                                     reinterpret_cast<u32x4*>((uint16_t*)base + i));
     }

@@ -74,11 +74,10 @@ __device__ __forceinline__ void wgrad_epilogue_t(const f32x16 (&acc)[C::MB][C::N
         } else {
             i32x4 w;
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint32_t lo = DT == kBF16 ? f32_to_bf16(v[2 * k]) : f32_to_f16(v[2 * k]);
-                const uint32_t hi = DT == kBF16 ? f32_to_bf16(v[2 * k + 1]) : f32_to_f16(v[2 * k + 1]);
-                w[k] = (int)(lo | (hi << 16));
-            }
+            for (int k = 0; k < 4; k++)
+                w[k] = DT == kBF16 ? (int)pack_bf16x2(v[2 * k], v[2 * k + 1])
+                                   : (int)((uint32_t)f32_to_f16(v[2 * k]) |
+                                           ((uint32_t)f32_to_f16(v[2 * k + 1]) << 16));
             __builtin_amdgcn_raw_buffer_store_b128(w, ro, o, 0, kNT);
         }
     };
