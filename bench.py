@@ -38,8 +38,9 @@ workloads (cpu_baseline).
 After the step, every op is launched --reps times on its own, back to back
 ("warm") and with a 512 MiB read-modify-write before each launch that evicts
 the 256 MB MALL ("cold"); the median, p10 and p90 of its HIP-event durations
-and the engine clock sampled meanwhile (amdsmi GPU metrics) go into its
-`kernels` entry.  With the default workload the MoE wgrad's other modes
+go into its `kernels` entry, with the median engine clock (amdsmi GPU
+metrics, mean over the XCDs) over a further 0.4 s of back-to-back
+launches.  With the default workload the MoE wgrad's other modes
 (A K-major; bf16 and fp32-discrete accumulate) are timed the same way
 beside the step.  Inside the step every op reads and writes 0.2-4.7 GB
 between two launches of the same op, more than the MALL holds, so the
@@ -415,6 +416,7 @@ class ClockSampler:
             m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
         except Exception:
             return None
+        # per-XCD engine clocks (MHz), averaged; else the single value
         for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
             v = m.get(key)
             if isinstance(v, (list, tuple)):
@@ -426,14 +428,14 @@ class ClockSampler:
 
     def __enter__(self):
         import threading
-        self.samples, self.stop = [], threading.Event()
+        self.samples, self.stop, self.t0 = [], threading.Event(), time.perf_counter()
         if self.h is not None:
             def loop():
                 while not self.stop.is_set():
                     v = self._read()
                     if v is not None:
-                        self.samples.append(v)
-                    self.stop.wait(0.002)
+                        self.samples.append((time.perf_counter(), v))
+                    self.stop.wait(0.005)
             self.t = threading.Thread(target=loop, daemon=True)
             self.t.start()
         return self
@@ -443,16 +445,23 @@ class ClockSampler:
         if self.h is not None:
             self.t.join()
 
-    def median(self):
-        v = sorted(self.samples)
+    def median(self, skip_s=0.0):
+        """Median of the samples taken at least skip_s after sampling began
+        (the metrics refresh about every 100 ms, so a value read right after
+        a change of load still describes the previous one)."""
+        v = sorted(x for t, x in self.samples if t >= self.t0 + skip_s)
         return v[len(v) // 2] if v else None
+
+
+CLOCK_RUN_S, CLOCK_SKIP_S = 0.4, 0.15
 
 
 def per_op_stats(ops, reps, dev, clock):
     """Median, p10 and p90 of each op's per-launch HIP-event durations over
     `reps` launches, warm (back to back) and cold (a read-modify-write of
-    FLUSH_BYTES before each launch, outside its events, evicts the MALL),
-    and the median engine clock sampled during them."""
+    FLUSH_BYTES before each launch, outside its events, evicts the MALL);
+    and the median engine clock over a separate CLOCK_RUN_S of back-to-back
+    launches (samples from its first CLOCK_SKIP_S dropped)."""
     import torch
     flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     out = {}
@@ -476,8 +485,15 @@ def per_op_stats(ops, reps, dev, clock):
             t = sorted(s.elapsed_time(e) for s, e in evs)
             q = lambda f: round(t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))], 4)
             st[mode] = {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9)}
-            clk = clock.median()
-            st[mode]["clock_mhz"] = None if clk is None else round(clk)
+        clk = None
+        if clock.h is not None:
+            n = max(1, int(CLOCK_RUN_S / (st["warm"]["p50"] * 1e-3)))
+            with clock:
+                for _ in range(n):
+                    op.run()
+                torch.cuda.synchronize()
+            clk = clock.median(CLOCK_SKIP_S)
+        st["clock_mhz"] = None if clk is None else round(clk)
         out[op.name] = st
     del flush
     return out
@@ -797,6 +813,7 @@ def main():
                 kernels[op.name]["in_step"] = False
             kernels[op.name]["warm"] = stats[op.name]["warm"]
             kernels[op.name]["cold"] = stats[op.name]["cold"]
+            kernels[op.name]["clock_mhz"] = stats[op.name]["clock_mhz"]
     total_flops = sum(op.flops for op in ops)
     value = total_flops / (ms_step * 1e-3) / 1e12
     dom = max(ops, key=lambda o: kernels[o.name]["ms"])
