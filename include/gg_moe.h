@@ -199,7 +199,7 @@ size_t gg_wgrad_workspace_size(int32_t num_experts);
  * flags        OR of GG_FLAG_VALIDATE_OFFSETS and GG_FLAG_TENSOR_RAGGED
  *              ("input_order": the K-major operands' storage, see the flag).
  * workspace    >= gg_wgrad_workspace_size(num_experts) bytes, 256-B aligned.
- *              Besides the error word and the expert order it holds the
+ *              Besides the error word and the experts' rank table it holds the
  *              work-queue counters of the kernel's scheduler, reset by every
  *              call; calls that may overlap must not share it.
  */
@@ -215,8 +215,8 @@ gg_status gg_wgrad(const void* a, gg_major a_major, const void* b, gg_major b_ma
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Every argument has gg_wgrad's meaning;
  * the scratch the kernels use (error word, work-queue counters, expert
- * order) is a static array of 4352 bytes inside the library, one per GPU,
- * held until the process ends, which limits num_experts to 1024 (beyond:
+ * rank table) is a static array of 16640 bytes inside the library, one per
+ * GPU, held until the process ends, which limits num_experts to 1024 (beyond:
  * GG_ERR_WORKSPACE; gg_wgrad's own limit is the same).  No path of the call
  * allocates memory, host or device.
  *   - All calls on one GPU share that GPU's scratch: calls that may overlap

@@ -37,6 +37,12 @@ def flags():
             # staging written as floats and read as vectors): no type-based
             # alias assumptions
             "-fno-strict-aliasing",
+            # atomics stay as written: every atomic here is issued by one
+            # lane or hits per-lane addresses, so the rewrite into a
+            # wave-wide scan buys nothing, and it awaits the returned value
+            # where the rewrite ends (the wgrad kernel's queue request must
+            # stay in flight through half of an epilogue)
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 

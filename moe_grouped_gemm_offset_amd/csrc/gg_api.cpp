@@ -103,11 +103,11 @@ gg_status validate_offsets_host(const int32_t* offsets, int n, int64_t total, bo
 }
 
 // Scratch of gg_wgrad_noalloc, for callers that cannot allocate: the
-// workspace of a wgrad call with up to 1024 experts (header, then the expert
-// order).  Each GPU holds its own copy for the life of the process; host
+// workspace of a wgrad call with up to 1024 experts (header, then the
+// 16-byte rank table).  Each GPU holds its own copy for the life of the process; host
 // code reaches it only through the address hipGetSymbolAddress returns for
 // the current device (the array's name is a host-side stand-in).
-constexpr size_t kNoallocBytes = gg::kWsHeader + sizeof(int32_t) * 1024;
+constexpr size_t kNoallocBytes = gg::kWsHeader + gg::kWsRankBytes * 1024;
 static __device__ __align__(256) int32_t scratch[kNoallocBytes / sizeof(int32_t)];
 
 // Device address of `scratch` on the current device, looked up once per
@@ -156,7 +156,7 @@ gg_status gg_device_error(const void* workspace, void* stream, int32_t* code) {
 size_t gg_wgrad_workspace_size(int32_t num_experts) {
     if (num_experts < 0)
         num_experts = 0;
-    return round256(gg::kWsHeader + sizeof(int32_t) * (size_t)num_experts);
+    return round256(gg::kWsHeader + gg::kWsRankBytes * (size_t)num_experts);
 }
 
 size_t gg_dglu_workspace_size(int32_t L, int32_t n, int32_t generate_dbias) {

@@ -14,6 +14,10 @@ constexpr size_t kWsHeader = 256;
 // int32 index, in the header, of the 8 work-queue counters of the persistent
 // wgrad kernel (one per XCD), cleared by the set-up kernel
 constexpr int kWsQueue = 16;
+// wgrad region after the header: by rank (experts by token count, largest
+// first) an int32 x 4 entry {expert, offsets[expert-1] (0 for the first),
+// offsets[expert], 0}, written by the set-up kernel
+constexpr size_t kWsRankBytes = 16;
 
 // Compute units of the current device (cached per device), and the grid of a
 // persistent kernel over `items` work items: one workgroup per CU, a multiple
@@ -59,7 +63,7 @@ struct WgradArgs {
     const uint8_t* sfa;       // block-scaled only: E8M0 scales of A and B
     const uint8_t* sfb;
     const int32_t* offsets;
-    int32_t* ws;              // header + int32 order[E]
+    int32_t* ws;              // header + rank table (E entries of kWsRankBytes)
     void* out_dense;
     const int64_t* out_ptrs;
     int64_t T;
@@ -128,8 +132,8 @@ hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s);
 
 // Prologue: clears the error word, `nclear` floats at `clear` and `nclear2`
 // floats at `clear2`, checks the offsets (wgrad: last == total; dgrad: last
-// <= total) and, when order is non-NULL, writes the experts sorted by count,
-// largest first.
+// <= total) and, when order is non-NULL, writes the rank table (kWsRankBytes
+// per expert, largest count first) there.
 hipError_t launch_prologue(const int32_t* offsets, int n, int64_t total, int dgrad,
                            int32_t* err, int32_t* order, float* clear, int64_t nclear,
                            float* clear2, int64_t nclear2, hipStream_t s);

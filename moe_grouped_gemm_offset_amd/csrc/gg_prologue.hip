@@ -6,7 +6,8 @@
 // the group offsets against the pages' rules (non-decreasing cumulative
 // ends, every group a multiple of 256, last end == total / <= rows), and for
 // wgrad ranks the experts by token count, largest first, so that the longest
-// reductions are dispatched first, and clears the work-queue counters.
+// reductions are dispatched first (a table of (expert, begin, end) by rank),
+// and clears the work-queue counters.
 #include "gg_internal.hpp"
 #include "gg_moe.h"
 
@@ -54,13 +55,19 @@ prologue_kernel(const int32_t* __restrict__ offsets, int n, int64_t total, int d
     if (t < 8)
         err[kWsQueue + t] = 0;
     if (order) {
+        // rank r's entry: the expert and its raw bounds (offsets[e-1] or 0,
+        // offsets[e]), so that a work item needs one 16-byte load to find
+        // its token range
         for (int i = t; i < n; i += blockDim.x) {
             int ci = cnt[i], rank = 0;
             for (int j = 0; j < n; j++) {
                 int cj = cnt[j];
                 rank += (cj > ci) | ((cj == ci) & (j < i));
             }
-            order[rank] = i;
+            order[4 * rank] = i;
+            order[4 * rank + 1] = i ? offsets[i - 1] : 0;
+            order[4 * rank + 2] = offsets[i];
+            order[4 * rank + 3] = 0;
         }
     }
 }

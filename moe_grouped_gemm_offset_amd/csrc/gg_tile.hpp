@@ -89,6 +89,16 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
     return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Read of a workgroup-uniform address whose contents no kernel of this
+// launch writes (tables from the set-up kernel, caller pointer arrays):
+// through the constant address space it becomes a scalar load, awaited with
+// the LDS counter, so that awaiting it leaves vector memory operations
+// (output stores, an atomic) in flight.
+template <class T>
+__device__ __forceinline__ T scalar_read(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
 __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * kRowBytes + ((chunk ^ swz(row)) << 4);
 }
@@ -566,13 +576,17 @@ __device__ __forceinline__ void pipeline5(char* smem, int nk, F (&f)[2], Issue i
 // memory phase -- in both cases with only A(u+2) left in flight, one to two
 // phases after issue.
 //   issue, read, mma as for pipeline5; f is a single fragment set.
-// With kPre, the caller has already issued unit 0 into slots 0 and 1 (other
-// vector memory operations may have followed; they are awaited with it).
+// With kPre, the caller has already issued unit 0 into slots 0 and 1, and
+// either at least kPending other vector memory operations after it (e.g. a
+// previous tile's output stores) or unit 0 has landed: since they complete
+// in issue order, the first wait leaves kPending of them in flight, to be
+// awaited with B(1), one window later.
 // ---------------------------------------------------------------------------
-template <class C, int VMA, int VM, int kMfma, int kGroups, bool kPre = false, class F, class Issue,
-          class Read, class Mma>
+template <class C, int VMA, int VM, int kMfma, int kGroups, bool kPre = false, int kPending = 0,
+          class F, class Issue, class Read, class Mma>
 __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issue, Read read,
                                             Mma mma) {
+    static_assert(kPending == 0 || kPre, "operations after unit 0 only when it is prefetched");
     static_assert(C::kWaves == 8 && VMA <= VM, "two groups of four waves");
     constexpr int kSlot = Slots5<C>::kSlot;
     if (nk <= 0) {
@@ -594,7 +608,7 @@ __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issu
 #pragma unroll
     for (int i = 0; i < VMA; i++)
         issue(sl(2), 0u, 1, i);
-    vm_wait<VMA>();                                      // A(0), B(0)
+    vm_wait<VMA + kPending>();                           // A(0), B(0)
     unit_barrier();
     if (second)
         unit_barrier();                                  // one phase behind
@@ -911,18 +925,22 @@ __device__ __forceinline__ void rawb8_store(__amdgpu_buffer_rsrc_t r, const Fmt8
 //   fn(t, r, c, v, pre)      process an item with its accumulators v (fp32)
 //                            and what load returned for it.
 // Only this wave touches `lds`; the caller separates it from the main loop
-// with a barrier.
+// with a barrier.  Items [kFrom, kTo) alone are visited (kTo < 0: to the
+// end), whole pieces, so that a caller can split the walk.
 // ---------------------------------------------------------------------------
 constexpr int kEpiHalfBytes = 32 * kEpiPitch * 4;
 
-template <class C, int kAhead, int kQR = 64, class Load, class Fn>
+template <class C, int kAhead, int kQR = 64, int kFrom = 0, int kTo = -1, class Load, class Fn>
 __device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB], float* lds, Load load,
                                               Fn fn) {
     static_assert(C::MB % 2 == 0 && C::NB % 2 == 0, "row walk expects 64 x 64 quadrants");
     static_assert(kQR == 64 || kQR == 32, "staged pieces of 64 or 32 rows");
     constexpr int kBR = kQR / 32;                        // block rows per piece
     constexpr int kPer = kQR / 8;                        // items per piece
-    constexpr int kItems = 8 * (C::MB / 2) * (C::NB / 2);
+    constexpr int kAll = 8 * (C::MB / 2) * (C::NB / 2);
+    constexpr int kItems = kTo < 0 ? kAll : kTo;
+    static_assert(kFrom % kPer == 0 && kItems % kPer == 0 && kFrom < kItems && kItems <= kAll,
+                  "whole pieces");
     const int l = threadIdx.x & 63;
     // item i: piece q = i / kPer (h = q / (MB/kBR), mh = q % (MB/kBR)), ti = i % kPer
     auto item = [&](int i, int& t, int& r, int& c) {
@@ -934,13 +952,13 @@ __device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB],
     using P = decltype(load(0, 0, 0));
     P pre[kItems];
 #pragma unroll
-    for (int i = 0; i < kAhead && i < kItems; i++) {
+    for (int i = kFrom; i < kFrom + kAhead && i < kItems; i++) {
         int t, r, c;
         item(i, t, r, c);
         pre[i] = load(t, r, c);
     }
 #pragma unroll
-    for (int i = 0; i < kItems; i++) {
+    for (int i = kFrom; i < kItems; i++) {
         if (i % kPer == 0) {
             const int q = i / kPer, h = q / (C::MB / kBR), mh = q % (C::MB / kBR);
 #pragma unroll

@@ -16,9 +16,12 @@
 // dispatcher's round-robin order) take items from it in order: a
 // longest-first greedy schedule per XCD, with every expert spread evenly
 // over the XCDs.  A workgroup asks for its next item when its main loop
-// ends, and loads the next item's first K unit while it writes the current
-// one's output, so that the fill of the next main loop overlaps the
-// epilogue.
+// ends; the request stays in flight while the first half of the output is
+// written, one wave then looks the item up (rank table, tile coordinates)
+// and hands it to the others through LDS, and the next item's first K unit
+// loads while the second half is written.  The next main loop leaves that
+// half's stores in flight at its first wait, so that they drain under its
+// first MFMAs.
 //
 // The reduction runs over the expert's tokens, 32 per stage and 64 per load
 // unit, through the ping-pong main loop of gg_tile.hpp: K-major operands are
@@ -43,7 +46,13 @@ constexpr int kWgradBcast = Slots5<WgradCfg>::kLds - 16;
 static_assert(kWgradEpiBase + WgradCfg::kWaves * kEpiHalfBytes <= kWgradBcast,
               "epilogue staging must leave slots 0, 1 and the broadcast word alone");
 
-template <class C, bool A_K, bool B_K>
+// OUT: the output format and mode, known at compile time for the common
+// cases (the epilogue is then straight-line code): kOutBf16 (bf16,
+// overwritten), kOutF32Acc (fp32, accumulated into); kOutAny reads dtype
+// and mode at run time.
+constexpr int kOutAny = 0, kOutBf16 = 1, kOutF32Acc = 2;
+
+template <class C, bool A_K, bool B_K, int OUT>
 __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     constexpr int TM = C::TM, TN = C::TN;
     constexpr int kSlot = Slots5<C>::kSlot;
@@ -55,13 +64,15 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     const int total = P * p.E;
     const int x = blockIdx.x & 7;                       // this workgroup's queue
     int32_t* queue = p.ws + kWsQueue + x;
-    const int32_t* order = p.ws + kWsHeader / 4;
+    const int32_t* ranks = p.ws + kWsHeader / 4;
     int* bcast = (int*)(smem + kWgradBcast);
 
     const int w = threadIdx.x >> 6;
     const int wm = w / C::WN, wn = w % C::WN;
     const int am0 = uniform(wm * (TM / C::WM)), bn0 = uniform(wn * (TN / C::WN));   // wave offsets in the tile
 
+    constexpr int kHalf = 4 * (C::MB / 2) * (C::NB / 2);   // half of the row walk's items
+    constexpr bool kSplit = OUT != kOutAny;
     using LA = std::conditional_t<A_K, LoadK<C, TM>, LoadMN<C>>;
     using LB = std::conditional_t<B_K, LoadK<C, TN>, LoadMN<C>>;
     LA la;
@@ -77,15 +88,18 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     int64_t begin = 0, end = 0, cnt = 0, ldk = 0;
     const char* ak = a;
     const char* bk = b;
-    auto decode = [&](int t) {
-        const int rank = uniform(t / P);
+    // Item t located: {expert, M tile | N tile << 16, first token, end
+    // token} from its rank-table entry, or {-1, ...} past the last item.
+    // (Scalar divisions: done by one wave, the others read the result.)
+    auto locate = [&](int t) {
+        if (t >= total)
+            return u32x4{~0u, 0u, 0u, 0u};
+        const int rank = t / P;
+        const u32x4 ent = scalar_read(reinterpret_cast<const u32x4*>(ranks + 4 * rank));
         int mt_, nt_;
-        xcd_remap2d(t % P, tiles_m, tiles_n, p.xcd_gm, mt_, nt_);
-        m0 = uniform(mt_) * TM;
-        n0 = uniform(nt_) * TN;
-        e = uniform(order[rank]);
-        int64_t bg = e ? (int64_t)uniform(p.offsets[e - 1]) : 0;
-        int64_t en = uniform(p.offsets[e]);
+        xcd_remap2d(t - rank * P, tiles_m, tiles_n, p.xcd_gm, mt_, nt_);
+        int64_t bg = (int)ent.y;
+        int64_t en = (int)ent.z;
         bg = bg < 0 ? 0 : (bg > p.T ? p.T : bg);
         en = en < bg ? bg : (en > p.T ? p.T : en);
         if (((bg | en) & 7) != 0) {       // not expressible in 16-byte chunks
@@ -93,9 +107,19 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
                 atomicOr(p.ws, GG_DEVERR_SKIPPED);
             en = bg;
         }
-        begin = bg;
-        end = en;
-        cnt = en - bg;
+        return u32x4{ent.x, (uint32_t)mt_ | ((uint32_t)nt_ << 16), (uint32_t)bg, (uint32_t)en};
+    };
+    auto decode = [&](u32x4 loc) {
+        e = uniform((int)loc.x);
+        const int mn = uniform((int)loc.y);
+        m0 = (mn & 0xffff) * TM;
+        n0 = (mn >> 16) * TN;
+        // token positions come from int32 offsets: kept workgroup-uniform,
+        // so that every branch on them is a scalar one
+        begin = uniform((int)loc.z);
+        end = uniform((int)loc.w);
+        const int64_t bg = begin;
+        cnt = end - begin;
         ldk = (p.ragged ? cnt : p.T) * 2;
         ak = a + (p.ragged ? (int64_t)p.hidden * bg : bg) * 2;
         bk = b + (p.ragged ? (int64_t)p.inter * bg : bg) * 2;
@@ -142,45 +166,109 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     const int t0 = 8 * uniform(*bcast) + x;
     if (t0 >= total)
         return;
-    decode(t0);
+    decode(locate(t0));
     prefetch();
+    wait_all();                       // later items: see the end of the loop
     for (;;) {
-        const bool skip = cnt == 0 && p.accumulate;     // nothing to add: output untouched
+        // nothing to add: output untouched (a uniform branch)
+        const bool skip = uniform(cnt == 0 && p.accumulate) != 0;
 #pragma unroll
         for (int i = 0; i < C::MB; i++)
 #pragma unroll
             for (int j = 0; j < C::NB; j++)
                 acc[i][j] = f32x16{0};
-        const int nk = skip ? 0 : (int)((cnt + 31) / 32);
-        pipeline_pp<C, LA::kN, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB, true>(
+        const int nk = skip ? 0 : uniform((int)((cnt + 31) / 32));
+        pipeline_pp<C, LA::kN, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB, true, kHalf>(
             smem, nk, frag, issue2, read2, mma);
+
+        // The next item is asked for once this one's main loop is done
+        // (asking earlier hands the queue out in start order rather than
+        // finish order, which scatters the tiles that share operand panels
+        // and measured 20% more HBM fetch).
+        int qpos = 0;
+        if (threadIdx.x == 0)
+            qpos = atomicAdd(queue, 1);
+        __builtin_amdgcn_sched_barrier(0);
 
         // this item's output
         void* out = p.out_dense
             ? (void*)((char*)p.out_dense +
                       (int64_t)e * p.hidden * p.inter * (p.out_dtype == kF32 ? 4 : 2))
-            : (void*)p.out_ptrs[e];
+            : (void*)scalar_read(p.out_ptrs + e);
         out = uniform_ptr(out);
-        const int accumulate = cnt > 0 ? p.accumulate : 0;
+        const int accumulate = uniform(cnt > 0 ? p.accumulate : 0);
         const int row0 = m0 + am0, col0 = n0 + bn0;
-
-        // the next item, asked for once this one's main loop is done (asking
-        // earlier hands the queue out in start order rather than finish
-        // order, which scatters the tiles that share operand panels and
-        // measured 20% more HBM fetch); its first unit loads while this
-        // one's output is written
-        if (threadIdx.x == 0)
-            *bcast = atomicAdd(queue, 1);
-        __syncthreads();
-        const int tn = 8 * uniform(*bcast) + x;
-        if (tn < total) {
-            decode(tn);
-            prefetch();
+        float* const stage = (float*)(smem + kWgradEpiBase + w * kEpiHalfBytes);
+        // A skipped item runs the same epilogue with every row masked (no
+        // access reaches memory), so that no branch goes around its stores.
+        const int rows = skip ? 0 : p.hidden;
+        auto first_half = [&]() {
+            if constexpr (OUT == kOutBf16)
+                wgrad_epilogue_t<C, 32, kBF16, false, 0, kHalf>(acc, stage, out, rows, p.inter,
+                                                                row0, col0);
+            else if constexpr (OUT == kOutF32Acc)
+                wgrad_epilogue_t<C, 32, kF32, true, 0, kHalf>(acc, stage, out, rows, p.inter,
+                                                              row0, col0);
+            else
+                wgrad_epilogue<C, 32, 0, kHalf>(acc, stage, out, p.out_dtype, rows, p.inter,
+                                                row0, col0, accumulate);
+        };
+        // Every wave reads lane 0's request result (only wave 0's is
+        // meaningful), so that the compiler awaits it here on every path and
+        // never inside the next main loop.  Wave 0 looks the item up in the
+        // rank table while the other waves catch up, and hands item and
+        // entry over through LDS; the next item's first unit is then issued.
+        auto next_item = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            qpos = __builtin_amdgcn_readfirstlane(qpos);
+            if (uniform(w) == 0) {
+                const u32x4 loc = locate(8 * qpos + x);
+                if (threadIdx.x == 0)
+                    *reinterpret_cast<u32x4*>(bcast) = loc;
+            }
+            lds_wait();
+            unit_barrier();
+            const u32x4 loc = *reinterpret_cast<const u32x4*>(bcast);
+            const bool more = uniform((int)loc.x) >= 0;
+            if (more) {
+                decode(loc);
+                prefetch();
+            }
+            return more;
+        };
+        // The next main loop leaves kHalf vector memory operations issued
+        // after the prefetch in flight at its first wait: the second half
+        // issues at least kHalf stores (one or two per item, masked ones
+        // included), or, when accumulating, waits for its loads of the old
+        // values, issued after the prefetch, which completes first.
+        auto second_half = [&]() {
+            if constexpr (OUT == kOutBf16)
+                wgrad_epilogue_t<C, 32, kBF16, false, kHalf, 2 * kHalf>(acc, stage, out, rows,
+                                                                        p.inter, row0, col0);
+            else if constexpr (OUT == kOutF32Acc)
+                wgrad_epilogue_t<C, 32, kF32, true, kHalf, 2 * kHalf>(acc, stage, out, rows,
+                                                                      p.inter, row0, col0);
+            else
+                wgrad_epilogue<C, 32, kHalf, 2 * kHalf>(acc, stage, out, p.out_dtype, rows,
+                                                        p.inter, row0, col0, accumulate);
+        };
+        // With the output format known at compile time (or both operands
+        // M/N-major) the request is awaited after the first half of the
+        // output, and the next item's first unit loads during the second
+        // half; otherwise (the registers of the run-time format dispatch,
+        // twice, and the K-major loaders would spill inside the main loop)
+        // both come before the output, written in one walk.
+        bool more;
+        if constexpr (kSplit) {
+            first_half();
+            more = next_item();
+            second_half();
+        } else {
+            more = next_item();
+            wgrad_epilogue<C, 32>(acc, stage, out, p.out_dtype, rows, p.inter, row0, col0,
+                                  accumulate);
         }
-        if (!skip)
-            wgrad_epilogue<C, 32>(acc, (float*)(smem + kWgradEpiBase + w * kEpiHalfBytes), out,
-                                  p.out_dtype, p.hidden, p.inter, row0, col0, accumulate);
-        if (tn >= total)
+        if (!more)
             break;
         // every wave's staging reads are done before slot 2 is loaded again;
         // the stores and the prefetch stay in flight
@@ -198,14 +286,25 @@ hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s) {
     if (total > (1 << 28))              // item numbers and queue positions stay in int32
         return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)persistent_grid(total)), block(C::kThreads);
+    auto go = [&](auto AK, auto BK) {
+        constexpr bool ak = decltype(AK)::value, bk = decltype(BK)::value;
+        if (p.out_dtype == kBF16 && !p.accumulate)
+            hipLaunchKernelGGL((wgrad_kernel<C, ak, bk, kOutBf16>), grid, block, 0, s, p);
+        else if (p.out_dtype == kF32 && p.accumulate)
+            hipLaunchKernelGGL((wgrad_kernel<C, ak, bk, kOutF32Acc>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((wgrad_kernel<C, ak, bk, kOutAny>), grid, block, 0, s, p);
+    };
+    const std::true_type yes;
+    const std::false_type no;
     if (p.a_kmajor && p.b_kmajor)
-        hipLaunchKernelGGL((wgrad_kernel<C, true, true>), grid, block, 0, s, p);
+        go(yes, yes);
     else if (p.a_kmajor)
-        hipLaunchKernelGGL((wgrad_kernel<C, true, false>), grid, block, 0, s, p);
+        go(yes, no);
     else if (p.b_kmajor)
-        hipLaunchKernelGGL((wgrad_kernel<C, false, true>), grid, block, 0, s, p);
+        go(no, yes);
     else
-        hipLaunchKernelGGL((wgrad_kernel<C, false, false>), grid, block, 0, s, p);
+        go(no, no);
     return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ namespace gg {
 // returns zeros, the store writes nothing).  The stores are non-temporal:
 // the output is not read again by the kernel, and streaming it past the
 // caches measured 3-6% faster on the MoE shapes.
-template <class C, int kQR, int DT, bool ACC>
+template <class C, int kQR, int DT, bool ACC, int kFrom, int kTo>
 __device__ __forceinline__ void wgrad_epilogue_t(const f32x16 (&acc)[C::MB][C::NB], float* lds,
                                                  void* out, int hidden, int inter, int row0,
                                                  int col0) {
@@ -81,31 +81,32 @@ __device__ __forceinline__ void wgrad_epilogue_t(const f32x16 (&acc)[C::MB][C::N
             __builtin_amdgcn_raw_buffer_store_b128(w, ro, o, 0, kNT);
         }
     };
-    for_each_row8<C, ACC ? 8 : 1, kQR>(acc, lds, load, fn);
+    for_each_row8<C, ACC ? 8 : 1, kQR, kFrom, kTo>(acc, lds, load, fn);
 }
 
 // Runtime dtype / mode (workgroup-uniform) to the compile-time epilogue;
 // kQR: rows of the pieces staged through the wave's LDS region (64:
-// kEpiWaveBytes per wave, 32: kEpiHalfBytes).
-template <class C, int kQR = 64>
+// kEpiWaveBytes per wave, 32: kEpiHalfBytes); items [kFrom, kTo) of the row
+// walk (kTo < 0: to the end).
+template <class C, int kQR = 64, int kFrom = 0, int kTo = -1>
 __device__ __forceinline__ void wgrad_epilogue(const f32x16 (&acc)[C::MB][C::NB], float* lds,
                                                void* out, int dtype, int hidden, int inter,
                                                int row0, int col0, int accumulate) {
     if (dtype == kBF16) {
         if (accumulate)
-            wgrad_epilogue_t<C, kQR, kBF16, true>(acc, lds, out, hidden, inter, row0, col0);
+            wgrad_epilogue_t<C, kQR, kBF16, true, kFrom, kTo>(acc, lds, out, hidden, inter, row0, col0);
         else
-            wgrad_epilogue_t<C, kQR, kBF16, false>(acc, lds, out, hidden, inter, row0, col0);
+            wgrad_epilogue_t<C, kQR, kBF16, false, kFrom, kTo>(acc, lds, out, hidden, inter, row0, col0);
     } else if (dtype == kF16) {
         if (accumulate)
-            wgrad_epilogue_t<C, kQR, kF16, true>(acc, lds, out, hidden, inter, row0, col0);
+            wgrad_epilogue_t<C, kQR, kF16, true, kFrom, kTo>(acc, lds, out, hidden, inter, row0, col0);
         else
-            wgrad_epilogue_t<C, kQR, kF16, false>(acc, lds, out, hidden, inter, row0, col0);
+            wgrad_epilogue_t<C, kQR, kF16, false, kFrom, kTo>(acc, lds, out, hidden, inter, row0, col0);
     } else {
         if (accumulate)
-            wgrad_epilogue_t<C, kQR, kF32, true>(acc, lds, out, hidden, inter, row0, col0);
+            wgrad_epilogue_t<C, kQR, kF32, true, kFrom, kTo>(acc, lds, out, hidden, inter, row0, col0);
         else
-            wgrad_epilogue_t<C, kQR, kF32, false>(acc, lds, out, hidden, inter, row0, col0);
+            wgrad_epilogue_t<C, kQR, kF32, false, kFrom, kTo>(acc, lds, out, hidden, inter, row0, col0);
     }
 }
 

@@ -35,11 +35,11 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_mx_kernel(WgradArgs p) {
     int mt_, nt_;
     xcd_remap2d(blockIdx.x % P, tiles_m, tiles_n, p.xcd_gm, mt_, nt_);
     const int mt = uniform(mt_), nt = uniform(nt_);
-    const int32_t* order = p.ws + kWsHeader / 4;
-    const int e = uniform(order[rank]);
+    const u32x4 ent = *reinterpret_cast<const u32x4*>(p.ws + kWsHeader / 4 + 4 * rank);
+    const int e = uniform((int)ent.x);
 
-    int64_t begin = e ? (int64_t)uniform(p.offsets[e - 1]) : 0;
-    int64_t end = uniform(p.offsets[e]);
+    int64_t begin = uniform((int)ent.y);
+    int64_t end = uniform((int)ent.z);
     begin = begin < 0 ? 0 : (begin > p.T ? p.T : begin);
     end = end < begin ? begin : (end > p.T ? p.T : end);
     if (((begin | end) & 127) != 0) {     // not whole load units

@@ -36,8 +36,8 @@ def test_loads_and_exports_every_declared_symbol():
 
 
 def test_workspace_sizes():
-    assert B.gg_wgrad_workspace_size(64) == 512
-    assert B.gg_wgrad_workspace_size(1024) == 256 + 4096
+    assert B.gg_wgrad_workspace_size(64) == 256 + 64 * 16
+    assert B.gg_wgrad_workspace_size(1024) == 256 + 1024 * 16
     assert B.gg_dglu_workspace_size(32, 1536, 1) == 256 + 32 * 3072 * 4
     assert B.gg_dglu_workspace_size(32, 1536, 0) == 256
     assert B.gg_dsrelu_workspace_size(16) == 256
