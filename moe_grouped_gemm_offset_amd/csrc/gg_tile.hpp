@@ -300,8 +300,12 @@ __device__ __forceinline__ void read_bf16(const char* sa, const char* sb, int a0
     }
 }
 
-// MFMAs m0 .. m1-1 of a stage, m = (ks MB + i) NB + j.
-template <class C>
+// MFMAs m0 .. m1-1 of a stage, m = (ks MB + i) NB + j.  With kT the
+// operands are swapped: block (i, j) then holds the transpose, so that a
+// lane owns one row of the block (row l % 32) and, in register r, column
+// 8 (r / 4) + 4 (l / 32) + r % 4 -- four consecutive columns per group of
+// four registers (see acc_row for the plain layout).
+template <class C, bool kT = false>
 __device__ __forceinline__ void mma_bf16(const FragBf16<C>& f, f32x16 (&acc)[C::MB][C::NB], int m0,
                                          int m1) {
 #pragma unroll
@@ -309,7 +313,12 @@ __device__ __forceinline__ void mma_bf16(const FragBf16<C>& f, f32x16 (&acc)[C::
         if (m < m0 || m >= m1)
             continue;
         const int ks = m / (C::MB * C::NB), i = (m / C::NB) % C::MB, j = m % C::NB;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
+        if constexpr (kT)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ks][j], f.a[ks][i], acc[i][j], 0,
+                                                                0, 0);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j], 0,
+                                                                0, 0);
     }
 }
 

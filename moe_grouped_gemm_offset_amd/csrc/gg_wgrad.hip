@@ -157,7 +157,10 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         read_bf16<C, A_K, B_K>(sa, sb, am0, bn0, kt & 1, f, g);
     };
     f32x16 acc[C::MB][C::NB];
-    auto mma = [&](const FragBf16<C>& f, int m0_, int m1_) { mma_bf16<C>(f, acc, m0_, m1_); };
+    // bf16 overwrite: transposed accumulators for the bf16-staged epilogue
+    auto mma = [&](const FragBf16<C>& f, int m0_, int m1_) {
+        mma_bf16<C, OUT == kOutBf16>(f, acc, m0_, m1_);
+    };
     FragBf16<C> frag;
 
     if (threadIdx.x == 0)
@@ -204,8 +207,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         const int rows = skip ? 0 : p.hidden;
         auto first_half = [&]() {
             if constexpr (OUT == kOutBf16)
-                wgrad_epilogue_t<C, 32, kBF16, false, 0, kHalf>(acc, stage, out, rows, p.inter,
-                                                                row0, col0);
+                wgrad_epilogue_bf16t<C, 0>(acc, (char*)stage, out, rows, p.inter, row0, col0);
             else if constexpr (OUT == kOutF32Acc)
                 wgrad_epilogue_t<C, 32, kF32, true, 0, kHalf>(acc, stage, out, rows, p.inter,
                                                               row0, col0);
@@ -243,8 +245,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         // values, issued after the prefetch, which completes first.
         auto second_half = [&]() {
             if constexpr (OUT == kOutBf16)
-                wgrad_epilogue_t<C, 32, kBF16, false, kHalf, 2 * kHalf>(acc, stage, out, rows,
-                                                                        p.inter, row0, col0);
+                wgrad_epilogue_bf16t<C, 1>(acc, (char*)stage, out, rows, p.inter, row0, col0);
             else if constexpr (OUT == kOutF32Acc)
                 wgrad_epilogue_t<C, 32, kF32, true, kHalf, 2 * kHalf>(acc, stage, out, rows,
                                                                       p.inter, row0, col0);

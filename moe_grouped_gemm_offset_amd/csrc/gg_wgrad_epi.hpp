@@ -84,6 +84,55 @@ __device__ __forceinline__ void wgrad_epilogue_t(const f32x16 (&acc)[C::MB][C::N
     for_each_row8<C, ACC ? 8 : 1, kQR, kFrom, kTo>(acc, lds, load, fn);
 }
 
+// bf16 output, overwritten, from accumulators in the transposed layout of
+// mma_bf16<C, true>: block row kI (32 rows x 32 NB columns of the wave
+// tile) is rounded to bf16 and staged through the wave's LDS region, rows
+// kPitchT bytes apart (8-byte writes of 32 rows at one column land on
+// distinct banks), then read back as 8 consecutive columns per lane, 4 rows
+// per instruction, and stored as 16-byte non-temporal stores: full 128-byte
+// lines, like the fp32 row walk, at half its LDS traffic.  Each lane issues
+// 8 stores per block row (the masked ones included).
+constexpr int kPitchT = 264;
+constexpr int kEpiBf16tBytes = 32 * kPitchT;
+static_assert(kEpiBf16tBytes <= kEpiHalfBytes, "fits the fp32 half-piece region");
+
+template <class C, int kI>
+__device__ __forceinline__ void wgrad_epilogue_bf16t(const f32x16 (&acc)[C::MB][C::NB], char* lds,
+                                                     void* out, int hidden, int inter, int row0,
+                                                     int col0) {
+    static_assert(C::NB == 4 && kI < C::MB, "a block row of the wave tile is 128 columns");
+    const int l = threadIdx.x & 63;
+    const int r = l & 31, h = l >> 5;
+#pragma unroll
+    for (int j = 0; j < C::NB; j++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const f32x16& a = acc[kI][j];
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 w = {pack_bf16x2(a[4 * g], a[4 * g + 1]),
+                             pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+            *reinterpret_cast<u32x2*>(lds + r * kPitchT + (32 * j + 8 * g + 4 * h) * 2) = w;
+        }
+    // offsets (rr inter + col) elements from the piece's first row: rr < 32,
+    // col < inter <= 2^21, so they fit 32 bits in bytes
+    const int prow0 = row0 + 32 * kI;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)out + ((int64_t)prow0 * inter << 1));
+    const int c = 8 * (l & 15);
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        const int rr = 4 * t + (l >> 4);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const char* src = lds + rr * kPitchT + c * 2;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
+        const bool ok = (prow0 + rr < hidden) & (col0 + c < inter);
+        const uint32_t off = ok ? (uint32_t)(((int64_t)rr * inter + col0 + c) << 1) : kInvalid;
+        __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y},
+                                               ro, off, 0, 2);
+    }
+}
+
 // Runtime dtype / mode (workgroup-uniform) to the compile-time epilogue;
 // kQR: rows of the pieces staged through the wave's LDS region (64:
 // kEpiWaveBytes per wave, 32: kEpiHalfBytes); items [kFrom, kTo) of the row
