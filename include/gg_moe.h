@@ -112,7 +112,16 @@ enum {
      * that block e starts at element rows * offsets[e-1] (0 for e = 0).
      * M-/N-major operands hold each token contiguously either way, so the
      * flag leaves them as they are. */
-    GG_FLAG_TENSOR_RAGGED = 8u
+    GG_FLAG_TENSOR_RAGGED = 8u,
+    /* Static scheduling (the pages' use_dynamic_sched=False, dGLU page
+     * "Class API").  The persistent bf16 wgrad kernel then walks its items in
+     * a fixed order -- workgroup j of an XCD's W workgroups takes that XCD's
+     * items j, j + W, j + 2W, ... -- instead of taking them from the XCD's
+     * atomic work queue in finish order.  The results are identical.  The
+     * other kernels launch one workgroup per tile, dispatched by the
+     * hardware in a fixed order, so for them both settings are the same
+     * schedule and the flag is accepted with no effect. */
+    GG_FLAG_STATIC_SCHED = 16u
 };
 
 /*
@@ -196,8 +205,9 @@ size_t gg_wgrad_workspace_size(int32_t num_experts);
  * accumulate   nonzero: out = round(old + result) (the caller initialises
  *              every output); zero: out = round(result), an empty expert
  *              gives exact zeros.  Rounding is to nearest even.
- * flags        OR of GG_FLAG_VALIDATE_OFFSETS and GG_FLAG_TENSOR_RAGGED
- *              ("input_order": the K-major operands' storage, see the flag).
+ * flags        OR of GG_FLAG_VALIDATE_OFFSETS, GG_FLAG_TENSOR_RAGGED
+ *              ("input_order": the K-major operands' storage, see the flag)
+ *              and GG_FLAG_STATIC_SCHED.
  * workspace    >= gg_wgrad_workspace_size(num_experts) bytes, 256-B aligned.
  *              Besides the error word and the experts' rank table it holds the
  *              work-queue counters of the kernel's scheduler, reset by every
@@ -318,7 +328,7 @@ size_t gg_dglu_workspace_size(int32_t L, int32_t n, int32_t generate_dbias);
  *            linear_offset are the dGeGLU constants (the pages' defaults:
  *            1.702, -7, 7, 1); ignored for dSwiGLU.
  * flags      OR of GG_FLAG_GATE_FIRST, GG_FLAG_GEGLU_MASK_FILTER,
- *            GG_FLAG_VALIDATE_OFFSETS.
+ *            GG_FLAG_VALIDATE_OFFSETS, GG_FLAG_STATIC_SCHED.
  * workspace  >= gg_dglu_workspace_size(L, n, dbias != NULL), 256-B aligned.
  */
 gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k,
@@ -432,7 +442,7 @@ size_t gg_dsrelu_workspace_size(int32_t L);
  * dprob      float[m_rows], caller-zeroed, accumulated into.
  * amax       float[L], written by the call (the library clears it first), or
  *            NULL.
- * flags      0 or GG_FLAG_VALIDATE_OFFSETS.
+ * flags      OR of GG_FLAG_VALIDATE_OFFSETS, GG_FLAG_STATIC_SCHED.
  * workspace  >= gg_dsrelu_workspace_size(L), 256-B aligned.
  */
 gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,

@@ -19,7 +19,7 @@ GG_BF16, GG_F16, GG_F32, GG_F8E4M3 = 0, 1, 2, 3
 GG_MAJOR_K, GG_MAJOR_M, GG_MAJOR_N = 0, 1, 2
 GG_DSWIGLU, GG_DGEGLU, GG_DSITUGLU = 0, 1, 2
 GG_FLAG_GATE_FIRST, GG_FLAG_GEGLU_MASK_FILTER, GG_FLAG_VALIDATE_OFFSETS = 1, 2, 4
-GG_FLAG_TENSOR_RAGGED = 8
+GG_FLAG_TENSOR_RAGGED, GG_FLAG_STATIC_SCHED = 8, 16
 GG_DEVERR_DECREASING, GG_DEVERR_GRANULE, GG_DEVERR_LAST, GG_DEVERR_SKIPPED = 1, 2, 4, 8
 STATUS_NAMES = ["GG_OK", "GG_ERR_NULL", "GG_ERR_SHAPE", "GG_ERR_DTYPE", "GG_ERR_LAYOUT",
                 "GG_ERR_ALIGN", "GG_ERR_MODE", "GG_ERR_WORKSPACE", "GG_ERR_UNSUPPORTED",
@@ -166,6 +166,12 @@ def _workspace(ws, nbytes, like, stream):
     return t, t.numel()
 
 
+def _sched(flags):
+    """GG_SCHED=static in the environment adds GG_FLAG_STATIC_SCHED (a
+    benchmarking override; GG_SCHED=dynamic or unset leaves flags alone)."""
+    return flags | GG_FLAG_STATIC_SCHED if os.environ.get("GG_SCHED") == "static" else flags
+
+
 def gg_device_error(workspace, stream=None):
     code = ctypes.c_int32(0)
     _check(load_library().gg_device_error(_ptr(workspace), _stream(stream), ctypes.byref(code)))
@@ -184,7 +190,7 @@ def gg_wgrad(a, a_major, b, b_major, offsets, tokens_sum, hidden, intermediate,
     ws, nbytes = _workspace(workspace, L.gg_wgrad_workspace_size(E), offsets, stream)
     _check(L.gg_wgrad(_ptr(a), a_major, _ptr(b), b_major, _ptr(offsets), E, tokens_sum, hidden,
                       intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
-                      int(bool(accumulate)), flags, _ptr(ws), nbytes, _stream(stream)))
+                      int(bool(accumulate)), _sched(flags), _ptr(ws), nbytes, _stream(stream)))
     return ws
 
 
@@ -199,7 +205,7 @@ def gg_wgrad_noalloc(a, a_major, b, b_major, offsets, tokens_sum, hidden, interm
         wgrad_dtype = _TORCH_DTYPE[wgrad_dense.dtype]
     _check(L.gg_wgrad_noalloc(_ptr(a), a_major, _ptr(b), b_major, _ptr(offsets), E, tokens_sum, hidden,
                               intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
-                              int(bool(accumulate)), flags, _stream(stream)))
+                              int(bool(accumulate)), _sched(flags), _stream(stream)))
 
 
 def gg_wgrad_mx(a, sfa, b, sfb, offsets, tokens_sum, hidden, intermediate, wgrad_dense=None,
@@ -214,7 +220,7 @@ def gg_wgrad_mx(a, sfa, b, sfb, offsets, tokens_sum, hidden, intermediate, wgrad
     ws, nbytes = _workspace(workspace, L.gg_wgrad_workspace_size(E), offsets, stream)
     _check(L.gg_wgrad_mx(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(offsets), E, tokens_sum,
                          hidden, intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
-                         int(bool(accumulate)), flags, _ptr(ws), nbytes, _stream(stream)))
+                         int(bool(accumulate)), _sched(flags), _ptr(ws), nbytes, _stream(stream)))
     return ws
 
 

@@ -11,6 +11,7 @@
 #include <cfloat>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -34,6 +35,19 @@ gg_status fail(gg_status s, const char* fmt, ...) {
 gg_status ok() {
     g_err[0] = '\0';
     return GG_OK;
+}
+
+// GG_LOG set (to anything but "0"): every launch reports the kernel variant
+// it chose, the workgroup tile and the grid on stderr, one line per call.
+// Read at every call (a getenv, no allocation).
+bool log_enabled() {
+    const char* v = getenv("GG_LOG");
+    return v && *v && strcmp(v, "0") != 0;
+}
+
+void log_launch(const char* op, const gg::LaunchInfo& i, const char* shape) {
+    fprintf(stderr, "[gg] %s %s: %s, tile %dx%d, %d waves, grid %lld\n", op, shape, i.kernel,
+            i.tm, i.tn, i.waves, (long long)i.grid);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -199,7 +213,7 @@ static gg_status wgrad_host_checks(const int32_t* offsets, int32_t num_experts, 
         return fail(GG_ERR_UNSUPPORTED, "more than 2^28 output tiles (256 x 256, all experts)");
     if (!aligned16(wgrad_dense) || !aligned16(wgrad_ptrs) || ((uintptr_t)offsets & 3u))
         return fail(GG_ERR_ALIGN, "the output must be 16-byte aligned, offsets 4-byte");
-    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_TENSOR_RAGGED))
+    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_TENSOR_RAGGED | GG_FLAG_STATIC_SCHED))
         return fail(GG_ERR_MODE, "unsupported flags 0x%x for %s", flags, name);
     return GG_OK;
 }
@@ -244,6 +258,7 @@ static gg_status run_wgrad(gg::WgradArgs& p, bool mx, const int32_t* offsets, in
     p.inter = intermediate;
     p.E = num_experts;
     p.ragged = (flags & GG_FLAG_TENSOR_RAGGED) != 0;
+    p.static_sched = (flags & GG_FLAG_STATIC_SCHED) != 0;
     // XCD blocks of an expert's tiles: the gm x (8/gm) grid that reads the
     // fewest operand panels (an A panel per M tile by 8/gm XCDs, a B panel
     // per N tile by gm), among those that divide the tile grid
@@ -262,9 +277,18 @@ static gg_status run_wgrad(gg::WgradArgs& p, bool mx, const int32_t* offsets, in
     }
     p.out_dtype = (int)wgrad_dtype;
     p.accumulate = accumulate ? 1 : 0;
-    e = mx ? gg::launch_wgrad_mx(p, s) : gg::launch_wgrad(p, s);
+    gg::LaunchInfo info{};
+    gg::LaunchInfo* li = log_enabled() ? &info : nullptr;
+    e = mx ? gg::launch_wgrad_mx(p, s, li) : gg::launch_wgrad(p, s, li);
     if (e != hipSuccess)
         return hip_fail(e, mx ? "launching gg_wgrad_mx" : "launching gg_wgrad");
+    if (li && info.grid > 0) {
+        char shape[128];
+        snprintf(shape, sizeof shape, "(E %d, hidden %d, intermediate %d, tokens %lld, out %s%s)",
+                 num_experts, hidden, intermediate, (long long)tokens_sum,
+                 gg::dtype_name(p.out_dtype), p.accumulate ? " +=" : "");
+        log_launch(mx ? "gg_wgrad_mx" : "gg_wgrad", info, shape);
+    }
     return ok();
 }
 
@@ -390,7 +414,8 @@ static gg_status check_dglu_common(gg_dtype c_dtype, gg_dtype d_dtype, gg_act ac
         return fail(GG_ERR_MODE, "act must be GG_DSWIGLU, GG_DGEGLU or GG_DSITUGLU");
     if (!aligned16(dbias) || ((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u))
         return fail(GG_ERR_ALIGN, "dbias must be 16-byte aligned, alpha and beta 4-byte");
-    if (flags & ~(uint32_t)(GG_FLAG_GATE_FIRST | GG_FLAG_GEGLU_MASK_FILTER | GG_FLAG_VALIDATE_OFFSETS))
+    if (flags & ~(uint32_t)(GG_FLAG_GATE_FIRST | GG_FLAG_GEGLU_MASK_FILTER | GG_FLAG_VALIDATE_OFFSETS |
+                            GG_FLAG_STATIC_SCHED))
         return fail(GG_ERR_MODE, "unsupported flags 0x%x for %s", flags, name);
     return GG_OK;
 }
@@ -445,9 +470,17 @@ static gg_status run_dglu(gg::DgluArgs& p, bool mx, const void* c, gg_dtype c_dt
     p.linear_offset = linear_offset;
     p.situ_b1 = situ_b1;
     p.situ_b2 = situ_b2;
-    e = mx ? gg::launch_dglu_mx(p, s) : gg::launch_dglu(p, s);
+    gg::LaunchInfo info{};
+    gg::LaunchInfo* li = log_enabled() ? &info : nullptr;
+    e = mx ? gg::launch_dglu_mx(p, s, li) : gg::launch_dglu(p, s, li);
     if (e != hipSuccess)
         return hip_fail(e, mx ? "launching gg_dglu_mx" : "launching gg_dglu");
+    if (li && info.grid > 0) {
+        char shape[128];
+        snprintf(shape, sizeof shape, "(L %d, m_rows %lld, k %d, n %d)", L, (long long)p.m_rows,
+                 p.K, p.N);
+        log_launch(mx ? "gg_dglu_mx" : "gg_dglu", info, shape);
+    }
     if (dbias) {
         e = gg::launch_dbias_finalize((uint16_t*)dbias, acc, nacc, s);
         if (e != hipSuccess)
@@ -609,7 +642,7 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
         ((uintptr_t)sfa & 3u) || ((uintptr_t)sfb & 3u) || ((uintptr_t)alpha & 3u) ||
         ((uintptr_t)amax & 3u))
         return fail(GG_ERR_ALIGN, "operands must be 16-byte aligned, scales 4-byte aligned");
-    if (flags & ~(uint32_t)GG_FLAG_VALIDATE_OFFSETS)
+    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_STATIC_SCHED))
         return fail(GG_ERR_MODE, "unsupported flags 0x%x for gg_dsrelu", flags);
     size_t need = gg_dsrelu_workspace_size(L);
     if (workspace_bytes < need)
@@ -654,9 +687,16 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
     p.L = L;
     p.c_dtype = (int)c_dtype;
     p.d_dtype = (int)d_dtype;
-    e = gg::launch_dsrelu(p, s);
+    gg::LaunchInfo info{};
+    gg::LaunchInfo* li = log_enabled() ? &info : nullptr;
+    e = gg::launch_dsrelu(p, s, li);
     if (e != hipSuccess)
         return hip_fail(e, "launching gg_dsrelu");
+    if (li && info.grid > 0) {
+        char shape[128];
+        snprintf(shape, sizeof shape, "(L %d, m_rows %lld, k %d, n %d)", L, (long long)m_rows, k, n);
+        log_launch("gg_dsrelu", info, shape);
+    }
     return ok();
 }
 

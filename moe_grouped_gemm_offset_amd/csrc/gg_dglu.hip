@@ -108,12 +108,22 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
                                                                        rows_valid, am0, bn0);
 }
 
-hipError_t launch_dglu(const DgluArgs& p, hipStream_t s) {
+hipError_t launch_dglu(const DgluArgs& p, hipStream_t s, LaunchInfo* info) {
     using C = DgluCfg;
     const int64_t tiles = ((p.m_rows + C::TM - 1) / C::TM) * ((p.N + C::TN - 1) / C::TN);
     if (tiles == 0)
         return hipSuccess;
     const dim3 grid((unsigned)tiles), block(C::kThreads);
+    if (info) {
+        static const char* const kAct[] = {"dSwiGLU", "dGeGLU", "dSiTU-GLU"};
+        snprintf(info->kernel, sizeof(info->kernel),
+                 "dglu_kernel<%s, B %s-major, C %s, D %s%s%s>", kAct[p.act], p.b_kmajor ? "K" : "N",
+                 dtype_name(p.c_dtype), dtype_name(p.d_dtype), p.dbias ? ", dbias" : "", p.act == 1 && p.mask_filter ? ", mask filter" : "");
+        info->tm = C::TM;
+        info->tn = C::TN;
+        info->waves = C::kWaves;
+        info->grid = tiles;
+    }
     auto go_act = [&](auto BK, auto W32, auto BF, auto DB) {
         constexpr bool bk = decltype(BK)::value, w32 = decltype(W32)::value;
         constexpr bool bf = decltype(BF)::value, db = decltype(DB)::value;

@@ -74,12 +74,22 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
         p, acc, smem, m0, n0, g, rows_valid, am0, bn0);
 }
 
-hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s) {
+hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s, LaunchInfo* info) {
     using C = DgluMxCfg;
     const int64_t tiles = ((p.m_rows + C::TM - 1) / C::TM) * ((p.N + C::TN - 1) / C::TN);
     if (tiles == 0)
         return hipSuccess;
     const dim3 grid((unsigned)tiles), block(C::kThreads);
+    if (info) {
+        static const char* const kAct[] = {"dSwiGLU", "dGeGLU", "dSiTU-GLU"};
+        snprintf(info->kernel, sizeof(info->kernel), "dglu_mx_kernel<%s, C %s, D %s%s>",
+                 kAct[p.act], dtype_name(p.c_dtype), dtype_name(p.d_dtype),
+                 p.dbias ? ", dbias" : "");
+        info->tm = C::TM;
+        info->tn = C::TN;
+        info->waves = C::kWaves;
+        info->grid = tiles;
+    }
     auto go = [&](auto W32, auto Q, auto BF) {
         constexpr bool w32 = decltype(W32)::value, q = decltype(Q)::value;
         constexpr bool bf = decltype(BF)::value;

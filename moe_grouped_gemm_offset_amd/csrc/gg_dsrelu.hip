@@ -169,12 +169,20 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     }
 }
 
-hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s) {
+hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s, LaunchInfo* info) {
     using C = DsreluCfg;
     const int64_t tiles = ((p.m_rows + C::TM - 1) / C::TM) * ((p.N + C::TN - 1) / C::TN);
     if (tiles == 0)
         return hipSuccess;
     const dim3 grid((unsigned)tiles), block(C::kThreads);
+    if (info) {
+        snprintf(info->kernel, sizeof(info->kernel), "dsrelu_kernel<C %s, D %s>",
+                 dtype_name(p.c_dtype), dtype_name(p.d_dtype));
+        info->tm = C::TM;
+        info->tn = C::TN;
+        info->waves = C::kWaves;
+        info->grid = tiles;
+    }
     if (p.d_dtype == kF8 && p.c_dtype == kBF16)
         hipLaunchKernelGGL((dsrelu_kernel<C, true, true>), grid, block, 0, s, p);
     else if (p.d_dtype == kF8)

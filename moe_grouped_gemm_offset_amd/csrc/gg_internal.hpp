@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cstdio>
 
 namespace gg {
 
@@ -70,6 +71,7 @@ struct WgradArgs {
     int hidden, inter, E;
     int a_kmajor, b_kmajor;
     int ragged;               // K-major operands stored tensor_ragged
+    int static_sched;         // persistent kernel: fixed item order, no queue
     int xcd_gm;               // XCD block grid rows for xcd_remap2d (0: 1-D remap)
     int out_dtype, accumulate;
 };
@@ -124,11 +126,25 @@ struct DsreluArgs {
 };
 
 // Launchers (return the HIP status of the launch).
-hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s);
-hipError_t launch_wgrad_mx(const WgradArgs& p, hipStream_t s);
-hipError_t launch_dglu(const DgluArgs& p, hipStream_t s);
-hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s);
-hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s);
+// Name of a gg_dtype code, for diagnostics.
+inline const char* dtype_name(int d) {
+    static const char* const kNames[] = {"bf16", "fp16", "fp32", "e4m3", "e5m2"};
+    return d >= 0 && d < 5 ? kNames[d] : "?";
+}
+
+// What a launcher chose (reported when GG_LOG is set): the kernel and its
+// variant, the workgroup tile, waves per workgroup and grid size.
+struct LaunchInfo {
+    char kernel[112];
+    int tm, tn, waves;
+    int64_t grid;
+};
+
+hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s, LaunchInfo* info);
+hipError_t launch_wgrad_mx(const WgradArgs& p, hipStream_t s, LaunchInfo* info);
+hipError_t launch_dglu(const DgluArgs& p, hipStream_t s, LaunchInfo* info);
+hipError_t launch_dglu_mx(const DgluArgs& p, hipStream_t s, LaunchInfo* info);
+hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s, LaunchInfo* info);
 
 // Prologue: clears the error word, `nclear` floats at `clear` and `nclear2`
 // floats at `clear2`, checks the offsets (wgrad: last == total; dgrad: last

@@ -163,10 +163,17 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     };
     FragBf16<C> frag;
 
+    // Static scheduling: workgroup j of the W that serve queue x takes its
+    // positions j, j + W, j + 2W, ... without the queue.  W = grid / 8 (the
+    // grid is a multiple of 8), or 1 when the grid has fewer than 8
+    // workgroups (one per item); W >= 1, so every workgroup's walk ends.
+    const int spos0 = blockIdx.x >> 3;
+    const int sstep = gridDim.x >= 8 ? (int)(gridDim.x >> 3) : 1;
     if (threadIdx.x == 0)
-        *bcast = atomicAdd(queue, 1);
+        *bcast = p.static_sched ? spos0 : atomicAdd(queue, 1);
     __syncthreads();
     const int t0 = 8 * uniform(*bcast) + x;
+    int spos = spos0;
     if (t0 >= total)
         return;
     decode(locate(t0));
@@ -188,9 +195,10 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         // (asking earlier hands the queue out in start order rather than
         // finish order, which scatters the tiles that share operand panels
         // and measured 20% more HBM fetch).
+        spos += sstep;
         int qpos = 0;
         if (threadIdx.x == 0)
-            qpos = atomicAdd(queue, 1);
+            qpos = p.static_sched ? spos : atomicAdd(queue, 1);
         __builtin_amdgcn_sched_barrier(0);
 
         // this item's output
@@ -278,7 +286,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
     }
 }
 
-hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s) {
+hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s, LaunchInfo* info) {
     using C = WgradCfg;
     const int64_t total = (int64_t)((p.hidden + C::TM - 1) / C::TM) *
                           ((p.inter + C::TN - 1) / C::TN) * p.E;
@@ -289,6 +297,20 @@ hipError_t launch_wgrad(const WgradArgs& p, hipStream_t s) {
     const dim3 grid((unsigned)persistent_grid(total)), block(C::kThreads);
     auto go = [&](auto AK, auto BK) {
         constexpr bool ak = decltype(AK)::value, bk = decltype(BK)::value;
+        if (info) {
+            const int out = p.out_dtype == kBF16 && !p.accumulate ? kOutBf16
+                          : p.out_dtype == kF32 && p.accumulate   ? kOutF32Acc
+                                                                  : kOutAny;
+            snprintf(info->kernel, sizeof(info->kernel),
+                     "wgrad_kernel<A %s-major, B %s-major, out %s> (%s scheduling)",
+                     ak ? "K" : "M", bk ? "K" : "N",
+                     out == kOutBf16 ? "bf16" : out == kOutF32Acc ? "fp32 +=" : "run-time",
+                     p.static_sched ? "static" : "dynamic");
+            info->tm = C::TM;
+            info->tn = C::TN;
+            info->waves = C::kWaves;
+            info->grid = grid.x;
+        }
         if (p.out_dtype == kBF16 && !p.accumulate)
             hipLaunchKernelGGL((wgrad_kernel<C, ak, bk, kOutBf16>), grid, block, 0, s, p);
         else if (p.out_dtype == kF32 && p.accumulate)

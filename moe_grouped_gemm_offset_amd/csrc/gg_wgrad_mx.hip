@@ -85,9 +85,16 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_mx_kernel(WgradArgs p) {
                       p.inter, m0 + am0, n0 + bn0, accumulate);
 }
 
-hipError_t launch_wgrad_mx(const WgradArgs& p, hipStream_t s) {
+hipError_t launch_wgrad_mx(const WgradArgs& p, hipStream_t s, LaunchInfo* info) {
     using C = WgradMxCfg;
     const int tiles = ((p.hidden + C::TM - 1) / C::TM) * ((p.inter + C::TN - 1) / C::TN);
+    if (info) {
+        snprintf(info->kernel, sizeof(info->kernel), "wgrad_mx_kernel (one tile per workgroup)");
+        info->tm = C::TM;
+        info->tn = C::TN;
+        info->waves = C::kWaves;
+        info->grid = (int64_t)tiles * p.E;
+    }
     hipLaunchKernelGGL((wgrad_mx_kernel<C>), dim3((unsigned)(tiles * p.E)), dim3(C::kThreads), 0,
                        s, p);
     return hipGetLastError();

@@ -73,6 +73,7 @@ def wgrad(**kw):
     (dict(ws=WS + 16), ALIGN),
     (dict(wsb=100), WORKSPACE),
     (dict(flags=1), MODE),
+    (dict(flags=32), MODE),
     (dict(T=1 << 22), UNSUPPORTED),
     (dict(hidden=1 << 20, inter=1 << 20, E=1024), UNSUPPORTED),
 ])
@@ -140,6 +141,7 @@ def dglu(**kw):
     (dict(L=1025), SHAPE),
     (dict(c=P + 2), ALIGN),
     (dict(flags=8), MODE),
+    (dict(flags=32), MODE),
     (dict(dbias=P, wsb=256), WORKSPACE),
 ])
 def test_dglu_rejects(kw, status):
@@ -167,9 +169,21 @@ def dsrelu(**kw):
     (dict(ddt=4), DTYPE),
     (dict(sfa=P + 1), ALIGN),
     (dict(wsb=16), WORKSPACE),
+    (dict(flags=8), MODE),
+    (dict(flags=32), MODE),
 ])
 def test_dsrelu_rejects(kw, status):
     assert dsrelu(**kw) == status
+
+
+@pytest.mark.parametrize("entry", ["wgrad", "wgrad_noalloc", "dglu", "dsrelu", "dglu_mx"])
+def test_static_sched_flag_accepted(entry):
+    """GG_FLAG_STATIC_SCHED passes every entry's flag check: the call gets as
+    far as it gets without it (the device check, where there is no GPU)."""
+    if torch.cuda.is_available():
+        pytest.skip("checks the no-device path")
+    call = globals()[entry]
+    assert call(flags=16) == call(flags=0) == DEVICE
 
 
 def fp8_out(**kw):

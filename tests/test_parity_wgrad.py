@@ -26,15 +26,16 @@ def gg():
     return binding
 
 
-def run_gpu(inp, out_dtype, accumulate=False, old=None, discrete=False, ragged=False):
+def run_gpu(inp, out_dtype, accumulate=False, old=None, discrete=False, ragged=False,
+            static=False):
     b = gg()
     E = len(inp["counts"])
     a, bb = inp["a"].cuda(), inp["b"].cuda()
-    flags = 0
+    flags = b.GG_FLAG_STATIC_SCHED if static else 0
     if ragged:
         # tensor_ragged storage of the K-major operands (the others are
         # per-token rows either way)
-        flags = b.GG_FLAG_TENSOR_RAGGED
+        flags |= b.GG_FLAG_TENSOR_RAGGED
         if inp["a_major"] == "k":
             a = synth.to_ragged(a, inp["counts"])
         if inp["b_major"] == "k":
@@ -256,3 +257,68 @@ def test_random_shapes(case):
     got, err = run_gpu(inp, dt, accumulate, old)
     assert err == 0
     compare(got, inp, dt, accumulate, old, name=f"random {case}")
+
+
+@pytest.mark.parametrize("a_major,b_major,dtype,accumulate", [
+    ("m", "n", torch.bfloat16, False),     # compile-time bf16 overwrite
+    ("k", "n", torch.bfloat16, False),
+    ("m", "n", torch.float32, True),       # compile-time fp32 accumulate
+    ("k", "k", torch.float16, False),      # run-time format
+    ("m", "n", torch.bfloat16, True),
+])
+def test_static_scheduling(a_major, b_major, dtype, accumulate):
+    """GG_FLAG_STATIC_SCHED (the pages' use_dynamic_sched=False): the items
+    are walked in a fixed order instead of taken from the work queues.  Each
+    tile is computed the same way either way, so the output is bit-identical
+    to the dynamic schedule's; the static one is also checked against the
+    oracle.  600 items (100 experts, some empty, on a 2 x 3 tile grid) give
+    every workgroup several."""
+    rng = np.random.default_rng(48)
+    counts = (rng.integers(0, 3, size=100) * 256).astype(np.int64)
+    counts[[3, 50, 99]] = 0
+    inp = synth.wgrad_inputs(512, 768, counts, a_major, b_major, seed=48)
+    old = synth.wgrad_initial(len(counts), 512, 768, dtype, seed=49) if accumulate else None
+    say("static scheduling", a_major, b_major, dtype, "acc" if accumulate else "overwrite")
+    dyn, err_d = run_gpu(inp, dtype, accumulate, old)
+    sta, err_s = run_gpu(inp, dtype, accumulate, old, static=True)
+    assert err_d == 0 and err_s == 0
+    assert torch.equal(dyn.view(torch.int16 if dtype != torch.float32 else torch.int32),
+                       sta.view(torch.int16 if dtype != torch.float32 else torch.int32)), \
+        "static and dynamic schedules differ"
+    compare(sta, inp, dtype, accumulate, old, name="static")
+
+
+@pytest.mark.parametrize("counts", [[256, 0, 512], [256, 256, 0, 512, 256, 0, 256]])
+def test_static_scheduling_small_grid(counts):
+    """Fewer items than 8 (a grid of one workgroup per item): each of them
+    serves its queue alone, under both schedules."""
+    inp = synth.wgrad_inputs(256, 256, counts, "m", "n", seed=50)
+    say("static scheduling, small grid", counts)
+    dyn, err_d = run_gpu(inp, torch.bfloat16)
+    sta, err_s = run_gpu(inp, torch.bfloat16, static=True)
+    assert err_d == 0 and err_s == 0
+    assert torch.equal(dyn.view(torch.int16), sta.view(torch.int16))
+    compare(sta, inp, torch.bfloat16, name="static small grid")
+
+
+def test_log_reports_launches(capfd, monkeypatch):
+    """GG_LOG=1: each launch reports the kernel variant, tile and grid on
+    stderr (the library reads GG_LOG at every call)."""
+    b = gg()
+    inp = synth.wgrad_inputs(256, 256, [256, 0, 512], "m", "n", seed=3)
+    out = torch.empty(3, 256, 256, dtype=torch.bfloat16, device="cuda")
+    args = (inp["a"].cuda(), 1, inp["b"].cuda(), 2, inp["offsets"].cuda(), inp["tokens_sum"], 256,
+            256)
+    capfd.readouterr()
+    monkeypatch.setenv("GG_LOG", "1")
+    b.gg_wgrad(*args, wgrad_dense=out)
+    b.gg_wgrad(*args, wgrad_dense=out, flags=b.GG_FLAG_STATIC_SCHED)
+    monkeypatch.setenv("GG_LOG", "0")
+    b.gg_wgrad(*args, wgrad_dense=out)
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    lines = [l for l in err.splitlines() if l.startswith("[gg] gg_wgrad")]
+    assert len(lines) == 2, err[-2000:]
+    assert "wgrad_kernel<A M-major, B N-major, out bf16> (dynamic scheduling)" in lines[0]
+    assert "(static scheduling)" in lines[1]
+    assert "tile 256x256, 8 waves, grid " in lines[0]
