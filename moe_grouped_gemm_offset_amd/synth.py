@@ -97,21 +97,25 @@ def small_ints(shape, lo, hi, gen, device, dtype=torch.bfloat16):
     return torch.randint(lo, hi + 1, shape, generator=gen, device=device).to(dtype)
 
 
-def mx_encode(x, block=32):
+FP8_MAX = {torch.float8_e4m3fn: 448.0, torch.float8_e5m2: 57344.0}
+
+
+def mx_encode(x, block=32, fmt=torch.float8_e4m3fn):
     """OCP MXFP8 encoding of an fp32 matrix (rows, K): one E8M0 scale per
-    `block` consecutive K values of each row and E4M3 codes.  The scale
-    exponent is e = ceil(log2(amax / 448)) over the block (so no code
-    saturates), the stored byte is e + 127, and each code is the E4M3 value
-    nearest to x / 2^e (torch's cast, ties to even).  An all-zero block takes
-    e = -127 (byte 0).  Returns (codes as torch.float8_e4m3fn, scales as
-    torch.uint8)."""
+    `block` consecutive K values of each row and FP8 codes (E4M3, or E5M2
+    with fmt=torch.float8_e5m2).  The scale exponent is
+    e = ceil(log2(amax / max)) over the block, max the format's largest
+    value (so no code saturates), the stored byte is e + 127, and each code
+    is the FP8 value nearest to x / 2^e (torch's cast, ties to even).  An
+    all-zero block takes e = -127 (byte 0).  Returns (codes as fmt, scales
+    as torch.uint8)."""
     rows, K = x.shape
     assert K % block == 0
     xb = x.reshape(rows, K // block, block)
     amax = xb.abs().amax(dim=2)
-    e = torch.ceil(torch.log2(amax / 448.0))
+    e = torch.ceil(torch.log2(amax / FP8_MAX[fmt]))
     e = torch.where(amax > 0, e, torch.full_like(e, -127.0)).clamp_(-127, 127)
-    q = (xb / torch.exp2(e).unsqueeze(2)).to(torch.float8_e4m3fn)
+    q = (xb / torch.exp2(e).unsqueeze(2)).to(fmt)
     return q.reshape(rows, K), (e + 127).to(torch.uint8)
 
 
@@ -141,7 +145,8 @@ def wgrad_inputs(hidden, inter, counts, a_major="k", b_major="n", seed=0,
                 counts=counts, hidden=hidden, inter=inter, tokens_sum=T)
 
 
-def wgrad_mx_inputs(hidden, inter, counts, seed=0, device="cpu", scale_spread=0, ints=False):
+def wgrad_mx_inputs(hidden, inter, counts, seed=0, device="cpu", scale_spread=0, ints=False,
+                    ab_dtype=torch.float8_e4m3fn):
     """Inputs of the block-scaled (MXFP8) grouped wgrad.
 
     A is the logical (hidden, T) matrix, stored K-major; B the logical
@@ -164,7 +169,7 @@ def wgrad_mx_inputs(hidden, inter, counts, seed=0, device="cpu", scale_spread=0,
             j = torch.randint(-scale_spread, scale_spread + 1, (rows, 1), generator=g,
                               device=device).float()
             x = x * torch.exp2(j)
-        return mx_encode(x)
+        return mx_encode(x, fmt=ab_dtype)
 
     a, sfa = draw(hidden)
     b, sfb = draw(inter)
@@ -232,7 +237,7 @@ def dglu_inputs(L, K, N, counts, a_std=0.02, b_std=0.02, c_std=2.0,
 
 
 def dsrelu_inputs(L, K, N, counts, c_dtype=torch.bfloat16, m_extra=0, seed=0,
-                  device="cpu", discrete=False, scale_spread=0):
+                  device="cpu", discrete=False, scale_spread=0, ab_dtype=torch.float8_e4m3fn):
     """Inputs of the grouped block-scaled dgrad + dsReLU.
 
     A (M, K) and B (N, K) per expert are N(0,1) values MXFP8-encoded by
@@ -251,7 +256,7 @@ def dsrelu_inputs(L, K, N, counts, c_dtype=torch.bfloat16, m_extra=0, seed=0,
             j = torch.randint(-scale_spread, scale_spread + 1, (rows, 1), generator=g,
                               device=device).float()
             x = x * torch.exp2(j)
-        return mx_encode(x)
+        return mx_encode(x, fmt=ab_dtype)
 
     a, sfa = draw(M)
     bl, sl = [], []
@@ -276,7 +281,8 @@ def dsrelu_inputs(L, K, N, counts, c_dtype=torch.bfloat16, m_extra=0, seed=0,
 
 
 def dglu_mx_inputs(L, K, N, counts, c_std=2.0, c_dtype=torch.bfloat16, m_extra=0,
-                   seed=0, device="cpu", discrete=True, scale_spread=0, ints=False):
+                   seed=0, device="cpu", discrete=True, scale_spread=0, ints=False,
+                   ab_dtype=torch.float8_e4m3fn):
     """Inputs of the grouped block-scaled dgrad + dGLU.
 
     A (M, K) and B (N, K) per expert are N(0,1) values (integers in [-2, 2]
@@ -298,7 +304,7 @@ def dglu_mx_inputs(L, K, N, counts, c_std=2.0, c_dtype=torch.bfloat16, m_extra=0
             j = torch.randint(-scale_spread, scale_spread + 1, (rows, 1), generator=g,
                               device=device).float()
             x = x * torch.exp2(j)
-        return mx_encode(x)
+        return mx_encode(x, fmt=ab_dtype)
 
     a, sfa = draw(M)
     bl, sl = [], []
@@ -354,7 +360,7 @@ def bits(t):
     t = t.detach().cpu().contiguous()
     if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         return t.view(torch.uint8).numpy()
     return t.numpy()
 

@@ -42,7 +42,7 @@
 int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* dtype codes used by this file (its own numbering) */
-enum { ORC_BF16 = 0, ORC_F16 = 1, ORC_F32 = 2 };
+enum { ORC_BF16 = 0, ORC_F16 = 1, ORC_F32 = 2, ORC_E4M3 = 3, ORC_E5M2 = 4 };
 
 /* ------------------------------------------------------------------------ */
 /* Decoders: bit pattern -> exact double.                                    */
@@ -84,6 +84,28 @@ double orc_e4m3_to_double(uint8_t q) {
     return s ? -v : v;
 }
 
+/* OCP FP8 E5M2 ("e5m2"): 1 sign, 5 exponent (bias 15), 2 fraction bits, with
+ * infinities (S.11111.00) and NaNs (S.11111.xx, xx != 0); largest finite
+ * 57344.  The pages list float8_e5m2 beside float8_e4m3fn for FP8 operands,
+ * C and D ("Grouped GEMM + dGLU (SM100)", "Support Surface and Constraints /
+ * Data Types"). */
+double orc_e5m2_to_double(uint8_t q) {
+    int s = (q >> 7) & 1, e = (q >> 2) & 0x1f, m = q & 3;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -16);                    /* subnormal: m/4 * 2^-14 */
+    else
+        v = ldexp((double)(m + 4), e - 15 - 2);       /* 1.m * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* E4M3 (fmt 0) or E5M2 (fmt 1) code to its exact value. */
+static double fp8_decode(uint8_t q, int fmt) {
+    return fmt ? orc_e5m2_to_double(q) : orc_e4m3_to_double(q);
+}
+
 /* OCP E8M0 scale ("float8_e8m0fnu"): the byte is a biased power-of-two
  * exponent, value 2^(e-127); 0xFF is NaN. */
 double orc_e8m0_to_double(uint8_t e) {
@@ -96,6 +118,8 @@ double orc_decode(const void* base, int dtype, int64_t i) {
     switch (dtype) {
     case ORC_BF16: return orc_bf16_to_double(((const uint16_t*)base)[i]);
     case ORC_F16:  return orc_f16_to_double(((const uint16_t*)base)[i]);
+    case ORC_E4M3: return orc_e4m3_to_double(((const uint8_t*)base)[i]);
+    case ORC_E5M2: return orc_e5m2_to_double(((const uint8_t*)base)[i]);
     default:       return (double)((const float*)base)[i];
     }
 }
@@ -163,28 +187,38 @@ float orc_double_to_f32(double x) {
     return signbit(x) ? -f : f;
 }
 
-/* OCP E4M3 ("float8_e4m3fn": 4 significand bits, minimum normal exponent
- * -6, largest finite 448, no infinity) of the exact value hi + lo, where lo
- * is the rounding error of hi (|lo| <= half an ulp of hi, the same sign
- * convention as the value), by round-to-nearest-even; magnitudes above 448
- * are clamped to 448 first.  hi is the double nearest to the value, so the
- * value and hi fall on the same side of every E4M3 rounding midpoint except
- * when hi is that midpoint: then lo decides the direction. */
-static uint8_t e4m3_of_sum(double hi, double lo) {
+/* The two FP8 formats' parameters: fraction bits, minimum normal exponent,
+ * exponent bias and largest finite value (E4M3 "float8_e4m3fn": 3, -6, 7,
+ * 448 = 7 * 2^6; E5M2 "float8_e5m2": 2, -14, 15, 57344 = 7 * 2^13). */
+static const int kFp8Frac[2] = {3, 2}, kFp8Emin[2] = {-6, -14}, kFp8Bias[2] = {7, 15};
+static const double kFp8Max[2] = {448.0, 57344.0};
+static const int kFp8MaxExp[2] = {6, 13};      /* max = 7 * 2^kFp8MaxExp */
+
+/* FP8 code (fmt 0: E4M3, 1: E5M2) of the exact value hi + lo, where lo is
+ * the rounding error of hi (|lo| <= half an ulp of hi, the same sign
+ * convention as the value), by round-to-nearest-even; magnitudes above the
+ * format's largest finite value are clamped to it first (so neither
+ * format's infinities or NaNs result from a finite input).  hi is the
+ * double nearest to the value, so the value and hi fall on the same side of
+ * every FP8 rounding midpoint except when hi is that midpoint: then lo
+ * decides the direction. */
+static uint8_t fp8_of_sum(double hi, double lo, int fmt) {
+    const int fb = kFp8Frac[fmt], emin = kFp8Emin[fmt], bias = kFp8Bias[fmt];
+    const double maxfin = kFp8Max[fmt];
     if (isnan(hi))
-        return 0x7f;
+        return 0x7f;                              /* NaN in both: S.1111.111, S.11111.11 */
     uint8_t s = signbit(hi) ? 0x80u : 0u;
     double ax = fabs(hi), alo = signbit(hi) ? -lo : lo;   /* value = ax + alo, >= 0 */
     double y;
-    if (ax >= 448.0) {
-        y = 448.0;
+    if (ax >= maxfin) {
+        y = maxfin;
     } else if (ax == 0.0) {
         y = 0.0;
     } else {
         int E;
         frexp(ax, &E);
-        int e = E - 1 < -6 ? -6 : E - 1;          /* ax in [2^e, 2^(e+1)) or subnormal */
-        int ulp = e - 3;
+        int e = E - 1 < emin ? emin : E - 1;      /* ax in [2^e, 2^(e+1)) or subnormal */
+        int ulp = e - fb;
         double q = ldexp(ax, -ulp);               /* exact */
         double fl = floor(q);
         double r;
@@ -193,37 +227,44 @@ static uint8_t e4m3_of_sum(double hi, double lo) {
         else
             r = nearbyint(q);                     /* ties to even */
         y = ldexp(r, ulp);
-        if (y > 448.0)
-            y = 448.0;
+        if (y > maxfin)
+            y = maxfin;
     }
     if (y == 0.0)
         return s;
     int E;
     frexp(y, &E);
     int e = E - 1;
-    if (e < -6)                                    /* subnormal: y = m * 2^-9 */
-        return s | (uint8_t)(int)ldexp(y, 9);
-    int m = (int)(ldexp(y, -e) * 8.0) - 8;         /* exact: 3 fraction bits */
-    return s | (uint8_t)(((e + 7) << 3) | m);
+    if (e < emin)                                  /* subnormal: y = m * 2^(emin - fb) */
+        return s | (uint8_t)(int)ldexp(y, fb - emin);
+    int m = (int)(ldexp(y, -e) * (double)(1 << fb)) - (1 << fb);   /* exact */
+    return s | (uint8_t)(((e + bias) << fb) | m);
 }
 
+static uint8_t e4m3_of_sum(double hi, double lo) { return fp8_of_sum(hi, lo, 0); }
+
 uint8_t orc_double_to_e4m3(double x) { return e4m3_of_sum(x, 0.0); }
+uint8_t orc_double_to_e5m2(double x) { return fp8_of_sum(x, 0.0, 1); }
 
 /* [G] "Block-scaled contract / Equations", step 3 (and the FP8 D_row / D_col
  * with SFD_row / SFD_col of [S] "Shapes"): blocks of 32 values (32 columns of
  * a row for D_row, 32 rows of a column for D_col) share one E8M0 scale
  *   SFD = norm_const * max|D| * rcp_max,   D_q = D * norm_const / SFD,
- * with rcp_max = 1/448 (E4M3).  E8M0 holds powers of two only: SFD is taken
- * as the smallest power of two 2^e not below the product (so |D_q| <= 448),
- * e clamped to [-127, 127], e = -127 for an all-zero block.  Both the
- * exponent and the codes are decided in exact arithmetic on the double D:
- * no intermediate rounding of D, of the product or of the quotient. */
+ * with rcp_max the reciprocal of the output format's largest value (1/448
+ * for E4M3, 1/57344 for E5M2: the reading of rcp_max used here).  E8M0
+ * holds powers of two only: SFD is taken as the smallest power of two 2^e
+ * not below the product (so |D_q| <= the largest value), e clamped to
+ * [-127, 127], e = -127 for an all-zero block.  Both the exponent and the
+ * codes are decided in exact arithmetic on the double D: no intermediate
+ * rounding of D, of the product or of the quotient. */
 
-/* Smallest integer e with 2^e >= norm_const * amax / 448, exactly: with
- * amax = ia 2^(ea-53) and norm_const = in 2^(en-24) (integer significands
- * from frexp; a float's fits 24 bits, a double's 53), the condition reads
- * 7 * 2^(e + 83 - ea - en) >= ia * in, a comparison of integers below 2^80. */
-static int fp8_block_exponent(double amax, float norm_const) {
+/* Smallest integer e with 2^e >= norm_const * amax / (7 * 2^k), k = 6 for
+ * E4M3 (448) and 13 for E5M2 (57344), exactly: with amax = ia 2^(ea-53) and
+ * norm_const = in 2^(en-24) (integer significands from frexp; a float's fits
+ * 24 bits, a double's 53), the condition reads
+ * 7 * 2^(e + k + 77 - ea - en) >= ia * in, a comparison of integers below
+ * 2^80. */
+static int fp8_block_exponent(double amax, float norm_const, int fmt) {
     double nc = (double)norm_const;
     if (!(amax > 0.0) || !(nc > 0.0))
         return -127;
@@ -236,25 +277,25 @@ static int fp8_block_exponent(double amax, float norm_const) {
     int s = 0;
     while (((unsigned __int128)7 << s) < prod)
         s++;
-    int e = s - 83 + ea + en;
+    int e = s - kFp8MaxExp[fmt] - 77 + ea + en;
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-/* E4M3 code of d * norm_const * 2^-e: the product is split exactly into
- * its double rounding and that rounding's error (a fused multiply-add
- * recovers the error exactly), and scaling by 2^-e is exact. */
-static uint8_t fp8_quantize(double d, float norm_const, int e) {
+/* FP8 code of d * norm_const * 2^-e: the product is split exactly into its
+ * double rounding and that rounding's error (a fused multiply-add recovers
+ * the error exactly), and scaling by 2^-e is exact. */
+static uint8_t fp8_quantize(double d, float norm_const, int e, int fmt) {
     double nc = (double)norm_const;
     double hi = d * nc;
     double lo = fma(d, nc, -hi);
-    return e4m3_of_sum(ldexp(hi, -e), ldexp(lo, -e));
+    return fp8_of_sum(ldexp(hi, -e), ldexp(lo, -e), fmt);
 }
 
-/* D (nrows, W) doubles, W a multiple of 32.  q_row (nrows, W) E4M3 and
- * sfd_row (nrows, W/32) E8M0: row blocks; if q_col is non-NULL (nrows a
- * multiple of 32, consecutive rows): q_col (nrows, W) and sfd_col
- * (W, nrows/32), column blocks of rows 32j .. 32j+31. */
-void orc_quant_fp8(const double* D, int64_t nrows, int W, float norm_const,
+/* D (nrows, W) doubles, W a multiple of 32; fmt 0: E4M3, 1: E5M2 codes.
+ * q_row (nrows, W) codes and sfd_row (nrows, W/32) E8M0: row blocks; if q_col
+ * is non-NULL (nrows a multiple of 32, consecutive rows): q_col (nrows, W)
+ * and sfd_col (W, nrows/32), column blocks of rows 32j .. 32j+31. */
+void orc_quant_fp8(const double* D, int64_t nrows, int W, float norm_const, int fmt,
                    uint8_t* q_row, uint8_t* sfd_row, uint8_t* q_col, uint8_t* sfd_col) {
     int WB = W / 32;
     for (int64_t r = 0; r < nrows; r++)
@@ -264,10 +305,10 @@ void orc_quant_fp8(const double* D, int64_t nrows, int W, float norm_const,
                 double v = fabs(D[r * W + 32 * b + k]);
                 amax = v > amax ? v : amax;
             }
-            int e = fp8_block_exponent(amax, norm_const);
+            int e = fp8_block_exponent(amax, norm_const, fmt);
             sfd_row[r * WB + b] = (uint8_t)(e + 127);
             for (int k = 0; k < 32; k++)
-                q_row[r * W + 32 * b + k] = fp8_quantize(D[r * W + 32 * b + k], norm_const, e);
+                q_row[r * W + 32 * b + k] = fp8_quantize(D[r * W + 32 * b + k], norm_const, e, fmt);
         }
     if (!q_col)
         return;
@@ -279,10 +320,11 @@ void orc_quant_fp8(const double* D, int64_t nrows, int W, float norm_const,
                 double v = fabs(D[(32 * j + k) * W + c]);
                 amax = v > amax ? v : amax;
             }
-            int e = fp8_block_exponent(amax, norm_const);
+            int e = fp8_block_exponent(amax, norm_const, fmt);
             sfd_col[(int64_t)c * RB + j] = (uint8_t)(e + 127);
             for (int k = 0; k < 32; k++)
-                q_col[(32 * j + k) * W + c] = fp8_quantize(D[(32 * j + k) * W + c], norm_const, e);
+                q_col[(32 * j + k) * W + c] =
+                    fp8_quantize(D[(32 * j + k) * W + c], norm_const, e, fmt);
         }
 }
 
@@ -347,7 +389,8 @@ void orc_wgrad(const uint16_t* A, int a_major, const uint16_t* B, int b_major,
 }
 
 /* [W] "Block-scaled contract" on MXFP8 operands: the "Operation" of the page
- * with every operand value dequantized, deq(q) = e4m3(q) * 2^(e8m0 - 127),
+ * with every operand value dequantized, deq(q) = fp8(q) * 2^(e8m0 - 127),
+ * fp8 the E4M3 (ab_fmt 0) or E5M2 (ab_fmt 1) value of the code,
  * one E8M0 scale per 32 consecutive tokens (the K axis) of a row.
  *   A (hidden, T) K-major codes: (h,t) at h*T + t; SFA (hidden, T/32):
  *     SFA[h*(T/32) + t/32].
@@ -356,7 +399,7 @@ void orc_wgrad(const uint16_t* A, int a_major, const uint16_t* B, int b_major,
  * Outputs as for orc_wgrad (exact products, in double, per listed row); the
  * accumulate rule and the rounding are orc_wgrad_finish's. */
 void orc_wgrad_mx(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
-                  const int32_t* offsets, int E, int64_t T, int hidden, int inter,
+                  int ab_fmt, const int32_t* offsets, int E, int64_t T, int hidden, int inter,
                   const int32_t* hrows, int nrows, double* out) {
     if (!hrows)
         nrows = hidden;
@@ -370,7 +413,7 @@ void orc_wgrad_mx(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const 
 #pragma omp parallel for schedule(static)
         for (int i = 0; i < inter; i++)
             for (int64_t t = begin; t < end; t++)
-                Bd[(t - begin) * inter + i] = orc_e4m3_to_double(B[(int64_t)i * T + t]) *
+                Bd[(t - begin) * inter + i] = fp8_decode(B[(int64_t)i * T + t], ab_fmt) *
                                               orc_e8m0_to_double(SFB[(int64_t)i * TB + t / 32]);
 #pragma omp parallel for schedule(dynamic, 1)
         for (int r = 0; r < nrows; r++) {
@@ -380,7 +423,7 @@ void orc_wgrad_mx(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const 
             for (int i = 0; i < inter; i++)
                 o[i] = 0.0;
             for (int64_t t = begin; t < end; t++) {
-                double av = orc_e4m3_to_double(A[(int64_t)h * T + t]) *
+                double av = fp8_decode(A[(int64_t)h * T + t], ab_fmt) *
                             orc_e8m0_to_double(SFA[(int64_t)h * TB + t / 32]);
                 const double* bt = Bd + (t - begin) * inter;
                 for (int i = 0; i < inter; i++)
@@ -619,17 +662,20 @@ void orc_dglu(const uint16_t* A, int64_t M, int K,
 }
 
 /* [G] "Block-scaled contract / Equations", steps 1 and 2, on MXFP8 operands:
- * R_g = alpha_g^2 * sum_k deq(A[m,k]) deq(B_g[n,k]), with deq(q) = e4m3(q) *
+ * R_g = alpha_g^2 * sum_k deq(A[m,k]) deq(B_g[n,k]), with deq(q) = fp8(q) *
  * 2^(e8m0 - 127) and one E8M0 scale per 32 K values of a row, then the dGLU
  * epilogue of orc_dglu (and dSiTU-GLU, act 2, of the same section).
- *   A (M, K) E4M3, K-major; SFA (M, K/32) E8M0: SFA[m*(K/32) + k/32].
- *   Bp[g] -> expert g's (N, K) E4M3, K-major; SFBp[g] -> its (N, K/32).
+ *   A (M, K) FP8 codes (ab_fmt 0: E4M3, 1: E5M2), K-major; SFA (M, K/32)
+ *   E8M0: SFA[m*(K/32) + k/32].
+ *   Bp[g] -> expert g's (N, K) codes, K-major; SFBp[g] -> its (N, K/32).
+ *   C may also hold E4M3 or E5M2 codes (c_dtype ORC_E4M3 / ORC_E5M2, the
+ *   block-scaled contract's FP8 C), decoded exactly.
  * Other arguments and outputs as for orc_dglu, plus
  *   amax[2g + h] (h 0: the input-gradient columns, 1: the gate-gradient
  *   columns) raised to max |D| over the listed rows of group g (the caller
  *   initialises it). */
 void orc_dglu_mx(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
-                 const uint8_t* const* Bp, const uint8_t* const* SFBp, int N,
+                 const uint8_t* const* Bp, const uint8_t* const* SFBp, int N, int ab_fmt,
                  const void* C, int c_dtype, const int32_t* po, int L,
                  const float* alpha, const float* beta, const float* prob,
                  int act, double ga, double clamp_lo, double clamp_hi, double lo,
@@ -653,7 +699,7 @@ void orc_dglu_mx(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
 #pragma omp parallel for schedule(static)
         for (int k = 0; k < K; k++)
             for (int n = 0; n < N; n++)
-                Bt[(int64_t)k * N + n] = orc_e4m3_to_double(Bg[(int64_t)n * K + k]) *
+                Bt[(int64_t)k * N + n] = fp8_decode(Bg[(int64_t)n * K + k], ab_fmt) *
                                          orc_e8m0_to_double(Sg[(int64_t)n * KB + k / 32]);
         double a2 = (double)alpha[g] * (double)alpha[g];
 #pragma omp parallel
@@ -665,7 +711,7 @@ void orc_dglu_mx(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
                 int64_t r = idx[j];
                 int64_t m = rows ? rows[r] : r;
                 for (int k = 0; k < K; k++)
-                    Ad[k] = orc_e4m3_to_double(A[m * K + k]) *
+                    Ad[k] = fp8_decode(A[m * K + k], ab_fmt) *
                             orc_e8m0_to_double(SFA[m * KB + k / 32]);
                 row_product(Ad, Bt, K, N, a2, R);
                 dprob_sum[r] = dglu_row(R, m, g, N, C, c_dtype, beta, prob, act, ga, clamp_lo,
@@ -703,12 +749,15 @@ void orc_dglu_mx(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
 /* ------------------------------------------------------------------------ */
 
 /* Inputs:
- *   A (M, K) e4m3 codes, row-major; SFA (M, K/32) e8m0, row-major: one scale
+ *   A (M, K) fp8 codes (ab_fmt 0: E4M3, 1: E5M2), row-major; SFA (M, K/32)
+ *   e8m0, row-major: one scale
  *   for each 32-element K block of each row.
- *   Bp[g] -> expert g's (N, K) e4m3 codes (n,k) at n*K + k; SFBp[g] -> its
+ *   Bp[g] -> expert g's (N, K) fp8 codes (n,k) at n*K + k; SFBp[g] -> its
  *   (N, K/32) e8m0 scales.
  *   C (M, N) row-major, c_dtype; alpha (L) fp32; prob (M) fp32.
- * With dequantize(q, s) = e4m3(q) * 2^(s-127):
+ *   C may also hold E4M3 or E5M2 codes (c_dtype ORC_E4M3 / ORC_E5M2, the
+ *   block-scaled contract's FP8 C), decoded exactly.
+ * With dequantize(q, s) = fp8(q) * 2^(s-127):
  *   G[m,n]     = alpha_g * sum_k deq(A[m,k]) * deq(B_g[n,k])
  *   D_row[m,n] = prob[m] * 2 * C[m,n] * relu(G[m,n])
  *   dprob[m]   = sum_n C[m,n] * relu(G[m,n])^2
@@ -716,7 +765,7 @@ void orc_dglu_mx(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
  *                amax is only raised here, the caller starts it at 0.
  * Outputs (double): D[r*N + n], dprob_sum[r], amax[g] for the listed rows. */
 void orc_dsrelu(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
-                const uint8_t* const* Bp, const uint8_t* const* SFBp, int N,
+                const uint8_t* const* Bp, const uint8_t* const* SFBp, int N, int ab_fmt,
                 const void* C, int c_dtype, const int32_t* po, int L,
                 const float* alpha, const float* prob,
                 const int64_t* rows, int64_t nrows,
@@ -737,7 +786,7 @@ void orc_dsrelu(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
 #pragma omp parallel for schedule(static)
         for (int k = 0; k < K; k++)
             for (int n = 0; n < N; n++)
-                Bt[(int64_t)k * N + n] = orc_e4m3_to_double(Bg[(int64_t)n * K + k]) *
+                Bt[(int64_t)k * N + n] = fp8_decode(Bg[(int64_t)n * K + k], ab_fmt) *
                                          orc_e8m0_to_double(Sg[(int64_t)n * KB + k / 32]);
 #pragma omp parallel
         {
@@ -748,7 +797,7 @@ void orc_dsrelu(const uint8_t* A, const uint8_t* SFA, int64_t M, int K,
                 int64_t r = idx[j];
                 int64_t m = rows ? rows[r] : r;
                 for (int k = 0; k < K; k++)
-                    Ad[k] = orc_e4m3_to_double(A[m * K + k]) *
+                    Ad[k] = fp8_decode(A[m * K + k], ab_fmt) *
                             orc_e8m0_to_double(SFA[m * KB + k / 32]);
                 /* G[m, n] = alpha_g * sum_k deq(A[m,k]) * deq(B_g[n,k]) */
                 row_product(Ad, Bt, K, N, (double)alpha[g], G);

@@ -15,7 +15,7 @@ marshals numpy arrays and applies the pages' output rules:
   sum, Amax is per expert (shape (L, 1)).
 
 All raw operands are numpy arrays of bit patterns: uint16 for bf16/fp16,
-uint8 for e4m3 codes and e8m0 scales, float32 for fp32.
+uint8 for FP8 (E4M3 or E5M2) codes and e8m0 scales, float32 for fp32.
 """
 import ctypes
 import os
@@ -24,8 +24,14 @@ import numpy as np
 
 from . import build as _build
 
-BF16, F16, F32 = 0, 1, 2
-_DT_NP = {BF16: np.uint16, F16: np.uint16, F32: np.float32}
+BF16, F16, F32, E4M3, E5M2 = 0, 1, 2, 3, 4
+_DT_NP = {BF16: np.uint16, F16: np.uint16, F32: np.float32, E4M3: np.uint8, E5M2: np.uint8}
+
+
+def _fmt(fp8_dtype):
+    """The C file's FP8 format index: 0 for E4M3, 1 for E5M2."""
+    assert fp8_dtype in (E4M3, E5M2), fp8_dtype
+    return fp8_dtype - E4M3
 
 _lib = None
 
@@ -45,6 +51,8 @@ def lib():
         L.orc_f16_to_double.restype = D
         L.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_to_double.restype = D
+        L.orc_e5m2_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e5m2_to_double.restype = D
         L.orc_e8m0_to_double.argtypes = [ctypes.c_uint8]
         L.orc_e8m0_to_double.restype = D
         L.orc_double_to_bf16.argtypes = [D]
@@ -58,20 +66,22 @@ def lib():
         L.orc_wgrad.argtypes = [P, I, P, I, P, I, I64, I, I, P, I, P]
         L.orc_wgrad.restype = None
         L.orc_wgrad_finish.argtypes = [P, I64, I, P, I, P]
-        L.orc_wgrad_mx.argtypes = [P, P, P, P, P, I, I64, I, I, P, I, P]
+        L.orc_wgrad_mx.argtypes = [P, P, P, P, I, P, I, I64, I, I, P, I, P]
         L.orc_double_to_e4m3.argtypes = [D]
         L.orc_double_to_e4m3.restype = ctypes.c_uint8
-        L.orc_quant_fp8.argtypes = [P, I64, I, ctypes.c_float, P, P, P, P]
+        L.orc_double_to_e5m2.argtypes = [D]
+        L.orc_double_to_e5m2.restype = ctypes.c_uint8
+        L.orc_quant_fp8.argtypes = [P, I64, I, ctypes.c_float, I, P, P, P, P]
         L.orc_quant_fp8.restype = None
         L.orc_wgrad_mx.restype = None
         L.orc_wgrad_finish.restype = None
         L.orc_dglu.argtypes = [P, I64, I, P, I, I, P, I, P, I, P, P, P,
                                I, D, D, D, D, I, I, P, I64, P, P, P]
         L.orc_dglu.restype = None
-        L.orc_dsrelu.argtypes = [P, P, I64, I, P, P, I, P, I, P, I, P, P,
+        L.orc_dsrelu.argtypes = [P, P, I64, I, P, P, I, I, P, I, P, I, P, P,
                                  P, I64, P, P, P]
         L.orc_dsrelu.restype = None
-        L.orc_dglu_mx.argtypes = [P, P, I64, I, P, P, I, P, I, P, I, P, P, P,
+        L.orc_dglu_mx.argtypes = [P, P, I64, I, P, P, I, I, P, I, P, I, P, P, P,
                                   I, D, D, D, D, D, D, I, I, P, I64, P, P, P, P]
         L.orc_dglu_mx.restype = None
         L.orc_num_threads.argtypes = []
@@ -112,6 +122,12 @@ def decode_e4m3(codes):
                     np.float64).reshape(codes.shape)
 
 
+def decode_e5m2(codes):
+    codes = np.asarray(codes)
+    return np.array([lib().orc_e5m2_to_double(int(c)) for c in codes.ravel()],
+                    np.float64).reshape(codes.shape)
+
+
 def decode_e8m0(codes):
     codes = np.asarray(codes)
     return np.array([lib().orc_e8m0_to_double(int(c)) for c in codes.ravel()],
@@ -133,19 +149,26 @@ def encode_e4m3(x):
     return np.array([lib().orc_double_to_e4m3(float(v)) for v in x], np.uint8)
 
 
-def quant_fp8(D, norm_const, with_col=True):
+def encode_e5m2(x):
+    """OCP E5M2 codes (uint8) of float64 values, RNE, magnitudes clamped to 57344."""
+    x = np.asarray(x, np.float64).ravel()
+    return np.array([lib().orc_double_to_e5m2(float(v)) for v in x], np.uint8)
+
+
+def quant_fp8(D, norm_const, with_col=True, d_dtype=E4M3):
     """Step 3 of the block-scaled dGLU contract (and the FP8 outputs of the
-    dsReLU page) on a float64 (nrows, W) D: row-quantized E4M3 codes and
-    E8M0 scales per 32 columns, and (with_col, nrows a multiple of 32) the
-    column-quantized codes with scales per 32 rows, laid out (W, nrows/32)."""
+    dsReLU page) on a float64 (nrows, W) D: row-quantized codes (E4M3, or
+    E5M2 with d_dtype=E5M2) and E8M0 scales per 32 columns, and (with_col,
+    nrows a multiple of 32) the column-quantized codes with scales per 32
+    rows, laid out (W, nrows/32)."""
     D = np.ascontiguousarray(D, np.float64)
     nrows, W = D.shape
     q_row = np.zeros((nrows, W), np.uint8)
     sfd_row = np.zeros((nrows, W // 32), np.uint8)
     q_col = np.zeros((nrows, W), np.uint8) if with_col else None
     sfd_col = np.zeros((W, nrows // 32), np.uint8) if with_col else None
-    lib().orc_quant_fp8(_p(D), nrows, W, float(norm_const), _p(q_row), _p(sfd_row), _p(q_col),
-                        _p(sfd_col))
+    lib().orc_quant_fp8(_p(D), nrows, W, float(norm_const), _fmt(d_dtype), _p(q_row),
+                        _p(sfd_row), _p(q_col), _p(sfd_col))
     return {"q_row": q_row, "sfd_row": sfd_row, "q_col": q_col, "sfd_col": sfd_col}
 
 
@@ -192,10 +215,11 @@ def wgrad(a, a_major, b, b_major, offsets, hidden, inter, tokens_sum,
 
 
 def wgrad_mx(a, sfa, b, sfb, offsets, hidden, inter, tokens_sum, out_dtype=F32,
-             accumulate=False, old=None, hrows=None):
+             accumulate=False, old=None, hrows=None, ab_dtype=E4M3):
     """Block-scaled (MXFP8) Wgrad[e] = deq(A)[:, begin:end] @ deq(B)[begin:end, :].
 
-    a: uint8 E4M3 codes of A (hidden, tokens_sum), K-major; sfa: uint8 E8M0
+    a: uint8 FP8 codes (E4M3, or E5M2 with ab_dtype=E5M2; B alike) of A
+    (hidden, tokens_sum), K-major; sfa: uint8 E8M0
     (hidden, tokens_sum/32).  b: codes of B stored K-major, i.e. an
     (inter, tokens_sum) array; sfb: (inter, tokens_sum/32).  Other arguments
     and the return value as for wgrad."""
@@ -208,8 +232,8 @@ def wgrad_mx(a, sfa, b, sfb, offsets, hidden, inter, tokens_sum, out_dtype=F32,
     hr = None if hrows is None else _c(hrows, np.int32)
     nrows = hidden if hr is None else hr.size
     prod = np.zeros((E, nrows, inter), np.float64)
-    lib().orc_wgrad_mx(_p(a), _p(sfa), _p(b), _p(sfb), _p(offsets), E, tokens_sum, hidden,
-                       inter, _p(hr), nrows, _p(prod))
+    lib().orc_wgrad_mx(_p(a), _p(sfa), _p(b), _p(sfb), _fmt(ab_dtype), _p(offsets), E, tokens_sum,
+                       hidden, inter, _p(hr), nrows, _p(prod))
     if accumulate:
         old = _c(old, _DT_NP[out_dtype])
         if hr is not None:
@@ -298,11 +322,12 @@ def dglu_mx(a, sfa, m_rows, k, b_list, sfb_list, n, c, c_dtype, padded_offsets,
             alpha, beta, prob, act=DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0,
             clamp_max=7.0, linear_offset=1.0, situ_beta1=4.0, situ_beta2=25.0,
             gate_first=False, mask_filter=False, d_dtype=BF16, dprob_in=None,
-            dbias_in=None, rows=None):
+            dbias_in=None, rows=None, ab_dtype=E4M3):
     """Block-scaled (MXFP8) grouped dgrad fused with dSwiGLU / dGeGLU /
     dSiTU-GLU (act DSITUGLU, tanh scales situ_beta1 and situ_beta2).
 
-    a: uint8 e4m3 codes (m_rows, k); sfa: uint8 e8m0 (m_rows, k/32);
+    a: uint8 FP8 codes (E4M3, or E5M2 with ab_dtype=E5M2; B alike)
+    (m_rows, k); sfa: uint8 e8m0 (m_rows, k/32);
     b_list / sfb_list: per expert K-major (n, k) codes and (n, k/32) scales;
     c: (m_rows, 2n) in c_dtype bits.  Returns what dglu returns, plus amax
     (float64 (L, 2): max |D| of the input-gradient and the gate-gradient
@@ -325,14 +350,15 @@ def dglu_mx(a, sfa, m_rows, k, b_list, sfb_list, n, c, c_dtype, padded_offsets,
     dbs = np.zeros((L, 2 * n), np.float64) if want_bias else None
     amax = np.zeros((L, 2), np.float64)
     lib().orc_dglu_mx(_p(a), _p(sfa), m_rows, k, ctypes.cast(bptr, ctypes.c_void_p),
-                      ctypes.cast(sptr, ctypes.c_void_p), n, _p(c), c_dtype, _p(po), L,
-                      _p(_c(alpha, np.float32)), _p(_c(beta, np.float32)),
+                      ctypes.cast(sptr, ctypes.c_void_p), n, _fmt(ab_dtype), _p(c), c_dtype,
+                      _p(po), L, _p(_c(alpha, np.float32)), _p(_c(beta, np.float32)),
                       _p(_c(prob, np.float32)), act, geglu_alpha, clamp_min, clamp_max,
                       linear_offset, situ_beta1, situ_beta2, int(bool(gate_first)),
                       int(bool(mask_filter)),
                       _p(rr), nrows, _p(D), _p(dps), _p(dbs), _p(amax))
     valid = _valid_rows(po, m_rows, rr)
-    out = {"D": D, "D_q": round_to(D, d_dtype), "valid": valid, "amax": amax}
+    out = {"D": D, "D_q": round_to(D, d_dtype) if d_dtype in (BF16, F16, F32) else None,
+           "valid": valid, "amax": amax}
     dp_in = np.zeros(m_rows, np.float32) if dprob_in is None else np.asarray(dprob_in, np.float32)
     dp_in = dp_in if rr is None else dp_in[rr]
     out["dprob"] = dp_in.astype(np.float64) + dps
@@ -347,10 +373,11 @@ def dglu_mx(a, sfa, m_rows, k, b_list, sfb_list, n, c, c_dtype, padded_offsets,
 # --------------------------------------------------------------------------
 
 def dsrelu(a, sfa, m_rows, k, b_list, sfb_list, n, c, c_dtype,
-           padded_offsets, alpha, prob, d_dtype=BF16, dprob_in=None, rows=None):
+           padded_offsets, alpha, prob, d_dtype=BF16, dprob_in=None, rows=None, ab_dtype=E4M3):
     """Grouped block-scaled dgrad fused with dsReLU.
 
-    a: uint8 e4m3 codes (m_rows, k); sfa: uint8 e8m0 (m_rows, k/32);
+    a: uint8 FP8 codes (E4M3, or E5M2 with ab_dtype=E5M2; B alike)
+    (m_rows, k); sfa: uint8 e8m0 (m_rows, k/32);
     b_list / sfb_list: per expert (n, k) codes and (n, k/32) scales;
     c: (m_rows, n) in c_dtype bits.
     Returns a dict with D (float64), D_q (rounded), dprob (float64:
@@ -370,10 +397,11 @@ def dsrelu(a, sfa, m_rows, k, b_list, sfb_list, n, c, c_dtype,
     dps = np.zeros(nrows, np.float64)
     amax = np.zeros(L, np.float64)
     lib().orc_dsrelu(_p(a), _p(sfa), m_rows, k, ctypes.cast(bptr, ctypes.c_void_p),
-                     ctypes.cast(sptr, ctypes.c_void_p), n, _p(c), c_dtype, _p(po), L,
-                     _p(_c(alpha, np.float32)), _p(_c(prob, np.float32)),
+                     ctypes.cast(sptr, ctypes.c_void_p), n, _fmt(ab_dtype), _p(c), c_dtype,
+                     _p(po), L, _p(_c(alpha, np.float32)), _p(_c(prob, np.float32)),
                      _p(rr), nrows, _p(D), _p(dps), _p(amax))
-    out = {"D": D, "D_q": round_to(D, d_dtype), "amax": amax,
+    out = {"D": D, "D_q": round_to(D, d_dtype) if d_dtype in (BF16, F16, F32) else None,
+           "amax": amax,
            "valid": _valid_rows(po, m_rows, rr)}
     dp_in = np.zeros(m_rows, np.float32) if dprob_in is None else np.asarray(dprob_in, np.float32)
     dp_in = dp_in if rr is None else dp_in[rr]
