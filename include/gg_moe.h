@@ -80,7 +80,8 @@ typedef enum {
     GG_BF16 = 0,
     GG_F16 = 1,
     GG_F32 = 2,
-    GG_F8E4M3 = 3            /* OCP E4M3 ("float8_e4m3fn"): max 448, no inf     */
+    GG_F8E4M3 = 3,           /* OCP E4M3 ("float8_e4m3fn"): max 448, no inf     */
+    GG_F8E5M2 = 4            /* OCP E5M2 ("float8_e5m2"): max 57344, inf / NaN  */
 } gg_dtype;
 
 typedef enum {
@@ -121,27 +122,37 @@ enum {
      * other kernels launch one workgroup per tile, dispatched by the
      * hardware in a fixed order, so for them both settings are the same
      * schedule and the flag is accepted with no effect. */
-    GG_FLAG_STATIC_SCHED = 16u
+    GG_FLAG_STATIC_SCHED = 16u,
+    /* Block-scaled entries (gg_wgrad_mx, gg_dglu_mx, gg_dsrelu): the FP8
+     * codes of A and B are E5M2 rather than E4M3 -- the other MXFP8 ab_dtype
+     * of the dGLU page's "Data Types" table; A and B always share one format
+     * ("Additional Type Constraints").  The dgrad entries take it with an
+     * FP8 d_dtype only (the same section pairs FP8 operands with FP8
+     * outputs), else GG_ERR_UNSUPPORTED; gg_wgrad_mx with any wgrad_dtype. */
+    GG_FLAG_AB_E5M2 = 32u
 };
 
 /*
  * FP8 outputs of the block-scaled dgrad entries (gg_dglu_mx, gg_dsrelu) when
- * d_dtype is GG_F8E4M3 ("Grouped GEMM + dGLU (SM100)", "Block-scaled
- * contract / Equations", step 3; the dsReLU page's FP8 D_row / D_col with
- * SFD_row / SFD_col).  W is the width of D (2n for dGLU, n for dsReLU).
- * Blocks of 32 values -- 32 columns of a row for d_row, 32 rows of a column
- * for d_col -- share one E8M0 scale SFD = 2^e, e the smallest integer with
- *   2^e >= fp32(fp32(norm_const * max|D|) * fp32(1/448))
- * (the page's norm_const * max|D| * rcp_max, rounded up to a power of two,
- * which keeps every code within E4M3's 448; e in [-127, 127], -127 for an
- * all-zero block), and each value is stored as E4M3(D * norm_const / 2^e),
- * round to nearest even.  D here is the fp32 result before any rounding.
+ * d_dtype is GG_F8E4M3 or GG_F8E5M2 ("Grouped GEMM + dGLU (SM100)",
+ * "Block-scaled contract / Equations", step 3, and its "Data Types" d_dtype
+ * column; the dsReLU page's FP8 D_row / D_col with SFD_row / SFD_col).  W is
+ * the width of D (2n for dGLU, n for dsReLU).  Blocks of 32 values -- 32
+ * columns of a row for d_row, 32 rows of a column for d_col -- share one
+ * E8M0 scale SFD = 2^e, e the smallest integer with
+ *   2^e >= fp32(fp32(norm_const * max|D|) * fp32(1/fmax))
+ * fmax the format's largest value (448 for E4M3, 57344 for E5M2; the page's
+ * norm_const * max|D| * rcp_max, rounded up to a power of two, which keeps
+ * every code within fmax; e in [-127, 127], -127 for an all-zero block), and
+ * each value is stored as fp8(D * norm_const / 2^e), clamped to +-fmax,
+ * round to nearest even.  D here is the fp32 result before any rounding;
+ * d_row and d_col share the one format.
  * A plain layout replaces the pages' MMA-interleaved scale tensors; the
  * column scales of one group occupy its own row-block range of every column
  * (groups are multiples of 256 rows, so no block straddles two).
  */
 typedef struct {
-    void* d_col;               /* (m_rows, W) E4M3 column-quantized D, row-major, 16-B
+    void* d_col;               /* (m_rows, W) FP8 column-quantized D, row-major, 16-B
                                   aligned; or NULL for no column output             */
     uint8_t* sfd_row;          /* (m_rows, W/32): row m, block b at m*(W/32) + b      */
     uint8_t* sfd_col;          /* (W, P), P = ceil(m_rows/32): column c, rows 32j ..
@@ -244,9 +255,10 @@ gg_status gg_wgrad_noalloc(const void* a, gg_major a_major, const void* b, gg_ma
 
 /*
  * The same operation on block-scaled operands ("Grouped GEMM + WGrad
- * (Unified)", "Block-scaled contract"), MXFP8: E4M3 codes with one E8M0
- * scale per 32 consecutive tokens of a row, deq(q, s) = e4m3(q) * 2^(s-127),
- * fp32 accumulation.  The reduction axis is contiguous in both operands:
+ * (Unified)", "Block-scaled contract"), MXFP8: E4M3 codes (E5M2 with
+ * GG_FLAG_AB_E5M2) with one E8M0 scale per 32 consecutive tokens of a row,
+ * deq(q, s) = fp8(q) * 2^(s-127), fp32 accumulation.  The reduction axis is
+ * contiguous in both operands:
  * a_fp8      A (hidden, tokens_sum) K-major: (h,t) at a[h*tokens_sum + t];
  * sfa        (hidden, tokens_sum/32): sfa[h*(tokens_sum/32) + t/32];
  * b_fp8      B (tokens_sum, intermediate) stored K-major, as an
@@ -260,6 +272,7 @@ gg_status gg_wgrad_noalloc(const void* a, gg_major a_major, const void* b, gg_ma
  *            for 256; a count that is not a multiple of 128 is skipped and
  *            flagged GG_DEVERR_SKIPPED, one of 128 but not 256 computed and
  *            flagged GG_DEVERR_GRANULE).
+ * flags      as for gg_wgrad, and GG_FLAG_AB_E5M2.
  * Codes 16-byte, scales 4-byte aligned.  Every other argument as for
  * gg_wgrad; the pages' global scales belong to formats other than MXFP8 and
  * are not taken.
@@ -358,7 +371,8 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k,
  *   amax[2g + 1] = max |D| over its gate-gradient columns,
  * taken before rounding (0 for an empty group).
  *
- * a_fp8      A (m_rows, k) E4M3 codes, K-major: a[m*k + kk].
+ * a_fp8      A (m_rows, k) FP8 codes (E4M3, or E5M2 with GG_FLAG_AB_E5M2),
+ *            K-major: a[m*k + kk].
  * sfa        E8M0 scales (m_rows, k/32), row-major: sfa[m*(k/32) + kk/32]
  *            (a plain layout; the pages' MMA-interleaved scale layout is not
  *            used).
@@ -371,8 +385,11 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k,
  *            the pointer pair is given.
  * n          compact width, a multiple of 32, at most 2^20
  *            (GG_ERR_UNSUPPORTED beyond either limit).
- * c, c_dtype, padded_offsets, L, alpha, beta, prob, d_row, d_dtype, dprob,
- * dbias, geglu_alpha, clamp_min, clamp_max, linear_offset
+ * b_fp8/b_ptrs codes share A's format.
+ * c_dtype    as for gg_dglu, or GG_F8E4M3 / GG_F8E5M2 (the dGLU page's
+ *            "Input tensor C" dtypes): an FP8 C is read as its exact value.
+ * c, padded_offsets, L, alpha, beta, prob, d_row, dprob, dbias, geglu_alpha,
+ * clamp_min, clamp_max, linear_offset
  *            as for gg_dglu.
  * act        GG_DSWIGLU, GG_DGEGLU, or GG_DSITUGLU: the page's dSiTU-GLU
  *            ("Block-scaled contract / Equations") on gate G and input U of
@@ -386,11 +403,11 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k,
  *              dprob   += R T_g T_u
  * amax       float[2L] ((L, 2) row-major), written by the call (the library
  *            clears it first), or NULL.
- * d_dtype    as for gg_dglu, or GG_F8E4M3: d_row then holds the
- *            row-quantized E4M3 D ((m_rows, 2n), 16-B aligned) and fp8_out
- *            [host] the rest of the FP8 output (see gg_fp8_out); fp8_out is
- *            ignored for the other dtypes.
- * flags      as for gg_dglu.
+ * d_dtype    as for gg_dglu, or GG_F8E4M3 / GG_F8E5M2: d_row then holds
+ *            the row-quantized FP8 D ((m_rows, 2n), 16-B aligned) and
+ *            fp8_out [host] the rest of the FP8 output (see gg_fp8_out);
+ *            fp8_out is ignored for the other dtypes.
+ * flags      as for gg_dglu, and GG_FLAG_AB_E5M2 (with an FP8 d_dtype).
  * workspace  >= gg_dglu_workspace_size(L, n, dbias != NULL), 256-B aligned.
  */
 gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
@@ -417,32 +434,38 @@ size_t gg_dsrelu_workspace_size(int32_t L);
  *   D_row[m,n] = prob[m] * 2 * C[m,n] * relu(G[m,n])
  *   dprob[m]  += sum_n C[m,n] * relu(G[m,n])^2
  *   amax[g]    = max |D_row| over the group, before rounding (0 if empty)
- * with deq(q, s) = e4m3(q) * 2^(s - 127): MXFP8, one E8M0 scale byte per 32
+ * with deq(q, s) = fp8(q) * 2^(s - 127): MXFP8, one E8M0 scale byte per 32
  * consecutive K values of a row ("sf_vec_size 32" for MXFP8 on the dGLU
- * page's data-type table).
+ * page's data-type table), the codes E4M3, or E5M2 with GG_FLAG_AB_E5M2 (A
+ * and B alike).
  *
- * a_fp8      A (m_rows, k) E4M3 codes, K-major: a[m*k + kk].
+ * a_fp8      A (m_rows, k) FP8 codes, K-major: a[m*k + kk].
  * sfa        E8M0 scales (m_rows, k/32), row-major: sfa[m*(k/32) + kk/32].
  *            (A plain row-major layout; the pages' 6-D MMA-interleaved scale
  *            layout is not used.)
  * m_rows     as for gg_dglu.  k: a multiple of 128, at most 2^21.
- * b_fp8,sfb  dense weights (L, n, k) E4M3, element at b[g*n*k + nn*k + kk],
- *            and scales (L, n, k/32) at sfb[(g*n + nn)*(k/32) + kk/32];
+ * b_fp8,sfb  dense weights (L, n, k) FP8 (A's format), element at
+ *            b[g*n*k + nn*k + kk], and scales (L, n, k/32) at
+ *            sfb[(g*n + nn)*(k/32) + kk/32];
  * b_ptrs, sfb_ptrs  or: int64[L] device arrays of per-expert (n, k) codes
  *            and (n, k/32) scales with the same in-matrix layout.
  *            Exactly one of the dense pair / the pointer pair is given.
  * n          a multiple of 32, at most 2^21 (GG_ERR_UNSUPPORTED beyond either
  *            limit).
- * c          (m_rows, n) row-major, c_dtype GG_BF16, GG_F16 or GG_F32.
+ * c          (m_rows, n) row-major, c_dtype GG_BF16, GG_F16, GG_F32,
+ *            GG_F8E4M3 or GG_F8E5M2 (the dsReLU page's "Input tensor C"
+ *            dtypes; an FP8 C is read as its exact value).
  * padded_offsets, L  as for gg_dglu.
  * alpha      float[L];  prob  float[m_rows].
  * d_row      (m_rows, n) row-major, d_dtype GG_BF16, GG_F16 or GG_F32; or
- *            GG_F8E4M3, the row-quantized D, with fp8_out [host] giving the
- *            rest of the FP8 output (see gg_fp8_out; ignored otherwise).
+ *            GG_F8E4M3 / GG_F8E5M2, the row-quantized D, with fp8_out [host]
+ *            giving the rest of the FP8 output (see gg_fp8_out; ignored
+ *            otherwise).
  * dprob      float[m_rows], caller-zeroed, accumulated into.
  * amax       float[L], written by the call (the library clears it first), or
  *            NULL.
- * flags      OR of GG_FLAG_VALIDATE_OFFSETS, GG_FLAG_STATIC_SCHED.
+ * flags      OR of GG_FLAG_VALIDATE_OFFSETS, GG_FLAG_STATIC_SCHED and
+ *            GG_FLAG_AB_E5M2 (with an FP8 d_dtype).
  * workspace  >= gg_dsrelu_workspace_size(L), 256-B aligned.
  */
 gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,

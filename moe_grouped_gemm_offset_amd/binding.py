@@ -15,11 +15,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgg_moe.so")
 
 # enums of gg_moe.h
-GG_BF16, GG_F16, GG_F32, GG_F8E4M3 = 0, 1, 2, 3
+GG_BF16, GG_F16, GG_F32, GG_F8E4M3, GG_F8E5M2 = 0, 1, 2, 3, 4
 GG_MAJOR_K, GG_MAJOR_M, GG_MAJOR_N = 0, 1, 2
 GG_DSWIGLU, GG_DGEGLU, GG_DSITUGLU = 0, 1, 2
 GG_FLAG_GATE_FIRST, GG_FLAG_GEGLU_MASK_FILTER, GG_FLAG_VALIDATE_OFFSETS = 1, 2, 4
-GG_FLAG_TENSOR_RAGGED, GG_FLAG_STATIC_SCHED = 8, 16
+GG_FLAG_TENSOR_RAGGED, GG_FLAG_STATIC_SCHED, GG_FLAG_AB_E5M2 = 8, 16, 32
 GG_DEVERR_DECREASING, GG_DEVERR_GRANULE, GG_DEVERR_LAST, GG_DEVERR_SKIPPED = 1, 2, 4, 8
 STATUS_NAMES = ["GG_OK", "GG_ERR_NULL", "GG_ERR_SHAPE", "GG_ERR_DTYPE", "GG_ERR_LAYOUT",
                 "GG_ERR_ALIGN", "GG_ERR_MODE", "GG_ERR_WORKSPACE", "GG_ERR_UNSUPPORTED",
@@ -29,7 +29,7 @@ EXPORTS = ["gg_abi_version", "gg_last_error", "gg_device_error", "gg_wgrad_works
            "gg_dsrelu_workspace_size", "gg_dsrelu"]
 
 _TORCH_DTYPE = {torch.bfloat16: GG_BF16, torch.float16: GG_F16, torch.float32: GG_F32,
-                torch.float8_e4m3fn: GG_F8E4M3}
+                torch.float8_e4m3fn: GG_F8E4M3, torch.float8_e5m2: GG_F8E5M2}
 
 
 class GGError(RuntimeError):
@@ -166,6 +166,12 @@ def _workspace(ws, nbytes, like, stream):
     return t, t.numel()
 
 
+def _ab(a, flags):
+    """Operand codes given as a float8_e5m2 tensor add GG_FLAG_AB_E5M2 (uint8
+    or float8_e4m3fn codes leave flags as they are)."""
+    return flags | GG_FLAG_AB_E5M2 if a is not None and a.dtype == torch.float8_e5m2 else flags
+
+
 def _sched(flags):
     """GG_SCHED=static in the environment adds GG_FLAG_STATIC_SCHED (a
     benchmarking override; GG_SCHED=dynamic or unset leaves flags alone)."""
@@ -211,8 +217,10 @@ def gg_wgrad_noalloc(a, a_major, b, b_major, offsets, tokens_sum, hidden, interm
 def gg_wgrad_mx(a, sfa, b, sfb, offsets, tokens_sum, hidden, intermediate, wgrad_dense=None,
                 wgrad_ptrs=None, wgrad_dtype=None, accumulate=False, flags=0, workspace=None,
                 stream=None):
-    """Grouped MXFP8 wgrad (gg_wgrad_mx of gg_moe.h): uint8 codes and E8M0
-    scales, both operands K-major.  Returns the workspace used."""
+    """Grouped MXFP8 wgrad (gg_wgrad_mx of gg_moe.h): FP8 codes (uint8 /
+    float8_e4m3fn tensors: E4M3; float8_e5m2 tensors or GG_FLAG_AB_E5M2:
+    E5M2) and E8M0 scales, both operands K-major.  Returns the workspace
+    used."""
     L = load_library()
     E = offsets.numel()
     if wgrad_dtype is None:
@@ -220,7 +228,8 @@ def gg_wgrad_mx(a, sfa, b, sfb, offsets, tokens_sum, hidden, intermediate, wgrad
     ws, nbytes = _workspace(workspace, L.gg_wgrad_workspace_size(E), offsets, stream)
     _check(L.gg_wgrad_mx(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(offsets), E, tokens_sum,
                          hidden, intermediate, _ptr(wgrad_dense), _ptr(wgrad_ptrs), wgrad_dtype,
-                         int(bool(accumulate)), _sched(flags), _ptr(ws), nbytes, _stream(stream)))
+                         int(bool(accumulate)), _sched(_ab(a, flags)), _ptr(ws), nbytes,
+                         _stream(stream)))
     return ws
 
 
@@ -244,8 +253,10 @@ def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, be
                dprob, dbias=None, amax=None, fp8_out=None, act=GG_DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0,
                clamp_max=7.0, linear_offset=1.0, situ_beta1=4.0, situ_beta2=25.0, flags=0,
                workspace=None, stream=None):
-    """Grouped MXFP8 dgrad + dSwiGLU/dGeGLU (gg_dglu_mx of gg_moe.h): a is an
-    (m_rows, k) uint8 tensor of E4M3 codes.  With a uint8 d_row (E4M3 codes)
+    """Grouped MXFP8 dgrad + dSwiGLU/dGeGLU/dSiTU-GLU (gg_dglu_mx of
+    gg_moe.h): a is an (m_rows, k) tensor of FP8 codes (uint8 or
+    float8_e4m3fn: E4M3; float8_e5m2: E5M2, as for gg_wgrad_mx).  c may be
+    float8_e4m3fn / float8_e5m2.  With a float8_e4m3fn / float8_e5m2 d_row
     fp8_out is a dict of the other FP8 outputs (sfd_row, norm_const and
     optionally d_col, sfd_col).  Returns the workspace used."""
     q = _fp8_out(fp8_out)
@@ -257,14 +268,14 @@ def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, be
                         _ptr(padded_offsets), nl, _ptr(alpha), _ptr(beta), _ptr(prob),
                         _ptr(d_row), _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(dbias),
                         _ptr(amax), _ref(q), act, geglu_alpha, clamp_min, clamp_max, linear_offset,
-                        situ_beta1, situ_beta2, flags, _ptr(ws), nbytes, _stream(stream)))
+                        situ_beta1, situ_beta2, _ab(a, flags), _ptr(ws), nbytes, _stream(stream)))
     return ws
 
 
 def gg_dsrelu(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, prob, d_row, dprob,
               amax=None, fp8_out=None, flags=0, workspace=None, stream=None):
-    """Grouped MXFP8 dgrad + dsReLU (gg_dsrelu of gg_moe.h); fp8_out as for
-    gg_dglu_mx.  Returns the workspace used."""
+    """Grouped MXFP8 dgrad + dsReLU (gg_dsrelu of gg_moe.h); operand, C and
+    D dtypes and fp8_out as for gg_dglu_mx.  Returns the workspace used."""
     q = _fp8_out(fp8_out)
     L = load_library()
     nl = padded_offsets.numel()
@@ -272,6 +283,6 @@ def gg_dsrelu(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, pro
     _check(L.gg_dsrelu(_ptr(a), _ptr(sfa), a.shape[0], a.shape[1], _ptr(b), _ptr(sfb),
                        _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
                        _ptr(padded_offsets), nl, _ptr(alpha), _ptr(prob), _ptr(d_row),
-                       _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(amax), _ref(q), flags, _ptr(ws),
+                       _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(amax), _ref(q), _ab(a, flags), _ptr(ws),
                        nbytes, _stream(stream)))
     return ws

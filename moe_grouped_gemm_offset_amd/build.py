@@ -14,7 +14,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgg_moe.so")
-SOURCES = ["gg_api.cpp", "gg_prologue.hip", "gg_wgrad.hip", "gg_wgrad_mx.hip", "gg_dglu.hip", "gg_dglu_mx.hip", "gg_dsrelu.hip"]
+SOURCES = ["gg_api.cpp", "gg_prologue.hip", "gg_wgrad.hip", "gg_wgrad_mx.hip", "gg_dglu.hip",
+           "gg_dglu_mx.hip", "gg_dglu_mx_dswiglu.hip", "gg_dglu_mx_dgeglu.hip",
+           "gg_dglu_mx_dsituglu.hip", "gg_dsrelu.hip"]
 ARCH = os.environ.get("GG_OFFLOAD_ARCH", "gfx950")
 
 

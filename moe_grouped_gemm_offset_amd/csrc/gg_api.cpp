@@ -54,9 +54,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int dtype_bytes(gg_dtype d) { return d == GG_F32 ? 4 : (d == GG_F8E4M3 ? 1 : 2); }
-
 bool is_out_dtype(gg_dtype d) { return d == GG_BF16 || d == GG_F16 || d == GG_F32; }
+
+bool is_fp8(gg_dtype d) { return d == GG_F8E4M3 || d == GG_F8E5M2; }
 
 // Current device must be a gfx950; the answer is cached per device ordinal.
 gg_status check_device() {
@@ -213,7 +213,8 @@ static gg_status wgrad_host_checks(const int32_t* offsets, int32_t num_experts, 
         return fail(GG_ERR_UNSUPPORTED, "more than 2^28 output tiles (256 x 256, all experts)");
     if (!aligned16(wgrad_dense) || !aligned16(wgrad_ptrs) || ((uintptr_t)offsets & 3u))
         return fail(GG_ERR_ALIGN, "the output must be 16-byte aligned, offsets 4-byte");
-    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_TENSOR_RAGGED | GG_FLAG_STATIC_SCHED))
+    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_TENSOR_RAGGED | GG_FLAG_STATIC_SCHED |
+                            (mx ? GG_FLAG_AB_E5M2 : 0u)))
         return fail(GG_ERR_MODE, "unsupported flags 0x%x for %s", flags, name);
     return GG_OK;
 }
@@ -259,6 +260,7 @@ static gg_status run_wgrad(gg::WgradArgs& p, bool mx, const int32_t* offsets, in
     p.E = num_experts;
     p.ragged = (flags & GG_FLAG_TENSOR_RAGGED) != 0;
     p.static_sched = (flags & GG_FLAG_STATIC_SCHED) != 0;
+    p.ab_e5m2 = (flags & GG_FLAG_AB_E5M2) != 0;
     // XCD blocks of an expert's tiles: the gm x (8/gm) grid that reads the
     // fewest operand panels (an A panel per M tile by 8/gm XCDs, a B panel
     // per N tile by gm), among those that divide the tile grid
@@ -404,9 +406,10 @@ static gg_status check_dglu_common(gg_dtype c_dtype, gg_dtype d_dtype, gg_act ac
                                    uint32_t flags, const char* name) {
     if (!alpha || !beta)
         return fail(GG_ERR_NULL, "alpha and beta must be non-NULL");
-    if (!is_out_dtype(c_dtype) || !(is_out_dtype(d_dtype) || (mx && d_dtype == GG_F8E4M3)))
-        return fail(GG_ERR_DTYPE, mx ? "c_dtype must be GG_BF16, GG_F16 or GG_F32, d_dtype one of "
-                                       "those or GG_F8E4M3"
+    if (!(is_out_dtype(c_dtype) || (mx && is_fp8(c_dtype))) ||
+        !(is_out_dtype(d_dtype) || (mx && is_fp8(d_dtype))))
+        return fail(GG_ERR_DTYPE, mx ? "c_dtype and d_dtype must be GG_BF16, GG_F16, GG_F32, "
+                                       "GG_F8E4M3 or GG_F8E5M2"
                                      : "c_dtype and d_dtype must be GG_BF16, GG_F16 or GG_F32");
     if (act == GG_DSITUGLU && !mx)
         return fail(GG_ERR_MODE, "GG_DSITUGLU is defined for the block-scaled gg_dglu_mx only");
@@ -415,8 +418,10 @@ static gg_status check_dglu_common(gg_dtype c_dtype, gg_dtype d_dtype, gg_act ac
     if (!aligned16(dbias) || ((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u))
         return fail(GG_ERR_ALIGN, "dbias must be 16-byte aligned, alpha and beta 4-byte");
     if (flags & ~(uint32_t)(GG_FLAG_GATE_FIRST | GG_FLAG_GEGLU_MASK_FILTER | GG_FLAG_VALIDATE_OFFSETS |
-                            GG_FLAG_STATIC_SCHED))
+                            GG_FLAG_STATIC_SCHED | (mx ? GG_FLAG_AB_E5M2 : 0u)))
         return fail(GG_ERR_MODE, "unsupported flags 0x%x for %s", flags, name);
+    if ((flags & GG_FLAG_AB_E5M2) && !is_fp8(d_dtype))
+        return fail(GG_ERR_UNSUPPORTED, "E5M2 operands (GG_FLAG_AB_E5M2) need an FP8 d_dtype");
     return GG_OK;
 }
 
@@ -489,12 +494,12 @@ static gg_status run_dglu(gg::DgluArgs& p, bool mx, const void* c, gg_dtype c_dt
     return ok();
 }
 
-// FP8 outputs (d_dtype GG_F8E4M3 of the block-scaled dgrad entries): checks
+// FP8 outputs (d_dtype GG_F8E4M3 / GG_F8E5M2 of the block-scaled dgrad entries): checks
 // them and fills q; width is W, the columns of D.
 static gg_status check_fp8_out(const gg_fp8_out* f, const void* d_row, int64_t m_rows, int64_t width,
                                gg::Fp8Out& q) {
     if (!f || !f->sfd_row || !f->norm_const)
-        return fail(GG_ERR_NULL, "GG_F8E4M3 output needs fp8_out with sfd_row and norm_const");
+        return fail(GG_ERR_NULL, "an FP8 d_dtype needs fp8_out with sfd_row and norm_const");
     if ((f->d_col != nullptr) != (f->sfd_col != nullptr))
         return fail(GG_ERR_MODE, "give both of fp8_out->d_col and fp8_out->sfd_col, or neither");
     if (!aligned16(f->d_col) || ((uintptr_t)f->norm_const & 3u))
@@ -590,7 +595,7 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
         ((uintptr_t)sfa & 3u) || ((uintptr_t)sfb & 3u) || ((uintptr_t)amax & 3u))
         return fail(GG_ERR_ALIGN, "operands must be 16-byte aligned, scales and amax 4-byte aligned");
     gg::DgluArgs p = {};
-    if (d_dtype == GG_F8E4M3) {
+    if (is_fp8(d_dtype)) {
         st = check_fp8_out(fp8_out, d_row, m_rows, 2 * (int64_t)n, p.q);
         if (st != GG_OK)
             return st;
@@ -605,6 +610,7 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
     p.K = k;
     p.N = n;
     p.b_kmajor = 1;
+    p.ab_e5m2 = (flags & GG_FLAG_AB_E5M2) != 0;
     return run_dglu(p, true, c, c_dtype, padded_offsets, L, alpha, beta, prob, d_row, d_dtype,
                     dprob, dbias, amax, act, geglu_alpha, clamp_min, clamp_max, linear_offset,
                     act == GG_DSITUGLU ? situ_beta1 : 1.0f, act == GG_DSITUGLU ? situ_beta2 : 1.0f,
@@ -627,9 +633,9 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
     const bool discrete = b_ptrs || sfb_ptrs;
     if (dense == discrete || (dense && (!b_fp8 || !sfb)) || (discrete && (!b_ptrs || !sfb_ptrs)))
         return fail(GG_ERR_MODE, "give exactly one of (b_fp8, sfb) and (b_ptrs, sfb_ptrs)");
-    if (!is_out_dtype(c_dtype) || !(is_out_dtype(d_dtype) || d_dtype == GG_F8E4M3))
-        return fail(GG_ERR_DTYPE, "c_dtype must be GG_BF16, GG_F16 or GG_F32, d_dtype one of those "
-                                  "or GG_F8E4M3");
+    if (!(is_out_dtype(c_dtype) || is_fp8(c_dtype)) || !(is_out_dtype(d_dtype) || is_fp8(d_dtype)))
+        return fail(GG_ERR_DTYPE, "c_dtype and d_dtype must be GG_BF16, GG_F16, GG_F32, GG_F8E4M3 or "
+                                  "GG_F8E5M2");
     if (n <= 0 || n % 32)
         return fail(GG_ERR_SHAPE, "n must be a positive multiple of 32 (got %d)", n);
     if (k <= 0)
@@ -642,13 +648,15 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
         ((uintptr_t)sfa & 3u) || ((uintptr_t)sfb & 3u) || ((uintptr_t)alpha & 3u) ||
         ((uintptr_t)amax & 3u))
         return fail(GG_ERR_ALIGN, "operands must be 16-byte aligned, scales 4-byte aligned");
-    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_STATIC_SCHED))
+    if (flags & ~(uint32_t)(GG_FLAG_VALIDATE_OFFSETS | GG_FLAG_STATIC_SCHED | GG_FLAG_AB_E5M2))
         return fail(GG_ERR_MODE, "unsupported flags 0x%x for gg_dsrelu", flags);
+    if ((flags & GG_FLAG_AB_E5M2) && !is_fp8(d_dtype))
+        return fail(GG_ERR_UNSUPPORTED, "E5M2 operands (GG_FLAG_AB_E5M2) need an FP8 d_dtype");
     size_t need = gg_dsrelu_workspace_size(L);
     if (workspace_bytes < need)
         return fail(GG_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     gg::DsreluArgs p = {};
-    if (d_dtype == GG_F8E4M3) {
+    if (is_fp8(d_dtype)) {
         st = check_fp8_out(fp8_out, d_row, m_rows, n, p.q);
         if (st != GG_OK)
             return st;
@@ -687,6 +695,7 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
     p.L = L;
     p.c_dtype = (int)c_dtype;
     p.d_dtype = (int)d_dtype;
+    p.ab_e5m2 = (flags & GG_FLAG_AB_E5M2) != 0;
     gg::LaunchInfo info{};
     gg::LaunchInfo* li = log_enabled() ? &info : nullptr;
     e = gg::launch_dsrelu(p, s, li);

@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_kernel(DgluArgs p) {
 
     // C of the items 6 ahead (3 for fp32 C) in flight in the epilogue: deeper
     // prefetch spilled registers and measured slower
-    dglu_epilogue<C, W32, ACT, false, W32 ? 3 : 6, false, BF, DB, FILT>(p, acc, smem, m0, n0, g,
+    dglu_epilogue<C, W32 ? 4 : 2, ACT, false, W32 ? 3 : 6, 0, BF, DB, FILT>(p, acc, smem, m0, n0, g,
                                                                        rows_valid, am0, bn0);
 }
 

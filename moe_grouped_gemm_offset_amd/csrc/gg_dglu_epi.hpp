@@ -44,24 +44,27 @@ __device__ __forceinline__ float scaled_x(float beta, float c) {
     return beta * c;
 }
 
-// W32: C is fp32 (else bf16 / fp16); ACT: 0 dSwiGLU, 1 dGeGLU, 2 dSiTU-GLU
+// CW: bytes per C element (4 fp32, 2 bf16 / fp16, 1 FP8 codes: E4M3 or
+// E5M2, the block-scaled contract's FP8 C); ACT: 0 dSwiGLU, 1 dGeGLU, 2 dSiTU-GLU
 // (the block-scaled contract's "Equations": T_g = b1 tanh(G/b1) sigmoid(G),
 // T_u = b2 tanh(U/b2), gradients R prob T_u dT_g/dG and R prob T_g dT_u/dU,
 // activation T_g T_u); AMAX: raise
-// p.amax[2 g + {0: input, 1: gate}]; Q: D as FP8 (E4M3) D_row / D_col with
-// E8M0 scales (gg_fp8out.hpp) instead of a 16/32-bit D; BF: C is bf16 and,
-// unless Q, so is D, known at compile time (no per-element format branches, which
+// p.amax[2 g + {0: input, 1: gate}]; QF: D as FP8 D_row / D_col with E8M0
+// scales (gg_fp8out.hpp; 1 E4M3, 2 E5M2) instead of a 16/32-bit D (0); BF:
+// C is bf16 and, unless QF, so is D, known at compile time (no per-element
+// format branches, which
 // also keeps the compiler's memory-counter waits exact); DB: accumulate the
 // dbias column sums (added only when p.dbias is set); FILT: dGeGLU's filters
 // carry the raw value (0) or are the 0/1 indicator (1,
 // GG_FLAG_GEGLU_MASK_FILTER), or follow p.mask_filter (2); kAhead: row-walk items
 // whose C loads are in flight while one is processed.  The caller has
 // passed the barrier that ends the main loop's use of smem.
-template <class C, bool W32, int ACT, bool AMAX, int kAhead, bool Q = false, bool BF = false,
+template <class C, int CW, int ACT, bool AMAX, int kAhead, int QF = 0, bool BF = false,
           bool DB = true, int FILT = 2>
 __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&acc)[C::MB][C::NB],
                                               char* smem, int64_t m0, int n0, int g,
                                               int rows_valid, int am0, int bn0) {
+    constexpr bool Q = QF != 0, BF8 = QF == 2;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const float al = p.alpha[g];
     const float a2 = al * al;
@@ -239,7 +242,7 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
         };
         for_each_row8<C, kAhead>(acc, elds, loadb, fnb);
     } else {
-        using Pre = Pre8<W32, 2>;
+        using Pre = Pre8<CW, 2>;
         auto load = [&](int, int r, int c) {
             const int rr = am0 + r;
             const bool ok = (rr < rows_valid) & (n0 + bn0 + c < p.N);
@@ -247,8 +250,8 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
             cols(c, c_in, c_gt);
             const int64_t row = m0 + (ok ? rr : 0);
             Pre pre;
-            pre.x[0] = raw8_load<W32>(p.c, row * N2 + (ok ? c_in : 0));
-            pre.x[1] = raw8_load<W32>(p.c, row * N2 + (ok ? c_gt : 0));
+            pre.x[0] = rawc_load<CW>(p.c, row * N2 + (ok ? c_in : 0));
+            pre.x[1] = rawc_load<CW>(p.c, row * N2 + (ok ? c_gt : 0));
             pre.row = p.prob[row];
             return pre;
         };
@@ -267,8 +270,8 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
             if (ok) {
                 const int64_t row = m0 + rr;
                 float xin[8], xgt[8];
-                raw8_cvt<W32>(pre.x[0], cdt, xin);
-                raw8_cvt<W32>(pre.x[1], cdt, xgt);
+                rawc_cvt<CW>(pre.x[0], cdt, xin);
+                rawc_cvt<CW>(pre.x[1], cdt, xgt);
                 grad8(t, v, xin, xgt, a2 * pre.row, din, dgt);
                 if constexpr (!Q) {
                     store8(p.d, ddt, row * N2 + c_in, din);
@@ -279,8 +282,8 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
                 // every lane takes part in the block reductions; lanes off the
                 // tile hold zeros and store nothing
                 int ein, egt;
-                const uint2 qin = fp8_row8(din, nc, ein);
-                const uint2 qgt = fp8_row8(dgt, nc, egt);
+                const uint2 qin = fp8_row8<BF8>(din, nc, ein);
+                const uint2 qgt = fp8_row8<BF8>(dgt, nc, egt);
                 if (ok) {
                     fp8_store_row(p.q, m0 + rr, c_in, qin, ein);
                     fp8_store_row(p.q, m0 + rr, c_gt, qgt, egt);
@@ -294,8 +297,8 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
                     const int r0 = r - 24;                 // this lane's row of item t-3
                     const int64_t rb0 = m0 + am0 + (r0 & ~31), row0 = m0 + am0 + r0;
                     const int left = rows_valid - (am0 + r0);
-                    fp8_col_block(p.q, nc, dcol_in, rb0, row0, c_in, n < p.N, left);
-                    fp8_col_block(p.q, nc, dcol_gt, rb0, row0, c_gt, n < p.N, left);
+                    fp8_col_block<BF8>(p.q, nc, dcol_in, rb0, row0, c_in, n < p.N, left);
+                    fp8_col_block<BF8>(p.q, nc, dcol_gt, rb0, row0, c_gt, n < p.N, left);
                 }
             }
             if (DB && t == kT - 1 && dbias_ws)

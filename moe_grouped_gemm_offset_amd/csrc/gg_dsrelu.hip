@@ -2,7 +2,8 @@
 // dsReLU backward on gfx950.
 //
 // For the rows of group g ("Grouped GEMM + dsReLU (SM100)", "Equations"):
-//   G = alpha_g * sum_k deq(A) deq(B_g)   (E4M3 values, one E8M0 scale per
+//   G = alpha_g * sum_k deq(A) deq(B_g)   (FP8 values -- E4M3 or E5M2, A and
+//                                          B alike -- with one E8M0 scale per
 //                                          32 K values of a row)
 //   D_row = prob * 2 * C * relu(G),  dprob = sum_n C relu(G)^2,
 // and the per-expert Amax of |D_row| ("Shapes").
@@ -21,13 +22,21 @@
 
 namespace gg {
 
+// The kernels' dtype codes are the ABI's gg_dtype values.
+static_assert(kBF16 == GG_BF16 && kF16 == GG_F16 && kF32 == GG_F32 && kF8 == GG_F8E4M3 &&
+                  kF8E5M2 == GG_F8E5M2,
+              "dtype codes");
+
 using DsreluCfg = Cfg<256, 256, 2, 2>;
 
-// Q: FP8 (E4M3) D_row / D_col with E8M0 scales (else a 16/32-bit D_row);
-// BF: C bf16 and, unless Q, D bf16, known at compile time.
-template <class C, bool Q, bool BF>
+// QF: FP8 D_row / D_col with E8M0 scales (1 E4M3, 2 E5M2; else a 16/32-bit
+// D_row, 0); BF: C bf16 and, unless QF, D bf16, known at compile time
+// (otherwise C's width -- fp32, 16-bit, FP8 -- is a run-time choice among
+// three epilogue walks); AB: the operands' FP8 format (0 E4M3, 1 E5M2).
+template <class C, int QF, bool BF, int AB>
 __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
+    constexpr bool Q = QF != 0, BF8 = QF == 2;
     __shared__ __attribute__((aligned(1024))) char smem[ScaleLds<C>::kSmem];
 
     const int tiles_n = (p.N + TN - 1) / TN;
@@ -66,7 +75,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                                : (const char*)p.b_ptrs[g] + (int64_t)n0 * K;
     const char* sfb = p.sfb_dense ? (const char*)p.sfb_dense + ((int64_t)g * p.N + n0) * KB
                                   : (const char*)p.sfb_ptrs[g] + (int64_t)n0 * KB;
-    mx_mainloop<C>(smem, a, sfa, bg, sfb, K, K, rows_valid, cols_valid, am0, bn0, acc);
+    mx_mainloop<C, AB>(smem, a, sfa, bg, sfb, K, K, rows_valid, cols_valid, am0, bn0, acc);
 
     // ---------------- epilogue ----------------
     // Rows of 8 columns per lane: C and D are 16-byte accesses (32 for fp32).
@@ -85,15 +94,15 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
     const float nc = Q ? *p.q.norm_const : 1.0f;
     const int cdt = BF ? kBF16 : p.c_dtype, ddt = BF ? kBF16 : p.d_dtype;
     float dcol[4][8];                              // Q: a column block's 4 items
-    auto epilogue = [&](auto W32) {
-        constexpr bool w32 = decltype(W32)::value;
-        using Pre = Pre8<w32, 1>;
+    auto epilogue = [&](auto CWc) {
+        constexpr int cw = decltype(CWc)::value;
+        using Pre = Pre8<cw, 1>;
         auto load = [&](int, int r, int c) {
             const int rr = am0 + r, col = n0 + bn0 + c;
             const bool ok = (rr < rows_valid) & (col < p.N);
             const int64_t row = m0 + (ok ? rr : 0);
             Pre pre;
-            pre.x[0] = raw8_load<w32>(p.c, row * N + (ok ? col : 0));
+            pre.x[0] = rawc_load<cw>(p.c, row * N + (ok ? col : 0));
             pre.row = p.prob[row];
             return pre;
         };
@@ -107,7 +116,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                 float d[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
                 if (ok) {
                     float cv[8];
-                    raw8_cvt<w32>(pre.x[0], cdt, cv);
+                    rawc_cvt<cw>(pre.x[0], cdt, cv);
                     const float pr2 = pre.row * 2.0f;
 #pragma unroll
                     for (int k = 0; k < 8; k++) {
@@ -121,18 +130,18 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                 for (int k = 0; k < 8; k++)
                     dcol[t & 3][k] = d[k];
                 int e;
-                const uint2 codes = fp8_row8(d, nc, e);
+                const uint2 codes = fp8_row8<BF8>(d, nc, e);
                 if (ok)
                     fp8_store_row(p.q, m0 + rr, col, codes, e);
                 if ((t & 3) == 3 && p.q.d_col) {
                     const int r0 = r - 24;             // this lane's row of item t-3
-                    fp8_col_block(p.q, nc, dcol, m0 + am0 + (r0 & ~31), m0 + am0 + r0, col,
+                    fp8_col_block<BF8>(p.q, nc, dcol, m0 + am0 + (r0 & ~31), m0 + am0 + r0, col,
                                   col < p.N, rows_valid - (am0 + r0));
                 }
             } else if (rr < rows_valid && col < p.N) {
                 const int64_t row = m0 + rr;
                 float cv[8], d[8];
-                raw8_cvt<w32>(pre.x[0], cdt, cv);
+                rawc_cvt<cw>(pre.x[0], cdt, cv);
                 const float pr2 = pre.row * 2.0f;
 #pragma unroll
                 for (int k = 0; k < 8; k++) {
@@ -144,12 +153,18 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                 store8(p.d, ddt, row * N + col, d);
             }
         };
-        for_each_row8<C, Q ? (w32 ? 6 : 12) : (w32 ? 12 : 24)>(acc, elds, load, fn);
+        for_each_row8<C, Q ? (cw == 4 ? 6 : 12) : (cw == 4 ? 12 : 24)>(acc, elds, load, fn);
     };
-    if (p.c_dtype == kF32)
-        epilogue(std::true_type());
-    else
-        epilogue(std::false_type());
+    if constexpr (BF) {
+        epilogue(std::integral_constant<int, 2>());
+    } else {
+        if (p.c_dtype == kF32)
+            epilogue(std::integral_constant<int, 4>());
+        else if (p.c_dtype == kF8 || p.c_dtype == kF8E5M2)
+            epilogue(std::integral_constant<int, 1>());
+        else
+            epilogue(std::integral_constant<int, 2>());
+    }
 #pragma unroll
     for (int t = 0; t < kT; t++) {
         float v = rowsum[t];
@@ -176,21 +191,35 @@ hipError_t launch_dsrelu(const DsreluArgs& p, hipStream_t s, LaunchInfo* info) {
         return hipSuccess;
     const dim3 grid((unsigned)tiles), block(C::kThreads);
     if (info) {
-        snprintf(info->kernel, sizeof(info->kernel), "dsrelu_kernel<C %s, D %s>",
-                 dtype_name(p.c_dtype), dtype_name(p.d_dtype));
+        snprintf(info->kernel, sizeof(info->kernel), "dsrelu_kernel<A/B %s, C %s, D %s>",
+                 p.ab_e5m2 ? "e5m2" : "e4m3", dtype_name(p.c_dtype), dtype_name(p.d_dtype));
         info->tm = C::TM;
         info->tn = C::TN;
         info->waves = C::kWaves;
         info->grid = tiles;
     }
-    if (p.d_dtype == kF8 && p.c_dtype == kBF16)
-        hipLaunchKernelGGL((dsrelu_kernel<C, true, true>), grid, block, 0, s, p);
-    else if (p.d_dtype == kF8)
-        hipLaunchKernelGGL((dsrelu_kernel<C, true, false>), grid, block, 0, s, p);
-    else if (p.c_dtype == kBF16 && p.d_dtype == kBF16)
-        hipLaunchKernelGGL((dsrelu_kernel<C, false, true>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((dsrelu_kernel<C, false, false>), grid, block, 0, s, p);
+    const int qf = p.d_dtype == kF8 ? 1 : p.d_dtype == kF8E5M2 ? 2 : 0;
+    const bool bf = p.c_dtype == kBF16 && (qf != 0 || p.d_dtype == kBF16);
+    auto go = [&](auto QFc, auto ABc) {
+        constexpr int qfc = decltype(QFc)::value, abc = decltype(ABc)::value;
+        if (bf)
+            hipLaunchKernelGGL((dsrelu_kernel<C, qfc, true, abc>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((dsrelu_kernel<C, qfc, false, abc>), grid, block, 0, s, p);
+    };
+    using A0 = std::integral_constant<int, 0>;
+    using A1 = std::integral_constant<int, 1>;
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
+    using Q2 = std::integral_constant<int, 2>;
+    // E5M2 operands come with FP8 D only (the host rejects the rest)
+    if (p.ab_e5m2) {
+        if (qf == 0)
+            return hipErrorInvalidValue;
+        qf == 1 ? go(Q1(), A1()) : go(Q2(), A1());
+    } else {
+        qf == 1 ? go(Q1(), A0()) : qf == 2 ? go(Q2(), A0()) : go(Q0(), A0());
+    }
     return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ struct Fp8Out {
 };
 
 struct WgradArgs {
-    const void* a;            // bf16, or E4M3 codes (block-scaled)
+    const void* a;            // bf16, or FP8 codes (block-scaled)
     const void* b;
     const uint8_t* sfa;       // block-scaled only: E8M0 scales of A and B
     const uint8_t* sfb;
@@ -72,6 +72,7 @@ struct WgradArgs {
     int a_kmajor, b_kmajor;
     int ragged;               // K-major operands stored tensor_ragged
     int static_sched;         // persistent kernel: fixed item order, no queue
+    int ab_e5m2;              // block-scaled only: codes E5M2 (else E4M3)
     int xcd_gm;               // XCD block grid rows for xcd_remap2d (0: 1-D remap)
     int out_dtype, accumulate;
 };
@@ -101,7 +102,8 @@ struct DgluArgs {
     int gate_first, mask_filter;
     float geglu_alpha, clamp_min, clamp_max, linear_offset;
     float situ_b1, situ_b2;   // dSiTU-GLU tanh scales
-    Fp8Out q;                 // block-scaled only, with d_dtype E4M3
+    int ab_e5m2;              // block-scaled only: codes E5M2 (else E4M3)
+    Fp8Out q;                 // block-scaled only, with an FP8 d_dtype
 };
 
 struct DsreluArgs {
@@ -122,7 +124,8 @@ struct DsreluArgs {
     int64_t m_rows;
     int K, N, L;
     int c_dtype, d_dtype;
-    Fp8Out q;                 // with d_dtype E4M3
+    int ab_e5m2;              // codes E5M2 (else E4M3)
+    Fp8Out q;                 // with an FP8 d_dtype
 };
 
 // Launchers (return the HIP status of the launch).

@@ -41,13 +41,14 @@ struct ScaleLds {
                   "scale slices must split evenly over waves and units");
 };
 
+// AB: the codes' FP8 format (0 E4M3, 1 E5M2, A and B alike).
 // acc[i][j] += the wave's (32 i, 32 j) blocks of deq(A) deq(B)^T over the
 // first K values of each row, for the tile whose A rows start at `a` (scales
 // `sfa`) and whose B rows start at `b` (scales `sfb`).  Rows are `ld` bytes
 // apart (codes) and ld / 32 bytes apart (scales); K and ld are multiples of
 // 128 (whole load units, 4-byte scale words), and rows at or past rows_valid
 // / cols_valid contribute zero.  smem holds ScaleLds<C>::kSmem bytes.
-template <class C>
+template <class C, int AB = 0>
 __device__ __forceinline__ void mx_mainloop(char* smem, const char* a, const char* sfa,
                                             const char* b, const char* sfb, int64_t ld, int64_t K,
                                             int rows_valid, int cols_valid, int am0, int bn0,
@@ -115,7 +116,7 @@ __device__ __forceinline__ void mx_mainloop(char* smem, const char* a, const cha
         else
             f.sb[g - MB] = *reinterpret_cast<const uint32_t*>(buf + (TM + bn0 + 32 * (g - MB) + lr) * 16) >> sh;
     };
-    auto mma = [&](const FragMx8<C>& f, int m0_, int m1_) { mma_mx8<C>(f, acc, m0_, m1_); };
+    auto mma = [&](const FragMx8<C>& f, int m0_, int m1_) { mma_mx8<C, AB>(f, acc, m0_, m1_); };
     FragMx8<C> frag[2];
     // Group 0 ahead of unit 0: complete whenever unit 0 is.
 #pragma unroll

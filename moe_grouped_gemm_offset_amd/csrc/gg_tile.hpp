@@ -351,7 +351,9 @@ __device__ __forceinline__ void read_mx8(const char* sa, const char* sb, int a0,
 }
 
 // MFMAs m0 .. m1-1 of a stage, m = i NB + j.
-template <class C>
+// AB: the operands' FP8 format, 0 E4M3 ("fp8"), 1 E5M2 ("bf8"): the MFMA's
+// cbsz / blgp format fields for A and B.
+template <class C, int AB = 0>
 __device__ __forceinline__ void mma_mx8(const FragMx8<C>& f, f32x16 (&acc)[C::MB][C::NB], int m0,
                                         int m1) {
 #pragma unroll
@@ -360,7 +362,7 @@ __device__ __forceinline__ void mma_mx8(const FragMx8<C>& f, f32x16 (&acc)[C::MB
             continue;
         const int i = m / C::NB, j = m % C::NB;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            f.a[i], f.b[j], acc[i][j], 0, 0, 0, (int)f.sa[i], 0, (int)f.sb[j]);
+            f.a[i], f.b[j], acc[i][j], AB, AB, 0, (int)f.sa[i], 0, (int)f.sb[j]);
     }
 }
 
@@ -744,7 +746,7 @@ __device__ __forceinline__ void store_bf16x8(__amdgpu_buffer_rsrc_t r, uint32_t 
 }
 
 // dtype codes (the gg_dtype values of the ABI)
-constexpr int kBF16 = 0, kF16 = 1, kF32 = 2, kF8 = 3;   // gg_dtype codes
+constexpr int kBF16 = 0, kF16 = 1, kF32 = 2, kF8 = 3, kF8E5M2 = 4;   // gg_dtype codes
 
 __device__ __forceinline__ float load_elem(const void* base, int dtype, int64_t i) {
     if (dtype == kBF16)
@@ -817,39 +819,71 @@ __device__ __forceinline__ void store8(void* base, int dtype, int64_t i, const f
     }
 }
 
+// Eight FP8 codes (E4M3, or E5M2 when dtype is kF8E5M2) to fp32, exactly.
+__device__ __forceinline__ void unpack8_8(uint32_t lo, uint32_t hi, int dtype, float (&v)[8]) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t ws[2] = {lo, hi};
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        f32x2 a, b;
+        if (dtype == kF8E5M2) {
+            a = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[h], false);
+            b = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[h], true);
+        } else {
+            a = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[h], false);
+            b = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[h], true);
+        }
+        v[4 * h] = a.x;
+        v[4 * h + 1] = a.y;
+        v[4 * h + 2] = b.x;
+        v[4 * h + 3] = b.y;
+    }
+}
+
 // ---------------------------------------------------------------------------
-// Raw loads of 8 consecutive elements (16 bytes for bf16 / fp16; W32: 32 for
-// fp32), converted to fp32 only when used, so that a caller can have many in
-// flight.  The element index is a multiple of 8.
+// Raw loads of 8 consecutive elements of CW bytes each (CW 1: FP8 codes, 8
+// bytes; 2: bf16 / fp16, 16 bytes; 4: fp32, 32 bytes), converted to fp32
+// only when used, so that a caller can have many in flight.  The element
+// index is a multiple of 8.
 // ---------------------------------------------------------------------------
-template <bool W32>
-struct Raw8 {
-    u32x4 w[W32 ? 2 : 1];
+template <int CW>
+struct RawC {
+    static_assert(CW == 1 || CW == 2 || CW == 4, "element widths 1, 2, 4");
+    uint32_t w[2 * CW];
 };
 
-template <bool W32>
-__device__ __forceinline__ Raw8<W32> raw8_load(const void* base, int64_t i) {
-    Raw8<W32> r;
-    if constexpr (W32) {
-        r.w[0] = *reinterpret_cast<const u32x4*>((const float*)base + i);
-        r.w[1] = *reinterpret_cast<const u32x4*>((const float*)base + i + 4);
+template <int CW>
+__device__ __forceinline__ RawC<CW> rawc_load(const void* base, int64_t i) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    RawC<CW> r;
+    if constexpr (CW == 1) {
+        const u32x2 q = *reinterpret_cast<const u32x2*>((const uint8_t*)base + i);
+        r.w[0] = q.x;
+        r.w[1] = q.y;
     } else {
-        r.w[0] = *reinterpret_cast<const u32x4*>((const uint16_t*)base + i);
+#pragma unroll
+        for (int h = 0; h < CW / 2; h++) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>((const char*)base + i * CW + 16 * h);
+            r.w[4 * h] = q.x;
+            r.w[4 * h + 1] = q.y;
+            r.w[4 * h + 2] = q.z;
+            r.w[4 * h + 3] = q.w;
+        }
     }
     return r;
 }
 
-// dtype: kF32 when W32, else kBF16 or kF16.
-template <bool W32>
-__device__ __forceinline__ void raw8_cvt(const Raw8<W32>& r, int dtype, float (&v)[8]) {
-    if constexpr (W32) {
-        const uint32_t ws[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w,
-                                r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
+// dtype: kF32 for CW 4; kBF16 or kF16 for CW 2; kF8 or kF8E5M2 for CW 1.
+template <int CW>
+__device__ __forceinline__ void rawc_cvt(const RawC<CW>& r, int dtype, float (&v)[8]) {
+    if constexpr (CW == 4) {
 #pragma unroll
         for (int k = 0; k < 8; k++)
-            v[k] = __builtin_bit_cast(float, ws[k]);
+            v[k] = __builtin_bit_cast(float, r.w[k]);
+    } else if constexpr (CW == 2) {
+        unpack8_16(u32x4{r.w[0], r.w[1], r.w[2], r.w[3]}, dtype, v);
     } else {
-        unpack8_16(r.w[0], dtype, v);
+        unpack8_8(r.w[0], r.w[1], dtype, v);
     }
 }
 
@@ -998,9 +1032,9 @@ __device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB],
 // Loads of one row-walk item: NC raw 8-element loads and one fp32 per-row
 // value (plain pointers, compile-time width; or buffer descriptors, runtime
 // width).
-template <bool W32, int NC>
+template <int CW, int NC>
 struct Pre8 {
-    Raw8<W32> x[NC];
+    RawC<CW> x[NC];
     float row;
 };
 template <int NC>

@@ -2,7 +2,8 @@
 //
 // Computes Wgrad[e] = deq(A)[:, begin:end] @ deq(B)[begin:end, :] for every
 // expert ("Grouped GEMM + WGrad (Unified)", "Operation", on the operands of
-// its "Block-scaled contract"): E4M3 codes with one E8M0 scale per 32 tokens
+// its "Block-scaled contract"): FP8 codes (E4M3, or E5M2 for both operands:
+// the FP8 formats the dGLU page's data-type table lists) with one E8M0 scale per 32 tokens
 // of a row, A (hidden, T) and B stored K-major as (inter, T), so that the
 // reduction axis is contiguous in both, as the scaled MFMA consumes it.
 // Either operand is a tensor2d (rows T tokens apart) or tensor_ragged (each
@@ -23,7 +24,8 @@ namespace gg {
 
 using WgradMxCfg = Cfg<256, 256, 2, 2>;
 
-template <class C>
+// AB: the codes' FP8 format (0 E4M3, 1 E5M2).
+template <class C, int AB>
 __global__ void __launch_bounds__(C::kThreads, 1) wgrad_mx_kernel(WgradArgs p) {
     constexpr int TM = C::TM, TN = C::TN;
     __shared__ __attribute__((aligned(1024))) char smem[ScaleLds<C>::kSmem];
@@ -73,7 +75,8 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_mx_kernel(WgradArgs p) {
     const char* sfa = (const char*)p.sfa + (a0 + (int64_t)m0 * ld) / 32;
     const char* sfb = (const char*)p.sfb + (b0 + (int64_t)n0 * ld) / 32;
     if (cnt > 0)
-        mx_mainloop<C>(smem, a, sfa, b, sfb, ld, cnt, p.hidden - m0, p.inter - n0, am0, bn0, acc);
+        mx_mainloop<C, AB>(smem, a, sfa, b, sfb, ld, cnt, p.hidden - m0, p.inter - n0, am0, bn0,
+                           acc);
 
     void* out = p.out_dense
         ? (void*)((char*)p.out_dense +
@@ -89,14 +92,19 @@ hipError_t launch_wgrad_mx(const WgradArgs& p, hipStream_t s, LaunchInfo* info) 
     using C = WgradMxCfg;
     const int tiles = ((p.hidden + C::TM - 1) / C::TM) * ((p.inter + C::TN - 1) / C::TN);
     if (info) {
-        snprintf(info->kernel, sizeof(info->kernel), "wgrad_mx_kernel (one tile per workgroup)");
+        snprintf(info->kernel, sizeof(info->kernel), "wgrad_mx_kernel<A/B %s> (one tile per workgroup)",
+                 p.ab_e5m2 ? "e5m2" : "e4m3");
         info->tm = C::TM;
         info->tn = C::TN;
         info->waves = C::kWaves;
         info->grid = (int64_t)tiles * p.E;
     }
-    hipLaunchKernelGGL((wgrad_mx_kernel<C>), dim3((unsigned)(tiles * p.E)), dim3(C::kThreads), 0,
-                       s, p);
+    if (p.ab_e5m2)
+        hipLaunchKernelGGL((wgrad_mx_kernel<C, 1>), dim3((unsigned)(tiles * p.E)), dim3(C::kThreads),
+                           0, s, p);
+    else
+        hipLaunchKernelGGL((wgrad_mx_kernel<C, 0>), dim3((unsigned)(tiles * p.E)), dim3(C::kThreads),
+                           0, s, p);
     return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@ from oracle import oracle as orc
 from moe_grouped_gemm_offset_amd import synth
 
 TOL = {orc.F32: 1e-3, orc.BF16: 1e-2, orc.F16: 1e-2}
-ORC_DT = {torch.float32: orc.F32, torch.bfloat16: orc.BF16, torch.float16: orc.F16}
+ORC_DT = {torch.float32: orc.F32, torch.bfloat16: orc.BF16, torch.float16: orc.F16,
+          torch.float8_e4m3fn: orc.E4M3, torch.float8_e5m2: orc.E5M2}
 
 
 def say(*a):

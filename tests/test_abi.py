@@ -166,11 +166,15 @@ def dsrelu(**kw):
     (dict(sfb=None), MODE),
     (dict(k=192), UNSUPPORTED),
     (dict(n=40), SHAPE),
-    (dict(ddt=4), DTYPE),
+    (dict(ddt=5), DTYPE),
+    (dict(cdt=5), DTYPE),
+    (dict(ddt=4), NULL),               # FP8 D without fp8_out
     (dict(sfa=P + 1), ALIGN),
     (dict(wsb=16), WORKSPACE),
     (dict(flags=8), MODE),
-    (dict(flags=32), MODE),
+    (dict(flags=64), MODE),
+    (dict(flags=32), UNSUPPORTED),     # E5M2 operands with a 16/32-bit D
+    (dict(flags=32, ddt=2), UNSUPPORTED),
 ])
 def test_dsrelu_rejects(kw, status):
     assert dsrelu(**kw) == status
@@ -204,8 +208,9 @@ def fp8_out(**kw):
     (dict(norm_const=P + 2), ALIGN),
 ])
 def test_fp8_out_checks(entry, kw, status):
-    """GG_F8E4M3 outputs: fp8_out is required and checked; valid ones reach
-    the device check (GG_ERR_DEVICE here, where there is no GPU)."""
+    """FP8 outputs (GG_F8E4M3, GG_F8E5M2): fp8_out is required and checked;
+    valid ones reach the device check (GG_ERR_DEVICE here, where there is no
+    GPU)."""
     f = fp8_out(**kw)                  # kept alive across the calls below
     call = dsrelu if entry == "dsrelu" else dglu_mx
     got = call(ddt=3, fp8=ctypes.addressof(f))
@@ -214,7 +219,9 @@ def test_fp8_out_checks(entry, kw, status):
         pytest.skip("checks the no-device path")
     assert got == want
     assert call(ddt=3, fp8=None) == NULL
-    assert call(ddt=4, fp8=ctypes.addressof(f)) == DTYPE
+    assert call(ddt=4, fp8=ctypes.addressof(f)) == got, "E5M2 outputs take the same checks"
+    assert call(ddt=4, fp8=None) == NULL
+    assert call(ddt=5, fp8=ctypes.addressof(f)) == DTYPE
 
 
 def dglu_mx(**kw):
@@ -246,7 +253,10 @@ def dglu_mx(**kw):
     (dict(k=192), UNSUPPORTED),
     (dict(n=1 << 21), UNSUPPORTED),
     (dict(n=40), SHAPE),
-    (dict(cdt=3), DTYPE),
+    (dict(cdt=5), DTYPE),
+    (dict(ddt=5), DTYPE),
+    (dict(flags=64), MODE),
+    (dict(flags=32), UNSUPPORTED),     # E5M2 operands with a 16/32-bit D
     (dict(amax=P + 2), ALIGN),
     (dict(a=P + 8), ALIGN),
     (dict(dbias=P, wsb=256), WORKSPACE),
@@ -263,3 +273,56 @@ def test_valid_call_without_a_gpu_reports_device():
     assert dglu_mx() == DEVICE
     assert dglu_mx(act=2) == DEVICE
     assert dglu_mx(act=0, b1=0.0) == DEVICE, "the dSiTU scales are ignored for other activations"
+
+
+def wgrad_mx(**kw):
+    args = dict(a=P, sfa=P, b=P, sfb=P, offsets=P, E=4, T=1024, hidden=256, inter=256, dense=P,
+                ptrs=None, dtype=2, acc=0, flags=0, ws=WS, wsb=4096)
+    args.update(kw)
+    lib = B.load_library()
+    return lib.gg_wgrad_mx(args["a"], args["sfa"], args["b"], args["sfb"], args["offsets"],
+                           args["E"], args["T"], args["hidden"], args["inter"], args["dense"],
+                           args["ptrs"], args["dtype"], args["acc"], args["flags"], args["ws"],
+                           args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sfa=None), NULL),
+    (dict(dtype=3), DTYPE),
+    (dict(dtype=4), DTYPE),
+    (dict(T=1000), ALIGN),
+    (dict(sfb=P + 2), ALIGN),
+    (dict(flags=64), MODE),
+    (dict(flags=1), MODE),
+])
+def test_wgrad_mx_rejects(kw, status):
+    assert wgrad_mx(**kw) == status
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+@pytest.mark.parametrize("entry,kw", [
+    ("wgrad_mx", dict(flags=32)),
+    ("wgrad_mx", dict(flags=32 | 8, dtype=0)),
+    ("dsrelu", dict(cdt=3)),
+    ("dsrelu", dict(cdt=4)),
+    ("dglu_mx", dict(cdt=3)),
+    ("dglu_mx", dict(cdt=4, act=2)),
+])
+def test_fp8_formats_accepted(entry, kw):
+    """E5M2 operands (GG_FLAG_AB_E5M2) on gg_wgrad_mx, and FP8 C (E4M3,
+    E5M2) on the block-scaled dgrad entries, pass the host checks."""
+    assert globals()[entry](**kw) == DEVICE
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+@pytest.mark.parametrize("entry", ["dsrelu", "dglu_mx"])
+@pytest.mark.parametrize("ddt", [3, 4])
+def test_e5m2_operands_with_fp8_out(entry, ddt):
+    """GG_FLAG_AB_E5M2 with an FP8 D (either format) passes the host checks;
+    the non-block-scaled entries reject the flag."""
+    f = fp8_out()
+    assert globals()[entry](flags=32, ddt=ddt, fp8=ctypes.addressof(f)) == DEVICE
+    assert globals()[entry](flags=32, ddt=ddt, cdt=4, fp8=ctypes.addressof(f)) == DEVICE
+    assert wgrad(flags=32) == MODE
+    assert dglu(flags=32) == MODE
+    assert dglu(cdt=3) == DTYPE

@@ -134,6 +134,21 @@ def test_dbias():
     assert torch.all(got["dbias"][2] == 0), "an empty expert's dbias stays 0"
 
 
+@pytest.mark.parametrize("c_dtype", [torch.float8_e4m3fn, torch.float8_e5m2])
+@pytest.mark.parametrize("act,d_dtype", [(orc.DSWIGLU, torch.bfloat16), (orc.DGEGLU, torch.float32),
+                                         (orc.DSITUGLU, torch.float16)])
+def test_fp8_c(c_dtype, act, d_dtype):
+    """An FP8 C (the dGLU page's "Input tensor C" dtypes) is read as its
+    exact value, with dbias."""
+    inp = small(85, True, c_dtype=c_dtype, c_std=4.0 if act == orc.DGEGLU else 2.0)
+    say("dglu_mx fp8 C", c_dtype, "act", act, "D", d_dtype)
+    got = run_gpu(inp, d_dtype, act=act, dbias=True)
+    ref = run_oracle(inp, d_dtype, act=act, dbias=True)
+    check(inp, got, ref, ORC_DT[d_dtype])
+    assert_close(values(got["dbias"]), ref["dbias"], orc.BF16, "dbias")
+    assert_close(got["amax"].numpy().ravel(), ref["amax"].ravel(), orc.F32, "amax")
+
+
 @pytest.mark.parametrize("c_dtype", [torch.float16, torch.float32])
 @pytest.mark.parametrize("d_dtype", [torch.float16, torch.float32])
 def test_dtypes(c_dtype, d_dtype):

@@ -97,6 +97,23 @@ def test_dtypes(c_dtype, d_dtype):
     assert_close(values(dprob[:vm]), ref["dprob"][:vm], orc.F32, "dprob")
 
 
+@pytest.mark.parametrize("c_dtype", [torch.float8_e4m3fn, torch.float8_e5m2])
+@pytest.mark.parametrize("d_dtype", [torch.bfloat16, torch.float32])
+def test_fp8_c(c_dtype, d_dtype):
+    """An FP8 C (the dsReLU page's "Input tensor C" dtypes) is read as its
+    exact value."""
+    inp = small(64, c_dtype=c_dtype, discrete=True)
+    say("dsrelu fp8 C", c_dtype, "D", d_dtype)
+    d, dprob, amax, err = run_gpu(inp, d_dtype)
+    assert err == 0
+    ref = run_oracle(inp, d_dtype)
+    vm = inp["valid_m"]
+    assert_close(values(d[:vm]), ref["D"][:vm], ORC_DT[d_dtype], "D_row")
+    assert torch.all(torch.isnan(d[vm:]))
+    assert_close(values(dprob[:vm]), ref["dprob"][:vm], orc.F32, "dprob")
+    assert_close(amax.numpy(), ref["amax"], orc.F32, "amax")
+
+
 def test_unit_scales_no_amax():
     inp = small(63, spread=0)
     inp["sfa"] = torch.full_like(inp["sfa"], 127)

@@ -1,16 +1,18 @@
-"""GPU parity of the FP8 (E4M3) outputs of gg_dsrelu and gg_dglu_mx against
-the oracle's step 3 (orc_quant_fp8) applied to the oracle's D.
+"""GPU parity of the FP8 (E4M3 and E5M2) outputs of gg_dsrelu and
+gg_dglu_mx against the oracle's step 3 (orc_quant_fp8) applied to the
+oracle's D, for E4M3 and E5M2 operands (GG_FLAG_AB_E5M2) and 16-bit or FP8
+C.
 
 The kernel's D (fp32 accumulation) and the oracle's D (double) differ by a
 few fp32 ulps, so a block's scale exponent may differ where
-norm_const * amax / 448 lies within that distance of a power of two, and a
-code may differ by one step where a value lies that close to a rounding
-midpoint.  The tests check: every scale that differs belongs to such a
-boundary block; at least 99% of the codes are identical; and the
-dequantized outputs (code * 2^e / norm_const) are within the E4M3 bound of
-the oracle's exact D, normwise 2^-4 (half a step of 3 fraction bits) plus
-the 1e-2 of the 16-bit outputs.  Rows past valid_m and their scales are not
-written.
+norm_const * amax / fmax (448 for E4M3, 57344 for E5M2) lies within that
+distance of a power of two, and a code may differ by one step where a value
+lies that close to a rounding midpoint.  The tests check: every scale that
+differs belongs to such a boundary block; at least 99% of the codes are
+identical; and the dequantized outputs (code * 2^e / norm_const) are within
+the format's bound of the oracle's exact D, normwise half a step of its
+fraction bits (2^-4 for E4M3's 3, 2^-3 for E5M2's 2) plus the 1e-2 of the
+16-bit outputs.  Rows past valid_m and their scales are not written.
 """
 import numpy as np
 import pytest
@@ -18,13 +20,19 @@ import torch
 
 from oracle import oracle as orc
 from moe_grouped_gemm_offset_amd import synth
-from tests.parity_util import normwise, say
+from tests.parity_util import ORC_DT, normwise, say
 
 pytestmark = pytest.mark.gpu
 
-FP8_TOL = 2.0 ** -4 + 1e-2
-SENT = 0x7F                                   # E4M3 NaN: "not written"
-E4M3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().double().numpy()
+SENT = 0x7F                                   # NaN in both formats: "not written"
+# per output format: code -> value table, largest value, normwise tolerance
+FMT = {
+    orc.E4M3: (torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().double().numpy(),
+               448.0, 2.0 ** -4 + 1e-2),
+    orc.E5M2: (torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).float().double().numpy(),
+               57344.0, 2.0 ** -3 + 1e-2),
+}
+TORCH_FP8 = {orc.E4M3: torch.float8_e4m3fn, orc.E5M2: torch.float8_e5m2}
 
 
 def gg():
@@ -42,10 +50,11 @@ def outputs(M, W):
     return d_row, dict(d_col=d_col, sfd_row=sfd_row, sfd_col=sfd_col)
 
 
-def check(name, got_row, fp8, D, nc, vm):
-    """got_row / fp8: the kernel's outputs (CPU tensors); D: the oracle's
-    float64 D of rows 0 .. vm-1."""
-    ref = orc.quant_fp8(D, nc, with_col=True)
+def check(name, got_row, fp8, D, nc, vm, fmt=orc.E4M3):
+    """got_row / fp8: the kernel's outputs (CPU tensors) in format fmt; D:
+    the oracle's float64 D of rows 0 .. vm-1."""
+    table, fmax, tol = FMT[fmt]
+    ref = orc.quant_fp8(D, nc, with_col=True, d_dtype=fmt)
     M, W = got_row.shape
     P = fp8["sfd_col"].shape[1]
     # untouched rows and scale blocks past valid_m
@@ -58,65 +67,86 @@ def check(name, got_row, fp8, D, nc, vm):
         if kind == "row":
             Db = D.reshape(vm, W // 32, 32)
             e = sfd.astype(np.int64) - 127
-            deq = E4M3[codes].reshape(vm, W // 32, 32) * np.exp2(e)[..., None] / nc
+            deq = table[codes].reshape(vm, W // 32, 32) * np.exp2(e)[..., None] / nc
             deq = deq.reshape(vm, W)
         else:
             Db = D.T.reshape(W, vm // 32, 32)
             e = sfd.astype(np.int64) - 127
-            deq = (E4M3[codes.T].reshape(W, vm // 32, 32) * np.exp2(e)[..., None] / nc).reshape(W, vm).T
+            deq = (table[codes.T].reshape(W, vm // 32, 32) * np.exp2(e)[..., None] / nc).reshape(W, vm).T
         amax = np.abs(Db.astype(np.float32)).max(axis=2).astype(np.float64)
-        lg = np.log2(np.maximum(nc * amax / 448.0, 1e-300))
+        lg = np.log2(np.maximum(nc * amax / fmax, 1e-300))
         boundary = np.abs(lg - np.round(lg)) < 1e-4
         differ = sfd != rs
         assert not np.any(differ & ~boundary), f"{name} {kind}: {int(np.sum(differ & ~boundary))} scales differ"
         same = np.mean(codes == rq)
         err = normwise(deq, D)
         say(f"  {name} {kind}: codes identical {same:.5f}, scales differing {int(differ.sum())}, "
-            f"dequantized normwise {err:.3e} (tol {FP8_TOL:.3e})")
+            f"dequantized normwise {err:.3e} (tol {tol:.3e})")
         assert same >= 0.99, f"{name} {kind}: only {same:.4f} of the codes agree"
-        assert err <= FP8_TOL
+        assert err <= tol
 
 
-def dsrelu_inputs(seed, discrete=False):
+def dsrelu_inputs(seed, discrete=False, ab=orc.E4M3, c_dtype=torch.bfloat16):
     counts = [256, 512, 0, 256]
     return synth.dsrelu_inputs(4, 512, 320, counts, m_extra=64, seed=seed, discrete=discrete,
-                               scale_spread=3)
+                               scale_spread=3, ab_dtype=TORCH_FP8[ab], c_dtype=c_dtype)
 
 
-@pytest.mark.parametrize("nc", [1.0, 0.25])
-def test_dsrelu_fp8(nc):
+# (operand format, output format, C dtype, norm_const)
+DSRELU_CASES = [
+    (orc.E4M3, orc.E4M3, torch.bfloat16, 1.0),
+    (orc.E4M3, orc.E4M3, torch.bfloat16, 0.25),
+    (orc.E4M3, orc.E5M2, torch.bfloat16, 1.0),
+    (orc.E5M2, orc.E4M3, torch.bfloat16, 0.25),
+    (orc.E5M2, orc.E5M2, torch.bfloat16, 1.0),
+    (orc.E5M2, orc.E5M2, torch.float8_e4m3fn, 1.0),
+    (orc.E4M3, orc.E4M3, torch.float8_e5m2, 1.0),
+    (orc.E5M2, orc.E5M2, torch.float32, 2.0),
+]
+
+
+@pytest.mark.parametrize("ab,fmt,c_dtype,nc", DSRELU_CASES)
+def test_dsrelu_fp8(ab, fmt, c_dtype, nc):
     b = gg()
-    inp = dsrelu_inputs(111)
+    inp = dsrelu_inputs(111, ab=ab, c_dtype=c_dtype)
     M, N, L = inp["M"], inp["N"], inp["L"]
     d_row, fp8 = outputs(M, N)
     ncd = torch.tensor([nc], dtype=torch.float32, device="cuda")
     dprob = torch.zeros(M, dtype=torch.float32, device="cuda")
     amax = torch.zeros(L, dtype=torch.float32, device="cuda")
-    say("dsrelu fp8 out, norm_const", nc)
-    ws = b.gg_dsrelu(inp["a"].cuda().view(torch.uint8), inp["sfa"].cuda(),
+    say("dsrelu fp8 out: operands", ab, "D", fmt, "C", c_dtype, "norm_const", nc)
+    ws = b.gg_dsrelu(inp["a"].cuda(), inp["sfa"].cuda(),
                      inp["b_dense"].cuda().view(torch.uint8), inp["sfb_dense"].cuda(), None, None, N,
                      inp["c"].cuda(), inp["padded_offsets"].cuda(), inp["alpha"].cuda(),
-                     inp["prob"].cuda(), d_row.view(torch.float8_e4m3fn), dprob, amax,
+                     inp["prob"].cuda(), d_row.view(TORCH_FP8[fmt]), dprob, amax,
                      fp8_out=dict(fp8, norm_const=ncd))
     torch.cuda.synchronize()
     assert b.gg_device_error(ws) == 0
     ref = orc.dsrelu(synth.bits(inp["a"]), synth.bits(inp["sfa"]), M, inp["K"],
                      [synth.bits(x) for x in inp["b_list"]], [synth.bits(x) for x in inp["sfb_list"]],
-                     N, synth.bits(inp["c"]), orc.BF16, inp["padded_offsets"].numpy(),
-                     inp["alpha"].numpy(), inp["prob"].numpy())
+                     N, synth.bits(inp["c"]), ORC_DT[c_dtype], inp["padded_offsets"].numpy(),
+                     inp["alpha"].numpy(), inp["prob"].numpy(), ab_dtype=ab)
     vm = inp["valid_m"]
-    check("dsrelu", d_row.cpu(), {k: v.cpu() for k, v in fp8.items()}, ref["D"][:vm], nc, vm)
+    check("dsrelu", d_row.cpu(), {k: v.cpu() for k, v in fp8.items()}, ref["D"][:vm], nc, vm, fmt)
     got_dp = dprob.cpu().double().numpy()[:vm]
     assert normwise(got_dp, ref["dprob"][:vm]) <= 1e-3
 
 
+FMT_CASES = [(orc.E4M3, orc.E4M3, torch.bfloat16), (orc.E4M3, orc.E5M2, torch.bfloat16),
+             (orc.E5M2, orc.E5M2, torch.float8_e5m2), (orc.E5M2, orc.E4M3, torch.float8_e4m3fn)]
+
+
+@pytest.mark.parametrize("ab,fmt,c_dtype", FMT_CASES)
 @pytest.mark.parametrize("act,flags", [(orc.DSWIGLU, 0), (orc.DGEGLU, 1), (orc.DSITUGLU, 0)])
 @pytest.mark.parametrize("with_col", [True, False])
-def test_dglu_mx_fp8(act, flags, with_col):
+def test_dglu_mx_fp8(act, flags, with_col, ab, fmt, c_dtype):
+    if not with_col and (ab, fmt) != (orc.E4M3, orc.E4M3):
+        pytest.skip("row-only output: one format case is enough")
     b = gg()
     counts = [256, 512, 0, 256]
     inp = synth.dglu_mx_inputs(4, 512, 320, counts, c_std=4.0, m_extra=64, seed=112,
-                               discrete=True, scale_spread=3)
+                               discrete=True, scale_spread=3, ab_dtype=TORCH_FP8[ab],
+                               c_dtype=c_dtype)
     M, N, L = inp["M"], inp["N"], inp["L"]
     d_row, fp8 = outputs(M, 2 * N)
     if not with_col:
@@ -129,21 +159,23 @@ def test_dglu_mx_fp8(act, flags, with_col):
     ks = [x.cuda() for x in inp["sfb_list"]]
     bp = torch.tensor([x.data_ptr() for x in kb], dtype=torch.int64, device="cuda")
     sp = torch.tensor([x.data_ptr() for x in ks], dtype=torch.int64, device="cuda")
-    say("dglu_mx fp8 out", act, flags, "with D_col" if with_col else "row only")
-    ws = b.gg_dglu_mx(inp["a"].cuda().view(torch.uint8), inp["sfa"].cuda(), None, None, bp, sp, N,
+    say("dglu_mx fp8 out", act, flags, "with D_col" if with_col else "row only", "operands", ab,
+        "D", fmt, "C", c_dtype)
+    ws = b.gg_dglu_mx(inp["a"].cuda(), inp["sfa"].cuda(), None, None, bp, sp, N,
                       inp["c"].cuda(), inp["padded_offsets"].cuda(), inp["alpha"].cuda(),
-                      inp["beta"].cuda(), inp["prob"].cuda(), d_row.view(torch.float8_e4m3fn), dprob,
+                      inp["beta"].cuda(), inp["prob"].cuda(), d_row.view(TORCH_FP8[fmt]), dprob,
                       amax=amax, fp8_out=dict(fp8, norm_const=ncd), act=act, flags=flags)
     torch.cuda.synchronize()
     assert b.gg_device_error(ws) == 0
     ref = orc.dglu_mx(synth.bits(inp["a"]), synth.bits(inp["sfa"]), M, inp["K"],
                       [synth.bits(x) for x in inp["b_list"]], [synth.bits(x) for x in inp["sfb_list"]],
-                      N, synth.bits(inp["c"]), orc.BF16, inp["padded_offsets"].numpy(),
+                      N, synth.bits(inp["c"]), ORC_DT[c_dtype], inp["padded_offsets"].numpy(),
                       inp["alpha"].numpy(), inp["beta"].numpy(), inp["prob"].numpy(), act=act,
-                      gate_first=bool(flags & 1))
+                      gate_first=bool(flags & 1), ab_dtype=ab)
     vm = inp["valid_m"]
     if with_col:
-        check("dglu_mx", d_row.cpu(), {k: v.cpu() for k, v in fp8.items()}, ref["D"][:vm], nc, vm)
+        check("dglu_mx", d_row.cpu(), {k: v.cpu() for k, v in fp8.items()}, ref["D"][:vm], nc, vm,
+              fmt)
     else:
         q = orc.quant_fp8(ref["D"][:vm], nc, with_col=False)
         got = d_row.cpu().numpy()

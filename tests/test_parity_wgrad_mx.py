@@ -30,9 +30,9 @@ def run_gpu(inp, out_dtype, accumulate=False, old=None, discrete=False, ragged=F
     E = len(inp["counts"])
     a, sfa = inp["a"].cuda().view(torch.uint8), inp["sfa"].cuda()
     bb, sfb = inp["b"].cuda().view(torch.uint8), inp["sfb"].cuda()
-    flags = 0
+    flags = b.GG_FLAG_AB_E5M2 if inp["a"].dtype == torch.float8_e5m2 else 0
     if ragged:
-        flags = b.GG_FLAG_TENSOR_RAGGED
+        flags |= b.GG_FLAG_TENSOR_RAGGED
         a, bb = synth.to_ragged(a, inp["counts"]), synth.to_ragged(bb, inp["counts"])
         sfa = synth.to_ragged(sfa, inp["counts"], per=32)
         sfb = synth.to_ragged(sfb, inp["counts"], per=32)
@@ -62,7 +62,8 @@ def run_oracle(inp, out_dtype, accumulate=False, old=None, hrows=None):
     return orc.wgrad_mx(synth.bits(inp["a"]), synth.bits(inp["sfa"]), synth.bits(inp["b"]),
                         synth.bits(inp["sfb"]), inp["offsets"].numpy(), inp["hidden"],
                         inp["inter"], inp["tokens_sum"], out_dtype=od, accumulate=accumulate,
-                        old=None if old is None else synth.bits(old), hrows=hrows), od
+                        old=None if old is None else synth.bits(old), hrows=hrows,
+                        ab_dtype=ORC_DT[inp["a"].dtype]), od
 
 
 def compare(got, inp, out_dtype, accumulate=False, old=None, hrows=None, name="", skipped=()):
@@ -107,6 +108,29 @@ def test_outputs_and_modes(dtype, discrete, accumulate):
     got, err = run_gpu(inp, dtype, accumulate, old, discrete)
     assert err == 0
     compare(got, inp, dtype, accumulate, old, name=f"{dtype} {discrete} {accumulate}")
+
+
+@pytest.mark.parametrize("dtype,discrete,ragged", [(torch.float32, False, False),
+                                                   (torch.bfloat16, True, True),
+                                                   (torch.float16, False, True)])
+def test_e5m2_operands(dtype, discrete, ragged):
+    """E5M2 codes for both operands (GG_FLAG_AB_E5M2): the MFMA's format
+    fields select E5M2 for A and B."""
+    counts = [256, 0, 768, 512]
+    inp = small(107, counts=counts, hidden=256, inter=320, ab_dtype=torch.float8_e5m2)
+    say("wgrad_mx e5m2", dtype, "discrete" if discrete else "dense", "ragged" if ragged else "")
+    got, err = run_gpu(inp, dtype, discrete=discrete, ragged=ragged)
+    assert err == 0
+    compare(got, inp, dtype, name=f"e5m2 {dtype}")
+
+
+def test_e5m2_exact_integers_bit_exact():
+    """Integers in [-2, 2] are exact in E5M2 too: bit-exact fp32 sums."""
+    inp = small(108, counts=(256, 512, 0, 256), hidden=256, inter=256, ints=True,
+                ab_dtype=torch.float8_e5m2)
+    got, _ = run_gpu(inp, torch.float32)
+    (exact, res), _ = run_oracle(inp, torch.float32)
+    assert np.array_equal(got.numpy(), res)
 
 
 def test_exact_integers_bit_exact():
