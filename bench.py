@@ -70,9 +70,9 @@ KERNEL_SOURCES = {
     "dglu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_fp8out.hpp", "gg_dglu_epi.hpp",
                     "gg_dglu.hip"],
     "dglu_mx_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_fp8out.hpp",
-                       "gg_dglu_epi.hpp", "gg_dglu_mx.hip"],
+                       "gg_dglu_epi.hpp", "gg_dglu_mx.hpp", "gg_dglu_mx_inst.hip"],
     "dsrelu_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_fp8out.hpp",
-                      "gg_dsrelu.hip"],
+                      "gg_dsrelu.hpp", "gg_dsrelu_inst.hip"],
     "wgrad_mx_kernel": ["gg_internal.hpp", "gg_tile.hpp", "gg_mx.hpp", "gg_wgrad_epi.hpp",
                         "gg_wgrad_mx.hip"],
 }

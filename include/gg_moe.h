@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define GG_ABI_VERSION 2
+#define GG_ABI_VERSION 3
 
 typedef enum {
     GG_OK = 0,
@@ -377,15 +377,19 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k,
  *            (a plain layout; the pages' MMA-interleaved scale layout is not
  *            used).
  * m_rows     as for gg_dglu.  k: a multiple of 128, at most 2^21.
- * b_fp8,sfb  dense weights (L, n, k) E4M3, element at b[g*n*k + nn*k + kk],
- *            and scales (L, n, k/32) at sfb[(g*n + nn)*(k/32) + kk/32];
+ * b_fp8,sfb  dense weights (L, n, k) FP8 (A's format), element at
+ *            b[g*n*k + nn*k + kk] (GG_MAJOR_K) or b[g*n*k + kk*n + nn]
+ *            (GG_MAJOR_N), and scales (L, n, k/32) at
+ *            sfb[(g*n + nn)*(k/32) + kk/32] for either major;
  * b_ptrs, sfb_ptrs  or: int64[L] device arrays of per-expert (n, k) codes
  *            and (n, k/32) scales with the same in-matrix layout (the page's
  *            discrete b_ptrs / sfb_ptrs).  Exactly one of the dense pair /
  *            the pointer pair is given.
+ * b_major    GG_MAJOR_K or GG_MAJOR_N ("Parameters / Input tensor B (dense
+ *            mode)": K-major or N-major), for dense and discrete B alike;
+ *            else GG_ERR_LAYOUT.
  * n          compact width, a multiple of 32, at most 2^20
  *            (GG_ERR_UNSUPPORTED beyond either limit).
- * b_fp8/b_ptrs codes share A's format.
  * c_dtype    as for gg_dglu, or GG_F8E4M3 / GG_F8E5M2 (the dGLU page's
  *            "Input tensor C" dtypes): an FP8 C is read as its exact value.
  * c, padded_offsets, L, alpha, beta, prob, d_row, dprob, dbias, geglu_alpha,
@@ -412,7 +416,7 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k,
  */
 gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
                      const void* b_fp8, const uint8_t* sfb,
-                     const int64_t* b_ptrs, const int64_t* sfb_ptrs, int32_t n,
+                     const int64_t* b_ptrs, const int64_t* sfb_ptrs, gg_major b_major, int32_t n,
                      const void* c, gg_dtype c_dtype,
                      const int32_t* padded_offsets, int32_t L,
                      const float* alpha, const float* beta, const float* prob,
@@ -445,11 +449,14 @@ size_t gg_dsrelu_workspace_size(int32_t L);
  *            layout is not used.)
  * m_rows     as for gg_dglu.  k: a multiple of 128, at most 2^21.
  * b_fp8,sfb  dense weights (L, n, k) FP8 (A's format), element at
- *            b[g*n*k + nn*k + kk], and scales (L, n, k/32) at
- *            sfb[(g*n + nn)*(k/32) + kk/32];
+ *            b[g*n*k + nn*k + kk] (GG_MAJOR_K) or b[g*n*k + kk*n + nn]
+ *            (GG_MAJOR_N), and scales (L, n, k/32) at
+ *            sfb[(g*n + nn)*(k/32) + kk/32] for either major;
  * b_ptrs, sfb_ptrs  or: int64[L] device arrays of per-expert (n, k) codes
  *            and (n, k/32) scales with the same in-matrix layout.
  *            Exactly one of the dense pair / the pointer pair is given.
+ * b_major    GG_MAJOR_K or GG_MAJOR_N (the page's "Layouts" allow an
+ *            N-major B for FP8 operands), else GG_ERR_LAYOUT.
  * n          a multiple of 32, at most 2^21 (GG_ERR_UNSUPPORTED beyond either
  *            limit).
  * c          (m_rows, n) row-major, c_dtype GG_BF16, GG_F16, GG_F32,
@@ -470,7 +477,7 @@ size_t gg_dsrelu_workspace_size(int32_t L);
  */
 gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
                     const void* b_fp8, const uint8_t* sfb,
-                    const int64_t* b_ptrs, const int64_t* sfb_ptrs, int32_t n,
+                    const int64_t* b_ptrs, const int64_t* sfb_ptrs, gg_major b_major, int32_t n,
                     const void* c, gg_dtype c_dtype,
                     const int32_t* padded_offsets, int32_t L,
                     const float* alpha, const float* prob,

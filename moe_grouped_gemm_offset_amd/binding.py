@@ -75,10 +75,10 @@ def load_library(path=LIB_PATH):
     L.gg_dglu.argtypes = [P, I64, I32, P, P, I32, I32, P, I32, P, I32, P, P, P, P, I32, P, P,
                           I32, F, F, F, F, U32, P, SZ, P]
     L.gg_dglu_mx.restype = ctypes.c_int
-    L.gg_dglu_mx.argtypes = [P, P, I64, I32, P, P, P, P, I32, P, I32, P, I32, P, P, P, P, I32, P,
+    L.gg_dglu_mx.argtypes = [P, P, I64, I32, P, P, P, P, I32, I32, P, I32, P, I32, P, P, P, P, I32, P,
                              P, P, P, I32, F, F, F, F, F, F, U32, P, SZ, P]
     L.gg_dsrelu.restype = ctypes.c_int
-    L.gg_dsrelu.argtypes = [P, P, I64, I32, P, P, P, P, I32, P, I32, P, I32, P, P, P, I32, P, P,
+    L.gg_dsrelu.argtypes = [P, P, I64, I32, P, P, P, P, I32, I32, P, I32, P, I32, P, P, P, I32, P, P,
                             P, U32, P, SZ, P]
     _lib = L
     return L
@@ -252,11 +252,12 @@ def gg_dglu(a, b_dense, b_ptrs, b_major, n, c, padded_offsets, alpha, beta, prob
 def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, beta, prob, d_row,
                dprob, dbias=None, amax=None, fp8_out=None, act=GG_DSWIGLU, geglu_alpha=1.702, clamp_min=-7.0,
                clamp_max=7.0, linear_offset=1.0, situ_beta1=4.0, situ_beta2=25.0, flags=0,
-               workspace=None, stream=None):
+               workspace=None, stream=None, b_major=GG_MAJOR_K):
     """Grouped MXFP8 dgrad + dSwiGLU/dGeGLU/dSiTU-GLU (gg_dglu_mx of
     gg_moe.h): a is an (m_rows, k) tensor of FP8 codes (uint8 or
-    float8_e4m3fn: E4M3; float8_e5m2: E5M2, as for gg_wgrad_mx).  c may be
-    float8_e4m3fn / float8_e5m2.  With a float8_e4m3fn / float8_e5m2 d_row
+    float8_e4m3fn: E4M3; float8_e5m2: E5M2, as for gg_wgrad_mx).  b / b_ptrs
+    hold (n, k) codes per expert with b_major GG_MAJOR_K, (k, n) ones with
+    GG_MAJOR_N.  c may be float8_e4m3fn / float8_e5m2.  With a float8_e4m3fn / float8_e5m2 d_row
     fp8_out is a dict of the other FP8 outputs (sfd_row, norm_const and
     optionally d_col, sfd_col).  Returns the workspace used."""
     q = _fp8_out(fp8_out)
@@ -264,7 +265,7 @@ def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, be
     nl = padded_offsets.numel()
     ws, nbytes = _workspace(workspace, L.gg_dglu_workspace_size(nl, n, dbias is not None), a, stream)
     _check(L.gg_dglu_mx(_ptr(a), _ptr(sfa), a.shape[0], a.shape[1], _ptr(b), _ptr(sfb),
-                        _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
+                        _ptr(b_ptrs), _ptr(sfb_ptrs), b_major, n, _ptr(c), _TORCH_DTYPE[c.dtype],
                         _ptr(padded_offsets), nl, _ptr(alpha), _ptr(beta), _ptr(prob),
                         _ptr(d_row), _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(dbias),
                         _ptr(amax), _ref(q), act, geglu_alpha, clamp_min, clamp_max, linear_offset,
@@ -273,7 +274,7 @@ def gg_dglu_mx(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, be
 
 
 def gg_dsrelu(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, prob, d_row, dprob,
-              amax=None, fp8_out=None, flags=0, workspace=None, stream=None):
+              amax=None, fp8_out=None, flags=0, workspace=None, stream=None, b_major=GG_MAJOR_K):
     """Grouped MXFP8 dgrad + dsReLU (gg_dsrelu of gg_moe.h); operand, C and
     D dtypes and fp8_out as for gg_dglu_mx.  Returns the workspace used."""
     q = _fp8_out(fp8_out)
@@ -281,7 +282,7 @@ def gg_dsrelu(a, sfa, b, sfb, b_ptrs, sfb_ptrs, n, c, padded_offsets, alpha, pro
     nl = padded_offsets.numel()
     ws, nbytes = _workspace(workspace, L.gg_dsrelu_workspace_size(nl), a, stream)
     _check(L.gg_dsrelu(_ptr(a), _ptr(sfa), a.shape[0], a.shape[1], _ptr(b), _ptr(sfb),
-                       _ptr(b_ptrs), _ptr(sfb_ptrs), n, _ptr(c), _TORCH_DTYPE[c.dtype],
+                       _ptr(b_ptrs), _ptr(sfb_ptrs), b_major, n, _ptr(c), _TORCH_DTYPE[c.dtype],
                        _ptr(padded_offsets), nl, _ptr(alpha), _ptr(prob), _ptr(d_row),
                        _TORCH_DTYPE[d_row.dtype], _ptr(dprob), _ptr(amax), _ref(q), _ab(a, flags), _ptr(ws),
                        nbytes, _stream(stream)))

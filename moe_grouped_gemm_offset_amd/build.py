@@ -14,9 +14,15 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgg_moe.so")
-SOURCES = ["gg_api.cpp", "gg_prologue.hip", "gg_wgrad.hip", "gg_wgrad_mx.hip", "gg_dglu.hip",
-           "gg_dglu_mx.hip", "gg_dglu_mx_dswiglu.hip", "gg_dglu_mx_dgeglu.hip",
-           "gg_dglu_mx_dsituglu.hip", "gg_dsrelu.hip"]
+# (source, object name, defines): the instantiation sources are compiled
+# once per kernel family member (activation, B major), in parallel
+SOURCES = [(f, os.path.splitext(f)[0], []) for f in
+           ("gg_api.cpp", "gg_prologue.hip", "gg_wgrad.hip", "gg_wgrad_mx.hip", "gg_dglu.hip",
+            "gg_dglu_mx.hip", "gg_dsrelu.hip")]
+SOURCES += [("gg_dglu_mx_inst.hip", f"gg_dglu_mx_a{act}{'k' if bk else 'n'}",
+             [f"-DGG_ACT={act}", f"-DGG_BK={bk}"]) for act in range(3) for bk in (1, 0)]
+SOURCES += [("gg_dsrelu_inst.hip", f"gg_dsrelu_{'k' if bk else 'n'}", [f"-DGG_BK={bk}"])
+            for bk in (1, 0)]
 ARCH = os.environ.get("GG_OFFLOAD_ARCH", "gfx950")
 
 
@@ -48,9 +54,10 @@ def flags():
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(entry):
+    src, name, defines = entry
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [hipcc(), *flags(), *defines, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

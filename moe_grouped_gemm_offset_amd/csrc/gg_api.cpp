@@ -560,7 +560,8 @@ gg_status gg_dglu(const void* a, int64_t m_rows, int32_t k, const void* b_dense,
 
 gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
                      const void* b_fp8, const uint8_t* sfb, const int64_t* b_ptrs,
-                     const int64_t* sfb_ptrs, int32_t n, const void* c, gg_dtype c_dtype,
+                     const int64_t* sfb_ptrs, gg_major b_major, int32_t n, const void* c,
+                     gg_dtype c_dtype,
                      const int32_t* padded_offsets, int32_t L, const float* alpha,
                      const float* beta, const float* prob, void* d_row, gg_dtype d_dtype,
                      float* dprob, void* dbias, float* amax, const gg_fp8_out* fp8_out, gg_act act,
@@ -577,6 +578,8 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
     const bool discrete = b_ptrs || sfb_ptrs;
     if (dense == discrete || (dense && (!b_fp8 || !sfb)) || (discrete && (!b_ptrs || !sfb_ptrs)))
         return fail(GG_ERR_MODE, "give exactly one of (b_fp8, sfb) and (b_ptrs, sfb_ptrs)");
+    if (b_major != GG_MAJOR_K && b_major != GG_MAJOR_N)
+        return fail(GG_ERR_LAYOUT, "b_major must be GG_MAJOR_K or GG_MAJOR_N");
     st = check_dglu_common(c_dtype, d_dtype, act, true, alpha, beta, dbias, flags, "gg_dglu_mx");
     if (st != GG_OK)
         return st;
@@ -609,7 +612,7 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
     p.m_rows = m_rows;
     p.K = k;
     p.N = n;
-    p.b_kmajor = 1;
+    p.b_kmajor = b_major == GG_MAJOR_K;
     p.ab_e5m2 = (flags & GG_FLAG_AB_E5M2) != 0;
     return run_dglu(p, true, c, c_dtype, padded_offsets, L, alpha, beta, prob, d_row, d_dtype,
                     dprob, dbias, amax, act, geglu_alpha, clamp_min, clamp_max, linear_offset,
@@ -619,7 +622,8 @@ gg_status gg_dglu_mx(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int3
 
 gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32_t k,
                     const void* b_fp8, const uint8_t* sfb, const int64_t* b_ptrs,
-                    const int64_t* sfb_ptrs, int32_t n, const void* c, gg_dtype c_dtype,
+                    const int64_t* sfb_ptrs, gg_major b_major, int32_t n, const void* c,
+                    gg_dtype c_dtype,
                     const int32_t* padded_offsets, int32_t L, const float* alpha,
                     const float* prob, void* d_row, gg_dtype d_dtype, float* dprob, float* amax,
                     const gg_fp8_out* fp8_out, uint32_t flags, void* workspace,
@@ -633,6 +637,8 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
     const bool discrete = b_ptrs || sfb_ptrs;
     if (dense == discrete || (dense && (!b_fp8 || !sfb)) || (discrete && (!b_ptrs || !sfb_ptrs)))
         return fail(GG_ERR_MODE, "give exactly one of (b_fp8, sfb) and (b_ptrs, sfb_ptrs)");
+    if (b_major != GG_MAJOR_K && b_major != GG_MAJOR_N)
+        return fail(GG_ERR_LAYOUT, "b_major must be GG_MAJOR_K or GG_MAJOR_N");
     if (!(is_out_dtype(c_dtype) || is_fp8(c_dtype)) || !(is_out_dtype(d_dtype) || is_fp8(d_dtype)))
         return fail(GG_ERR_DTYPE, "c_dtype and d_dtype must be GG_BF16, GG_F16, GG_F32, GG_F8E4M3 or "
                                   "GG_F8E5M2");
@@ -693,6 +699,7 @@ gg_status gg_dsrelu(const void* a_fp8, const uint8_t* sfa, int64_t m_rows, int32
     p.K = k;
     p.N = n;
     p.L = L;
+    p.b_kmajor = b_major == GG_MAJOR_K;
     p.c_dtype = (int)c_dtype;
     p.d_dtype = (int)d_dtype;
     p.ab_e5m2 = (flags & GG_FLAG_AB_E5M2) != 0;

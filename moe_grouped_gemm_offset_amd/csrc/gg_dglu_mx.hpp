@@ -1,8 +1,7 @@
 // gg_dglu_mx.hpp -- M-grouped block-scaled (MXFP8) dgrad fused with the
 // dSwiGLU / dGeGLU / dSiTU-GLU backward on gfx950: the kernel template and
-// its per-activation launcher, instantiated once per activation in
-// gg_dglu_mx_dswiglu.hip, gg_dglu_mx_dgeglu.hip and gg_dglu_mx_dsituglu.hip
-// (separate translation units, compiled in parallel).
+// its launcher per activation and B major, instantiated by
+// gg_dglu_mx_inst.hip (one object per pair, compiled in parallel).
 //
 // For the rows of group g ("Grouped GEMM + dGLU (SM100)", "Block-scaled
 // contract / Equations"):
@@ -14,7 +13,9 @@
 // yields D, dprob and the optional dbias, and by the per-expert amax of the
 // input-gradient and gate-gradient halves of D ("Shapes": (L, 2, 1)).  Each
 // expert's codes and scales may sit at their own addresses (pointer arrays),
-// as well as in one dense (L, N, K) tensor.  C may be fp32, bf16, fp16 or
+// as well as in one dense (L, N, K) tensor; the codes K-major or N-major
+// ("Parameters / Input tensor B (dense mode)": (N, K) per expert with N
+// contiguous), the scales (N, K/32) either way.  C may be fp32, bf16, fp16 or
 // FP8 codes ("Parameters / Input tensor C"); D is 16/32-bit or FP8 with E8M0
 // block scales (step 3).
 //
@@ -33,8 +34,9 @@ using DgluMxCfg = Cfg<256, 256, 2, 2>;
 // CW: bytes per C element (4 fp32, 2 bf16 / fp16, 1 FP8); ACT: 0 dSwiGLU,
 // 1 dGeGLU, 2 dSiTU-GLU; QF: D 16/32-bit (0) or FP8 E4M3 (1) / E5M2 (2)
 // D_row / D_col with E8M0 scales; BF: C bf16 and, unless QF, D bf16; AB:
-// the operands' FP8 format (0 E4M3, 1 E5M2).
-template <class C, int CW, int ACT, int QF, bool BF, int AB>
+// the operands' FP8 format (0 E4M3, 1 E5M2); BK: B's codes K-major (else
+// N-major).
+template <class C, int CW, int ACT, int QF, bool BF, int AB, bool BK>
 __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
     __shared__ __attribute__((aligned(1024))) char smem[ScaleLds<C>::kSmem];
@@ -71,11 +73,15 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
     const int64_t K = p.K, KB = p.K / 32;        // scale bytes per row
     const char* a = (const char*)p.a + m0 * K;
     const char* sfa = (const char*)p.sfa + m0 * KB;
-    const char* bg = p.b_dense ? (const char*)p.b_dense + ((int64_t)g * p.N + n0) * K
-                               : (const char*)p.b_ptrs[g] + (int64_t)n0 * K;
+    // B's tile: row n0 of the expert's (N, K) codes, or column n0 of its
+    // (K, N) ones
+    const int64_t bt = BK ? (int64_t)n0 * K : n0;
+    const char* bg = p.b_dense ? (const char*)p.b_dense + (int64_t)g * p.N * K + bt
+                               : (const char*)p.b_ptrs[g] + bt;
     const char* sfb = p.sfb_dense ? (const char*)p.sfb_dense + ((int64_t)g * p.N + n0) * KB
                                   : (const char*)p.sfb_ptrs[g] + (int64_t)n0 * KB;
-    mx_mainloop<C, AB>(smem, a, sfa, bg, sfb, K, K, rows_valid, cols_valid, am0, bn0, acc);
+    mx_mainloop<C, AB, BK>(smem, a, sfa, bg, sfb, K, K, rows_valid, cols_valid, am0, bn0, acc,
+                           p.N);
 
     // C of the items 10 ahead (6 for fp32 C; 8 and 4 with FP8 output) in
     // flight in the epilogue (more spilled registers in the dSwiGLU and
@@ -89,7 +95,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dglu_mx_kernel(DgluArgs p) {
 // operands with FP8 D (the pages pair FP8 operands with FP8 outputs; the
 // host rejects the rest); C fp32, bf16 (compile-time with a bf16 D or an
 // FP8 one), fp16 / bf16 (run time) or FP8.
-template <int ACT>
+template <int ACT, bool BK>
 hipError_t launch_dglu_mx_act(const DgluArgs& p, hipStream_t s) {
     using C = DgluMxCfg;
     const int64_t tiles = ((p.m_rows + C::TM - 1) / C::TM) * ((p.N + C::TN - 1) / C::TN);
@@ -101,7 +107,7 @@ hipError_t launch_dglu_mx_act(const DgluArgs& p, hipStream_t s) {
         constexpr int cwc = decltype(CWc)::value, qfc = decltype(QFc)::value;
         constexpr bool bfc = decltype(BFc)::value;
         constexpr int abc = decltype(ABc)::value;
-        hipLaunchKernelGGL((dglu_mx_kernel<C, cwc, ACT, qfc, bfc, abc>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((dglu_mx_kernel<C, cwc, ACT, qfc, bfc, abc, BK>), grid, block, 0, s, p);
     };
     auto by_c = [&](auto QFc, auto ABc) {
         using I4 = std::integral_constant<int, 4>;
@@ -138,8 +144,11 @@ hipError_t launch_dglu_mx_act(const DgluArgs& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-extern template hipError_t launch_dglu_mx_act<0>(const DgluArgs&, hipStream_t);
-extern template hipError_t launch_dglu_mx_act<1>(const DgluArgs&, hipStream_t);
-extern template hipError_t launch_dglu_mx_act<2>(const DgluArgs&, hipStream_t);
+extern template hipError_t launch_dglu_mx_act<0, true>(const DgluArgs&, hipStream_t);
+extern template hipError_t launch_dglu_mx_act<1, true>(const DgluArgs&, hipStream_t);
+extern template hipError_t launch_dglu_mx_act<2, true>(const DgluArgs&, hipStream_t);
+extern template hipError_t launch_dglu_mx_act<0, false>(const DgluArgs&, hipStream_t);
+extern template hipError_t launch_dglu_mx_act<1, false>(const DgluArgs&, hipStream_t);
+extern template hipError_t launch_dglu_mx_act<2, false>(const DgluArgs&, hipStream_t);
 
 }  // namespace gg

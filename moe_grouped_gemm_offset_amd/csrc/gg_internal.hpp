@@ -123,6 +123,7 @@ struct DsreluArgs {
     int32_t* ws;
     int64_t m_rows;
     int K, N, L;
+    int b_kmajor;             // B's codes (N, K) per expert (else (K, N))
     int c_dtype, d_dtype;
     int ab_e5m2;              // codes E5M2 (else E4M3)
     Fp8Out q;                 // with an FP8 d_dtype

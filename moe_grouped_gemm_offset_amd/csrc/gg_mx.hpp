@@ -1,9 +1,9 @@
 // gg_mx.hpp -- the block-scaled (MXFP8) main loop of the M-grouped dgrad
-// kernels on gfx950: A (M, K) and the expert's B (N, K), both K-major E4M3
-// codes with one E8M0 scale byte per 32 consecutive K values of a row
-// (row-major (rows, K/32) scale arrays), contracted by
-// v_mfma_scale_f32_32x32x64_f8f6f4 with 64 values of K per stage and 128 per
-// load unit.
+// kernels on gfx950: A (M, K) K-major and the expert's B (N, K), K-major or
+// N-major, FP8 codes with one E8M0 scale byte per 32 consecutive K values of
+// a row (row-major (rows, K/32) scale arrays whatever the codes' major),
+// contracted by v_mfma_scale_f32_32x32x64_f8f6f4 with 64 values of K per
+// stage and 128 per load unit.
 //
 // The scales of 8 stages at a time (16 bytes of each of the tile's operand
 // rows) are staged in LDS by dword LDS-writing loads, four row-contiguous
@@ -47,12 +47,15 @@ struct ScaleLds {
 // `sfa`) and whose B rows start at `b` (scales `sfb`).  Rows are `ld` bytes
 // apart (codes) and ld / 32 bytes apart (scales); K and ld are multiples of
 // 128 (whole load units, 4-byte scale words), and rows at or past rows_valid
-// / cols_valid contribute zero.  smem holds ScaleLds<C>::kSmem bytes.
-template <class C, int AB = 0>
+// / cols_valid contribute zero.  With !B_K, B's codes are N-major instead:
+// `b` is the tile's first column at K = 0, K rows ldb bytes apart (its
+// scales are as for B_K), and cols_valid is a multiple of 16.  smem holds
+// ScaleLds<C>::kSmem bytes.
+template <class C, int AB = 0, bool B_K = true>
 __device__ __forceinline__ void mx_mainloop(char* smem, const char* a, const char* sfa,
                                             const char* b, const char* sfb, int64_t ld, int64_t K,
                                             int rows_valid, int cols_valid, int am0, int bn0,
-                                            f32x16 (&acc)[C::MB][C::NB]) {
+                                            f32x16 (&acc)[C::MB][C::NB], int64_t ldb = 0) {
     constexpr int TM = C::TM, TN = C::TN, MB = C::MB, NB = C::NB;
     using S = ScaleLds<C>;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -86,17 +89,21 @@ __device__ __forceinline__ void mx_mainloop(char* smem, const char* a, const cha
         const uint32_t lds = sbuf32 + (grp & 1) * S::kBuf + (is_a ? 0 : TM * 16) + slot0 * 16;
         dma4(is_a ? rsa : rsb, lds, sc_off + (uint32_t)((kSliceSlots * half + 16 * t) * KB + 16 * grp));
     };
+    using LB = std::conditional_t<B_K, LoadK<C, TN>, LoadMN8<C>>;
     LoadK<C, TM> la;
-    LoadK<C, TN> lb;
+    LB lb;
     la.init(ld, rows_valid);
-    lb.init(ld, cols_valid);
-    constexpr int kLA = LoadK<C, TM>::kN, kLB = LoadK<C, TN>::kN;
+    lb.init(B_K ? ld : ldb, cols_valid);
+    constexpr int kLA = LoadK<C, TM>::kN, kLB = LB::kN;
     auto issue = [&](uint32_t st, int u, int i) {
         const int64_t kb = (int64_t)u * 128;
         if (i < kLA) {
             la.template issue<false>(st, a + kb, K - kb, i);
         } else if (i < kLA + kLB) {
-            lb.template issue<false>(st + TM * kRowBytes, b + kb, K - kb, i - kLA);
+            if constexpr (B_K)
+                lb.template issue<false>(st + TM * kRowBytes, b + kb, K - kb, i - kLA);
+            else
+                lb.issue(st + TM * kRowBytes, b + kb * ldb, K - kb, i - kLA);
         } else {
             // units 1 .. 4 carry group 1, 5 .. 8 group 2, ...; unit 0
             // carries a slice of group 0 again (identical words)
@@ -106,7 +113,7 @@ __device__ __forceinline__ void mx_mainloop(char* smem, const char* a, const cha
     };
     const int lsh = 8 * lq;
     auto read = [&](const char* st, int kt, FragMx8<C>& f, int g) {
-        read_mx8<C>(st, st + TM * kRowBytes, am0, bn0, kt & 1, f, g);
+        read_mx8<C, B_K>(st, st + TM * kRowBytes, am0, bn0, kt & 1, f, g);
         // this stage's scale word of the group's row, shifted so byte 0 is
         // this lane's K block
         const char* buf = sbuf + ((kt / 8) & 1) * S::kBuf + 4 * ((kt % 8) >> 1);

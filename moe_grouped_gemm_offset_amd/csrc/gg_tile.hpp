@@ -37,8 +37,15 @@
 //    12+q; when lane 4e + q addresses K row kb + e at columns c + 4q, lane i
 //    gets column c + i at K rows kb..kb+3 -- the K-contiguous register
 //    fragment the MFMA needs.
-// Both layouts read without bank conflicts (64 banks of 4 bytes; a 16-byte
-// read is served 16 lanes at a time).
+//  * N-contiguous 8-bit operand ("MN8 layout", 256 columns, 128 K rows):
+//    K row k holds the 256 columns as 16 chunks of 16 bytes; chunk u sits at
+//    position u ^ (2 (k & 7)).  Stage h is K rows 64h .. 64h+63.  Fragments
+//    are read with ds_read_b64_tr_b8: within a 16-lane group, lane 8q + j
+//    receives, as byte m, byte j of the 8-byte piece addressed by lane
+//    2m + q; when lane 2e + q addresses K row kb + e at columns c + 8q, lane
+//    i gets column c + i at K rows kb..kb+7.
+// All layouts read without bank conflicts (64 banks of 4 bytes; a 16-byte
+// read is served 16 lanes at a time, an 8-byte one 32).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -241,6 +248,37 @@ struct LoadMN {
     }
 };
 
+// MN8 layout (8-bit codes, 256 columns, 128 K rows), K rows `ld` bytes
+// apart; columns at or past cols_valid (a multiple of 16) load zeros.
+// issue() loads the K rows starting at `tile` (the unit's first K row at the
+// tile's first column) with krows valid K rows left from there.
+template <class C>
+struct LoadMN8 {
+    static constexpr int kN = 32 / C::kWaves;            // 1 KiB loads (4 K rows) per wave
+    static_assert(kN * C::kWaves == 32 && C::TN == 256, "K rows must split evenly over waves");
+    uint32_t off[kN];
+    uint32_t ld;
+    __device__ __forceinline__ void init(int64_t ld_, int cols_valid) {
+        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+        ld = (uint32_t)ld_;
+#pragma unroll
+        for (int i = 0; i < kN; i++) {
+            const int k = 4 * (w * kN + i) + (l >> 4);
+            const int u = (l & 15) ^ (2 * (k & 7));
+            off[i] = u * 16 < cols_valid ? (uint32_t)(k * ld_) + u * 16 : kInvalid;
+        }
+    }
+    // A lane at K row k < krows and a valid column has k ld + 16 u + 16 <=
+    // k ld + cols_valid <= krows ld, so the record count krows ld masks
+    // exactly the K rows past the end.
+    __device__ __forceinline__ void issue(uint32_t lds, const char* tile, int64_t krows, int i) const {
+        const int w = uniform(threadIdx.x >> 6);
+        const uint32_t kr = (uint32_t)(krows < 128 ? (krows < 0 ? 0 : krows) : 128);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(tile), (uint32_t)uniform((int)(kr * ld)));
+        dma16(rs, lds + (w * kN + i) * 1024, off[i]);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Fragment readers (bf16, v_mfma_f32_32x32x16_bf16: lane l supplies row / col
 // l % 32 with K values 8 (l / 32) .. 8 (l / 32) + 7 of a 16-value sub-step;
@@ -332,8 +370,30 @@ struct FragMx8 {
     uint32_t sa[C::MB], sb[C::NB];
 };
 
-// Fragment group g of stage h: A row block g (g < MB) or B row block g - MB.
-template <class C>
+__device__ __forceinline__ int mn8_addr(int k, int col) {
+    return k * 256 + (((col >> 4) ^ (2 * (k & 7))) << 4) + (col & 15);
+}
+
+// Columns col0 .. col0+31 of stage K rows k0 .. k0+63 (MN8 layout) as MX
+// fragments: lane l (column col0 + l % 32, q = l / 32) gets K rows
+// k0 + 16q .. +15 and k0 + 32 + 16q .. +15, eight per transposing read.
+__device__ __forceinline__ i32x8 frag_mn8(const char* lds, int col0, int k0) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    const int l = threadIdx.x & 63;
+    const int grp = l >> 4, s = l & 15;
+    const int col = col0 + 16 * (grp & 1) + 8 * (s & 1);
+    const int kq = k0 + 16 * (grp >> 1) + (s >> 1);
+    i32x2 v[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+        v[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)GG_LDS(
+            lds + mn8_addr(kq + 32 * (r >> 1) + 8 * (r & 1), col)));
+    return i32x8{v[0].x, v[0].y, v[1].x, v[1].y, v[2].x, v[2].y, v[3].x, v[3].y};
+}
+
+// Fragment group g of stage h: A row block g (g < MB) or B row block g - MB
+// (K layout; with !B_K the MN8 layout).
+template <class C, bool B_K = true>
 __device__ __forceinline__ void read_mx8(const char* sa, const char* sb, int a0, int b0, int h,
                                          FragMx8<C>& f, int g) {
     const int l = threadIdx.x & 63;
@@ -346,8 +406,10 @@ __device__ __forceinline__ void read_mx8(const char* sa, const char* sb, int a0,
     };
     if (g < C::MB)
         f.a[g] = frag(sa, a0 + 32 * g + lr);
-    else
+    else if constexpr (B_K)
         f.b[g - C::MB] = frag(sb, b0 + 32 * (g - C::MB) + lr);
+    else
+        f.b[g - C::MB] = frag_mn8(sb, b0 + 32 * (g - C::MB), 64 * h);
 }
 
 // MFMAs m0 .. m1-1 of a stage, m = i NB + j.

@@ -32,7 +32,7 @@ def test_loads_and_exports_every_declared_symbol():
     assert set(names) == set(B.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert B.gg_abi_version() == 2
+    assert B.gg_abi_version() == 3
 
 
 def test_workspace_sizes():
@@ -149,12 +149,13 @@ def test_dglu_rejects(kw, status):
 
 
 def dsrelu(**kw):
-    args = dict(a=P, sfa=P, M=1024, k=512, b=P, sfb=P, bp=None, sp=None, n=256, c=P, cdt=0, po=P,
-                L=4, alpha=P, prob=P, d=P, ddt=0, dprob=P, amax=P, fp8=None, flags=0, ws=WS, wsb=256)
+    args = dict(a=P, sfa=P, M=1024, k=512, b=P, sfb=P, bp=None, sp=None, bm=0, n=256, c=P, cdt=0,
+                po=P, L=4, alpha=P, prob=P, d=P, ddt=0, dprob=P, amax=P, fp8=None, flags=0, ws=WS,
+                wsb=256)
     args.update(kw)
     lib = B.load_library()
     return lib.gg_dsrelu(args["a"], args["sfa"], args["M"], args["k"], args["b"], args["sfb"],
-                         args["bp"], args["sp"], args["n"], args["c"], args["cdt"], args["po"],
+                         args["bp"], args["sp"], args["bm"], args["n"], args["c"], args["cdt"], args["po"],
                          args["L"], args["alpha"], args["prob"], args["d"], args["ddt"], args["dprob"],
                          args["amax"], args["fp8"], args["flags"], args["ws"], args["wsb"], None)
 
@@ -166,6 +167,8 @@ def dsrelu(**kw):
     (dict(sfb=None), MODE),
     (dict(k=192), UNSUPPORTED),
     (dict(n=40), SHAPE),
+    (dict(bm=1), LAYOUT),
+    (dict(bm=3), LAYOUT),
     (dict(ddt=5), DTYPE),
     (dict(cdt=5), DTYPE),
     (dict(ddt=4), NULL),               # FP8 D without fp8_out
@@ -225,13 +228,13 @@ def test_fp8_out_checks(entry, kw, status):
 
 
 def dglu_mx(**kw):
-    args = dict(a=P, sfa=P, M=1024, k=512, b=P, sfb=P, bp=None, sp=None, n=256, c=P, cdt=0, po=P,
-                L=4, alpha=P, beta=P, prob=P, d=P, ddt=0, dprob=P, dbias=None, amax=P, fp8=None, act=0,
-                flags=0, ws=WS, wsb=1 << 20, b1=4.0, b2=25.0)
+    args = dict(a=P, sfa=P, M=1024, k=512, b=P, sfb=P, bp=None, sp=None, bm=0, n=256, c=P, cdt=0,
+                po=P, L=4, alpha=P, beta=P, prob=P, d=P, ddt=0, dprob=P, dbias=None, amax=P, fp8=None,
+                act=0, flags=0, ws=WS, wsb=1 << 20, b1=4.0, b2=25.0)
     args.update(kw)
     lib = B.load_library()
     return lib.gg_dglu_mx(args["a"], args["sfa"], args["M"], args["k"], args["b"], args["sfb"],
-                          args["bp"], args["sp"], args["n"], args["c"], args["cdt"], args["po"],
+                          args["bp"], args["sp"], args["bm"], args["n"], args["c"], args["cdt"], args["po"],
                           args["L"], args["alpha"], args["beta"], args["prob"], args["d"],
                           args["ddt"], args["dprob"], args["dbias"], args["amax"], args["fp8"], args["act"],
                           1.702, -7.0, 7.0, 1.0, args["b1"], args["b2"], args["flags"], args["ws"],
@@ -246,6 +249,7 @@ def dglu_mx(**kw):
     (dict(b=None, sfb=None, bp=P), MODE),
     (dict(act=3), MODE),
     (dict(flags=8), MODE),
+    (dict(bm=1), LAYOUT),
     (dict(act=2, b1=0.0), VALUE),
     (dict(act=2, b2=-1.0), VALUE),
     (dict(act=2, b1=float("inf")), VALUE),
@@ -273,6 +277,10 @@ def test_valid_call_without_a_gpu_reports_device():
     assert dglu_mx() == DEVICE
     assert dglu_mx(act=2) == DEVICE
     assert dglu_mx(act=0, b1=0.0) == DEVICE, "the dSiTU scales are ignored for other activations"
+    assert dsrelu(bm=2) == DEVICE, "N-major B"
+    assert dsrelu(bm=2, b=None, sfb=None, bp=P, sp=P) == DEVICE
+    assert dglu_mx(bm=2) == DEVICE
+    assert dglu_mx(bm=2, b=None, sfb=None, bp=P, sp=P, act=2) == DEVICE
 
 
 def wgrad_mx(**kw):

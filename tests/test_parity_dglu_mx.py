@@ -35,17 +35,22 @@ def column_maps(N, gate_first=False):
 
 
 def run_gpu(inp, d_dtype=torch.bfloat16, with_amax=True, dbias=False, act=orc.DSWIGLU, flags=0,
-            situ=(4.0, 25.0)):
+            situ=(4.0, 25.0), b_major="k"):
+    """b_major "n" hands the kernel B's codes N-major ((N, K) per expert
+    transposed to (K, N), the same values; the oracle reads the K-major
+    ones); the scales keep their (N, K/32) layout."""
     b = gg()
     dev = lambda x: x.cuda()
+    nmaj = b_major == "n"
+    lay = (lambda x: x.transpose(-1, -2).contiguous()) if nmaj else (lambda x: x)
     M, N, L = inp["M"], inp["N"], inp["L"]
     a = dev(inp["a"]).view(torch.uint8)
     keep = []
     if inp["b_dense"] is not None:
-        bd, sd = dev(inp["b_dense"]).view(torch.uint8), dev(inp["sfb_dense"])
+        bd, sd = lay(dev(inp["b_dense"]).view(torch.uint8)), dev(inp["sfb_dense"])
         bp = sp = None
     else:
-        kb = [dev(x).view(torch.uint8) for x in inp["b_list"]]
+        kb = [lay(dev(x).view(torch.uint8)) for x in inp["b_list"]]
         ks = [dev(x) for x in inp["sfb_list"]]
         keep += kb + ks
         bp = torch.tensor([x.data_ptr() for x in kb], dtype=torch.int64, device="cuda")
@@ -58,7 +63,8 @@ def run_gpu(inp, d_dtype=torch.bfloat16, with_amax=True, dbias=False, act=orc.DS
     ws = b.gg_dglu_mx(a, dev(inp["sfa"]), bd, sd, bp, sp, N, dev(inp["c"]),
                       dev(inp["padded_offsets"]), dev(inp["alpha"]), dev(inp["beta"]),
                       dev(inp["prob"]), d, dprob, dbias=db, amax=amax, act=act, flags=flags,
-                      situ_beta1=situ[0], situ_beta2=situ[1])
+                      situ_beta1=situ[0], situ_beta2=situ[1],
+                      b_major=b.GG_MAJOR_N if nmaj else b.GG_MAJOR_K)
     torch.cuda.synchronize()
     err = b.gg_device_error(ws)
     return dict(d=d.cpu(), dprob=dprob.cpu(), amax=(amax.cpu() if with_amax else None),
@@ -132,6 +138,20 @@ def test_dbias():
     check(inp, got, ref)
     assert_close(values(got["dbias"]), ref["dbias"], orc.BF16, "dbias")
     assert torch.all(got["dbias"][2] == 0), "an empty expert's dbias stays 0"
+
+
+@pytest.mark.parametrize("act", [orc.DSWIGLU, orc.DGEGLU, orc.DSITUGLU])
+@pytest.mark.parametrize("discrete", [False, True])
+def test_n_major(discrete, act):
+    """N-major B ("Parameters / Input tensor B (dense mode)": K-major or
+    N-major), dense and discrete, all three activations, with dbias."""
+    inp = small(86, discrete, c_std=4.0 if act == orc.DGEGLU else 2.0)
+    say("dglu_mx N-major", "discrete" if discrete else "dense", act)
+    got = run_gpu(inp, act=act, dbias=True, b_major="n")
+    ref = run_oracle(inp, act=act, dbias=True)
+    check(inp, got, ref)
+    assert_close(values(got["dbias"]), ref["dbias"], orc.BF16, "dbias")
+    assert_close(got["amax"].numpy().ravel(), ref["amax"].ravel(), orc.F32, "amax")
 
 
 @pytest.mark.parametrize("c_dtype", [torch.float8_e4m3fn, torch.float8_e5m2])

@@ -23,16 +23,21 @@ def gg():
     return binding
 
 
-def run_gpu(inp, d_dtype=torch.bfloat16, with_amax=True):
+def run_gpu(inp, d_dtype=torch.bfloat16, with_amax=True, b_major="k"):
+    """b_major "n" hands the kernel B's codes N-major: each expert's (N, K)
+    codes transposed to (K, N), the same values (the oracle reads the K-major
+    ones); the scales keep their (N, K/32) layout."""
     b = gg()
     dev = lambda x: x.cuda()
+    nmaj = b_major == "n"
+    lay = (lambda x: x.transpose(-1, -2).contiguous()) if nmaj else (lambda x: x)
     M, N, L = inp["M"], inp["N"], inp["L"]
     a = dev(inp["a"]).view(torch.uint8)
     if inp["b_dense"] is not None:
-        bd, sd = dev(inp["b_dense"]).view(torch.uint8), dev(inp["sfb_dense"])
+        bd, sd = lay(dev(inp["b_dense"]).view(torch.uint8)), dev(inp["sfb_dense"])
         bp = sp = None
     else:
-        kb = [dev(x).view(torch.uint8) for x in inp["b_list"]]
+        kb = [lay(dev(x).view(torch.uint8)) for x in inp["b_list"]]
         ks = [dev(x) for x in inp["sfb_list"]]
         bp = torch.tensor([x.data_ptr() for x in kb], dtype=torch.int64, device="cuda")
         sp = torch.tensor([x.data_ptr() for x in ks], dtype=torch.int64, device="cuda")
@@ -41,7 +46,8 @@ def run_gpu(inp, d_dtype=torch.bfloat16, with_amax=True):
     dprob = torch.zeros(M, dtype=torch.float32, device="cuda")
     amax = torch.full((L,), -1.0, dtype=torch.float32, device="cuda") if with_amax else None
     ws = b.gg_dsrelu(a, dev(inp["sfa"]), bd, sd, bp, sp, N, dev(inp["c"]), dev(inp["padded_offsets"]),
-                     dev(inp["alpha"]), dev(inp["prob"]), d, dprob, amax)
+                     dev(inp["alpha"]), dev(inp["prob"]), d, dprob, amax,
+                     b_major=b.GG_MAJOR_N if nmaj else b.GG_MAJOR_K)
     torch.cuda.synchronize()
     err = b.gg_device_error(ws)
     if not inp["b_dense"] is None:
@@ -123,17 +129,20 @@ def test_unit_scales_no_amax():
     assert_close(values(d[:vm]), ref["D"][:vm], orc.BF16, "D_row")
 
 
-def test_workload_sampled():
-    """The dsReLU workload at full size (L 16, K 7168, N 2048, M 65536): the
-    first and last rows of every group and every row of a smallest group
-    (2816 rows) against the oracle; that group's Amax equals the oracle's,
-    and every other group's Amax is at least the oracle's |D| on its listed
-    rows."""
+@pytest.mark.parametrize("b_major", ["k", "n"])
+def test_workload_sampled(b_major):
+    """The dsReLU workload at full size (L 16, K 7168, N 2048, M 65536), with
+    dense K-major B (the bench's launch) and with discrete N-major B (the
+    page's FP8 discrete b_major "n"): the first and last rows of every group
+    and every row of a smallest group (2816 rows) against the oracle; that
+    group's Amax equals the oracle's, and every other group's Amax is at
+    least the oracle's |D| on its listed rows."""
     w = synth.WORKLOADS["dsrelu_mxfp8"]
     counts = synth.workload_counts("dsrelu_mxfp8")
-    inp = synth.dsrelu_inputs(w["L"], w["K"], w["N"], counts, seed=w["seed"], device="cuda")
-    say("dsrelu_mxfp8 counts", counts.tolist())
-    d, dprob, amax, err = run_gpu(inp)
+    inp = synth.dsrelu_inputs(w["L"], w["K"], w["N"], counts, seed=w["seed"], device="cuda",
+                              discrete=b_major == "n")
+    say("dsrelu_mxfp8 counts", counts.tolist(), "B", b_major)
+    d, dprob, amax, err = run_gpu(inp, b_major=b_major)
     assert err == 0
     cpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     cpu["b_list"] = [x.cpu() for x in inp["b_list"]]
@@ -187,5 +196,36 @@ def test_random_shapes(case):
     for g, c in enumerate(counts):
         if c == 0:
             assert amax[g] == 0.0, "an empty expert's amax is 0"
+        else:
+            assert abs(amax[g].item() - ref["amax"][g]) <= 1e-3 * ref["amax"][g]
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_n_major(case):
+    """N-major B (the page's FP8 b_major "n"), dense and discrete, partial N
+    tiles (N not a multiple of 256), K of one to several load units, with
+    C/D dtypes varied: every row, dprob and amax against the oracle."""
+    rng = np.random.default_rng(800 + case)
+    K = [128, 512, 1152, 2048][case]
+    N = [32, 320, 544, 256][case]
+    L = [1, 4, 3, 5][case]
+    counts = [int(c) * 256 for c in rng.integers(0, 3, size=L)]
+    if sum(counts) == 0:
+        counts[0] = 256
+    c_dtype = [torch.bfloat16, torch.float32, torch.float8_e4m3fn, torch.float16][case]
+    d_dtype = [torch.bfloat16, torch.float16, torch.bfloat16, torch.float32][case]
+    inp = synth.dsrelu_inputs(L, K, N, counts, c_dtype=c_dtype, m_extra=64 * (case % 2),
+                              seed=800 + case, discrete=bool(case % 2), scale_spread=3)
+    say("dsrelu N-major", case, "K", K, "N", N, "L", L, counts, c_dtype, d_dtype)
+    d, dprob, amax, err = run_gpu(inp, d_dtype, b_major="n")
+    assert err == 0
+    ref = run_oracle(inp, d_dtype)
+    vm = inp["valid_m"]
+    assert_close(values(d[:vm]), ref["D"][:vm], ORC_DT[d_dtype], "D_row")
+    assert torch.all(torch.isnan(d[vm:]))
+    assert_close(values(dprob[:vm]), ref["dprob"][:vm], orc.F32, "dprob")
+    for g, c in enumerate(counts):
+        if c == 0:
+            assert amax[g] == 0.0
         else:
             assert abs(amax[g].item() - ref["amax"][g]) <= 1e-3 * ref["amax"][g]

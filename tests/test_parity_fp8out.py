@@ -102,12 +102,15 @@ DSRELU_CASES = [
     (orc.E5M2, orc.E5M2, torch.float8_e4m3fn, 1.0),
     (orc.E4M3, orc.E4M3, torch.float8_e5m2, 1.0),
     (orc.E5M2, orc.E5M2, torch.float32, 2.0),
+    (orc.E5M2, orc.E4M3, torch.bfloat16, "n"),      # N-major B, norm_const 1
 ]
 
 
 @pytest.mark.parametrize("ab,fmt,c_dtype,nc", DSRELU_CASES)
 def test_dsrelu_fp8(ab, fmt, c_dtype, nc):
     b = gg()
+    nmaj = nc == "n"
+    nc = 1.0 if nmaj else nc
     inp = dsrelu_inputs(111, ab=ab, c_dtype=c_dtype)
     M, N, L = inp["M"], inp["N"], inp["L"]
     d_row, fp8 = outputs(M, N)
@@ -116,10 +119,12 @@ def test_dsrelu_fp8(ab, fmt, c_dtype, nc):
     amax = torch.zeros(L, dtype=torch.float32, device="cuda")
     say("dsrelu fp8 out: operands", ab, "D", fmt, "C", c_dtype, "norm_const", nc)
     ws = b.gg_dsrelu(inp["a"].cuda(), inp["sfa"].cuda(),
-                     inp["b_dense"].cuda().view(torch.uint8), inp["sfb_dense"].cuda(), None, None, N,
+                     (inp["b_dense"].transpose(1, 2).contiguous() if nmaj else inp["b_dense"]).cuda()
+                     .view(torch.uint8), inp["sfb_dense"].cuda(), None, None, N,
                      inp["c"].cuda(), inp["padded_offsets"].cuda(), inp["alpha"].cuda(),
                      inp["prob"].cuda(), d_row.view(TORCH_FP8[fmt]), dprob, amax,
-                     fp8_out=dict(fp8, norm_const=ncd))
+                     fp8_out=dict(fp8, norm_const=ncd),
+                     b_major=b.GG_MAJOR_N if nmaj else b.GG_MAJOR_K)
     torch.cuda.synchronize()
     assert b.gg_device_error(ws) == 0
     ref = orc.dsrelu(synth.bits(inp["a"]), synth.bits(inp["sfa"]), M, inp["K"],
