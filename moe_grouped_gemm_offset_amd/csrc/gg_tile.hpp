@@ -908,29 +908,23 @@ __device__ __forceinline__ void unpack8_8(uint32_t lo, uint32_t hi, int dtype, f
 // only when used, so that a caller can have many in flight.  The element
 // index is a multiple of 8.
 // ---------------------------------------------------------------------------
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int CW>
 struct RawC {
     static_assert(CW == 1 || CW == 2 || CW == 4, "element widths 1, 2, 4");
-    uint32_t w[2 * CW];
+    std::conditional_t<CW == 1, u32x2, u32x4> w[CW == 4 ? 2 : 1];
 };
 
 template <int CW>
 __device__ __forceinline__ RawC<CW> rawc_load(const void* base, int64_t i) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     RawC<CW> r;
-    if constexpr (CW == 1) {
-        const u32x2 q = *reinterpret_cast<const u32x2*>((const uint8_t*)base + i);
-        r.w[0] = q.x;
-        r.w[1] = q.y;
+    if constexpr (CW == 4) {
+        r.w[0] = *reinterpret_cast<const u32x4*>((const float*)base + i);
+        r.w[1] = *reinterpret_cast<const u32x4*>((const float*)base + i + 4);
+    } else if constexpr (CW == 2) {
+        r.w[0] = *reinterpret_cast<const u32x4*>((const uint16_t*)base + i);
     } else {
-#pragma unroll
-        for (int h = 0; h < CW / 2; h++) {
-            const u32x4 q = *reinterpret_cast<const u32x4*>((const char*)base + i * CW + 16 * h);
-            r.w[4 * h] = q.x;
-            r.w[4 * h + 1] = q.y;
-            r.w[4 * h + 2] = q.z;
-            r.w[4 * h + 3] = q.w;
-        }
+        r.w[0] = *reinterpret_cast<const u32x2*>((const uint8_t*)base + i);
     }
     return r;
 }
@@ -939,13 +933,15 @@ __device__ __forceinline__ RawC<CW> rawc_load(const void* base, int64_t i) {
 template <int CW>
 __device__ __forceinline__ void rawc_cvt(const RawC<CW>& r, int dtype, float (&v)[8]) {
     if constexpr (CW == 4) {
+        const uint32_t ws[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w,
+                                r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
 #pragma unroll
         for (int k = 0; k < 8; k++)
-            v[k] = __builtin_bit_cast(float, r.w[k]);
+            v[k] = __builtin_bit_cast(float, ws[k]);
     } else if constexpr (CW == 2) {
-        unpack8_16(u32x4{r.w[0], r.w[1], r.w[2], r.w[3]}, dtype, v);
+        unpack8_16(r.w[0], dtype, v);
     } else {
-        unpack8_8(r.w[0], r.w[1], dtype, v);
+        unpack8_8(r.w[0].x, r.w[0].y, dtype, v);
     }
 }
 
