@@ -21,6 +21,7 @@ and, as single-op workloads outside the default step:
   dsrelu_mxfp8_fp8out, dglu_mxfp8_fp8out
                 the two block-scaled dgrad workloads with FP8 (E4M3) D_row
                 and D_col and their E8M0 scales instead of a bf16 D
+  dsrelu_mxfp8_nmajor  the dsReLU workload with discrete N-major B
   wgrad_moe_kmajor  the wgrad workload with A K-major
   wgrad_moe_f32acc  the wgrad workload into discrete per-expert fp32
                 outputs (int64 pointer array), accumulate mode: the
@@ -45,6 +46,13 @@ launches.  With the default workload the MoE wgrad's other modes
 beside the step.  Inside the step every op reads and writes 0.2-4.7 GB
 between two launches of the same op, more than the MALL holds, so the
 step's own launches are cold as well.
+
+`measured_peaks` holds this GPU's sustained dense MFMA rates (bf16 and
+MXFP8 probe kernels with no memory traffic, and the engine clock under
+them) and its device-to-device copy rate; every `kernels` entry gives its
+fraction of the measured MFMA peak and of the roofline built from the
+measured peaks, beside the published ones.  `cpu_baseline.per_core` is
+the oracle on one thread over the small wgrad workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--reps R]
                   [--no-extras] [--no-cpu-baseline]
@@ -236,14 +244,17 @@ def make_wgrad_mx(dev):
               sample)
 
 
-def make_dsrelu(dev, fp8out=False):
+def make_dsrelu(dev, fp8out=False, nmajor=False):
+    """The dsReLU workload; nmajor: B as discrete per-expert (K, N) N-major
+    codes (the same values, transposed), scales unchanged."""
     import numpy as np
     import torch
     from moe_grouped_gemm_offset_amd import binding as B, synth
     from oracle import oracle as orc
     w = synth.WORKLOADS["dsrelu_mxfp8"]
     counts = synth.workload_counts("dsrelu_mxfp8")
-    inp = synth.dsrelu_inputs(w["L"], w["K"], w["N"], counts, seed=w["seed"], device=dev)
+    inp = synth.dsrelu_inputs(w["L"], w["K"], w["N"], counts, seed=w["seed"], device=dev,
+                              discrete=nmajor)
     M, N, K, L = inp["M"], inp["N"], inp["K"], inp["L"]
     d = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     q = None
@@ -253,11 +264,23 @@ def make_dsrelu(dev, fp8out=False):
     amax = torch.zeros(L, dtype=torch.float32, device=dev)
     ws = torch.empty(B.gg_dsrelu_workspace_size(L), dtype=torch.uint8, device=dev)
     a8 = inp["a"].view(torch.uint8)
-    b8 = inp["b_dense"].view(torch.uint8)
+    if nmajor:
+        bl = [x.view(torch.uint8).t().contiguous() for x in inp["b_list"]]
+        bp = torch.tensor([x.data_ptr() for x in bl], dtype=torch.int64, device=dev)
+        sp = torch.tensor([x.data_ptr() for x in inp["sfb_list"]], dtype=torch.int64, device=dev)
 
-    def run():
-        B.gg_dsrelu(a8, inp["sfa"], b8, inp["sfb_dense"], None, None, N, inp["c"], inp["padded_offsets"],
-                    inp["alpha"], inp["prob"], d, dprob, amax, fp8_out=q, workspace=ws)
+        def run():
+            B.gg_dsrelu(a8, inp["sfa"], None, None, bp, sp, N, inp["c"], inp["padded_offsets"],
+                        inp["alpha"], inp["prob"], d, dprob, amax, fp8_out=q, workspace=ws,
+                        b_major=B.GG_MAJOR_N)
+        run.keep = bl
+    else:
+        b8 = inp["b_dense"].view(torch.uint8)
+
+        def run():
+            B.gg_dsrelu(a8, inp["sfa"], b8, inp["sfb_dense"], None, None, N, inp["c"],
+                        inp["padded_offsets"], inp["alpha"], inp["prob"], d, dprob, amax, fp8_out=q,
+                        workspace=ws)
 
     vm = inp["valid_m"]
     d_bytes = M * N * 2 if not fp8out else 2 * M * N + 2 * M * N // 32
@@ -273,8 +296,8 @@ def make_dsrelu(dev, fp8out=False):
                    cpu["alpha"].numpy(), cpu["prob"].numpy(), rows=rows)
         return time.perf_counter() - t0, 2.0 * nrows * N * K
 
-    return Op("dsrelu_mxfp8_fp8out" if fp8out else "dsrelu_mxfp8", "dsrelu_kernel",
-              synth.flops_dgrad(vm, N, K), "fp8", run, alg, sample)
+    name = "dsrelu_mxfp8" + ("_fp8out" if fp8out else "") + ("_nmajor" if nmajor else "")
+    return Op(name, "dsrelu_kernel", synth.flops_dgrad(vm, N, K), "fp8", run, alg, sample)
 
 
 def _fp8_outputs(M, W, dev):
@@ -349,6 +372,7 @@ WORKLOAD_OPS = {
     "wgrad_mxfp8": ["wgrad_mxfp8"],
     "dsrelu_mxfp8_fp8out": ["dsrelu_mxfp8_fp8out"],
     "dglu_mxfp8_fp8out": ["dglu_mxfp8_fp8out"],
+    "dsrelu_mxfp8_nmajor": ["dsrelu_mxfp8_nmajor"],
 }
 
 
@@ -377,6 +401,8 @@ def build_op(name, dev):
         return make_dglu_mx(dev, fp8out=True)
     if name == "dsrelu_mxfp8_fp8out":
         return make_dsrelu(dev, fp8out=True)
+    if name == "dsrelu_mxfp8_nmajor":
+        return make_dsrelu(dev, nmajor=True)
     return make_dsrelu(dev)
 
 
@@ -385,7 +411,8 @@ KERNEL_OF = {"dswiglu": "dglu_kernel", "dgeglu": "dglu_kernel", "wgrad_moe": "wg
              "wgrad_moe_kmajor": "wgrad_kernel", "wgrad_moe_f32acc": "wgrad_kernel",
              "wgrad_moe_bf16acc": "wgrad_kernel", "dsrelu_mxfp8": "dsrelu_kernel",
              "dglu_mxfp8": "dglu_mx_kernel", "wgrad_mxfp8": "wgrad_mx_kernel",
-             "dsrelu_mxfp8_fp8out": "dsrelu_kernel", "dglu_mxfp8_fp8out": "dglu_mx_kernel"}
+             "dsrelu_mxfp8_fp8out": "dsrelu_kernel", "dglu_mxfp8_fp8out": "dglu_mx_kernel",
+             "dsrelu_mxfp8_nmajor": "dsrelu_kernel"}
 
 # Ops timed beside a workload's step (per-op statistics only; not part of the
 # step or its value): the MoE wgrad's other output modes and A major.
@@ -527,11 +554,88 @@ def cpu_baseline(ops, budget_s):
         parts.append(f"{op.name}: {n} rows, {t:.1f} s, {rate / 1e9:.2f} GFLOP/s")
     total = sum(op.flops for op in ops)
     return {"value": total / proj / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model(),
+            "cpu_model": cpu_model(), "per_core": per_core_rate(),
             "sample": "; ".join(parts) + " (rows spread over every group, extrapolated by FLOPs)"}
 
 
+def per_core_rate():
+    """The oracle on one thread over the whole small wgrad workload (hidden
+    256, intermediate 256, counts [256, 0, 512, 256]): one core's rate."""
+    from oracle import oracle as orc
+    from moe_grouped_gemm_offset_amd import synth
+    w = synth.WORKLOADS["wgrad_small"]
+    inp = synth.wgrad_inputs(w["hidden"], w["inter"], w["counts"], a_major=w["a_major"],
+                             b_major=w["b_major"], seed=w["seed"])
+    threads = orc.num_threads()
+    orc.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        orc.wgrad(synth.bits(inp["a"]), 0 if inp["a_major"] == "k" else 1, synth.bits(inp["b"]),
+                  0 if inp["b_major"] == "k" else 1, inp["offsets"].numpy(), inp["hidden"],
+                  inp["inter"], inp["tokens_sum"])
+        t = time.perf_counter() - t0
+    finally:
+        orc.set_threads(threads)
+    flops = 2.0 * w["hidden"] * w["inter"] * int(inp["tokens_sum"])
+    return {"workload": "wgrad_small", "threads": 1, "s": round(t, 3),
+            "gflop_s": round(flops / t / 1e9, 3)}
+
+
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
+PEAK_LIB = os.path.join(ROOT, "moe_grouped_gemm_offset_amd", "libgg_peak.so")
+
+
+def measured_peaks(dev, clock):
+    """This GPU's sustained rates, measured here: dense MFMA from the probe
+    kernels of libgg_peak.so (four independent MFMAs per wave per round,
+    register operands, no memory traffic; 1024 workgroups of 8 waves), with
+    the engine clock during them; and HBM from a device-to-device copy of
+    COPY_BYTES (read plus written bytes).  Each rate is the best of 20 MFMA
+    runs (about 18 ms each) or 5 copies."""
+    import ctypes
+    import torch
+    if not os.path.exists(PEAK_LIB):
+        return None
+    L = ctypes.CDLL(PEAK_LIB)
+    L.gg_peak_mfma.restype = ctypes.c_double
+    L.gg_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                               ctypes.c_void_p]
+    out = torch.zeros(1024, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    res = {}
+    for kind, name, iters in ((0, "mfma_bf16", 32768), (1, "mfma_fp8", 16384)):
+        if L.gg_peak_mfma(kind, 1024, iters, ctypes.c_void_p(out.data_ptr()), stream) <= 0:
+            return None
+        torch.cuda.synchronize()
+        evs = []
+        with clock:
+            for _ in range(20):
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                f = L.gg_peak_mfma(kind, 1024, iters, ctypes.c_void_p(out.data_ptr()), stream)
+                e.record()
+                evs.append((s, e))
+            torch.cuda.synchronize()
+        ms = min(s.elapsed_time(e) for s, e in evs)
+        clk = clock.median(CLOCK_SKIP_S) if clock.h is not None else None
+        res[name] = {"tflops": round(f / (ms * 1e-3) / 1e12, 1),
+                     "clock_mhz": None if clk is None else round(clk)}
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src)
+        e.record()
+        ts.append((s, e))
+    torch.cuda.synchronize()
+    ms = min(s.elapsed_time(e) for s, e in ts)
+    res["hbm_copy_gb_s"] = round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    return res
 
 
 def calibrate_copy(dev, reps=3):
@@ -814,6 +918,15 @@ def main():
             kernels[op.name]["warm"] = stats[op.name]["warm"]
             kernels[op.name]["cold"] = stats[op.name]["cold"]
             kernels[op.name]["clock_mhz"] = stats[op.name]["clock_mhz"]
+    # the chip's measured peaks, and each op against them
+    mpk = None if args.reps <= 0 else measured_peaks(dev, ClockSampler())
+    if mpk:
+        for op in ops + extras:
+            k = kernels[op.name]
+            mf = mpk["mfma_bf16" if op.dtype == "bf16" else "mfma_fp8"]["tflops"]
+            k["measured_peak_frac"] = round(k["tflops"] / mf, 4)
+            t_roof = max(op.flops / (mf * 1e12), op.alg_bytes / (mpk["hbm_copy_gb_s"] * 1e9))
+            k["measured_roofline_frac"] = round(t_roof / (k["ms"] * 1e-3), 4)
     total_flops = sum(op.flops for op in ops)
     value = total_flops / (ms_step * 1e-3) / 1e12
     dom = max(ops, key=lambda o: kernels[o.name]["ms"])
@@ -842,6 +955,7 @@ def main():
         "config": {"workload": args.workload, "ops": [op.name for op in ops],
                    "gflop_per_step": round(total_flops / 1e9, 1), "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "measured_peaks": mpk,
         "cpu_baseline": cpu,
         "kernels": kernels,
     }

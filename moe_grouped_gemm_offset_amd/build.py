@@ -1,4 +1,5 @@
-"""Builds libgg_moe.so (the HIP library) in-tree for gfx950.
+"""Builds libgg_moe.so (the HIP library) in-tree for gfx950, and beside it
+libgg_peak.so (the MFMA rate probe the benchmark loads).
 
 Each translation unit under csrc/ is compiled by hipcc in parallel into
 _build/, then linked into moe_grouped_gemm_offset_amd/libgg_moe.so.  No GPU is
@@ -14,6 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgg_moe.so")
+PEAK_LIB = os.path.join(HERE, "libgg_peak.so")
+PEAK_SOURCE = ("gg_peak.hip", "gg_peak", [])
 # (source, object name, defines): the instantiation sources are compiled
 # once per kernel family member (activation, B major), in parallel
 SOURCES = [(f, os.path.splitext(f)[0], []) for f in
@@ -64,18 +67,25 @@ def _compile(entry):
     return obj
 
 
-def build(jobs=None):
-    """Compile every source and link libgg_moe.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs=None):
+    """Compile every source, link libgg_moe.so and libgg_peak.so; returns the
+    path of libgg_moe.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    entries = SOURCES + [PEAK_SOURCE]
+    jobs = jobs or min(len(entries), os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, entries))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PEAK_LIB)
     return LIB
 
 

@@ -41,6 +41,9 @@
 /* Threads the OpenMP loops of this file use (reported with its timings). */
 int orc_num_threads(void) { return omp_get_max_threads(); }
 
+/* Sets that thread count (n >= 1), e.g. 1 to time a single core. */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* dtype codes used by this file (its own numbering) */
 enum { ORC_BF16 = 0, ORC_F16 = 1, ORC_F32 = 2, ORC_E4M3 = 3, ORC_E5M2 = 4 };
 

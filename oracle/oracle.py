@@ -86,6 +86,8 @@ def lib():
         L.orc_dglu_mx.restype = None
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = I
+        L.orc_set_threads.argtypes = [I]
+        L.orc_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -93,6 +95,11 @@ def lib():
 def num_threads():
     """Threads the oracle's OpenMP loops use."""
     return lib().orc_num_threads()
+
+
+def set_threads(n):
+    """Sets the threads of the oracle's OpenMP loops (n >= 1)."""
+    lib().orc_set_threads(int(n))
 
 
 def _p(a):
