@@ -35,6 +35,20 @@ def test_loads_and_exports_every_declared_symbol():
     assert B.gg_abi_version() == 3
 
 
+def test_peak_probe_library():
+    """The benchmark's MFMA rate probe is built beside the library, exports its
+    one function and rejects invalid arguments without launching."""
+    path = os.path.join(ROOT, "moe_grouped_gemm_offset_amd", "libgg_peak.so")
+    lib = ctypes.CDLL(path)
+    f = lib.gg_peak_mfma
+    f.restype = ctypes.c_double
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(2, 1, 1, P, None) == -1.0
+    assert f(0, 0, 1, P, None) == -1.0
+    assert f(1, 1, 0, P, None) == -1.0
+    assert f(0, 1, 1, None, None) == -1.0
+
+
 def test_workspace_sizes():
     assert B.gg_wgrad_workspace_size(64) == 256 + 64 * 16
     assert B.gg_wgrad_workspace_size(1024) == 256 + 1024 * 16
