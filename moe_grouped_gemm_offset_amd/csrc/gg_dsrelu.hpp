@@ -83,9 +83,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
 
     // ---------------- epilogue ----------------
     // Rows of 8 columns per lane: C and D are 16-byte accesses (32 for fp32).
-    // C and prob of the items 24 ahead (12 for fp32 C) are in flight while an
-    // item is processed; items off the tile load row 0 / column 0 (always
-    // present) and store nothing.
+    // C (and, off the bf16 path, prob) of the items 24 ahead (12 for fp32 C)
+    // are in flight while an item is processed.  Per element: r = relu(alpha
+    // G), t = C r, D = 2 prob t, row sum += t r.
     const float al = p.alpha[g];
     const int64_t N = p.N;
     float amax = 0.0f;
@@ -124,9 +124,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                     const float pr2 = pre.row * 2.0f;
 #pragma unroll
                     for (int k = 0; k < 8; k++) {
-                        const float rl = fmaxf(al * v[k], 0.0f);
-                        d[k] = pr2 * cv[k] * rl;
-                        rowsum[t] += cv[k] * rl * rl;
+                        const float rl = fmaxf(al * v[k], 0.0f), cr = cv[k] * rl;
+                        d[k] = pr2 * cr;
+                        rowsum[t] = fmaf(cr, rl, rowsum[t]);
                         amax = fmaxf(amax, fabsf(d[k]));
                     }
                 }
@@ -149,9 +149,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                 const float pr2 = pre.row * 2.0f;
 #pragma unroll
                 for (int k = 0; k < 8; k++) {
-                    const float rl = fmaxf(al * v[k], 0.0f);
-                    d[k] = pr2 * cv[k] * rl;
-                    rowsum[t] += cv[k] * rl * rl;
+                    const float rl = fmaxf(al * v[k], 0.0f), cr = cv[k] * rl;
+                    d[k] = pr2 * cr;
+                    rowsum[t] = fmaf(cr, rl, rowsum[t]);
                     amax = fmaxf(amax, fabsf(d[k]));
                 }
                 store8(p.d, ddt, row * N + col, d);
@@ -159,7 +159,55 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
         };
         for_each_row8<C, Q ? (cw == 4 ? 6 : 12) : (cw == 4 ? 12 : 24)>(acc, elds, load, fn);
     };
-    if constexpr (BF) {
+    if constexpr (BF && !Q) {
+        // bf16 C and D through buffer descriptors over the wave's rows: 32-bit
+        // offsets from the wave's first row, record counts that end at its
+        // last valid row, columns past N at an invalid offset.  Masked
+        // accesses load zeros and store nothing, and zeros add nothing to
+        // dprob or amax, so an item needs no test of its own; prob is loaded
+        // once per row.
+        constexpr int kWaveRows = TM / C::WM;
+        const int rows_left = rows_valid - am0 < 0 ? 0
+                            : (rows_valid - am0 > kWaveRows ? kWaveRows : rows_valid - am0);
+        const int64_t wrow0 = m0 + am0;
+        const uint32_t rowb = (uint32_t)(N * 2);             // bytes per row of C and D
+        const uint32_t rec = (uint32_t)uniform((int)((uint32_t)rows_left * rowb));
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(uniform_ptr((const char*)p.c + wrow0 * (int64_t)rowb), rec);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(uniform_ptr((char*)p.d + wrow0 * (int64_t)rowb), rec);
+        const __amdgpu_buffer_rsrc_t rp =
+            make_rsrc(uniform_ptr(p.prob + wrow0), (uint32_t)uniform(rows_left * 4));
+        float pr2[kT];                                   // 2 prob of the lane's rows
+#pragma unroll
+        for (int t = 0; t < kT; t++)
+            pr2[t] = 2.0f * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          rp, (uint32_t)((l >> 3) + 8 * t) * 4, 0, 0));
+        auto colb = [&](int c) -> uint32_t {
+            const int col = n0 + bn0 + c;
+            return col < p.N ? (uint32_t)col * 2 : kInvalid;
+        };
+        auto loadb = [&](int, int r, int c) {
+            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rc, (uint32_t)r * rowb + colb(c), 0, 0));
+        };
+        auto fnb = [&](int t, int r, int c, float (&v)[8], const u32x4& x) {
+            // (a uniform branch: without one per item the compiler
+            // interleaves the unrolled items and spills)
+            if (uniform(rows_left) > 0) {
+                float cv[8], d[8];
+                unpack8_16(x, kBF16, cv);
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    const float rl = fmaxf(al * v[k], 0.0f), cr = cv[k] * rl;
+                    d[k] = pr2[t] * cr;
+                    rowsum[t] = fmaf(cr, rl, rowsum[t]);
+                    amax = fmaxf(amax, fabsf(d[k]));
+                }
+                store_bf16x8(rd, (uint32_t)r * rowb + colb(c), d);
+            }
+        };
+        for_each_row8<C, 24>(acc, elds, loadb, fnb);
+    } else if constexpr (BF) {
         epilogue(std::integral_constant<int, 2>());
     } else {
         if (p.c_dtype == kF32)
