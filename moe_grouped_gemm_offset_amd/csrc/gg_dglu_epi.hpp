@@ -310,12 +310,9 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
     // and wave.
 #pragma unroll
     for (int t = 0; t < kT; t++) {
-        float v = rowsum[t] * a2;
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
+        const float v = row8_sum(rowsum[t] * a2);
         const int rr = am0 + (l >> 3) + 8 * t;
-        if ((l & 7) == 0 && rr < rows_valid && n0 + bn0 < p.N)
+        if ((l & 7) == 4 && rr < rows_valid && n0 + bn0 < p.N)
             atomicAdd(p.dprob + m0 + rr, v);
     }
     if constexpr (AMAX) {

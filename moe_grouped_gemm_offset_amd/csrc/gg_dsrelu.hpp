@@ -217,14 +217,13 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
         else
             epilogue(std::integral_constant<int, 2>());
     }
+    // dprob: the 8 lanes of a row hold its partial sums; one atomic per row
+    // and wave
 #pragma unroll
     for (int t = 0; t < kT; t++) {
-        float v = rowsum[t];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
+        const float v = row8_sum(rowsum[t]);
         const int rr = am0 + (l >> 3) + 8 * t;
-        if ((l & 7) == 0 && rr < rows_valid && n0 + bn0 < p.N)
+        if ((l & 7) == 4 && rr < rows_valid && n0 + bn0 < p.N)
             atomicAdd(p.dprob + m0 + rr, v);
     }
     if (p.amax) {

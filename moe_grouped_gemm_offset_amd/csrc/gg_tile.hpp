@@ -1011,6 +1011,21 @@ __device__ __forceinline__ void rawb8_store(__amdgpu_buffer_rsrc_t r, const Fmt8
                                            fm.w32 ? off + 16 : kInvalid, 0, 0);
 }
 
+// Sum of v over the 8 lanes that share lane >> 3 (a row of the row walk),
+// complete in the lanes with (lane & 7) >= 4; lanes 0 .. 3 of each group end
+// with a partial sum.  Two quad permutations (lane ^ 1, lane ^ 2) and a shift
+// by 4 within the 16-lane DPP row, all in the vector ALU: the same pairwise
+// tree as a lane ^ 1, ^ 2, ^ 4 butterfly, so the same sum.
+__device__ __forceinline__ float row8_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                0xB1, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                0x4E, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                0x114, 0xF, 0xF, true));
+    return v;
+}
+
 // ---------------------------------------------------------------------------
 // Row walk of a wave's accumulators (32 MB rows x 32 NB columns, MB and NB
 // even).  The MFMA layout gives a lane one column and 16 rows of a block;
