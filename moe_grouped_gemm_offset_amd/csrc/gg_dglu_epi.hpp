@@ -164,11 +164,8 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
         cols(c, c_in, c_gt);
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-#pragma unroll
-            for (int o = 8; o < 64; o <<= 1) {
-                bs_in[k] += __shfl_xor(bs_in[k], o);
-                bs_gt[k] += __shfl_xor(bs_gt[k], o);
-            }
+            bs_in[k] = cols8(bs_in[k], AddOp());
+            bs_gt[k] = cols8(bs_gt[k], AddOp());
         }
         if (l < 8 && n < p.N) {
 #pragma unroll
@@ -317,11 +314,8 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
     }
     if constexpr (AMAX) {
         if (p.amax) {
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                amax_in = fmaxf(amax_in, __shfl_xor(amax_in, o));
-                amax_gt = fmaxf(amax_gt, __shfl_xor(amax_gt, o));
-            }
+            amax_in = wave_max(amax_in);
+            amax_gt = wave_max(amax_gt);
             if (l == 0) {
                 atomicMax((int*)p.amax + 2 * g, __float_as_int(amax_in));
                 atomicMax((int*)p.amax + 2 * g + 1, __float_as_int(amax_gt));

@@ -227,9 +227,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
             atomicAdd(p.dprob + m0 + rr, v);
     }
     if (p.amax) {
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1)
-            amax = fmaxf(amax, __shfl_xor(amax, o));
+        amax = wave_max(amax);
         if (l == 0)
             atomicMax((int*)p.amax + g, __float_as_int(amax));
     }

@@ -77,8 +77,7 @@ __device__ __forceinline__ uint2 fp8_row8(const float (&v)[8], float nc, int& e)
 #pragma unroll
     for (int k = 0; k < 8; k++)
         m = fmaxf(m, fabsf(v[k]));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
+    m = quad_max(m);
     e = fp8_exponent<BF8>(m, nc);
     return uint2{fp8_pack4<BF8>(v[0], v[1], v[2], v[3], e, nc),
                  fp8_pack4<BF8>(v[4], v[5], v[6], v[7], e, nc)};
@@ -105,9 +104,7 @@ __device__ __forceinline__ void fp8_col_block(const Fp8Out& q, float nc, const f
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         float m = fmaxf(fmaxf(fabsf(d[0][k]), fabsf(d[1][k])), fmaxf(fabsf(d[2][k]), fabsf(d[3][k])));
-        m = fmaxf(m, __shfl_xor(m, 8));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
+        m = cols8(m, MaxOp());
         e[k] = fp8_exponent<BF8>(m, nc);
     }
 #pragma unroll

@@ -1011,6 +1011,59 @@ __device__ __forceinline__ void rawb8_store(__amdgpu_buffer_rsrc_t r, const Fmt8
                                            fm.w32 ? off + 16 : kInvalid, 0, 0);
 }
 
+// Cross-lane steps in the vector ALU (no LDS round trip).  dpp<CTRL>(v):
+// the value of the lane a DPP control selects (0xB1: lane ^ 1, 0x4E: lane ^
+// 2, 0x124 / 0x128: lane - 4 / - 8 within the 16-lane row, rotating).
+// x16 / x32(v, op): op of v and its lane ^ 16 / lane ^ 32 partner's, through
+// v_permlane16_swap / v_permlane32_swap, whose two results (both operands v)
+// hold the lane's own v and its partner's -- the order does not matter to a
+// commutative op.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, true));
+}
+template <class Op>
+__device__ __forceinline__ float x16(float v, Op op) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                    __builtin_bit_cast(unsigned, v), false, false);
+    return op(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+template <class Op>
+__device__ __forceinline__ float x32(float v, Op op) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                    __builtin_bit_cast(unsigned, v), false, false);
+    return op(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+struct MaxOp {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct AddOp {
+    __device__ float operator()(float a, float b) const { return a + b; }
+};
+
+// Max of v over the lanes of a quad (lane ^ 1, ^ 2), in every lane.
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    return fmaxf(v, dpp<0x4E>(v));
+}
+
+// Max of v over the wave, in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+    v = quad_max(v);
+    v = fmaxf(v, dpp<0x124>(v));              // the 16-lane row: quads q, q - 1, ...
+    v = fmaxf(v, dpp<0x128>(v));
+    return x32(x16(v, MaxOp()), MaxOp());
+}
+
+// op of v over the lanes that differ in bits 3, 4 and 5 (lane ^ 8, ^ 16,
+// ^ 32), in every lane: the pairwise tree of a butterfly on those bits.
+template <class Op>
+__device__ __forceinline__ float cols8(float v, Op op) {
+    v = op(v, dpp<0x128>(v));
+    return x32(x16(v, op), op);
+}
+
 // Sum of v over the 8 lanes that share lane >> 3 (a row of the row walk),
 // complete in the lanes with (lane & 7) >= 4; lanes 0 .. 3 of each group end
 // with a partial sum.  Two quad permutations (lane ^ 1, lane ^ 2) and a shift
