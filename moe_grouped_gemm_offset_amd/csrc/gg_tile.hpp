@@ -630,24 +630,32 @@ __device__ __forceinline__ void pipeline5(char* smem, int nk, F (&f)[2], Issue i
 // ---------------------------------------------------------------------------
 // Ping-pong variant of the five-slot loop, for 8 waves (TM == TN).  Waves
 // 0-3 and 4-7 form two groups with one wave of each on every SIMD.  Each
-// wave alternates a memory phase (its fragment reads of one stage and its
-// share of one half-unit's loads) and a compute phase (that stage's MFMAs,
-// at raised issue priority), and the second group runs one phase behind the
-// first: in every phase one wave per SIMD feeds the MFMA pipe while the
-// other waits on the LDS and the load path, so a load that stalls at issue
-// never holds up an MFMA.  One barrier separates consecutive phases; one
-// fragment set per wave suffices, since a wave never reads while it
-// computes.
+// wave alternates a memory phase (its fragment reads of one stage) and a
+// compute phase (that stage's MFMAs at raised issue priority, with its
+// share of one half-unit's loads issued between them), and the second group
+// runs one phase behind the first: in every phase one wave per SIMD feeds
+// the MFMA pipe while the other reads its next fragments from LDS.  One
+// barrier separates consecutive phases; one fragment set per wave
+// suffices, since a wave never reads while it computes.  (Issuing the loads
+// in the memory phases instead made those the longer phases: fragment reads
+// plus load issue took ~600 clocks against the 512 of a compute phase.)
 //
 // Slots (32 KiB each) at the start of window u (stages 2u, 2u+1): A(u) and
 // B(u) are read, A(u+1) has landed or is landing, and two are free (unit
-// u-1's, whose last reads ended before the window's first barrier).  In
-// window u each wave issues B(u+1) into the first free slot in its first
-// memory phase and A(u+2) into the second in its second memory phase.
-// B(u+1) must land before window u+1: the first group waits for it at the
-// end of its second compute phase, the second at the end of its second
-// memory phase -- in both cases with only A(u+2) left in flight, one to two
-// phases after issue.
+// u-1's, whose last reads ended before the window's first barrier).  The
+// first group issues its share of B(u+1) into the first free slot in its
+// first compute phase of window u, and of A(u+2) into the second in its
+// second.  The second group, one phase behind, would have only its second
+// memory phase left before B(u+1) must have landed; it therefore issues its
+// share of B(u+1) one phase earlier, in its last compute phase of window
+// u-1 (which coincides with the first group's first memory phase of window
+// u, after the barrier that freed the slot), and its share of A(u+2) in its
+// first compute phase of window u.  B(u+1) must land before window u+1: the
+// first group waits for it at the end of its second compute phase, the
+// second at the end of its second memory phase -- both with only A(u+2)
+// left in flight.  Each group runs its own copy of the loop, so that no
+// group-dependent branch inside it lets the compiler merge the two groups'
+// compute phases (which spilled the accumulators).
 //   issue, read, mma as for pipeline5; f is a single fragment set.
 // With kPre, the caller has already issued unit 0 into slots 0 and 1, and
 // either at least kPending other vector memory operations after it (e.g. a
@@ -661,6 +669,7 @@ __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issu
                                             Mma mma) {
     static_assert(kPending == 0 || kPre, "operations after unit 0 only when it is prefetched");
     static_assert(C::kWaves == 8 && VMA <= VM, "two groups of four waves");
+    static_assert(VM + kPending < 64, "vmcnt is 6 bits");
     constexpr int kSlot = Slots5<C>::kSlot;
     if (nk <= 0) {
         if constexpr (kPre)
@@ -681,55 +690,98 @@ __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issu
 #pragma unroll
     for (int i = 0; i < VMA; i++)
         issue(sl(2), 0u, 1, i);
-    vm_wait<VMA + kPending>();                           // A(0), B(0)
+    if (second) {
+        // the second group's share of B(1), ahead of its first window
+#pragma unroll
+        for (int i = VMA; i < VM; i++)
+            issue(0u, sl(3), 1, i);
+        vm_wait<VM + kPending>();                        // A(0), B(0)
+    } else {
+        vm_wait<VMA + kPending>();                       // A(0), B(0)
+    }
     unit_barrier();
     if (second)
         unit_barrier();                                  // one phase behind
-    auto compute = [&]() {
+    // compute phase: the stage's MFMAs with this wave's A loads (compute_a)
+    // or B loads (compute_b) of unit uu spread between them
+    auto compute_a = [&](uint32_t la, int uu) {
         __builtin_amdgcn_s_setprio(1);
-        mma(f, 0, kMfma);
+#pragma unroll
+        for (int m = 0; m < kMfma; m++) {
+            mma(f, m, m + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < VMA; i++)
+                if (i * kMfma / VMA == m)
+                    issue(la, 0u, uu, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    for (int u = 0; u < nu; u++) {
-        const char* ra = sb(a);
-        const char* rb = sb(b);
-        // memory: stage 2u, B(u+1)
+    auto compute_b = [&](uint32_t lb, int uu) {
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int g = 0; g < kGroups; g++)
-            read(ra, rb, 2 * u, f, g);
+        for (int m = 0; m < kMfma; m++) {
+            mma(f, m, m + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = VMA; i < VM; i++)
+                if ((i - VMA) * kMfma / (VM - VMA) == m)
+                    issue(0u, lb, uu, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
+    };
+    auto run = [&](auto G2) {
+        constexpr bool kG2 = decltype(G2)::value;
+        for (int u = 0; u < nu; u++) {
+            const char* ra = sb(a);
+            const char* rb = sb(b);
+            // memory: stage 2u
 #pragma unroll
-        for (int i = VMA; i < VM; i++)
-            issue(0u, sl(f1), u + 1, i);
-        lds_wait();
-        unit_barrier();
-        compute();
-        unit_barrier();
-        // memory: stage 2u+1, A(u+2)
-#pragma unroll
-        for (int g = 0; g < kGroups; g++)
-            read(ra, rb, 2 * u + 1, f, g);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < VMA; i++)
-            issue(sl(f2), 0u, u + 2, i);
-        if (second)
-            vm_wait<VMA>();                         // B(u+1) has landed
-        else
+            for (int g = 0; g < kGroups; g++)
+                read(ra, rb, 2 * u, f, g);
             lds_wait();
-        unit_barrier();
-        compute();
-        if (!second)
-            vm_wait<VMA>();                         // B(u+1) has landed
-        unit_barrier();
-        const int na = a1, nb = f1, na1 = f2;
-        f1 = a;
-        f2 = b;
-        a = na;
-        b = nb;
-        a1 = na1;
-    }
+            unit_barrier();
+            // compute: stage 2u; group 1: B(u+1), group 2: A(u+2)
+            if constexpr (kG2)
+                compute_a(sl(f2), u + 2);
+            else
+                compute_b(sl(f1), u + 1);
+            unit_barrier();
+            // memory: stage 2u+1
+#pragma unroll
+            for (int g = 0; g < kGroups; g++)
+                read(ra, rb, 2 * u + 1, f, g);
+            if constexpr (kG2)
+                vm_wait<VMA>();                          // B(u+1) has landed
+            else
+                lds_wait();
+            unit_barrier();
+            // compute: stage 2u+1; group 1: A(u+2), group 2: B(u+2) into
+            // unit u's A slot (read for the last time in the phase just
+            // ended), the first free slot of window u+1
+            if constexpr (kG2) {
+                compute_b(sl(a), u + 2);
+            } else {
+                compute_a(sl(f2), u + 2);
+                vm_wait<VMA>();                          // B(u+1) has landed
+            }
+            unit_barrier();
+            const int na = a1, nb = f1, na1 = f2;
+            f1 = a;
+            f2 = b;
+            a = na;
+            b = nb;
+            a1 = na1;
+        }
+    };
+    if (second)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
     if (!second)
         unit_barrier();                                  // the second group's last phase
     wait_all();
