@@ -630,32 +630,35 @@ __device__ __forceinline__ void pipeline5(char* smem, int nk, F (&f)[2], Issue i
 // ---------------------------------------------------------------------------
 // Ping-pong variant of the five-slot loop, for 8 waves (TM == TN).  Waves
 // 0-3 and 4-7 form two groups with one wave of each on every SIMD.  Each
-// wave alternates a memory phase (its fragment reads of one stage) and a
-// compute phase (that stage's MFMAs at raised issue priority, with its
-// share of one half-unit's loads issued between them), and the second group
-// runs one phase behind the first: in every phase one wave per SIMD feeds
-// the MFMA pipe while the other reads its next fragments from LDS.  One
-// barrier separates consecutive phases; one fragment set per wave
-// suffices, since a wave never reads while it computes.  (Issuing the loads
-// in the memory phases instead made those the longer phases: fragment reads
-// plus load issue took ~600 clocks against the 512 of a compute phase.)
+// wave alternates a memory phase (its fragment reads of one stage, then
+// half of its share of one half-unit's loads) and a compute phase (that
+// stage's MFMAs at raised issue priority, with the other half of those loads
+// issued between them), and the second group runs one phase behind the
+// first: in every phase one wave per SIMD feeds the MFMA pipe while the
+// other reads its next fragments from LDS.  One barrier separates
+// consecutive phases; one fragment set per wave suffices, since a wave never
+// reads while it computes.  (With all loads in the memory phases those were
+// the longer phases: fragment reads plus load issue took ~600 clocks
+// against the 512 of a compute phase; with all of them in the compute
+// phases, the MFMAs waited on load issue instead.)
 //
 // Slots (32 KiB each) at the start of window u (stages 2u, 2u+1): A(u) and
 // B(u) are read, A(u+1) has landed or is landing, and two are free (unit
 // u-1's, whose last reads ended before the window's first barrier).  The
 // first group issues its share of B(u+1) into the first free slot in its
-// first compute phase of window u, and of A(u+2) into the second in its
-// second.  The second group, one phase behind, would have only its second
-// memory phase left before B(u+1) must have landed; it therefore issues its
-// share of B(u+1) one phase earlier, in its last compute phase of window
-// u-1 (which coincides with the first group's first memory phase of window
-// u, after the barrier that freed the slot), and its share of A(u+2) in its
-// first compute phase of window u.  B(u+1) must land before window u+1: the
-// first group waits for it at the end of its second compute phase, the
-// second at the end of its second memory phase -- both with only A(u+2)
-// left in flight.  Each group runs its own copy of the loop, so that no
-// group-dependent branch inside it lets the compiler merge the two groups'
-// compute phases (which spilled the accumulators).
+// first memory and compute phases of window u, and of A(u+2) into the
+// second in its second ones.  The second group, one phase behind, would
+// have only its second memory phase left before B(u+1) must have landed; it
+// therefore issues its share of B(u+1) one phase earlier, in its last
+// memory and compute phases of window u-1 (into unit u-1's A slot once its
+// own reads of it have completed, and after the barrier that freed it), and
+// its share of A(u+2) in its first ones of window u.  B(u+1) must land
+// before window u+1: the first group waits for it at the end of its second
+// compute phase, the second at the end of its second memory phase -- both
+// with only the loads issued after it left in flight.  Each group runs its
+// own copy of the loop, so that no group-dependent branch inside it lets the
+// compiler merge the two groups' compute phases (which spilled the
+// accumulators).
 //   issue, read, mma as for pipeline5; f is a single fragment set.
 // With kPre, the caller has already issued unit 0 into slots 0 and 1, and
 // either at least kPending other vector memory operations after it (e.g. a
@@ -702,8 +705,20 @@ __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issu
     unit_barrier();
     if (second)
         unit_barrier();                                  // one phase behind
-    // compute phase: the stage's MFMAs with this wave's A loads (compute_a)
-    // or B loads (compute_b) of unit uu spread between them
+    // of each half-unit's loads, the first kMem* go out at the end of a
+    // memory phase, the rest between the next compute phase's MFMAs
+    constexpr int kMemA = VMA / 2, kMemB = (VM - VMA) / 2;
+    auto mem_a = [&](uint32_t la, int uu) {
+#pragma unroll
+        for (int i = 0; i < kMemA; i++)
+            issue(la, 0u, uu, i);
+    };
+    auto mem_b = [&](uint32_t lb, int uu) {
+#pragma unroll
+        for (int i = VMA; i < VMA + kMemB; i++)
+            issue(0u, lb, uu, i);
+    };
+    // compute phase: the stage's MFMAs with the rest spread between them
     auto compute_a = [&](uint32_t la, int uu) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -711,8 +726,8 @@ __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issu
             mma(f, m, m + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < VMA; i++)
-                if (i * kMfma / VMA == m)
+            for (int i = kMemA; i < VMA; i++)
+                if ((i - kMemA) * kMfma / (VMA - kMemA) == m)
                     issue(la, 0u, uu, i);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -726,8 +741,8 @@ __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issu
             mma(f, m, m + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = VMA; i < VM; i++)
-                if ((i - VMA) * kMfma / (VM - VMA) == m)
+            for (int i = VMA + kMemB; i < VM; i++)
+                if ((i - VMA - kMemB) * kMfma / (VM - VMA - kMemB) == m)
                     issue(0u, lb, uu, i);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -739,30 +754,34 @@ __device__ __forceinline__ void pipeline_pp(char* smem, int nk, F& f, Issue issu
         for (int u = 0; u < nu; u++) {
             const char* ra = sb(a);
             const char* rb = sb(b);
-            // memory: stage 2u
 #pragma unroll
             for (int g = 0; g < kGroups; g++)
                 read(ra, rb, 2 * u, f, g);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (kG2)
+                mem_a(sl(f2), u + 2);
+            else
+                mem_b(sl(f1), u + 1);
             lds_wait();
             unit_barrier();
-            // compute: stage 2u; group 1: B(u+1), group 2: A(u+2)
             if constexpr (kG2)
                 compute_a(sl(f2), u + 2);
             else
                 compute_b(sl(f1), u + 1);
             unit_barrier();
-            // memory: stage 2u+1
 #pragma unroll
             for (int g = 0; g < kGroups; g++)
                 read(ra, rb, 2 * u + 1, f, g);
-            if constexpr (kG2)
-                vm_wait<VMA>();                          // B(u+1) has landed
-            else
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (kG2) {
+                lds_wait();                              // own reads of slot a done
+                mem_b(sl(a), u + 2);
+                vm_wait<VMA + kMemB>();                  // B(u+1) has landed
+            } else {
+                mem_a(sl(f2), u + 2);
                 lds_wait();
+            }
             unit_barrier();
-            // compute: stage 2u+1; group 1: A(u+2), group 2: B(u+2) into
-            // unit u's A slot (read for the last time in the phase just
-            // ended), the first free slot of window u+1
             if constexpr (kG2) {
                 compute_b(sl(a), u + 2);
             } else {
