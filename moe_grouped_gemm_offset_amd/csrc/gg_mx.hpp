@@ -131,7 +131,8 @@ __device__ __forceinline__ void mx_mainloop(char* smem, const char* a, const cha
 #pragma unroll
         for (int t = 0; t < S::kPerUnit; t++)
             scale_load(0, s4, t);
-    pipeline<C, kLA + kLB + S::kPerUnit, MB * NB, MB + NB>(smem, nk, frag, issue, read, mma);
+    // (N-major B: the early loads' live ranges spill the main loop)
+    pipeline<C, kLA + kLB + S::kPerUnit, MB * NB, MB + NB, B_K>(smem, nk, frag, issue, read, mma);
 }
 
 }  // namespace gg
