@@ -368,6 +368,9 @@ template <class C>
 struct FragMx8 {
     i32x8 a[C::MB], b[C::NB];
     uint32_t sa[C::MB], sb[C::NB];
+    // the scale words as read; sh brings this stage's byte of a lane's K
+    // block to byte 0, at the MFMA (a shift at the read would wait for it)
+    uint32_t sh;
 };
 
 __device__ __forceinline__ int mn8_addr(int k, int col) {
@@ -424,7 +427,8 @@ __device__ __forceinline__ void mma_mx8(const FragMx8<C>& f, f32x16 (&acc)[C::MB
             continue;
         const int i = m / C::NB, j = m % C::NB;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            f.a[i], f.b[j], acc[i][j], AB, AB, 0, (int)f.sa[i], 0, (int)f.sb[j]);
+            f.a[i], f.b[j], acc[i][j], AB, AB, 0, (int)(f.sa[i] >> f.sh), 0,
+            (int)(f.sb[j] >> f.sh));
     }
 }
 
