@@ -237,7 +237,7 @@ __device__ __forceinline__ void dglu_epilogue(const DgluArgs& p, const f32x16 (&
                     dbias_flush(c);
             }
         };
-        for_each_row8<C, kAhead>(acc, elds, loadb, fnb);
+        for_each_row8<C, kAhead, 64, 0, -1, C::kWaves == 4>(acc, elds, loadb, fnb);
     } else {
         using Pre = Pre8<CW, 2>;
         auto load = [&](int, int r, int c) {

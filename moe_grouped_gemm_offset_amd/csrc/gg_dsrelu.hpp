@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) dsrelu_kernel(DsreluArgs p) {
                 store_bf16x8(rd, (uint32_t)r * rowb + colb(c), d);
             }
         };
-        for_each_row8<C, 24>(acc, elds, loadb, fnb);
+        for_each_row8<C, 24, 64, 0, -1, true>(acc, elds, loadb, fnb);
     } else if constexpr (BF) {
         epilogue(std::integral_constant<int, 2>());
     } else {

@@ -1201,11 +1201,16 @@ __device__ __forceinline__ float row8_sum(float v) {
 //                            and what load returned for it.
 // Only this wave touches `lds`; the caller separates it from the main loop
 // with a barrier.  Items [kFrom, kTo) alone are visited (kTo < 0: to the
-// end), whole pieces, so that a caller can split the walk.
+// end), whole pieces, so that a caller can split the walk.  kLdsAhead reads
+// each item's accumulators one item early (for one wave per SIMD, where
+// nothing else covers the LDS latency: 2-3% on the block-scaled dsReLU and
+// dGLU; with two waves per SIMD it measured no gain, and it cost registers
+// in the FP8-output and run-time-format walks).
 // ---------------------------------------------------------------------------
 constexpr int kEpiHalfBytes = 32 * kEpiPitch * 4;
 
-template <class C, int kAhead, int kQR = 64, int kFrom = 0, int kTo = -1, class Load, class Fn>
+template <class C, int kAhead, int kQR = 64, int kFrom = 0, int kTo = -1, bool kLdsAhead = false,
+          class Load, class Fn>
 __device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB], float* lds, Load load,
                                               Fn fn) {
     static_assert(C::MB % 2 == 0 && C::NB % 2 == 0, "row walk expects 64 x 64 quadrants");
@@ -1232,32 +1237,64 @@ __device__ __forceinline__ void for_each_row8(const f32x16 (&acc)[C::MB][C::NB],
         item(i, t, r, c);
         pre[i] = load(t, r, c);
     }
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    // the piece that item i starts, into the wave's region
+    auto stage = [&](int i) {
+        const int q = i / kPer, h = q / (C::MB / kBR), mh = q % (C::MB / kBR);
+#pragma unroll
+        for (int b = 0; b < kBR; b++)
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++)
+#pragma unroll
+                for (int e = 0; e < 16; e++)
+                    lds[(32 * b + acc_row(e, l)) * kEpiPitch + 32 * jj + (l & 31)] =
+                        acc[kBR * mh + b][2 * h + jj][e];
+    };
+    auto fetch = [&](int i, f32x4& a, f32x4& b) {
+        int t, r, c;
+        item(i, t, r, c);
+        const int rq = r % kQR, cq = c & 63;
+        a = *reinterpret_cast<const f32x4*>(lds + rq * kEpiPitch + cq);
+        b = *reinterpret_cast<const f32x4*>(lds + rq * kEpiPitch + cq + 4);
+    };
+    // kLdsAhead: item i+1's accumulators are read before item i is
+    // processed, so that the LDS latency hides behind item i's arithmetic
+    // (a wave's LDS accesses complete in issue order, so the next piece may
+    // be written over the one whose last reads are still in flight).
+    // Otherwise each item's reads come right before its use.
+    f32x4 ca, cb;
+    stage(kFrom);
+    if constexpr (kLdsAhead)
+        fetch(kFrom, ca, cb);
 #pragma unroll
     for (int i = kFrom; i < kItems; i++) {
-        if (i % kPer == 0) {
-            const int q = i / kPer, h = q / (C::MB / kBR), mh = q % (C::MB / kBR);
-#pragma unroll
-            for (int b = 0; b < kBR; b++)
-#pragma unroll
-                for (int jj = 0; jj < 2; jj++)
-#pragma unroll
-                    for (int e = 0; e < 16; e++)
-                        lds[(32 * b + acc_row(e, l)) * kEpiPitch + 32 * jj + (l & 31)] =
-                            acc[kBR * mh + b][2 * h + jj][e];
+        f32x4 na, nb;
+        if constexpr (kLdsAhead) {
+            if (i + 1 < kItems) {
+                if ((i + 1) % kPer == 0)
+                    stage(i + 1);
+                fetch(i + 1, na, nb);
+            }
+        } else if (i > kFrom && i % kPer == 0) {
+            stage(i);
         }
         if (i + kAhead < kItems) {
             int t, r, c;
             item(i + kAhead, t, r, c);
             pre[i + kAhead] = load(t, r, c);
         }
+        if constexpr (!kLdsAhead)
+            fetch(i, ca, cb);
         int t, r, c;
         item(i, t, r, c);
-        const int rq = r % kQR, cq = c & 63;
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        const f32x4 a = *reinterpret_cast<const f32x4*>(lds + rq * kEpiPitch + cq);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(lds + rq * kEpiPitch + cq + 4);
-        float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        float v[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
         fn(t, r, c, v, pre[i]);
+        if constexpr (kLdsAhead) {
+            if (i + 1 < kItems) {
+                ca = na;
+                cb = nb;
+            }
+        }
     }
 }
 
