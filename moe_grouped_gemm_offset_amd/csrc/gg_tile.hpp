@@ -489,11 +489,14 @@ __device__ __forceinline__ void pipeline(char* smem, int nk, F (&f)[2], Issue is
     for (int g = 0; g < kGroups; g++)
         read(buf(0), 0, f[0], g);
     // stage 2u, reading stage 2u+1 from the same unit, two fragment groups
-    // per MFMA; once every wave has read all of unit u (after the first kH
-    // MFMAs), the first kEarly loads of unit u+2 go into its buffer between
-    // the remaining MFMAs
+    // per MFMA (the first kH MFMAs); once every wave has read all of unit u
+    // (a barrier after MFMA kW-1), the first kEarly loads of unit u+2 go
+    // into its buffer between the remaining MFMAs
     constexpr int kEarly = kEarlyLoads ? VM / 3 : 0;
     constexpr int kH = (kGroups + 1) / 2;
+    // the barrier a few MFMAs after the last read, so that the wait for the
+    // reads rarely stalls (4 more MFMAs measured 1% faster on the dsReLU)
+    constexpr int kW = kH + 4 < kMfma ? kH + 4 : kH;
     static_assert(kGroups < kMfma, "MFMAs left after the reads");
     auto even = [&](int u, auto LOADS) {
 #pragma unroll
@@ -510,13 +513,13 @@ __device__ __forceinline__ void pipeline(char* smem, int nk, F (&f)[2], Issue is
             }
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (decltype(LOADS)::value && kEarly > 0) {
-                if (m == kH - 1) {
+                if (m == kW - 1) {
                     lds_wait();
                     unit_barrier();
                 }
 #pragma unroll
                 for (int i = 0; i < kEarly; i++)
-                    if (m >= kH && i * (kMfma - kH) / kEarly == m - kH)
+                    if (m >= kW && i * (kMfma - kW) / kEarly == m - kW)
                         issue(lds(u), u + 2, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
