@@ -15,13 +15,14 @@
 // its items, and the workgroups dispatched to that XCD (blockIdx % 8, the
 // dispatcher's round-robin order) take items from it in order: a
 // longest-first greedy schedule per XCD, with every expert spread evenly
-// over the XCDs.  A workgroup asks for its next item when its main loop
-// ends; the request stays in flight while the first half of the output is
-// written, one wave then looks the item up (rank table, tile coordinates)
-// and hands it to the others through LDS, and the next item's first K unit
-// loads while the second half is written.  The next main loop leaves that
-// half's stores in flight at its first wait, so that they drain under its
-// first MFMAs.
+// over the XCDs.  A workgroup holds one item in reserve: when a main loop
+// ends it asks for the item after the reserve, and one wave looks that up
+// (rank table, tile coordinates) at the end of the item and hands it to the
+// others through LDS, so that neither the request nor the look-up is
+// waited for.  With a bf16 output the reserve's first K unit is issued
+// before the output is written, and the next main loop leaves the output
+// stores in flight at its first wait, so that they drain under its first
+// MFMAs; otherwise the unit loads between the two halves of the output.
 //
 // The reduction runs over the expert's tokens, 32 per stage and 64 per load
 // unit, through the ping-pong main loop of gg_tile.hpp: K-major operands are
@@ -173,12 +174,32 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         *bcast = p.static_sched ? spos0 : atomicAdd(queue, 1);
     __syncthreads();
     const int t0 = 8 * uniform(*bcast) + x;
-    int spos = spos0;
     if (t0 >= total)
         return;
     decode(locate(t0));
     prefetch();
+    // The workgroup holds one item in reserve: the item after the one being
+    // computed is asked for and looked up one whole item ahead, so that the
+    // queue request and the rank-table read are never waited for.  Wave 0
+    // looks it up and hands it to the others through LDS; the barrier that
+    // ends each item publishes it.
+    int spos = spos0 + sstep;                         // static position of the reserve
+    int qpos = 0;
+    if (threadIdx.x == 0)
+        qpos = p.static_sched ? spos : atomicAdd(queue, 1);
+    auto lookup = [&]() {                             // wave 0: qpos -> bcast
+        if (uniform(w) == 0) {
+            qpos = __builtin_amdgcn_readfirstlane(qpos);
+            const u32x4 loc = locate(8 * qpos + x);
+            if (threadIdx.x == 0)
+                *reinterpret_cast<u32x4*>(bcast) = loc;
+        }
+    };
+    unit_barrier();                   // every wave has read the first item
+    lookup();
     wait_all();                       // later items: see the end of the loop
+    unit_barrier();
+    u32x4 nxt = *reinterpret_cast<const u32x4*>(bcast);
     for (;;) {
         // nothing to add: output untouched (a uniform branch)
         const bool skip = uniform(cnt == 0 && p.accumulate) != 0;
@@ -188,15 +209,14 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
             for (int j = 0; j < C::NB; j++)
                 acc[i][j] = f32x16{0};
         const int nk = skip ? 0 : uniform((int)((cnt + 31) / 32));
-        pipeline_pp<C, LA::kN, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB, true, kHalf>(
-            smem, nk, frag, issue2, read2, mma);
+        pipeline_pp<C, LA::kN, LA::kN + LB::kN, 2 * C::MB * C::NB, C::MB + C::NB, true,
+                    OUT == kOutBf16 ? 2 * kHalf : kHalf>(smem, nk, frag, issue2, read2, mma);
 
-        // The next item is asked for once this one's main loop is done
+        // The new reserve is asked for once this item's main loop is done
         // (asking earlier hands the queue out in start order rather than
         // finish order, which scatters the tiles that share operand panels
         // and measured 20% more HBM fetch).
         spos += sstep;
-        int qpos = 0;
         if (threadIdx.x == 0)
             qpos = p.static_sched ? spos : atomicAdd(queue, 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -213,76 +233,48 @@ __global__ void __launch_bounds__(C::kThreads, 1) wgrad_kernel(WgradArgs p) {
         // A skipped item runs the same epilogue with every row masked (no
         // access reaches memory), so that no branch goes around its stores.
         const int rows = skip ? 0 : p.hidden;
-        auto first_half = [&]() {
-            if constexpr (OUT == kOutBf16)
-                wgrad_epilogue_bf16t<C, 0>(acc, (char*)stage, out, rows, p.inter, row0, col0);
-            else if constexpr (OUT == kOutF32Acc)
-                wgrad_epilogue_t<C, 32, kF32, true, 0, kHalf>(acc, stage, out, rows, p.inter,
-                                                              row0, col0);
-            else
-                wgrad_epilogue<C, 32, 0, kHalf>(acc, stage, out, p.out_dtype, rows, p.inter,
-                                                row0, col0, accumulate);
-        };
-        // Every wave reads lane 0's request result (only wave 0's is
-        // meaningful), so that the compiler awaits it here on every path and
-        // never inside the next main loop.  Wave 0 looks the item up in the
-        // rank table while the other waves catch up, and hands item and
-        // entry over through LDS; the next item's first unit is then issued.
+        // the reserve becomes the next item: its first unit is issued
+        const bool more = uniform((int)nxt.x) >= 0;
         auto next_item = [&]() {
             __builtin_amdgcn_sched_barrier(0);
-            qpos = __builtin_amdgcn_readfirstlane(qpos);
-            if (uniform(w) == 0) {
-                const u32x4 loc = locate(8 * qpos + x);
-                if (threadIdx.x == 0)
-                    *reinterpret_cast<u32x4*>(bcast) = loc;
-            }
-            lds_wait();
-            unit_barrier();
-            const u32x4 loc = *reinterpret_cast<const u32x4*>(bcast);
-            const bool more = uniform((int)loc.x) >= 0;
             if (more) {
-                decode(loc);
+                decode(nxt);
                 prefetch();
             }
-            return more;
         };
-        // The next main loop leaves kHalf vector memory operations issued
-        // after the prefetch in flight at its first wait: the second half
-        // issues at least kHalf stores (one or two per item, masked ones
-        // included), or, when accumulating, waits for its loads of the old
-        // values, issued after the prefetch, which completes first.
-        auto second_half = [&]() {
-            if constexpr (OUT == kOutBf16)
-                wgrad_epilogue_bf16t<C, 1>(acc, (char*)stage, out, rows, p.inter, row0, col0);
-            else if constexpr (OUT == kOutF32Acc)
-                wgrad_epilogue_t<C, 32, kF32, true, kHalf, 2 * kHalf>(acc, stage, out, rows,
-                                                                      p.inter, row0, col0);
-            else
-                wgrad_epilogue<C, 32, kHalf, 2 * kHalf>(acc, stage, out, p.out_dtype, rows,
-                                                        p.inter, row0, col0, accumulate);
-        };
-        // With the output format known at compile time (or both operands
-        // M/N-major) the request is awaited after the first half of the
-        // output, and the next item's first unit loads during the second
-        // half; otherwise (the registers of the run-time format dispatch,
-        // twice, and the K-major loaders would spill inside the main loop)
-        // both come before the output, written in one walk.
-        bool more;
-        if constexpr (kSplit) {
-            first_half();
-            more = next_item();
-            second_half();
+        // bf16 output: the next item's first unit is issued before the
+        // output, whose 2 kHalf stores the next main loop leaves in flight at
+        // its first wait (issued before the stores, the unit lands under
+        // them: 2.4% on the MoE shape).  fp32 accumulate: the unit loads
+        // between the two halves of the output, after whose loads of the old
+        // values, awaited there, only the second half's stores remain in
+        // flight.  Run-time format: the unit comes before the output, written
+        // in one walk (the registers of the run-time dispatch, twice, would
+        // spill inside the main loop).
+        if constexpr (OUT == kOutBf16) {
+            next_item();
+            wgrad_epilogue_bf16t<C, 0>(acc, (char*)stage, out, rows, p.inter, row0, col0);
+            wgrad_epilogue_bf16t<C, 1>(acc, (char*)stage, out, rows, p.inter, row0, col0);
+        } else if constexpr (kSplit) {
+            wgrad_epilogue_t<C, 32, kF32, true, 0, kHalf>(acc, stage, out, rows, p.inter,
+                                                          row0, col0);
+            next_item();
+            wgrad_epilogue_t<C, 32, kF32, true, kHalf, 2 * kHalf>(acc, stage, out, rows,
+                                                                  p.inter, row0, col0);
         } else {
-            more = next_item();
+            next_item();
             wgrad_epilogue<C, 32>(acc, stage, out, p.out_dtype, rows, p.inter, row0, col0,
                                   accumulate);
         }
         if (!more)
             break;
-        // every wave's staging reads are done before slot 2 is loaded again;
-        // the stores and the prefetch stay in flight
+        lookup();
+        // every wave's staging reads are done before slot 2 is loaded again,
+        // and the new reserve is published; the stores and the prefetch stay
+        // in flight
         lds_wait();
         unit_barrier();
+        nxt = *reinterpret_cast<const u32x4*>(bcast);
     }
 }
 
